@@ -1,0 +1,354 @@
+"""Pins of the float64 oracle to facts that do not come from the oracle.
+
+Each test checks one oracle function against something fixed by the pages or
+by mathematics: central finite differences of the associative loss, the
+linearity of the chunk gradient in its tokens, brute-force scalar loops, the
+SVD closed form of the Newton-Schulz polynomial, closed forms of the renorm
+and of momentum, the printed constants, and the causality structure of the
+orderings.  CPU only.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lact_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_state(rng, d, dh, scale=None):
+    s = 1.0 / math.sqrt(d) if scale is None else scale
+    return (rng.standard_normal((dh, d)) * s, rng.standard_normal((dh, d)) * s,
+            rng.standard_normal((d, dh)) * s)
+
+
+# ------------------------------------------------------------ scalars ----
+def test_silu_and_derivative():
+    x = np.linspace(-12, 12, 2001)
+    h = 1e-5
+    fd = (O.silu(x + h) - O.silu(x - h)) / (2 * h)
+    assert np.max(np.abs(fd - O.silu_grad(x))) < 1e-9
+    assert O.silu(0.0) == 0.0 and O.silu_grad(0.0) == 0.5
+    # silu(x) = x / (1 + e^-x) written with math.exp
+    for v in (-3.0, -0.5, 0.25, 2.0, 7.0):
+        assert abs(O.silu(v) - v / (1.0 + math.exp(-v))) < 1e-15
+
+
+# -------------------------------------------------------------- apply ----
+def test_apply_brute_force():
+    rng = np.random.default_rng(1)
+    d, dh, n = 4, 6, 5
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    X = rng.standard_normal((n, d))
+    out = O.apply(W1, W3, W2, X)
+    for t in range(n):
+        hidden = []
+        for j in range(dh):
+            g = sum(W1[j][i] * X[t][i] for i in range(d))
+            u = sum(W3[j][i] * X[t][i] for i in range(d))
+            hidden.append(g / (1.0 + math.exp(-g)) * u)
+        for i in range(d):
+            ref = sum(W2[i][j] * hidden[j] for j in range(dh))
+            assert abs(out[t][i] - ref) < 1e-13
+
+
+# ----------------------------------------------------------- gradient ----
+def _loss(W1, W3, W2, K, V, eta):
+    """L = -sum_t eta_t <f_W(k_t), v_t>, scalar loops (no oracle code)."""
+    total = 0.0
+    d, dh = W2.shape
+    for t in range(K.shape[0]):
+        h = []
+        for j in range(dh):
+            g = float(np.dot(W1[j], K[t]))
+            u = float(np.dot(W3[j], K[t]))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        f = [sum(W2[i][j] * h[j] for j in range(dh)) for i in range(d)]
+        total -= eta[t] * sum(f[i] * V[t][i] for i in range(d))
+    return total
+
+
+def test_gradient_finite_differences():
+    rng = np.random.default_rng(2)
+    d, dh, n = 3, 5, 7
+    W1, W3, W2 = _rand_state(rng, d, dh, scale=0.7)
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    e1, e3, e2 = (np.abs(rng.standard_normal(n)) + 0.1 for _ in range(3))
+    G1, G3, G2 = O.chunk_gradient(W1, W3, W2, K, V, e1, e3, e2)
+    h = 1e-6
+    for G, idx, eta in ((G1, 0, e1), (G3, 1, e3), (G2, 2, e2)):
+        Ws = [W1, W3, W2]
+        fd = np.zeros_like(G)
+        for a in range(G.shape[0]):
+            for b in range(G.shape[1]):
+                Wp = [w.copy() for w in Ws]
+                Wm = [w.copy() for w in Ws]
+                Wp[idx][a, b] += h
+                Wm[idx][a, b] -= h
+                fd[a, b] = -(_loss(*Wp, K, V, eta) - _loss(*Wm, K, V, eta)) / (2 * h)
+        rel = np.linalg.norm(G - fd) / np.linalg.norm(fd)
+        assert rel < 1e-7, (idx, rel)
+
+
+def test_gradient_matches_autograd():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    d, dh, n = 16, 40, 33
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    eta = np.abs(rng.standard_normal(n)) * 1e-2
+    G1, G3, G2 = O.chunk_gradient(W1, W3, W2, K, V, eta, eta, eta)
+    t = [torch.tensor(w, dtype=torch.float64, requires_grad=True) for w in (W1, W3, W2)]
+    Kt, Vt, Et = (torch.tensor(a, dtype=torch.float64) for a in (K, V, eta))
+    hid = torch.nn.functional.silu(Kt @ t[0].T) * (Kt @ t[1].T)
+    L = -(Et[:, None] * (hid @ t[2].T) * Vt).sum()
+    L.backward()
+    for G, w in zip((G1, G3, G2), t):
+        assert np.max(np.abs(G + w.grad.numpy())) < 1e-13 * max(1.0, np.max(np.abs(G)))
+
+
+def test_gradient_linearity_and_permutation():
+    rng = np.random.default_rng(4)
+    d, dh, n = 8, 24, 50
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    e1, e3, e2 = (np.abs(rng.standard_normal(n)) for _ in range(3))
+    full = O.chunk_gradient(W1, W3, W2, K, V, e1, e3, e2)
+    a = O.chunk_gradient(W1, W3, W2, K[:17], V[:17], e1[:17], e3[:17], e2[:17])
+    b = O.chunk_gradient(W1, W3, W2, K[17:], V[17:], e1[17:], e3[17:], e2[17:])
+    p = rng.permutation(n)
+    perm = O.chunk_gradient(W1, W3, W2, K[p], V[p], e1[p], e3[p], e2[p])
+    for f, x, y, z in zip(full, a, b, perm):
+        assert np.max(np.abs(f - (x + y))) < 1e-12 * np.max(np.abs(f))
+        assert np.max(np.abs(f - z)) < 1e-12 * np.max(np.abs(f))
+
+
+def test_gradient_eta_selects_matrix():
+    """eta1 only reaches G1, eta3 only G3, eta2 only G2 (page: lr0/lr1/lr2)."""
+    rng = np.random.default_rng(5)
+    d, dh, n = 4, 8, 9
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    z, one = np.zeros(n), np.ones(n)
+    G1, G3, G2 = O.chunk_gradient(W1, W3, W2, K, V, one, z, z)
+    assert np.abs(G1).max() > 0 and np.abs(G3).max() == 0 and np.abs(G2).max() == 0
+    G1, G3, G2 = O.chunk_gradient(W1, W3, W2, K, V, z, z, one)
+    assert np.abs(G1).max() == 0 and np.abs(G3).max() == 0 and np.abs(G2).max() > 0
+
+
+# ----------------------------------------------------- Newton-Schulz ----
+def _golden_coeffs():
+    rows = []
+    with open(os.path.join(GOLDEN, "ns_coefficients.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append(tuple(float(x) for x in line.split()))
+    return rows
+
+
+def _phi(x):
+    for a, b, c in _golden_coeffs():
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+def test_ns_coefficients_are_the_pages():
+    assert [tuple(c) for c in O.NS_COEFFS] == _golden_coeffs()
+    assert O.NS_EPS == 1e-7 and O.RENORM_EPS == 1e-5
+
+
+@pytest.mark.parametrize("shape", [(12, 30), (30, 12), (16, 16), (128, 512)])
+def test_ns_svd_closed_form(shape):
+    """NS(G) = U phi(S / (||G||_F + eps)) V^T with phi the scalar quintic chain."""
+    rng = np.random.default_rng(6)
+    G = rng.standard_normal(shape) * 3.0
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    ref = (U * _phi(S / (np.linalg.norm(G) + 1e-7))) @ Vt
+    out = O.newton_schulz5(G)
+    assert out.shape == G.shape
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_ns_singular_values_approach_one():
+    rng = np.random.default_rng(7)
+    m, n = 32, 96
+    U, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, m)))
+    s = np.geomspace(0.02, 1.0, m)
+    G = (U * s) @ V.T
+    out = O.newton_schulz5(G)
+    sv = np.linalg.svd(out, compute_uv=False)
+    grid = np.linspace(0.01, 1.0, 200001)
+    lo, hi = _phi(grid).min(), _phi(grid).max()
+    assert 0.977 < lo < 0.978 and 1.031 < hi < 1.032
+    assert sv.min() >= lo - 1e-12 and sv.max() <= hi + 1e-12
+    # a rank-1 input maps to phi(||G|| / (||G|| + eps)) u v^T
+    u, v = rng.standard_normal(m), rng.standard_normal(n)
+    r1 = np.outer(u, v)
+    out1 = O.newton_schulz5(r1)
+    nr = np.linalg.norm(r1)
+    ref = _phi(nr / (nr + 1e-7)) * r1 / nr
+    assert np.max(np.abs(out1 - ref)) < 1e-13
+
+
+def test_ns_scale_invariance():
+    rng = np.random.default_rng(8)
+    G = rng.standard_normal((20, 50))
+    a, b = O.newton_schulz5(G), O.newton_schulz5(G * 37.0)
+    assert np.max(np.abs(a - b)) < 1e-6
+
+
+# ----------------------------------------------------- renorm, momentum ----
+def test_step_renorm_closed_form():
+    rng = np.random.default_rng(9)
+    W, U = rng.standard_normal((10, 7)), rng.standard_normal((10, 7)) * 0.3
+    n0 = np.abs(rng.standard_normal(10)) + 0.5
+    out = O.step_renorm(W, U, n0)
+    r = W + U
+    nr = np.sqrt((r * r).sum(1))
+    assert np.max(np.abs(np.sqrt((out * out).sum(1)) - n0 * nr / (nr + 1e-5))) < 1e-14
+    # direction unchanged
+    cos = (out * r).sum(1) / (np.sqrt((out * out).sum(1)) * nr)
+    assert np.max(np.abs(cos - 1.0)) < 1e-14
+
+
+def test_momentum_closed_form():
+    rng = np.random.default_rng(10)
+    beta = 0.9
+    Gs = [rng.standard_normal((5, 6)) for _ in range(6)]
+    M = np.zeros((5, 6))
+    for c, G in enumerate(Gs):
+        out, M = O.momentum_step(G, M, beta)
+        ref = sum(beta ** (c - s) * Gs[s] for s in range(c + 1))
+        assert np.max(np.abs(out - ref)) < 1e-12
+        assert np.max(np.abs(M - ref)) < 1e-12
+
+
+def test_update_eta_zero_is_pure_renorm():
+    rng = np.random.default_rng(11)
+    d, dh, n = 8, 16, 12
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    st = O.HeadState(W1, W3, W2)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    z = np.zeros(n)
+    new = O.update(st, K, V, z, z, z, use_muon=False)
+    for W, Wn in ((W1, new.W1), (W3, new.W3), (W2, new.W2)):
+        nr = np.sqrt((W * W).sum(1))
+        assert np.max(np.abs(Wn - W * (nr / (nr + 1e-5))[:, None])) < 1e-15
+
+
+def test_update_momentum_beta_is_chunk_mean():
+    rng = np.random.default_rng(12)
+    d, dh, n = 4, 8, 10
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    st = O.HeadState(W1, W3, W2)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    eta = np.full(n, 0.01)
+    mom = rng.uniform(0.5, 1.0, n)
+    st.M1 = rng.standard_normal(st.M1.shape)
+    _, parts = O.update(st, K, V, eta, eta, eta, mom=mom, use_momentum=True, return_parts=True)
+    raw1 = parts["raw"][0]
+    assert np.max(np.abs(parts["pre_ns"][0] - (raw1 + mom.mean() * st.M1))) < 1e-15
+
+
+# ---------------------------------------------------------- orderings ----
+def _seq_inputs(rng, T, d, dh):
+    W = _rand_state(rng, d, dh)
+    Q = rng.standard_normal((T, d))
+    Q /= np.linalg.norm(Q, axis=1, keepdims=True)
+    K = rng.standard_normal((T, d))
+    K /= np.linalg.norm(K, axis=1, keepdims=True)
+    V = rng.standard_normal((T, d))
+    eta = np.log1p(np.exp(rng.standard_normal(T))) * 1e-2
+    return W, Q, K, V, eta
+
+
+def test_causal_ordering_is_shifted_block_causal():
+    rng = np.random.default_rng(13)
+    T, C, d, dh = 80, 16, 8, 16
+    W, Q, K, V, eta = _seq_inputs(rng, T, d, dh)
+    mom = np.full(T, 0.9)
+    kw = dict(chunk=C, mom=mom, use_muon=True, use_momentum=True)
+    base, st = O.sequence(*W, Q, K, V, eta, eta, eta, **kw)
+    # chunk 0 is read with the initial weights
+    assert np.max(np.abs(base[:C] - O.apply(*W, Q[:C]))) < 1e-15
+    for c in range(T // C):
+        K2, V2, e2 = K.copy(), V.copy(), eta.copy()
+        K2[c * C:] += 1.0
+        V2[c * C:] -= 0.5
+        e2[c * C:] *= 3.0
+        out, _ = O.sequence(*W, Q, K2, V2, e2, e2, e2, **kw)
+        # outputs of chunks <= c do not see keys/values of chunk c or later
+        assert np.array_equal(out[: (c + 1) * C], base[: (c + 1) * C])
+        if c < T // C - 1:
+            assert not np.allclose(out[(c + 1) * C:], base[(c + 1) * C:])
+    # the last chunk is never written: final state == state before the last chunk
+    _, st_last, states = O.sequence(*W, Q, K, V, eta, eta, eta, return_states=True, **kw)
+    assert np.array_equal(st_last.W1, states[-1].W1)
+
+
+def test_causal_loop_bound_ragged():
+    """Chunks that start before T - C are written; the tail is read only."""
+    rng = np.random.default_rng(14)
+    d, dh, C = 6, 12, 10
+    T = 35
+    W, Q, K, V, eta = _seq_inputs(rng, T, d, dh)
+    out, st, states = O.sequence(*W, Q, K, V, eta, eta, eta, chunk=C, return_states=True)
+    assert len(states) == 4   # chunks [0,10) [10,20) [20,30) [30,35)
+    K2 = K.copy()
+    K2[30:] += 1.0
+    out2, st2 = O.sequence(*W, Q, K2, V, eta, eta, eta, chunk=C)
+    assert np.array_equal(out, out2) and np.array_equal(st.W1, st2.W1)
+
+
+def test_ar_video_subset_ordering():
+    rng = np.random.default_rng(15)
+    T, C, d, dh = 64, 16, 8, 16
+    W, Q, K, V, eta = _seq_inputs(rng, T, d, dh)
+    kw = dict(chunk=C, subset=(8, 8), use_muon=True)
+    base, _ = O.sequence(*W, Q, K, V, eta, eta, eta, **kw)
+    K2, V2 = K.copy(), V.copy()
+    for s in range(0, T, C):
+        K2[s:s + 8] += 2.0   # noisy half never writes
+        V2[s:s + 8] *= -1.0
+    out, _ = O.sequence(*W, Q, K2, V2, eta, eta, eta, **kw)
+    assert np.array_equal(out, base)
+    # the clean half of chunk 0 reaches chunk 1's reads
+    K3 = K.copy()
+    K3[8:16] += 1.0
+    out3, _ = O.sequence(*W, Q, K3, V, eta, eta, eta, **kw)
+    assert np.array_equal(out3[:C], base[:C]) and not np.allclose(out3[C:2 * C], base[C:2 * C])
+
+
+def test_bidirectional_subset_ordering():
+    rng = np.random.default_rng(16)
+    T, d, dh = 48, 8, 16
+    W, Q, K, V, eta = _seq_inputs(rng, T, d, dh)
+    kw = dict(chunk=T, order=O.ORDER_UPDATE_THEN_APPLY, subset=(0, 36))
+    base, st = O.sequence(*W, Q, K, V, eta, eta, eta, **kw)
+    K2 = K.copy()
+    K2[36:] += 1.0   # target tokens do not write
+    out, _ = O.sequence(*W, Q, K2, V, eta, eta, eta, **kw)
+    assert np.array_equal(out, base)
+    # every token, including the first, sees the write of the input tokens
+    out_nowrite = O.apply(*W, Q)
+    assert not np.allclose(out[:1], out_nowrite[:1])
+
+
+def test_page_flops_model():
+    vals = {}
+    with open(os.path.join(GOLDEN, "flops_model.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    # count the multiply-adds of one token through the oracle's contractions
+    d, dh = 1, 1
+    fwd_key = 2 * (2 * d * dh)          # W1 k, W3 k
+    backward = 2 * (d * dh) + 3 * 2 * (d * dh)   # W2^T v, three outer products
+    fwd_query = 3 * 2 * d * dh           # W1 q, W3 q, W2 h
+    assert (fwd_key, backward, fwd_query) == (vals["forward_with_key"], vals["backward"], vals["forward_with_query"])
+    assert fwd_key + backward + fwd_query == vals["total"]
