@@ -1,0 +1,423 @@
+// Fused SwiGLU fast-weight kernels: read (apply) and the chunk gradient.
+//
+// Read (LaCT rebuttal page, apply step of both pseudocode functions):
+//   o_t = W2 (silu(W1 q_t) * (W3 q_t)).
+// Write gradient (same page, "compute the gradient" block; summary page
+// section 3.2, Eq. 4-5), descent direction of -sum_t eta_t <f_W(k_t), v_t>:
+//   g = W1 k, u = W3 k, e = W2^T v, s = silu(g), h = s * u,
+//   G2 += eta2 v h^T, G3 += eta3 (e * s) k^T, G1 += eta1 (e * u * silu'(g)) k^T.
+// The hidden activations never leave the chip: they are produced in MFMA
+// accumulators and consumed from registers by the next contraction.
+#include "lact_internal.hpp"
+#include "mfma.hpp"
+
+namespace lact {
+
+// ----------------------------------------------------------------- apply --
+// One workgroup = WAVES waves x NTW tokens of one head.  The hidden dim is
+// streamed in blocks of 32 rows: W1/W3 rows and W2 columns of the block are
+// staged in LDS (double buffered) and shared by all waves; each wave keeps its
+// q fragments and its output accumulators (o^T, d x NTW) in registers.
+template <class T, int D, int NTW, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
+  constexpr int NTH = WAVES * 64;
+  constexpr int HB = 32;                 // hidden rows per stage
+  constexpr int NT = NTW / 16;           // 16-token tiles per wave
+  constexpr int KS = D / 32;             // K slabs over d
+  constexpr int IT = D / 16;             // output feature tiles
+  constexpr int V = 16 / sizeof(T);      // elements per 16-byte vector
+  constexpr int P1 = D + V;              // LDS pitch of W1/W3 block rows
+  constexpr int P2 = HB + 4;             // LDS pitch of W2 block rows
+  constexpr int STAGE = 2 * HB * P1 + D * P2;
+  constexpr int NV1 = HB * D / V / NTH;  // 16-byte vectors per thread (W1 / W3)
+  constexpr int NV2 = D * HB / V / NTH;  // (W2)
+  static_assert(NV1 * V * NTH == HB * D && NV2 * V * NTH == D * HB, "stage split");
+
+  __shared__ __attribute__((aligned(16))) T lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int tiles = (int)((a.n_tok + (int64_t)WAVES * NTW - 1) / ((int64_t)WAVES * NTW));
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int head = lid / tiles, tile = lid % tiles;
+  if (head >= a.bh) return;
+  const int dh = a.dh;
+  const int64_t tok0 = (int64_t)tile * WAVES * NTW + (int64_t)wave * NTW;
+
+  const T* q = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.q_sbh;
+  T* o = reinterpret_cast<T*>(a.o) + (int64_t)head * a.o_sbh;
+  const T* sb = reinterpret_cast<const T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+  const T* w1 = sb + a.sh.off_w1;
+  const T* w3 = sb + a.sh.off_w3;
+  const T* w2 = sb + a.sh.off_w2;
+
+  // q^T fragments (B operand, K = d): lane holds q[token 16tt + c][32ks + 8g ..]
+  frag_t<T> qf[NT][KS];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (t < a.n_tok) {
+        qf[tt][ks] = ld8(q + t * a.q_st + 32 * ks + 8 * g);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) qf[tt][ks][m] = to_t<T>(0.f);
+      }
+    }
+  }
+
+  f32x4 acc[IT][NT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 r1[NV1], r3[NV1], r2[NV2];
+  auto gload = [&](int jb) {
+#pragma unroll
+    for (int x = 0; x < NV1; ++x) {
+      const int vi = tid + x * NTH;  // vector index inside the HB x D block
+      r1[x] = *reinterpret_cast<const uint4*>(w1 + (int64_t)jb * HB * D + (int64_t)vi * V);
+      r3[x] = *reinterpret_cast<const uint4*>(w3 + (int64_t)jb * HB * D + (int64_t)vi * V);
+    }
+#pragma unroll
+    for (int x = 0; x < NV2; ++x) {
+      const int vi = tid + x * NTH;
+      const int row = vi / (HB / V), col = (vi % (HB / V)) * V;
+      r2[x] = *reinterpret_cast<const uint4*>(w2 + (int64_t)row * dh + jb * HB + col);
+    }
+  };
+  auto lstore = [&](int buf) {
+    T* s1 = lds + buf * STAGE;
+    T* s3 = s1 + HB * P1;
+    T* s2 = s3 + HB * P1;
+#pragma unroll
+    for (int x = 0; x < NV1; ++x) {
+      const int vi = tid + x * NTH;
+      const int row = vi / (D / V), col = (vi % (D / V)) * V;
+      *reinterpret_cast<uint4*>(s1 + row * P1 + col) = r1[x];
+      *reinterpret_cast<uint4*>(s3 + row * P1 + col) = r3[x];
+    }
+#pragma unroll
+    for (int x = 0; x < NV2; ++x) {
+      const int vi = tid + x * NTH;
+      const int row = vi / (HB / V), col = (vi % (HB / V)) * V;
+      // P2 rows are 8-byte aligned for bf16: store as two 8-byte halves.
+      uint2* dst = reinterpret_cast<uint2*>(s2 + row * P2 + col);
+      if constexpr (sizeof(T) == 2) {
+        dst[0] = uint2{r2[x].x, r2[x].y};
+        dst[1] = uint2{r2[x].z, r2[x].w};
+      } else {
+        *reinterpret_cast<uint4*>(s2 + row * P2 + col) = r2[x];
+      }
+    }
+  };
+
+  const int NB = dh / HB;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int jb = 0; jb < NB; ++jb) {
+    const int buf = jb & 1;
+    if (jb + 1 < NB) gload(jb + 1);
+    const T* s1 = lds + buf * STAGE;
+    const T* s3 = s1 + HB * P1;
+    const T* s2 = s3 + HB * P1;
+
+    // gate / up pre-activations, transposed: P^T[hidden][token]
+    f32x4 P[2][NT], U[2][NT];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const frag_t<T> a1 = ld8(s1 + (16 * jt + c) * P1 + 32 * ks + 8 * g);
+        const frag_t<T> a3 = ld8(s3 + (16 * jt + c) * P1 + 32 * ks + 8 * g);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          mma(P[jt][tt], a1, qf[tt][ks]);
+          mma(U[jt][tt], a3, qf[tt][ks]);
+        }
+      }
+    }
+    // h = silu(P) * U, packed as the B operand (K = the 32 hidden rows).
+    frag_t<T> hf[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = P[0][tt][i], p1 = P[1][tt][i];
+        hf[tt][i] = to_t<T>(p0 * sigmoidf_(p0) * U[0][tt][i]);
+        hf[tt][4 + i] = to_t<T>(p1 * sigmoidf_(p1) * U[1][tt][i]);
+      }
+    // o^T[feature][token] += W2[:, block] h^T
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const T* row = s2 + (16 * it + c) * P2;
+      const frag_t<T> a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
+    }
+    if (jb + 1 < NB) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+    if (t < a.n_tok) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+        st4(o + t * a.o_st + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
+            acc[it][tt][3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------- gradient --
+// One workgroup = WAVES waves x JW hidden units each, over one token split of
+// one head.  Each wave keeps, for the whole token loop:
+//   * its W1 / W3 / W2^T rows as B fragments (K = d),
+//   * fp32 accumulators of G1^T, G3^T (d x JW) and G2 (d x JW).
+// Per token tile (32 tokens): k, v are staged in LDS both row-major (A
+// operand of the forward contractions, K = d) and transposed (A operand of
+// the gradient contractions, K = tokens).  The forward results (tokens x
+// hidden, in MFMA accumulators) go through the SwiGLU backward and the eta
+// scaling in registers and feed the gradient contractions directly.
+template <class T, int D, int JW, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
+  constexpr int NTH = WAVES * 64;
+  constexpr int NT = 32;                 // tokens per tile (one K slab)
+  constexpr int KS = D / 32;
+  constexpr int JT = JW / 16;
+  constexpr int IT = D / 16;
+  constexpr int V = 16 / sizeof(T);
+  constexpr int PR = D + V;              // pitch of row-major k / v tiles
+  constexpr int PT = NT + 8;             // pitch of transposed tiles (elements)
+  constexpr int NVT = NT * D / V;        // 16-byte vectors per tile
+  static_assert(NVT % NTH == 0 || NTH % NVT == 0, "tile split");
+
+  __shared__ __attribute__((aligned(16))) T sK[NT * PR];
+  __shared__ __attribute__((aligned(16))) T sV[NT * PR];
+  __shared__ __attribute__((aligned(16))) T sKt[D * PT];
+  __shared__ __attribute__((aligned(16))) T sVt[D * PT];
+  __shared__ float sEta[3][NT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int hblocks = (a.dh + WAVES * JW - 1) / (WAVES * JW);
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  // logical id -> (head, split, hidden block); hidden blocks of one head and
+  // split are neighbours so they share k / v tiles in L2.
+  const int hb = lid % hblocks;
+  const int rest = lid / hblocks;
+  const int split = rest % a.nsplit;
+  const int head = rest / a.nsplit;
+  if (head >= a.bh) return;
+  const int64_t s0 = (int64_t)split * a.split_len;
+  const int64_t s1 = (s0 + a.split_len < a.n_tok) ? s0 + a.split_len : a.n_tok;
+  const int jw0 = hb * WAVES * JW + wave * JW;
+  const bool active = jw0 < a.dh;  // dh need not fill the last block
+
+  const T* kp = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.k_sbh;
+  const T* vp = reinterpret_cast<const T*>(a.v) + (int64_t)head * a.v_sbh;
+  const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh;
+  const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh;
+  const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
+  const T* sb = reinterpret_cast<const T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+  const T* w1 = sb + a.sh.off_w1;
+  const T* w3 = sb + a.sh.off_w3;
+  const T* w2t = sb + a.sh.off_w2t;
+
+  // Weight B fragments: lane holds W[j = jw0 + 16jt + c][32ks + 8g ..].
+  frag_t<T> b1[JT][KS], b3[JT][KS], b2[JT][KS];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int jrow = active ? jw0 + 16 * jt + c : c;  // idle waves read row c
+      const int64_t off = (int64_t)jrow * D + 32 * ks + 8 * g;
+      b1[jt][ks] = ld8(w1 + off);
+      b3[jt][ks] = ld8(w3 + off);
+      b2[jt][ks] = ld8(w2t + off);
+    }
+
+  f32x4 G1[IT][JT], G3[IT][JT], G2[IT][JT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      G1[it][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      G3[it][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      G2[it][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  for (int64_t t0 = s0; t0 < s1; t0 += NT) {
+    // ---- stage the token tile (zero beyond the split end) ----
+    for (int vi = tid; vi < NVT; vi += NTH) {
+      const int r = vi / (D / V), col = (vi % (D / V)) * V;
+      const int64_t t = t0 + r;
+      uint4 kv = uint4{0u, 0u, 0u, 0u}, vv = uint4{0u, 0u, 0u, 0u};
+      if (t < s1) {
+        kv = *reinterpret_cast<const uint4*>(kp + t * a.k_st + col);
+        vv = *reinterpret_cast<const uint4*>(vp + t * a.v_st + col);
+      }
+      *reinterpret_cast<uint4*>(sK + r * PR + col) = kv;
+      *reinterpret_cast<uint4*>(sV + r * PR + col) = vv;
+      const T* ke = reinterpret_cast<const T*>(&kv);
+      const T* ve = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sKt[(col + e) * PT + r] = ke[e];
+        sVt[(col + e) * PT + r] = ve[e];
+      }
+    }
+    if (tid < NT) {
+      const int64_t t = t0 + tid;
+      const bool in = t < s1;
+      sEta[0][tid] = in ? e1[t] : 0.f;
+      sEta[1][tid] = in ? e3[t] : 0.f;
+      sEta[2][tid] = in ? e2[t] : 0.f;
+    }
+    __syncthreads();
+    if (active) {
+    // ---- forward on keys / back-prop of v: tokens x hidden ----
+    f32x4 P[2][JT], U[2][JT], E[2][JT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        P[tt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        U[tt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        E[tt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const frag_t<T> ak = ld8(sK + (16 * tt + c) * PR + 32 * ks + 8 * g);
+        const frag_t<T> av = ld8(sV + (16 * tt + c) * PR + 32 * ks + 8 * g);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          mma(P[tt][jt], ak, b1[jt][ks]);
+          mma(U[tt][jt], ak, b3[jt][ks]);
+          mma(E[tt][jt], av, b2[jt][ks]);
+        }
+      }
+
+    // ---- SwiGLU backward + eta, packed as B operands (K = 32 tokens) ----
+    frag_t<T> fh[JT], fu[JT], fg[JT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * tt + 4 * g + i;   // token row inside the tile
+          const float p = P[tt][jt][i], u = U[tt][jt][i], e = E[tt][jt][i];
+          const float sg = sigmoidf_(p);
+          const float sl = p * sg;
+          const float dsl = sg * (1.f + p * (1.f - sg));
+          fh[jt][4 * tt + i] = to_t<T>(sEta[2][r] * sl * u);
+          fu[jt][4 * tt + i] = to_t<T>(sEta[1][r] * e * sl);
+          fg[jt][4 * tt + i] = to_t<T>(sEta[0][r] * e * u * dsl);
+        }
+
+    // ---- gradient contractions over the tile's tokens ----
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const T* kr = sKt + (16 * it + c) * PT;
+      const T* vr = sVt + (16 * it + c) * PT;
+      const frag_t<T> akt = ld4x2(kr + 4 * g, kr + 16 + 4 * g);
+      const frag_t<T> avt = ld4x2(vr + 4 * g, vr + 16 + 4 * g);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        mma(G1[it][jt], akt, fg[jt]);
+        mma(G3[it][jt], akt, fu[jt]);
+        mma(G2[it][jt], avt, fh[jt]);
+      }
+    }
+    }  // active
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // ---- partials, [split][head][3][dh][d]: lane holds 4 consecutive d ----
+  const int64_t mat = (int64_t)a.dh * D;
+  float* out = a.partial + ((int64_t)split * a.bh + head) * 3 * mat;
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const int64_t off = (int64_t)(jw0 + 16 * jt + c) * D + 16 * it + 4 * g;
+      st4(out + off, G1[it][jt][0], G1[it][jt][1], G1[it][jt][2], G1[it][jt][3]);
+      st4(out + mat + off, G3[it][jt][0], G3[it][jt][1], G3[it][jt][2], G3[it][jt][3]);
+      st4(out + 2 * mat + off, G2[it][jt][0], G2[it][jt][1], G2[it][jt][2], G2[it][jt][3]);
+    }
+}
+
+// --------------------------------------------------------------- launch --
+template <class T, int D, int NTW, int WAVES>
+static hipError_t run_apply(const ApplyArgs& a, hipStream_t s) {
+  const int64_t tiles = (a.n_tok + (int64_t)WAVES * NTW - 1) / ((int64_t)WAVES * NTW);
+  const int64_t blocks = tiles * a.bh;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_apply<T, D, NTW, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
+  if (dtype == 1) {
+    switch (a.d) {
+      case 64: return run_apply<bf16, 64, 64, 4>(a, s);
+      case 128: return run_apply<bf16, 128, 64, 4>(a, s);
+      case 256: return run_apply<bf16, 256, 32, 4>(a, s);
+    }
+  } else {
+    switch (a.d) {
+      case 64: return run_apply<float, 64, 32, 4>(a, s);
+      case 128: return run_apply<float, 128, 32, 4>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+int grad_hidden_per_block(int dtype, int d) {
+  // WAVES * JW; JW * d = 4096 (bf16) / 2048 (fp32) keeps registers bounded.
+  if (dtype == 1) return 4 * (d == 64 ? 64 : d == 128 ? 32 : 16);
+  return 4 * (d == 64 ? 32 : 16);
+}
+
+template <class T, int D, int JW, int WAVES>
+static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
+  const int hblocks = (a.dh + WAVES * JW - 1) / (WAVES * JW);
+  const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_grad<T, D, JW, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
+  if (dtype == 1) {
+    switch (a.d) {
+      case 64: return run_grad<bf16, 64, 64, 4>(a, s);
+      case 128: return run_grad<bf16, 128, 32, 4>(a, s);
+      case 256: return run_grad<bf16, 256, 16, 4>(a, s);
+    }
+  } else {
+    switch (a.d) {
+      case 64: return run_grad<float, 64, 32, 4>(a, s);
+      case 128: return run_grad<float, 128, 16, 4>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lact

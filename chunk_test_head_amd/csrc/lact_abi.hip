@@ -1,0 +1,491 @@
+// C ABI of the LaCT fast-weight layer: host-side validation, workspace
+// layout and the chunk sequence driver.  Every entry point checks all of its
+// arguments before it enqueues anything, allocates nothing and never
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/lact.h"
+#include "lact_internal.hpp"
+
+namespace lact {
+
+static thread_local int g_last_hip_error = 0;
+
+static lact_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return LACT_ERR_HIP;
+}
+
+Shadow make_shadow(void* base, int d, int dh) {
+  Shadow s;
+  s.base = base;
+  const int64_t m = (int64_t)d * dh;
+  s.per_head = 4 * m;
+  s.off_w1 = 0;
+  s.off_w3 = m;
+  s.off_w2 = 2 * m;
+  s.off_w2t = 3 * m;
+  return s;
+}
+
+static int elem_size(int dtype) { return dtype == LACT_BF16 ? 2 : 4; }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static lact_status check_shape(const lact_shape* sh) {
+  if (sh == nullptr) return LACT_ERR_INVALID_ARG;
+  if (sh->bh < 1 || sh->d < 1 || sh->dh < 1) return LACT_ERR_INVALID_ARG;
+  if (sh->dtype != LACT_F32 && sh->dtype != LACT_BF16) return LACT_ERR_INVALID_ARG;
+  if (sh->d != 64 && sh->d != 128 && sh->d != 256) return LACT_ERR_UNSUPPORTED;
+  if (sh->dh % 64 != 0 || sh->dh < sh->d || sh->dh > 4096) return LACT_ERR_UNSUPPORTED;
+  if (sh->dtype == LACT_F32 && sh->d > 128) return LACT_ERR_UNSUPPORTED;
+  return LACT_OK;
+}
+
+static lact_status check_state(const lact_shape* sh, const lact_state* st, bool need_m) {
+  if (st == nullptr) return LACT_ERR_INVALID_ARG;
+  const void* req[] = {st->w1, st->w3, st->w2, st->n1, st->n3, st->n2, st->shadow};
+  for (const void* p : req) {
+    if (p == nullptr) return LACT_ERR_INVALID_ARG;
+    if (!aligned16(p)) return LACT_ERR_ALIGNMENT;
+  }
+  if (need_m) {
+    const void* m[] = {st->m1, st->m3, st->m2};
+    for (const void* p : m) {
+      if (p == nullptr) return LACT_ERR_INVALID_ARG;
+      if (!aligned16(p)) return LACT_ERR_ALIGNMENT;
+    }
+  }
+  (void)sh;
+  return LACT_OK;
+}
+
+static lact_status check_act(const lact_shape* sh, const void* p, lact_layout l, int64_t n_tok) {
+  if (n_tok == 0) return LACT_OK;
+  if (p == nullptr) return LACT_ERR_INVALID_ARG;
+  if (l.stride_tok < sh->d || l.stride_bh < 0) return LACT_ERR_INVALID_ARG;
+  const int es = elem_size(sh->dtype);
+  if (!aligned16(p) || (l.stride_tok * es) % 16 != 0 || (l.stride_bh * es) % 16 != 0)
+    return LACT_ERR_ALIGNMENT;
+  return LACT_OK;
+}
+
+static lact_status check_opts(const lact_update_opts* o) {
+  if (o == nullptr) return LACT_ERR_INVALID_ARG;
+  if (!(o->renorm_eps >= 0.f) || !(o->ns_eps >= 0.f)) return LACT_ERR_INVALID_ARG;
+  return LACT_OK;
+}
+
+// ------------------------------------------------------------ workspace --
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+static int choose_nsplit(const lact_shape* sh, int64_t n_tok) {
+  const int hpb = grad_hidden_per_block(sh->dtype, sh->d);
+  const int64_t hblocks = (sh->dh + hpb - 1) / hpb;
+  const int64_t base = (int64_t)sh->bh * hblocks;
+  int64_t ns = (512 + base - 1) / base;
+  const int64_t cap = (n_tok + 255) / 256;
+  if (ns > cap) ns = cap;
+  if (ns < 1) ns = 1;
+  if (ns > 64) ns = 64;
+  return (int)ns;
+}
+
+struct Workspace {
+  float* beta;
+  float* partial;
+  float* g;       // 3 wide matrices per head: [3][bh][d][dh]
+  float* xa;      // Newton-Schulz buffers
+  float* xb;
+  float* amat;    // [3 bh][d][d]
+  float* bmat;
+  float* rowpart;
+  int64_t bytes;
+};
+
+static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* base) {
+  Workspace w;
+  const int64_t msz = (int64_t)sh->d * sh->dh;
+  int64_t off = 0;
+  auto take = [&](int64_t nfloat) {
+    float* p = base ? reinterpret_cast<float*>(base + off) : nullptr;
+    off += align256(nfloat * 4);
+    return p;
+  };
+  w.beta = take(sh->bh);
+  w.partial = take((int64_t)nsplit * sh->bh * 3 * msz);
+  w.g = take((int64_t)3 * sh->bh * msz);
+  if (muon) {
+    w.xa = take((int64_t)3 * sh->bh * msz);
+    w.xb = take((int64_t)3 * sh->bh * msz);
+    w.amat = take((int64_t)3 * sh->bh * sh->d * sh->d);
+    w.bmat = take((int64_t)3 * sh->bh * sh->d * sh->d);
+  } else {
+    w.xa = w.xb = w.amat = w.bmat = nullptr;
+  }
+  w.rowpart = take(step_rowpart_elems(sh->bh, sh->d, sh->dh));
+  w.bytes = off;
+  return w;
+}
+
+// ------------------------------------------------------- Newton-Schulz --
+static const float kNS[5][3] = {
+    {4.0848f, -6.8946f, 2.9270f}, {3.9505f, -6.3029f, 2.6377f}, {3.7418f, -5.5913f, 2.3037f},
+    {2.8769f, -3.1427f, 1.2046f}, {2.8366f, -3.0525f, 1.2012f}};
+
+static int64_t ns_ws_bytes(int count, int rows, int cols) {
+  const int64_t m = (int64_t)rows * cols;
+  return 2 * align256((int64_t)count * m * 4) + 2 * align256((int64_t)count * rows * rows * 4);
+}
+
+static hipError_t run_ns(int dtype, int count, int rows, int cols, const float* g, float* u,
+                         float eps, float* xa, float* xb, float* am, float* bm, hipStream_t s) {
+  const int64_t m = (int64_t)rows * cols;
+  NsNormArgs na{g, xa, count, m, eps};
+  hipError_t e = launch_ns_norm(na, s);
+  if (e != hipSuccess) return e;
+  float* x = xa;
+  float* y = xb;
+  for (int it = 0; it < 5; ++it) {
+    const float ca = kNS[it][0], cb = kNS[it][1], cc = kNS[it][2];
+    // A = X X^T
+    GemmArgs ga{x, m, x, m, 0, nullptr, 0, am, (int64_t)rows * rows, rows, rows, cols, count, 1.f, 0.f};
+    if ((e = launch_gemm(dtype, ga, s)) != hipSuccess) return e;
+    // B = c A A + b A
+    GemmArgs gb{am, (int64_t)rows * rows, am, (int64_t)rows * rows, 1, am, (int64_t)rows * rows,
+                bm, (int64_t)rows * rows, rows, rows, rows, count, cc, cb};
+    if ((e = launch_gemm(dtype, gb, s)) != hipSuccess) return e;
+    // X' = B X + a X
+    float* out = (it == 4) ? u : y;
+    GemmArgs gx{bm, (int64_t)rows * rows, x, m, 1, x, m, out, m, rows, cols, rows, count, 1.f, ca};
+    if ((e = launch_gemm(dtype, gx, s)) != hipSuccess) return e;
+    float* t = x;
+    x = y;
+    y = t;
+  }
+  return hipSuccess;
+}
+
+// -------------------------------------------------------------- pieces --
+static lact_status do_apply(const lact_shape* sh, const lact_state* st, const void* q,
+                            lact_layout ql, void* o, lact_layout ol, int64_t n_tok,
+                            hipStream_t s) {
+  if (n_tok == 0) return LACT_OK;
+  ApplyArgs a;
+  a.q = q; a.q_sbh = ql.stride_bh; a.q_st = ql.stride_tok;
+  a.o = o; a.o_sbh = ol.stride_bh; a.o_st = ol.stride_tok;
+  a.sh = make_shadow(st->shadow, sh->d, sh->dh);
+  a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh; a.n_tok = n_tok;
+  hipError_t e = launch_apply(sh->dtype, a, s);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+static lact_status do_grad(const lact_shape* sh, const lact_state* st, const void* k,
+                           lact_layout kl, const void* v, lact_layout vl, const float* e1,
+                           const float* e3, const float* e2, int64_t esbh, int64_t n_tok,
+                           const Workspace& w, int nsplit, float* o1, float* o3, float* o2,
+                           float* m1, float* m3, float* m2, hipStream_t s) {
+  GradArgs a;
+  a.k = k; a.k_sbh = kl.stride_bh; a.k_st = kl.stride_tok;
+  a.v = v; a.v_sbh = vl.stride_bh; a.v_st = vl.stride_tok;
+  a.eta1 = e1; a.eta3 = e3; a.eta2 = e2; a.eta_sbh = esbh;
+  a.sh = make_shadow(st->shadow, sh->d, sh->dh);
+  a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh; a.n_tok = n_tok;
+  a.nsplit = nsplit;
+  int64_t sl = (n_tok + nsplit - 1) / nsplit;
+  sl = (sl + 31) / 32 * 32;
+  a.split_len = sl > 0 ? sl : 32;
+  a.partial = w.partial;
+  hipError_t e = launch_grad(sh->dtype, a, s);
+  if (e != hipSuccess) return hip_fail(e);
+  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
+  e = launch_reduce(r, s);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+static lact_status do_step(const lact_shape* sh, const lact_state* st, const float* u1,
+                           const float* u3, const float* u2, int renorm, float eps,
+                           float* rowpart, hipStream_t s) {
+  StepArgs a;
+  a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
+  a.u1 = u1; a.u3 = u3; a.u2 = u2;
+  a.n1 = st->n1; a.n3 = st->n3; a.n2 = st->n2;
+  a.rowpart = rowpart;
+  a.sh = make_shadow(st->shadow, sh->d, sh->dh);
+  a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
+  a.renorm = renorm; a.eps = eps; a.write_w = 1;
+  hipError_t e = launch_step(sh->dtype, a, s);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+static lact_status do_update(const lact_shape* sh, const lact_state* st, const void* k,
+                             lact_layout kl, const void* v, lact_layout vl, const float* e1,
+                             const float* e3, const float* e2, const float* mom, int64_t esbh,
+                             int64_t n_tok, const lact_update_opts* op, void* ws,
+                             hipStream_t s) {
+  const int nsplit = choose_nsplit(sh, n_tok);
+  Workspace w = layout_ws(sh, nsplit, op->use_muon != 0, reinterpret_cast<char*>(ws));
+  const int64_t msz = (int64_t)sh->d * sh->dh;
+  const int64_t mall = (int64_t)sh->bh * msz;
+  float* g1 = w.g;
+  float* g3 = w.g + mall;
+  float* g2 = w.g + 2 * mall;
+  if (op->use_momentum) {
+    BetaArgs b{mom, esbh, n_tok, sh->bh, w.beta};
+    hipError_t e = launch_beta(b, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit, g1, g3, g2,
+                          op->use_momentum ? st->m1 : nullptr, op->use_momentum ? st->m3 : nullptr,
+                          op->use_momentum ? st->m2 : nullptr, s);
+  if (r != LACT_OK) return r;
+  if (op->use_muon) {
+    hipError_t e = run_ns(sh->dtype, 3 * sh->bh, sh->d, sh->dh, w.g, w.g, op->ns_eps, w.xa, w.xb,
+                          w.amat, w.bmat, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return do_step(sh, st, g1, g3, g2, op->renorm ? 1 : 0, op->renorm_eps, w.rowpart, s);
+}
+
+static lact_status check_update_args(const lact_shape* sh, const lact_state* st, const void* k,
+                                     lact_layout kl, const void* v, lact_layout vl,
+                                     const float* e1, const float* e3, const float* e2,
+                                     const float* mom, int64_t esbh, int64_t n_tok,
+                                     const lact_update_opts* op, const void* ws,
+                                     size_t ws_bytes) {
+  lact_status r;
+  if ((r = check_shape(sh)) != LACT_OK) return r;
+  if ((r = check_opts(op)) != LACT_OK) return r;
+  if ((r = check_state(sh, st, op->use_momentum != 0)) != LACT_OK) return r;
+  if (n_tok < 0) return LACT_ERR_INVALID_ARG;
+  if ((r = check_act(sh, k, kl, n_tok)) != LACT_OK) return r;
+  if ((r = check_act(sh, v, vl, n_tok)) != LACT_OK) return r;
+  if (n_tok > 0 && (e1 == nullptr || e3 == nullptr || e2 == nullptr)) return LACT_ERR_INVALID_ARG;
+  if (op->use_momentum && n_tok > 0 && mom == nullptr) return LACT_ERR_INVALID_ARG;
+  if (esbh < 0) return LACT_ERR_INVALID_ARG;
+  const size_t need = lact_workspace_bytes(sh, n_tok, op);
+  if (ws == nullptr || ws_bytes < need) return LACT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
+  return LACT_OK;
+}
+
+}  // namespace lact
+
+using namespace lact;
+
+extern "C" {
+
+size_t lact_shadow_bytes(const lact_shape* sh) {
+  if (check_shape(sh) != LACT_OK) return 0;
+  return (size_t)sh->bh * 4 * (size_t)sh->d * sh->dh * elem_size(sh->dtype);
+}
+
+size_t lact_workspace_bytes(const lact_shape* sh, int64_t max_update_tokens,
+                            const lact_update_opts* opts) {
+  if (check_shape(sh) != LACT_OK || max_update_tokens < 0) return 0;
+  const bool muon = opts != nullptr && opts->use_muon != 0;
+  const int ns = choose_nsplit(sh, max_update_tokens);
+  return (size_t)layout_ws(sh, ns, muon, nullptr).bytes;
+}
+
+size_t lact_ns_workspace_bytes(int32_t count, int32_t rows, int32_t cols) {
+  if (count < 1 || rows < 1 || cols < 1) return 0;
+  return (size_t)ns_ws_bytes(count, rows, cols);
+}
+
+lact_status lact_init_state(const lact_shape* sh, const lact_state* st, void* stream) {
+  lact_status r;
+  if ((r = check_shape(sh)) != LACT_OK) return r;
+  if ((r = check_state(sh, st, false)) != LACT_OK) return r;
+  for (float* m : {st->m1, st->m3, st->m2})
+    if (m != nullptr && !aligned16(m)) return LACT_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t mall = (int64_t)sh->bh * sh->d * sh->dh;
+  for (float* m : {st->m1, st->m3, st->m2}) {
+    if (m == nullptr) continue;
+    hipError_t e = launch_fill(m, mall, 0.f, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
+  a.n1 = st->n1; a.n3 = st->n3; a.n2 = st->n2;
+  a.sh = make_shadow(st->shadow, sh->d, sh->dh);
+  a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
+  a.renorm = 0;
+  hipError_t e = launch_row_norms(a, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_step(sh->dtype, a, s);  // operand copies only
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+lact_status lact_apply(const lact_shape* sh, const lact_state* st, const void* q,
+                       lact_layout ql, void* o, lact_layout ol, int64_t n_tok, void* stream) {
+  lact_status r;
+  if ((r = check_shape(sh)) != LACT_OK) return r;
+  if ((r = check_state(sh, st, false)) != LACT_OK) return r;
+  if (n_tok < 0) return LACT_ERR_INVALID_ARG;
+  if ((r = check_act(sh, q, ql, n_tok)) != LACT_OK) return r;
+  if ((r = check_act(sh, o, ol, n_tok)) != LACT_OK) return r;
+  if (n_tok > 0 && q == o) return LACT_ERR_INVALID_ARG;
+  return do_apply(sh, st, q, ql, o, ol, n_tok, (hipStream_t)stream);
+}
+
+lact_status lact_gradient(const lact_shape* sh, const lact_state* st, const void* k,
+                          lact_layout kl, const void* v, lact_layout vl, const float* e1,
+                          const float* e3, const float* e2, int64_t esbh, int64_t n_tok,
+                          float* g1, float* g3, float* g2, void* ws, size_t ws_bytes,
+                          void* stream) {
+  lact_update_opts op;
+  memset(&op, 0, sizeof(op));
+  lact_status r = check_update_args(sh, st, k, kl, v, vl, e1, e3, e2, nullptr, esbh, n_tok, &op,
+                                    ws, ws_bytes);
+  if (r != LACT_OK) return r;
+  for (float* gp : {g1, g3, g2}) {
+    if (gp == nullptr) return LACT_ERR_INVALID_ARG;
+    if (!aligned16(gp)) return LACT_ERR_ALIGNMENT;
+  }
+  const int nsplit = choose_nsplit(sh, n_tok);
+  Workspace w = layout_ws(sh, nsplit, false, reinterpret_cast<char*>(ws));
+  return do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit, g1, g3, g2, nullptr,
+                 nullptr, nullptr, (hipStream_t)stream);
+}
+
+lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_t dtype,
+                               const float* g, float* u, float eps, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (count < 1 || rows < 1 || cols < 1 || g == nullptr || u == nullptr) return LACT_ERR_INVALID_ARG;
+  if (dtype != LACT_F32 && dtype != LACT_BF16) return LACT_ERR_INVALID_ARG;
+  if (!(eps >= 0.f)) return LACT_ERR_INVALID_ARG;
+  if (rows % 64 != 0 || cols % 64 != 0 || rows > cols) return LACT_ERR_UNSUPPORTED;
+  if (!aligned16(g) || !aligned16(u)) return LACT_ERR_ALIGNMENT;
+  if (ws == nullptr || ws_bytes < (size_t)ns_ws_bytes(count, rows, cols)) return LACT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
+  char* b = reinterpret_cast<char*>(ws);
+  const int64_t xm = align256((int64_t)count * rows * cols * 4);
+  const int64_t am = align256((int64_t)count * rows * rows * 4);
+  float* xa = reinterpret_cast<float*>(b);
+  float* xb = reinterpret_cast<float*>(b + xm);
+  float* a_ = reinterpret_cast<float*>(b + 2 * xm);
+  float* b_ = reinterpret_cast<float*>(b + 2 * xm + am);
+  hipError_t e = run_ns(dtype, count, rows, cols, g, u, eps, xa, xb, a_, b_, (hipStream_t)stream);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+lact_status lact_step_renorm(const lact_shape* sh, const lact_state* st, const float* u1,
+                             const float* u3, const float* u2, const lact_update_opts* op,
+                             void* ws, size_t ws_bytes, void* stream) {
+  lact_status r;
+  if ((r = check_shape(sh)) != LACT_OK) return r;
+  if ((r = check_opts(op)) != LACT_OK) return r;
+  if ((r = check_state(sh, st, false)) != LACT_OK) return r;
+  for (const float* up : {u1, u3, u2}) {
+    if (up == nullptr) return LACT_ERR_INVALID_ARG;
+    if (!aligned16(up)) return LACT_ERR_ALIGNMENT;
+  }
+  if (ws == nullptr || ws_bytes < lact_workspace_bytes(sh, 0, op)) return LACT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps,
+                 reinterpret_cast<float*>(ws), (hipStream_t)stream);
+}
+
+lact_status lact_update(const lact_shape* sh, const lact_state* st, const void* k,
+                        lact_layout kl, const void* v, lact_layout vl, const float* e1,
+                        const float* e3, const float* e2, const float* mom, int64_t esbh,
+                        int64_t n_tok, const lact_update_opts* op, void* ws, size_t ws_bytes,
+                        void* stream) {
+  lact_status r = check_update_args(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws,
+                                    ws_bytes);
+  if (r != LACT_OK) return r;
+  if (n_tok == 0) return LACT_OK;
+  return do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws,
+                   (hipStream_t)stream);
+}
+
+lact_status lact_chunk_step(const lact_shape* sh, const lact_state* st, const void* q,
+                            lact_layout ql, const void* k, lact_layout kl, const void* v,
+                            lact_layout vl, void* o, lact_layout ol, const float* e1,
+                            const float* e3, const float* e2, const float* mom, int64_t esbh,
+                            int64_t n_tok, const lact_update_opts* op, void* ws,
+                            size_t ws_bytes, void* stream) {
+  lact_status r = check_update_args(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws,
+                                    ws_bytes);
+  if (r != LACT_OK) return r;
+  if ((r = check_act(sh, q, ql, n_tok)) != LACT_OK) return r;
+  if ((r = check_act(sh, o, ol, n_tok)) != LACT_OK) return r;
+  if (n_tok > 0 && q == o) return LACT_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if ((r = do_apply(sh, st, q, ql, o, ol, n_tok, s)) != LACT_OK) return r;
+  if (n_tok == 0) return LACT_OK;
+  return do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s);
+}
+
+lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void* q,
+                          lact_layout ql, const void* k, lact_layout kl, const void* v,
+                          lact_layout vl, void* o, lact_layout ol, const float* e1,
+                          const float* e3, const float* e2, const float* mom, int64_t esbh,
+                          int64_t T, int64_t chunk, int32_t order, int64_t sub_off,
+                          int64_t sub_len, int32_t update_last, const lact_update_opts* op,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || chunk < 1) return LACT_ERR_INVALID_ARG;
+  if (order != LACT_APPLY_THEN_UPDATE && order != LACT_UPDATE_THEN_APPLY) return LACT_ERR_INVALID_ARG;
+  if (sub_len >= 0 && (sub_off < 0 || sub_off >= chunk)) return LACT_ERR_INVALID_ARG;
+  int64_t max_upd = chunk < T ? chunk : T;
+  if (sub_len >= 0) {
+    const int64_t room = chunk - sub_off;
+    max_upd = sub_len < room ? sub_len : room;
+    if (max_upd > T) max_upd = T;
+  }
+  lact_status r = check_update_args(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, max_upd, op, ws,
+                                    ws_bytes);
+  if (r != LACT_OK) return r;
+  if ((r = check_act(sh, q, ql, T)) != LACT_OK) return r;
+  if ((r = check_act(sh, o, ol, T)) != LACT_OK) return r;
+  if (T > 0 && q == o) return LACT_ERR_INVALID_ARG;
+  if (T > 0 && (e1 == nullptr || e3 == nullptr || e2 == nullptr)) return LACT_ERR_INVALID_ARG;
+  if (op->use_momentum && T > 0 && mom == nullptr) return LACT_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int es = elem_size(sh->dtype);
+  auto at = [&](const void* base, lact_layout l, int64_t t) {
+    return reinterpret_cast<const char*>(base) + t * l.stride_tok * es;
+  };
+  for (int64_t s0 = 0; s0 < T; s0 += chunk) {
+    const int64_t e0 = s0 + chunk < T ? s0 + chunk : T;
+    const bool last = e0 == T;
+    int64_t a0 = s0, a1 = e0;
+    if (sub_len >= 0) {
+      a0 = s0 + sub_off;
+      a1 = a0 + sub_len < e0 ? a0 + sub_len : e0;
+    }
+    const bool write = (order == LACT_UPDATE_THEN_APPLY) || !last || update_last;
+    auto upd = [&]() -> lact_status {
+      if (!write || a1 <= a0) return LACT_OK;
+      return do_update(sh, st, at(k, kl, a0), kl, at(v, vl, a0), vl, e1 + a0, e3 + a0, e2 + a0,
+                       mom ? mom + a0 : nullptr, esbh, a1 - a0, op, ws, s);
+    };
+    if (order == LACT_UPDATE_THEN_APPLY && (r = upd()) != LACT_OK) return r;
+    r = do_apply(sh, st, at(q, ql, s0), ql, const_cast<char*>(at(o, ol, s0)), ol, e0 - s0, s);
+    if (r != LACT_OK) return r;
+    if (order == LACT_APPLY_THEN_UPDATE && (r = upd()) != LACT_OK) return r;
+  }
+  return LACT_OK;
+}
+
+const char* lact_status_string(lact_status st) {
+  switch (st) {
+    case LACT_OK: return "ok";
+    case LACT_ERR_INVALID_ARG: return "invalid argument";
+    case LACT_ERR_UNSUPPORTED: return "unsupported shape";
+    case LACT_ERR_ALIGNMENT: return "pointer or stride not 16-byte aligned";
+    case LACT_ERR_WORKSPACE: return "workspace missing or too small";
+    case LACT_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int lact_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

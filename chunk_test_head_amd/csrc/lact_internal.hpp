@@ -1,0 +1,92 @@
+// Internal launch interface between the C ABI driver and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lact {
+
+// Operand copies of the weights, per head, in the MFMA operand type:
+//   w1s, w3s : [dh][d]   w2s : [d][dh]   w2ts : [dh][d] (W2 transposed)
+struct Shadow {
+  void* base;
+  int64_t per_head;  // elements per head (4 d dh)
+  int64_t off_w1, off_w3, off_w2, off_w2t;
+};
+Shadow make_shadow(void* base, int d, int dh);
+
+struct ApplyArgs {
+  const void* q; int64_t q_sbh, q_st;
+  void* o; int64_t o_sbh, o_st;
+  Shadow sh;
+  int bh, d, dh;
+  int64_t n_tok;
+};
+
+struct GradArgs {
+  const void* k; int64_t k_sbh, k_st;
+  const void* v; int64_t v_sbh, v_st;
+  const float* eta1; const float* eta3; const float* eta2; int64_t eta_sbh;
+  Shadow sh;
+  int bh, d, dh;
+  int64_t n_tok;
+  int nsplit;
+  int64_t split_len;
+  float* partial;  // [nsplit][bh][3][dh][d] fp32
+};
+
+// Sum of split partials, transpose to the wide orientation, momentum.
+struct ReduceArgs {
+  const float* partial;  // [nsplit][bh][3][dh][d]
+  int nsplit;
+  int bh, d, dh;
+  float* out1; float* out3; float* out2;  // [bh][d][dh] each
+  float* m1; float* m3; float* m2;        // momentum (NULL = off)
+  const float* beta;                      // [bh]
+};
+
+struct BetaArgs {
+  const float* mom; int64_t sbh; int64_t n_tok; int bh; float* beta;
+};
+
+// Batched C = alpha * A B + beta * Dm, fp32 storage, MFMA operands in T.
+// A is [M][K] (K contiguous).  B is [N][K] (b_kn = 0) or [K][N] (b_kn = 1).
+struct GemmArgs {
+  const float* A; int64_t a_bs;
+  const float* B; int64_t b_bs; int b_kn;
+  const float* Dm; int64_t d_bs;
+  float* C; int64_t c_bs;
+  int M, N, K, batch;
+  float alpha, beta;
+};
+
+struct NsNormArgs {
+  const float* g; float* x; int64_t count, n; float eps;
+};
+
+// Step: W <- W + U (wide U), per-row partial sums of squares.
+struct StepArgs {
+  float* w1; float* w3; float* w2;
+  const float* u1; const float* u3; const float* u2;  // wide [bh][d][dh]; NULL = no add
+  float* n1; float* n3; float* n2;                    // renorm targets
+  float* rowpart;   // workspace: row partial sums
+  Shadow sh;
+  int bh, d, dh;
+  int renorm;  // 0: factor 1 (copies only), 1: n0 / (||row|| + eps)
+  float eps;
+  int write_w;
+};
+
+hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
+hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
+int grad_hidden_per_block(int dtype, int d);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_beta(const BetaArgs& a, hipStream_t s);
+hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
+hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
+hipError_t launch_row_norms(const StepArgs& a, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+int64_t step_rowpart_elems(int bh, int d, int dh);
+
+}  // namespace lact

@@ -1,0 +1,211 @@
+"""GPU parity of every C-ABI entry point against the float64 oracle, at sizes
+the oracle finishes in seconds that still span several tiles and a ragged
+tail.  Bar: relative Frobenius error 2e-2 (bf16 operands) / 1e-4 (fp32)."""
+import numpy as np
+import pytest
+
+from chunk_test_head_amd import _lib as L
+from chunk_test_head_amd import workloads as WL
+from oracle import lact_oracle as O
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+# one reduced case per workload family: (workload, bh, n_tok)
+FAMILIES = {
+    0: dict(heads=1, batch=1),
+    1: dict(heads=2, batch=1),
+    2: dict(heads=2, batch=1),
+    3: dict(heads=2, batch=1),
+    4: dict(heads=1, batch=2),
+}
+
+
+def small(wi, T, chunk, subset=None):
+    w = WL.WORKLOADS[wi]
+    kw = dict(FAMILIES[wi])
+    kw.update(T=T, chunk=chunk)
+    if w.subset is not None or subset is not None:
+        kw["subset"] = subset if subset is not None else (w.subset and (0, 0))
+    return w.scaled(**kw)
+
+
+def inputs(w):
+    return WL.weights(w), WL.tokens(w)
+
+
+@pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("n_tok", [1, 300, 613])
+def test_apply(device, wi, n_tok):
+    import torch
+    w = small(wi, n_tok, n_tok, subset=(0, n_tok))
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    q = H.act_to_dev(w, inp, "q", device)
+    out = H.out_buffer(w, n_tok, device)
+    print(f"apply wl={wi} bh={w.bh} n={n_tok}", flush=True)
+    L.lact_apply(fw.shape, fw, q, out)
+    torch.cuda.synchronize()
+    got = H.to64(out)
+    for b in range(w.bh):
+        ref = O.apply(W[0][b], W[1][b], W[2][b], inp["q"][b])
+        assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
+    # state untouched and the shadow consistent with it
+    assert np.array_equal(H.to64(fw.w1), W[0].astype(np.float64))
+
+
+@pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("n_tok", [37, 700])
+def test_gradient(device, wi, n_tok):
+    import torch
+    w = small(wi, n_tok, n_tok, subset=(0, n_tok))
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    k = H.act_to_dev(w, inp, "k", device)
+    v = H.act_to_dev(w, inp, "v", device)
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    g = [torch.full((w.bh, w.d, w.dh), float("nan"), device=device) for _ in range(3)]
+    ws = H.workspace(w, n_tok, device, muon=False)
+    print(f"gradient wl={wi} bh={w.bh} n={n_tok}", flush=True)
+    L.lact_gradient(fw.shape, fw, k, v, eta, eta, eta, g[0], g[1], g[2], ws)
+    torch.cuda.synchronize()
+    got = [H.to64(x) for x in g]
+    for b in range(w.bh):
+        e = inp["eta"][b]
+        G1, G3, G2 = O.chunk_gradient(W[0][b], W[1][b], W[2][b], inp["k"][b], inp["v"][b], e, e, e)
+        for name, x, ref in (("G1", got[0][b].T, G1), ("G3", got[1][b].T, G3), ("G2", got[2][b], G2)):
+            assert H.rel(x, ref) < H.TOL[w.dtype], (name, b, H.rel(x, ref))
+
+
+def test_gradient_distinct_etas(device):
+    """eta1 / eta3 / eta2 reach only their own matrix."""
+    import torch
+    w = small(1, 200, 200, subset=(0, 200))
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    k = H.act_to_dev(w, inp, "k", device)
+    v = H.act_to_dev(w, inp, "v", device)
+    rng = np.random.default_rng(5)
+    etas = [np.abs(rng.standard_normal((w.bh, w.T))).astype(np.float32) * 0.01 for _ in range(3)]
+    et = [torch.from_numpy(e).to(device) for e in etas]
+    g = [torch.empty((w.bh, w.d, w.dh), device=device) for _ in range(3)]
+    ws = H.workspace(w, w.T, device, muon=False)
+    L.lact_gradient(fw.shape, fw, k, v, et[0], et[1], et[2], g[0], g[1], g[2], ws)
+    torch.cuda.synchronize()
+    for b in range(w.bh):
+        G1, G3, G2 = O.chunk_gradient(W[0][b], W[1][b], W[2][b], inp["k"][b], inp["v"][b],
+                                      etas[0][b], etas[1][b], etas[2][b])
+        assert H.rel(H.to64(g[0])[b].T, G1) < 2e-2
+        assert H.rel(H.to64(g[1])[b].T, G3) < 2e-2
+        assert H.rel(H.to64(g[2])[b], G2) < 2e-2
+
+
+@pytest.mark.parametrize("dtype,tol", [(L.BF16, 2e-2), (L.F32, 1e-4)])
+@pytest.mark.parametrize("rows,cols", [(128, 512), (128, 256), (256, 1024), (64, 128)])
+def test_newton_schulz(device, dtype, tol, rows, cols):
+    import torch
+    # a gradient-like input: oracle chunk gradient of a random head
+    w = WL.WORKLOADS[1].scaled(heads=1, batch=1, T=512, chunk=512)
+    rng = np.random.default_rng(rows + cols)
+    Gs = []
+    for i in range(3):
+        A = rng.standard_normal((rows, 8)) @ rng.standard_normal((8, cols))
+        Gs.append(A + 0.05 * rng.standard_normal((rows, cols)))
+    g = torch.from_numpy(np.stack(Gs).astype(np.float32)).to(device)
+    u = torch.full_like(g, float("nan"))
+    ws = torch.empty(L.ns_workspace_bytes(3, rows, cols) // 4 + 1, device=device)
+    print(f"ns dtype={dtype} {rows}x{cols}", flush=True)
+    L.lact_newton_schulz(g, u, ws, dtype=dtype)
+    torch.cuda.synchronize()
+    got = H.to64(u)
+    for i in range(3):
+        ref = O.newton_schulz5(g[i].cpu().numpy().astype(np.float64))
+        assert H.rel(got[i], ref) < tol, (i, H.rel(got[i], ref))
+
+
+@pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
+def test_step_renorm(device, wi):
+    import torch
+    w = small(wi, 64, 64, subset=(0, 64))
+    W, _ = inputs(w)
+    fw = H.make_state(w, W, device)
+    rng = np.random.default_rng(wi)
+    U = [rng.standard_normal((w.bh, w.d, w.dh)).astype(np.float32) * 0.05 for _ in range(3)]
+    u = [torch.from_numpy(x).to(device) for x in U]
+    ws = H.workspace(w, 0, device)
+    L.lact_step_renorm(fw.shape, fw, u[0], u[1], u[2], H.opts_of(w), ws)
+    torch.cuda.synchronize()
+    W1, W3, W2 = H.to64(fw.w1), H.to64(fw.w3), H.to64(fw.w2)
+    for b in range(w.bh):
+        n1, n3, n2 = O.row_norms(W[0][b]), O.row_norms(W[1][b]), O.row_norms(W[2][b])
+        assert H.rel(W1[b], O.step_renorm(W[0][b], U[0][b].T, n1)) < 1e-5
+        assert H.rel(W3[b], O.step_renorm(W[1][b], U[1][b].T, n3)) < 1e-5
+        assert H.rel(W2[b], O.step_renorm(W[2][b], U[2][b], n2)) < 1e-5
+    assert H.rel(H.to64(fw.n1), np.stack([O.row_norms(x) for x in W[0]])) < 1e-6
+
+
+@pytest.mark.parametrize("wi", [0, 1, 3, 4])
+def test_update_twice(device, wi):
+    """Two writes (momentum buffer non-zero on the second) from the same state."""
+    import torch
+    w = small(wi, 2 * 320, 320, subset=(0, 320))
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    k = H.act_to_dev(w, inp, "k", device)
+    v = H.act_to_dev(w, inp, "v", device)
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    mom = torch.from_numpy(inp["mom"]).to(device) if inp["mom"] is not None else None
+    ws = H.workspace(w, 320, device)
+    o = H.opts_of(w)
+    sts = [O.HeadState(W[0][b], W[1][b], W[2][b]) for b in range(w.bh)]
+    for c in range(2):
+        sl = slice(320 * c, 320 * (c + 1))
+        L.lact_update(fw.shape, fw, k[:, sl], v[:, sl], eta[:, sl], eta[:, sl], eta[:, sl],
+                      None if mom is None else mom[:, sl], o, ws)
+        torch.cuda.synchronize()
+        W1, W3, W2, M1, M3, M2 = H.state64(fw)
+        for b in range(w.bh):
+            e = inp["eta"][b, sl]
+            m = None if inp["mom"] is None else inp["mom"][b, sl]
+            # teacher-forced: the oracle step starts from the GPU's W_c
+            ref = O.update(sts[b], inp["k"][b, sl], inp["v"][b, sl], e, e, e, mom=m,
+                           use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+            for name, x, y in (("W1", W1[b], ref.W1), ("W3", W3[b], ref.W3), ("W2", W2[b], ref.W2)):
+                assert H.rel(x, y) < H.TOL[w.dtype], (c, name, b, H.rel(x, y))
+            if w.use_momentum:
+                assert H.rel(M1[b], ref.M1) < H.TOL[w.dtype]
+                assert H.rel(M2[b], ref.M2) < H.TOL[w.dtype]
+            st = H.oracle_state(O, W1[b], W3[b], W2[b], sts[b].n1, sts[b].n3, sts[b].n2,
+                                None if M1 is None else (M1[b], M3[b], M2[b]))
+            sts[b] = st
+
+
+SEQ_CASES = {
+    # workload: (T, chunk, subset)
+    0: (1024, 256, None),
+    1: (4 * 256 + 100, 256, None),
+    2: (1024, 1024, (0, 768)),
+    3: (3 * 512, 512, (256, 256)),
+    4: (3 * 384, 384, None),
+}
+
+
+@pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
+def test_sequence_end_to_end(device, wi):
+    T, C, sub = SEQ_CASES[wi]
+    w = small(wi, T, C, subset=sub)
+    if wi == 0:
+        w = WL.WORKLOADS[0]   # the tiny fp32 workload at its full size
+    W, inp = inputs(w)
+    print(f"sequence wl={wi} T={w.T} C={w.chunk}", flush=True)
+    got, fw = H.run_sequence(w, inp, W, device)
+    W1, W3, W2, *_ = H.state64(fw)
+    for b in range(w.bh):
+        m = None if inp["mom"] is None else inp["mom"][b]
+        e = inp["eta"][b]
+        ref, st = O.sequence(W[0][b], W[1][b], W[2][b], inp["q"][b], inp["k"][b], inp["v"][b], e, e, e,
+                             w.chunk, mom=m, order=w.order, subset=w.subset, update_last=w.update_last,
+                             use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+        assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
+        assert H.rel(W1[b], st.W1) < H.TOL[w.dtype]
+        assert H.rel(W2[b], st.W2) < H.TOL[w.dtype]
