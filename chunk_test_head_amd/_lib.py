@@ -78,6 +78,9 @@ def load():
         "lact_chunk_step": (I32, [pS, pSt, P, L, P, L, P, L, P, L, P, P, P, P, I64, I64, pO, P, SZ, P]),
         "lact_sequence": (I32, [pS, pSt, P, L, P, L, P, L, P, L, P, P, P, P, I64, I64, I64, I32,
                                 I64, I64, I32, pO, P, SZ, P]),
+        "lact_prof_begin": (I32, [I32, I32]),
+        "lact_prof_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(F), ctypes.POINTER(F),
+                                ctypes.POINTER(F)]),
         "lact_status_string": (ctypes.c_char_p, [I32]),
         "lact_last_hip_error": (ctypes.c_int, []),
     }
@@ -166,6 +169,22 @@ class FastWeights:
 
     def ref(self):
         return ctypes.byref(self.struct)
+
+
+PROF_APPLY, PROF_GRAD, PROF_REDUCE, PROF_NS, PROF_STEP = 1, 2, 3, 4, 5
+
+
+def lact_prof_begin(kind, max_launches):
+    _check(load().lact_prof_begin(kind, max_launches), "lact_prof_begin")
+
+
+def lact_prof_end():
+    """-> (launches, total_ms, min_ms, max_ms)"""
+    n = ctypes.c_int32()
+    t, lo, hi = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    _check(load().lact_prof_end(ctypes.byref(n), ctypes.byref(t), ctypes.byref(lo), ctypes.byref(hi)),
+           "lact_prof_end")
+    return n.value, t.value, lo.value, hi.value
 
 
 # ------------------------------------------------------------ entry points --

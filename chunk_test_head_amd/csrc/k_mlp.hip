@@ -74,53 +74,51 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
     for (int tt = 0; tt < NT; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 r1[NV1], r3[NV1], r2[NV2];
-  auto gload = [&](int jb) {
-#pragma unroll
-    for (int x = 0; x < NV1; ++x) {
-      const int vi = tid + x * NTH;  // vector index inside the HB x D block
-      r1[x] = *reinterpret_cast<const uint4*>(w1 + (int64_t)jb * HB * D + (int64_t)vi * V);
-      r3[x] = *reinterpret_cast<const uint4*>(w3 + (int64_t)jb * HB * D + (int64_t)vi * V);
-    }
-#pragma unroll
-    for (int x = 0; x < NV2; ++x) {
-      const int vi = tid + x * NTH;
-      const int row = vi / (HB / V), col = (vi % (HB / V)) * V;
-      r2[x] = *reinterpret_cast<const uint4*>(w2 + (int64_t)row * dh + jb * HB + col);
-    }
-  };
-  auto lstore = [&](int buf) {
-    T* s1 = lds + buf * STAGE;
-    T* s3 = s1 + HB * P1;
-    T* s2 = s3 + HB * P1;
-#pragma unroll
-    for (int x = 0; x < NV1; ++x) {
-      const int vi = tid + x * NTH;
-      const int row = vi / (D / V), col = (vi % (D / V)) * V;
-      *reinterpret_cast<uint4*>(s1 + row * P1 + col) = r1[x];
-      *reinterpret_cast<uint4*>(s3 + row * P1 + col) = r3[x];
-    }
-#pragma unroll
-    for (int x = 0; x < NV2; ++x) {
-      const int vi = tid + x * NTH;
-      const int row = vi / (HB / V), col = (vi % (HB / V)) * V;
-      // P2 rows are 8-byte aligned for bf16: store as two 8-byte halves.
-      uint2* dst = reinterpret_cast<uint2*>(s2 + row * P2 + col);
-      if constexpr (sizeof(T) == 2) {
-        dst[0] = uint2{r2[x].x, r2[x].y};
-        dst[1] = uint2{r2[x].z, r2[x].w};
-      } else {
-        *reinterpret_cast<uint4*>(s2 + row * P2 + col) = r2[x];
-      }
-    }
-  };
+  // stage jb: W1 / W3 rows [jb HB, +HB) (contiguous) and W2 columns (rows of
+  // HB elements at pitch dh), as 16-byte vectors
+#define LACT_APPLY_GLOAD(JB)                                                        \
+  {                                                                                 \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      r1[x] = *reinterpret_cast<const uint4*>(w1 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
+      r3[x] = *reinterpret_cast<const uint4*>(w3 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
+    }                                                                               \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      r2[x] = *reinterpret_cast<const uint4*>(w2 + (int64_t)(vi / (HB / V)) * dh + (JB) * HB + (vi % (HB / V)) * V); \
+    }                                                                               \
+  }
+#define LACT_APPLY_LSTORE(BUF)                                                      \
+  {                                                                                 \
+    T* s1_ = lds + (BUF) * STAGE;                                                   \
+    T* s3_ = s1_ + HB * P1;                                                         \
+    T* s2_ = s3_ + HB * P1;                                                         \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      const int row = vi / (D / V), col = (vi % (D / V)) * V;                       \
+      *reinterpret_cast<uint4*>(s1_ + row * P1 + col) = r1[x];                      \
+      *reinterpret_cast<uint4*>(s3_ + row * P1 + col) = r3[x];                      \
+    }                                                                               \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      const int row = vi / (HB / V), col = (vi % (HB / V)) * V;                     \
+      if constexpr (sizeof(T) == 2) {                                               \
+        uint2* dst = reinterpret_cast<uint2*>(s2_ + row * P2 + col);                \
+        dst[0] = uint2{r2[x].x, r2[x].y};                                           \
+        dst[1] = uint2{r2[x].z, r2[x].w};                                           \
+      } else {                                                                      \
+        *reinterpret_cast<uint4*>(s2_ + row * P2 + col) = r2[x];                    \
+      }                                                                             \
+    }                                                                               \
+  }
 
   const int NB = dh / HB;
-  gload(0);
-  lstore(0);
+  LACT_APPLY_GLOAD(0);
+  LACT_APPLY_LSTORE(0);
   __syncthreads();
   for (int jb = 0; jb < NB; ++jb) {
     const int buf = jb & 1;
-    if (jb + 1 < NB) gload(jb + 1);
+    if (jb + 1 < NB) LACT_APPLY_GLOAD(jb + 1);
     const T* s1 = lds + buf * STAGE;
     const T* s3 = s1 + HB * P1;
     const T* s2 = s3 + HB * P1;
@@ -154,8 +152,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p0 = P[0][tt][i], p1 = P[1][tt][i];
-        hf[tt][i] = to_t<T>(p0 * sigmoidf_(p0) * U[0][tt][i]);
-        hf[tt][4 + i] = to_t<T>(p1 * sigmoidf_(p1) * U[1][tt][i]);
+        hf[tt][i] = to_t<T>(p0 * sigmoid_fast(p0) * U[0][tt][i]);
+        hf[tt][4 + i] = to_t<T>(p1 * sigmoid_fast(p1) * U[1][tt][i]);
       }
     // o^T[feature][token] += W2[:, block] h^T
 #pragma unroll
@@ -165,9 +163,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
     }
-    if (jb + 1 < NB) lstore(buf ^ 1);
+    if (jb + 1 < NB) LACT_APPLY_LSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef LACT_APPLY_GLOAD
+#undef LACT_APPLY_LSTORE
 
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
@@ -363,6 +363,196 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
     }
 }
 
+// ----------------------------------------------------- gradient, bf16 --
+// bf16 operands.  One workgroup = WAVES waves x 16 hidden units each (one MFMA
+// column tile), over one token split of one head.  Per wave, for the whole
+// token loop: its W1 / W3 / W2^T rows as B fragments (K = d) and the fp32
+// accumulators of G1^T, G3^T, G2 (d x 16).  Token tiles of 32 are staged once
+// in LDS, row-major and double buffered (the next tile's global loads are in
+// flight while the current one is computed).  The forward contractions read
+// k / v rows (K = d); the gradient contractions read k^T / v^T fragments
+// (K = tokens) from the same tiles with LDS transpose reads.
+// Tile layout: row r (token), 16-byte chunk q of the row stored at chunk
+// q ^ s(r), s(r) = 2 (r % 4) + (r / 4) % 2 (within each 128-byte window).
+// Eight consecutive rows then put one chunk in eight distinct bank groups
+// (row reads of the forward contractions), and four consecutive rows put two
+// adjacent chunks in eight distinct bank groups (transpose reads).
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  const int s = ((r & 3) << 1) | ((r >> 2) & 1);
+  return r * D + (((col >> 3) ^ s) << 3) + (col & 7);
+}
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
+  constexpr int NTH = WAVES * 64;
+  constexpr int NT = 32;
+  constexpr int KS = D / 32;
+  constexpr int IT = D / 16;
+  constexpr int TILE = NT * D;             // one k or v tile (no padding: swizzled)
+  constexpr int NV = NT * D / 8;           // 16-byte vectors per tile
+  constexpr int VPT = (NV + NTH - 1) / NTH;
+  static_assert(NV % NTH == 0 || NTH % NV == 0, "tile split");
+
+  __shared__ __attribute__((aligned(16))) bf16 sKV[2][2 * TILE];
+  __shared__ float sEta[2][3][NT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int hblocks = (a.dh + WAVES * 16 - 1) / (WAVES * 16);
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int hb = lid % hblocks;
+  const int rest = lid / hblocks;
+  const int split = rest % a.nsplit;
+  const int head = rest / a.nsplit;
+  if (head >= a.bh) return;
+  const int64_t s0 = (int64_t)split * a.split_len;
+  const int64_t s1 = (s0 + a.split_len < a.n_tok) ? s0 + a.split_len : a.n_tok;
+  const int j0 = hb * WAVES * 16 + wave * 16;
+  const bool active = j0 < a.dh;
+
+  const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (int64_t)head * a.k_sbh;
+  const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (int64_t)head * a.v_sbh;
+  const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh;
+  const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh;
+  const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
+  const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+
+  // W B fragments: lane holds W[j0 + c][32 ks + 8 g ..]
+  bf16x8 b1[KS], b3[KS], b2[KS];
+  {
+    const int64_t row = (int64_t)(active ? j0 + c : c) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      b1[ks] = ld8(sb + a.sh.off_w1 + row + 32 * ks);
+      b3[ks] = ld8(sb + a.sh.off_w3 + row + 32 * ks);
+      b2[ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
+    }
+  }
+  f32x4 G1[IT], G3[IT], G2[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    G1[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    G3[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    G2[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // staging: thread tid moves 16-byte vectors vi = tid + x NTH of the k and v
+  // tiles (row vi / (D/8), chunk vi % (D/8)) and, for tid < 3 NT, one eta
+  const float* ep = tid < NT ? e1 : (tid < 2 * NT ? e3 : e2);
+  const int er = tid % NT;
+  uint4 rk[VPT], rv[VPT];
+  float re = 0.f;
+#define LACT_GRAD_GLOAD(T0)                                                         \
+  {                                                                                 \
+    _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      const int64_t t = (T0) + vi / (D / 8);                                        \
+      rk[x] = uint4{0u, 0u, 0u, 0u};                                                \
+      rv[x] = uint4{0u, 0u, 0u, 0u};                                                \
+      if (vi < NV && t < s1) {                                                      \
+        rk[x] = *reinterpret_cast<const uint4*>(kp + t * a.k_st + (vi % (D / 8)) * 8); \
+        rv[x] = *reinterpret_cast<const uint4*>(vp + t * a.v_st + (vi % (D / 8)) * 8); \
+      }                                                                             \
+    }                                                                               \
+    if (tid < 3 * NT) re = ((T0) + er < s1) ? ep[(T0) + er] : 0.f;                  \
+  }
+#define LACT_GRAD_LSTORE(BUF)                                                       \
+  {                                                                                 \
+    bf16* sK_ = sKV[BUF];                                                           \
+    _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      if (vi < NV) {                                                                \
+        const int o = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                     \
+        *reinterpret_cast<uint4*>(sK_ + o) = rk[x];                                 \
+        *reinterpret_cast<uint4*>(sK_ + TILE + o) = rv[x];                          \
+      }                                                                             \
+    }                                                                               \
+    if (tid < 3 * NT) sEta[BUF][tid / NT][er] = re;                                 \
+  }
+
+  int buf = 0;
+  if (s0 < s1) {
+    LACT_GRAD_GLOAD(s0);
+    LACT_GRAD_LSTORE(0);
+  }
+  __syncthreads();
+  for (int64_t t0 = s0; t0 < s1; t0 += NT) {
+    const bool more = t0 + NT < s1;
+    if (more) LACT_GRAD_GLOAD(t0 + NT);
+    if (active) {
+      const bf16* sK = sKV[buf];
+      const bf16* sV = sK + TILE;
+      // ---- forward on keys / back-prop of v: tokens x 16 hidden ----
+      f32x4 P[2], U[2], E[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        E[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bf16x8 ak = ld8(sK + swz<D>(16 * tt + c, 32 * ks + 8 * g));
+          const bf16x8 av = ld8(sV + swz<D>(16 * tt + c, 32 * ks + 8 * g));
+          mma(P[tt], ak, b1[ks]);
+          mma(U[tt], ak, b3[ks]);
+          mma(E[tt], av, b2[ks]);
+        }
+      // ---- SwiGLU backward + eta: B operands, K = 32 tokens (kappa order) ----
+      bf16x8 fh, fu, fg;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[buf][0][16 * tt + 4 * g]);
+        const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[buf][1][16 * tt + 4 * g]);
+        const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[buf][2][16 * tt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
+          const float sg = sigmoid_fast(p);
+          const float sl = p * sg;
+          const float dsl = sg * __builtin_fmaf(p, 1.f - sg, 1.f);
+          fh[4 * tt + i] = (bf16)(n2[i] * sl * u);
+          fu[4 * tt + i] = (bf16)(n3[i] * e * sl);
+          fg[4 * tt + i] = (bf16)(n1[i] * e * u * dsl);
+        }
+      }
+      // ---- gradient contractions over the tile's tokens ----
+      // lane j of each 16-lane group reads token row 4g + j/4 (+16),
+      // features 16 it + 4 (j%4): transposed, that is the A fragment with
+      // tokens in kappa order.
+      const int tr = 4 * g + (c >> 2);
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int fc = 16 * it + 4 * (c & 3);
+        const bf16x8 akt = cat8(ld_tr4(sK + swz<D>(tr, fc)), ld_tr4(sK + swz<D>(tr + 16, fc)));
+        const bf16x8 avt = cat8(ld_tr4(sV + swz<D>(tr, fc)), ld_tr4(sV + swz<D>(tr + 16, fc)));
+        mma(G1[it], akt, fg);
+        mma(G3[it], akt, fu);
+        mma(G2[it], avt, fh);
+      }
+    }
+    if (more) LACT_GRAD_LSTORE(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#undef LACT_GRAD_GLOAD
+#undef LACT_GRAD_LSTORE
+  if (!active) return;
+
+  // ---- partials, [split][head][3][dh][d]: lane holds 4 consecutive d ----
+  const int64_t mat = (int64_t)a.dh * D;
+  float* out = a.partial + ((int64_t)split * a.bh + head) * 3 * mat + (int64_t)(j0 + c) * D + 4 * g;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    st4(out + 16 * it, G1[it][0], G1[it][1], G1[it][2], G1[it][3]);
+    st4(out + mat + 16 * it, G3[it][0], G3[it][1], G3[it][2], G3[it][3]);
+    st4(out + 2 * mat + 16 * it, G2[it][0], G2[it][1], G2[it][2], G2[it][3]);
+  }
+}
+
 // --------------------------------------------------------------- launch --
 template <class T, int D, int NTW, int WAVES>
 static hipError_t run_apply(const ApplyArgs& a, hipStream_t s) {
@@ -390,9 +580,17 @@ hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
 }
 
 int grad_hidden_per_block(int dtype, int d) {
-  // WAVES * JW; JW * d = 4096 (bf16) / 2048 (fp32) keeps registers bounded.
-  if (dtype == 1) return 4 * (d == 64 ? 64 : d == 128 ? 32 : 16);
+  if (dtype == 1) return 16 * (d == 256 ? 4 : 8);   // k_grad_bf16: WAVES x 16
   return 4 * (d == 64 ? 32 : 16);
+}
+
+template <int D, int WAVES>
+static hipError_t run_grad_bf16(const GradArgs& a, hipStream_t s) {
+  const int hblocks = (a.dh + WAVES * 16 - 1) / (WAVES * 16);
+  const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_grad_bf16<D, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  return hipGetLastError();
 }
 
 template <class T, int D, int JW, int WAVES>
@@ -407,9 +605,9 @@ static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
   if (dtype == 1) {
     switch (a.d) {
-      case 64: return run_grad<bf16, 64, 64, 4>(a, s);
-      case 128: return run_grad<bf16, 128, 32, 4>(a, s);
-      case 256: return run_grad<bf16, 256, 16, 4>(a, s);
+      case 64: return run_grad_bf16<64, 8>(a, s);
+      case 128: return run_grad_bf16<128, 8>(a, s);
+      case 256: return run_grad_bf16<256, 4>(a, s);
     }
   } else {
     switch (a.d) {

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/lact.h"
 #include "lact_internal.hpp"
 
@@ -18,6 +20,29 @@ static lact_status hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
   return LACT_ERR_HIP;
 }
+
+// ------------------------------------------------------------ profiling --
+struct Prof {
+  int kind = 0;
+  int cap = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev;
+};
+static Prof g_prof;
+
+struct ProfScope {
+  bool on;
+  hipStream_t s;
+  ProfScope(int kind, hipStream_t st) : on(g_prof.kind == kind && g_prof.n < g_prof.cap), s(st) {
+    if (on) hipEventRecord(g_prof.ev[2 * g_prof.n], s);
+  }
+  ~ProfScope() {
+    if (on) {
+      hipEventRecord(g_prof.ev[2 * g_prof.n + 1], s);
+      ++g_prof.n;
+    }
+  }
+};
 
 Shadow make_shadow(void* base, int d, int dh) {
   Shadow s;
@@ -86,7 +111,8 @@ static int choose_nsplit(const lact_shape* sh, int64_t n_tok) {
   const int hpb = grad_hidden_per_block(sh->dtype, sh->d);
   const int64_t hblocks = (sh->dh + hpb - 1) / hpb;
   const int64_t base = (int64_t)sh->bh * hblocks;
-  int64_t ns = (512 + base - 1) / base;
+  // one resident workgroup per CU: aim at 256 workgroups in all
+  int64_t ns = (256 + base - 1) / base;
   const int64_t cap = (n_tok + 255) / 256;
   if (ns > cap) ns = cap;
   if (ns < 1) ns = 1;
@@ -144,8 +170,10 @@ static int64_t ns_ws_bytes(int count, int rows, int cols) {
 static hipError_t run_ns(int dtype, int count, int rows, int cols, const float* g, float* u,
                          float eps, float* xa, float* xb, float* am, float* bm, hipStream_t s) {
   const int64_t m = (int64_t)rows * cols;
+  hipError_t e = launch_ns_fused(dtype, count, rows, cols, g, u, eps, s);
+  if (e != hipErrorNotSupported) return e;
   NsNormArgs na{g, xa, count, m, eps};
-  hipError_t e = launch_ns_norm(na, s);
+  e = launch_ns_norm(na, s);
   if (e != hipSuccess) return e;
   float* x = xa;
   float* y = xb;
@@ -179,7 +207,11 @@ static lact_status do_apply(const lact_shape* sh, const lact_state* st, const vo
   a.o = o; a.o_sbh = ol.stride_bh; a.o_st = ol.stride_tok;
   a.sh = make_shadow(st->shadow, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh; a.n_tok = n_tok;
-  hipError_t e = launch_apply(sh->dtype, a, s);
+  hipError_t e;
+  {
+    ProfScope p(LACT_PROF_APPLY, s);
+    e = launch_apply(sh->dtype, a, s);
+  }
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
@@ -199,10 +231,17 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
   sl = (sl + 31) / 32 * 32;
   a.split_len = sl > 0 ? sl : 32;
   a.partial = w.partial;
-  hipError_t e = launch_grad(sh->dtype, a, s);
+  hipError_t e;
+  {
+    ProfScope p(LACT_PROF_GRAD, s);
+    e = launch_grad(sh->dtype, a, s);
+  }
   if (e != hipSuccess) return hip_fail(e);
   ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
-  e = launch_reduce(r, s);
+  {
+    ProfScope p(LACT_PROF_REDUCE, s);
+    e = launch_reduce(r, s);
+  }
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
@@ -217,7 +256,11 @@ static lact_status do_step(const lact_shape* sh, const lact_state* st, const flo
   a.sh = make_shadow(st->shadow, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
   a.renorm = renorm; a.eps = eps; a.write_w = 1;
-  hipError_t e = launch_step(sh->dtype, a, s);
+  hipError_t e;
+  {
+    ProfScope p(LACT_PROF_STEP, s);
+    e = launch_step(sh->dtype, a, s);
+  }
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
@@ -243,6 +286,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                           op->use_momentum ? st->m2 : nullptr, s);
   if (r != LACT_OK) return r;
   if (op->use_muon) {
+    ProfScope p(LACT_PROF_NS, s);
     hipError_t e = run_ns(sh->dtype, 3 * sh->bh, sh->d, sh->dh, w.g, w.g, op->ns_eps, w.xa, w.xb,
                           w.amat, w.bmat, s);
     if (e != hipSuccess) return hip_fail(e);
@@ -472,6 +516,52 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
     if (order == LACT_APPLY_THEN_UPDATE && (r = upd()) != LACT_OK) return r;
   }
   return LACT_OK;
+}
+
+lact_status lact_prof_begin(int32_t kind, int32_t max_launches) {
+  if (kind < LACT_PROF_APPLY || kind > LACT_PROF_STEP || max_launches < 1) return LACT_ERR_INVALID_ARG;
+  if (g_prof.kind != 0) return LACT_ERR_INVALID_ARG;
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : g_prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (auto& x : g_prof.ev)
+        if (x) hipEventDestroy(x);
+      g_prof.ev.clear();
+      return hip_fail(r);
+    }
+  }
+  g_prof.kind = kind;
+  g_prof.cap = max_launches;
+  g_prof.n = 0;
+  return LACT_OK;
+}
+
+lact_status lact_prof_end(int32_t* launches, float* total_ms, float* min_ms, float* max_ms) {
+  if (g_prof.kind == 0) return LACT_ERR_INVALID_ARG;
+  float tot = 0.f, mn = 0.f, mx = 0.f;
+  lact_status st = LACT_OK;
+  for (int i = 0; i < g_prof.n; ++i) {
+    hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    float ms = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      st = hip_fail(r);
+      break;
+    }
+    tot += ms;
+    mn = (i == 0 || ms < mn) ? ms : mn;
+    mx = (i == 0 || ms > mx) ? ms : mx;
+  }
+  if (launches) *launches = g_prof.n;
+  if (total_ms) *total_ms = tot;
+  if (min_ms) *min_ms = mn;
+  if (max_ms) *max_ms = mx;
+  for (auto& e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.kind = 0;
+  g_prof.n = g_prof.cap = 0;
+  return st;
 }
 
 const char* lact_status_string(lact_status st) {

@@ -83,6 +83,8 @@ int grad_hidden_per_block(int dtype, int d);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_beta(const BetaArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, const float* g, float* u,
+                           float eps, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
 hipError_t launch_row_norms(const StepArgs& a, hipStream_t s);

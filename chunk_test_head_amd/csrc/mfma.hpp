@@ -68,6 +68,23 @@ __device__ __forceinline__ f32x8 ld4x2(const float* p0, const float* p1) {
   return r;
 }
 
+// LDS transpose read (ds_read_b64_tr_b16), per 16-lane group: lane j gives
+// the address of 4 consecutive 16-bit elements of row j/4 (columns
+// 4 (j%4) .. +3) of a 4 x 16 block; lane i receives column i of the 4 rows.
+// Stored N-contiguous, this is the K-per-lane MFMA fragment layout.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 ld_tr4(const bf16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 template <class T> __device__ __forceinline__ T to_t(float x);
 template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
@@ -88,6 +105,10 @@ __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8).  Renumber them so
 // that each XCD runs one contiguous range of logical ids: neighbouring tiles

@@ -193,6 +193,20 @@ lact_status lact_sequence(const lact_shape* shape, const lact_state* state,
                           int32_t update_last, const lact_update_opts* opts,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernel timing for benchmarks.  lact_prof_begin(kind, max_launches)
+ * creates 2 * max_launches HIP events; until lact_prof_end, every launch of
+ * the kernel `kind` made by the calls above is bracketed by events recorded
+ * on the stream it runs on (at most max_launches).  lact_prof_end waits for
+ * the events, returns the number of bracketed launches and the total, min and
+ * max duration in milliseconds, and destroys the events.  Not for use under
+ * graph capture; one profiling window per process at a time.
+ * kinds: 1 apply (k_apply), 2 gradient (k_grad), 3 split reduction,
+ *        4 Newton-Schulz (whole iteration per write), 5 step + renorm. */
+enum { LACT_PROF_APPLY = 1, LACT_PROF_GRAD = 2, LACT_PROF_REDUCE = 3, LACT_PROF_NS = 4,
+       LACT_PROF_STEP = 5 };
+lact_status lact_prof_begin(int32_t kind, int32_t max_launches);
+lact_status lact_prof_end(int32_t* launches, float* total_ms, float* min_ms, float* max_ms);
+
 const char* lact_status_string(lact_status status);
 
 /* hipError_t of the last failed HIP call on this thread (0 if none). */
