@@ -567,7 +567,7 @@ hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
   if (dtype == 1) {
     switch (a.d) {
       case 64: return run_apply<bf16, 64, 64, 4>(a, s);
-      case 128: return run_apply<bf16, 128, 64, 4>(a, s);
+      case 128: return run_apply<bf16, 128, 32, 8>(a, s);
       case 256: return run_apply<bf16, 256, 32, 4>(a, s);
     }
   } else {
