@@ -38,7 +38,7 @@ class Layout(ctypes.Structure):
 class UpdateOpts(ctypes.Structure):
     _fields_ = [("use_muon", ctypes.c_int32), ("use_momentum", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("renorm_eps", ctypes.c_float),
-                ("ns_eps", ctypes.c_float)]
+                ("ns_eps", ctypes.c_float), ("ns_fp32", ctypes.c_int32)]
 
 
 class LactError(RuntimeError):
@@ -127,8 +127,8 @@ def layout_of(t):
     return Layout(t.stride(0), t.stride(1))
 
 
-def opts(use_muon=False, use_momentum=False, renorm=True, renorm_eps=1e-5, ns_eps=1e-7):
-    return UpdateOpts(int(use_muon), int(use_momentum), int(renorm), renorm_eps, ns_eps)
+def opts(use_muon=False, use_momentum=False, renorm=True, renorm_eps=1e-5, ns_eps=1e-7, ns_fp32=False):
+    return UpdateOpts(int(use_muon), int(use_momentum), int(renorm), renorm_eps, ns_eps, int(ns_fp32))
 
 
 def shadow_bytes(shape):

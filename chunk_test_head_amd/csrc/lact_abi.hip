@@ -101,6 +101,7 @@ static lact_status check_act(const lact_shape* sh, const void* p, lact_layout l,
 static lact_status check_opts(const lact_update_opts* o) {
   if (o == nullptr) return LACT_ERR_INVALID_ARG;
   if (!(o->renorm_eps >= 0.f) || !(o->ns_eps >= 0.f)) return LACT_ERR_INVALID_ARG;
+  if (o->ns_fp32 != 0 && o->ns_fp32 != 1) return LACT_ERR_INVALID_ARG;
   return LACT_OK;
 }
 
@@ -287,7 +288,8 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   if (r != LACT_OK) return r;
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
-    hipError_t e = run_ns(sh->dtype, 3 * sh->bh, sh->d, sh->dh, w.g, w.g, op->ns_eps, w.xa, w.xb,
+    hipError_t e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, w.g, w.g,
+                          op->ns_eps, w.xa, w.xb,
                           w.amat, w.bmat, s);
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -171,18 +171,20 @@ def weights(w: Workload):
     return W1, W3, W2
 
 
-def tokens(w: Workload, threads: int = 8):
+def tokens(w: Workload, threads: int = 8, values: bool = True):
     """q, k, v as [bh, T, d] arrays (float32 values; for bf16 workloads also
     the uint16 bit patterns), eta [bh, T] and momentum [bh, T] (or None).
 
     Returns a dict: q, k, v (float32 values, already bf16-representable for
     bf16 workloads), q_bits/k_bits/v_bits (uint16, bf16 workloads only),
-    eta, mom.
+    eta, mom.  values=False (bf16 workloads only) skips the float32 copies;
+    token_values() widens any token range of the bits on demand.
     """
     bounds = w.chunk_bounds()
     out = {}
     for name, tid in (("q", TID_Q), ("k", TID_K), ("v", TID_V)):
-        arr = np.empty((w.bh, w.T, w.d), dtype=np.float32)
+        keep = values or w.dtype != "bf16"
+        arr = np.empty((w.bh, w.T, w.d), dtype=np.float32) if keep else None
         bits = np.empty((w.bh, w.T, w.d), dtype=np.uint16) if w.dtype == "bf16" else None
 
         def fill(args, tid=tid, arr=arr, bits=bits):
@@ -191,13 +193,15 @@ def tokens(w: Workload, threads: int = 8):
             if bits is not None:
                 b = round_to_bf16_bits(x)
                 bits[:, s:e] = b
-                arr[:, s:e] = bf16_bits_to_f32(b)
+                if arr is not None:
+                    arr[:, s:e] = bf16_bits_to_f32(b)
             else:
                 arr[:, s:e] = x
 
         with ThreadPoolExecutor(max(1, threads)) as ex:
             list(ex.map(fill, list(enumerate(bounds))))
-        out[name] = arr
+        if arr is not None:
+            out[name] = arr
         if bits is not None:
             out[name + "_bits"] = bits
     eta = np.empty((w.bh, w.T), dtype=np.float32)
@@ -206,6 +210,14 @@ def tokens(w: Workload, threads: int = 8):
     out["eta"] = eta
     out["mom"] = np.full((w.bh, w.T), w.momentum, dtype=np.float32) if w.use_momentum else None
     return out
+
+
+def token_values(inp, name, b, s, e):
+    """float32 values of tokens [s, e) of head b (from the bf16 bits when the
+    float32 copy was not kept)."""
+    if name in inp:
+        return inp[name][b, s:e]
+    return bf16_bits_to_f32(inp[name + "_bits"][b, s:e])
 
 
 def get(index_or_name):

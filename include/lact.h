@@ -90,6 +90,9 @@ typedef struct {
   int32_t renorm;        /* rescale rows to their sequence-start norms       */
   float renorm_eps;      /* added to the row norm (page: 1e-5)               */
   float ns_eps;          /* added to the Frobenius norm (page: 1e-7)         */
+  int32_t ns_fp32;       /* 0: Newton-Schulz products on bf16 operands, as
+                            the page (X stays fp32 between steps);
+                            1: fp32 operands (slower, for precision)         */
 } lact_update_opts;
 
 /* Bytes of lact_state.shadow for this shape. */
