@@ -32,7 +32,39 @@ def parse():
     p.add_argument("--workload", default="lm-causal")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=8, help="heads of the oracle sample")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES (counter calibration)")
     return p.parse_args()
+
+
+def copy_probe(nbytes):
+    """A plain device-to-device copy of a known size, to calibrate the
+    FETCH_SIZE / WRITE_SIZE counters against a kernel whose traffic is
+    known exactly (nbytes read, nbytes written)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def measured_traffic(kernel_src, workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    profile (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when the
+    profile is for another workload or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_grad_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        return rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, W, inp, heads):
@@ -66,6 +98,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import numpy as np
     import torch
 
@@ -158,7 +193,8 @@ def main():
         "pct_of_peak": 100.0 * tflops / peak,
         "tflops_page_convention": WL.page_convention_flops(w) / (ms_per_step * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": "k_grad", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic("k_mlp.hip", w.name),
                      "launch_ms_avg": grad_avg_ms, "launch_ms_min": grad_min,
                      "launch_ms_max": grad_max, "launches": launches,
                      "flops_per_launch": grad_flops},
