@@ -383,7 +383,7 @@ __device__ __forceinline__ int swz(int r, int col) {
   return r * D + (((col >> 3) ^ s) << 3) + (col & 7);
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, bool PIPE>
 __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int NTH = WAVES * 64;
   constexpr int NT = 32;
@@ -394,8 +394,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int VPT = (NV + NTH - 1) / NTH;
   static_assert(NV % NTH == 0 || NTH % NV == 0, "tile split");
 
-  __shared__ __attribute__((aligned(16))) bf16 sKV[2][2 * TILE];
-  __shared__ float sEta[2][3][NT];
+  // PIPE: tiles n-1 (read), n (read), n+1 (written); else n (read), n+1 (written)
+  constexpr int NBUF = PIPE ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF][2 * TILE];
+  __shared__ float sEta[NBUF][3][NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -471,73 +473,106 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
     if (tid < 3 * NT) sEta[BUF][tid / NT][er] = re;                                 \
   }
 
-  int buf = 0;
-  if (s0 < s1) {
+  // PIPE: software pipeline over token tiles: iteration n runs the forward
+  // contractions of tile n and the gradient contractions of tile n-1 (both
+  // MFMA, independent of each other), and the SwiGLU backward of tile n (VALU)
+  // can issue while those MFMAs run.  It needs more live registers, so it is
+  // used where it pays (d = 256).
+#define LACT_GRAD_FWD(BUF)                                                          \
+  {                                                                                 \
+    const bf16* sK_ = sKV[BUF];                                                     \
+    const bf16* sV_ = sK_ + TILE;                                                   \
+    _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                              \
+      P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                            \
+      U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                            \
+      E[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                            \
+    }                                                                               \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
+      _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                            \
+        const bf16x8 ak = ld8(sK_ + swz<D>(16 * tt + c, 32 * ks + 8 * g));           \
+        const bf16x8 av = ld8(sV_ + swz<D>(16 * tt + c, 32 * ks + 8 * g));           \
+        mma(P[tt], ak, b1[ks]);                                                     \
+        mma(U[tt], ak, b3[ks]);                                                     \
+        mma(E[tt], av, b2[ks]);                                                     \
+      }                                                                             \
+  }
+  // SwiGLU backward + eta, packed as B operands (K = 32 tokens, kappa order)
+#define LACT_GRAD_EW(BUF)                                                           \
+  {                                                                                 \
+    _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                              \
+      const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[BUF][0][16 * tt + 4 * g]); \
+      const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[BUF][1][16 * tt + 4 * g]); \
+      const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[BUF][2][16 * tt + 4 * g]); \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                               \
+        const float p = P[tt][i], u = U[tt][i], e = E[tt][i];                       \
+        const float sg = sigmoid_fast(p);                                           \
+        const float sl = p * sg;                                                    \
+        const float dsl = sg * __builtin_fmaf(p, 1.f - sg, 1.f);                    \
+        fh[4 * tt + i] = (bf16)(n2[i] * sl * u);                                    \
+        fu[4 * tt + i] = (bf16)(n3[i] * e * sl);                                    \
+        fg[4 * tt + i] = (bf16)(n1[i] * e * u * dsl);                               \
+      }                                                                             \
+    }                                                                               \
+  }
+  // gradient contractions: lane j of each 16-lane group reads token row
+  // 4g + j/4 (+16), features 16 it + 4 (j%4); transposed, that is the A
+  // fragment with tokens in kappa order.
+#define LACT_GRAD_GG(BUF)                                                           \
+  {                                                                                 \
+    const bf16* sK_ = sKV[BUF];                                                     \
+    const bf16* sV_ = sK_ + TILE;                                                   \
+    const int tr = 4 * g + (c >> 2);                                                \
+    _Pragma("unroll") for (int it = 0; it < IT; ++it) {                             \
+      const int fc = 16 * it + 4 * (c & 3);                                         \
+      const bf16x8 akt = cat8(ld_tr4(sK_ + swz<D>(tr, fc)), ld_tr4(sK_ + swz<D>(tr + 16, fc))); \
+      const bf16x8 avt = cat8(ld_tr4(sV_ + swz<D>(tr, fc)), ld_tr4(sV_ + swz<D>(tr + 16, fc))); \
+      mma(G1[it], akt, fg);                                                         \
+      mma(G3[it], akt, fu);                                                         \
+      mma(G2[it], avt, fh);                                                         \
+    }                                                                               \
+  }
+
+  const int ntile = s0 < s1 ? (int)((s1 - s0 + NT - 1) / NT) : 0;
+  f32x4 P[2], U[2], E[2];
+  bf16x8 fh, fu, fg;
+  if (ntile > 0) {
     LACT_GRAD_GLOAD(s0);
     LACT_GRAD_LSTORE(0);
   }
   __syncthreads();
-  for (int64_t t0 = s0; t0 < s1; t0 += NT) {
-    const bool more = t0 + NT < s1;
-    if (more) LACT_GRAD_GLOAD(t0 + NT);
+  int n0 = 0;
+  if (PIPE && ntile > 0) {
+    // tile 0: forward + backward only
+    if (ntile > 1) LACT_GRAD_GLOAD(s0 + NT);
     if (active) {
-      const bf16* sK = sKV[buf];
-      const bf16* sV = sK + TILE;
-      // ---- forward on keys / back-prop of v: tokens x 16 hidden ----
-      f32x4 P[2], U[2], E[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        E[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 ak = ld8(sK + swz<D>(16 * tt + c, 32 * ks + 8 * g));
-          const bf16x8 av = ld8(sV + swz<D>(16 * tt + c, 32 * ks + 8 * g));
-          mma(P[tt], ak, b1[ks]);
-          mma(U[tt], ak, b3[ks]);
-          mma(E[tt], av, b2[ks]);
-        }
-      // ---- SwiGLU backward + eta: B operands, K = 32 tokens (kappa order) ----
-      bf16x8 fh, fu, fg;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[buf][0][16 * tt + 4 * g]);
-        const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[buf][1][16 * tt + 4 * g]);
-        const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[buf][2][16 * tt + 4 * g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
-          const float sg = sigmoid_fast(p);
-          const float sl = p * sg;
-          const float dsl = sg * __builtin_fmaf(p, 1.f - sg, 1.f);
-          fh[4 * tt + i] = (bf16)(n2[i] * sl * u);
-          fu[4 * tt + i] = (bf16)(n3[i] * e * sl);
-          fg[4 * tt + i] = (bf16)(n1[i] * e * u * dsl);
-        }
-      }
-      // ---- gradient contractions over the tile's tokens ----
-      // lane j of each 16-lane group reads token row 4g + j/4 (+16),
-      // features 16 it + 4 (j%4): transposed, that is the A fragment with
-      // tokens in kappa order.
-      const int tr = 4 * g + (c >> 2);
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int fc = 16 * it + 4 * (c & 3);
-        const bf16x8 akt = cat8(ld_tr4(sK + swz<D>(tr, fc)), ld_tr4(sK + swz<D>(tr + 16, fc)));
-        const bf16x8 avt = cat8(ld_tr4(sV + swz<D>(tr, fc)), ld_tr4(sV + swz<D>(tr + 16, fc)));
-        mma(G1[it], akt, fg);
-        mma(G3[it], akt, fu);
-        mma(G2[it], avt, fh);
+      LACT_GRAD_FWD(0);
+      LACT_GRAD_EW(0);
+    }
+    if (ntile > 1) LACT_GRAD_LSTORE(1);
+    __syncthreads();
+    n0 = 1;
+  }
+  for (int n = n0; n < ntile; ++n) {
+    const int cur = n % NBUF, prev = (n + NBUF - 1) % NBUF, nxt = (n + 1) % NBUF;
+    const bool more = n + 1 < ntile;
+    if (more) LACT_GRAD_GLOAD(s0 + (int64_t)(n + 1) * NT);
+    if (active) {
+      LACT_GRAD_FWD(cur);
+      if constexpr (PIPE) {
+        LACT_GRAD_GG(prev);   // reads fh/fu/fg of tile n-1 ...
+        LACT_GRAD_EW(cur);    // ... before they are replaced by tile n's
+      } else {
+        LACT_GRAD_EW(cur);
+        LACT_GRAD_GG(cur);
       }
     }
-    if (more) LACT_GRAD_LSTORE(buf ^ 1);
+    if (more) LACT_GRAD_LSTORE(nxt);  // slot of tile n-2, consumed last iteration
     __syncthreads();
-    buf ^= 1;
   }
+  if (PIPE && ntile > 0 && active) LACT_GRAD_GG((ntile - 1) % NBUF);
+#undef LACT_GRAD_FWD
+#undef LACT_GRAD_EW
+#undef LACT_GRAD_GG
 #undef LACT_GRAD_GLOAD
 #undef LACT_GRAD_LSTORE
   if (!active) return;
@@ -584,12 +619,12 @@ int grad_hidden_per_block(int dtype, int d) {
   return 4 * (d == 64 ? 32 : 16);
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, bool PIPE>
 static hipError_t run_grad_bf16(const GradArgs& a, hipStream_t s) {
   const int hblocks = (a.dh + WAVES * 16 - 1) / (WAVES * 16);
   const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_grad_bf16<D, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_grad_bf16<D, WAVES, PIPE>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -605,9 +640,9 @@ static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
   if (dtype == 1) {
     switch (a.d) {
-      case 64: return run_grad_bf16<64, 8>(a, s);
-      case 128: return run_grad_bf16<128, 8>(a, s);
-      case 256: return run_grad_bf16<256, 4>(a, s);
+      case 64: return run_grad_bf16<64, 8, false>(a, s);
+      case 128: return run_grad_bf16<128, 8, false>(a, s);
+      case 256: return run_grad_bf16<256, 4, true>(a, s);
     }
   } else {
     switch (a.d) {
