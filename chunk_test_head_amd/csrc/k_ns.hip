@@ -268,6 +268,286 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(const float* g, float* u, 
   step(4, true);
 }
 
+// ---------------------------------------------------------------------------
+// Newton-Schulz-5 for 128-row matrices (d = 128): one workgroup of 8 waves per
+// matrix, the fp32 iterate in registers, everything else in LDS:
+//   sX [128][COLS] bf16  operand copy of the iterate (row-major)
+//   sA [128][128]  bf16  A = X X^T, then B (in place)
+// i.e. 160 KiB for COLS = 512.
+//
+// The iterate is kept rescaled, Y_k = X_k / P_k with P_k = a_0 ... a_{k-1}:
+//   A_k = P_k^2 Y Y^T,  B'_k = (b A_k + c A_k A_k) / a_k,  Y <- Y + B'_k Y
+// which is the same quintic step (X_{k+1} = a X + B X = P_{k+1} Y_{k+1})
+// with the fp32 term a X kept exact and no rescaling of the registers;
+// X_5 = P_5 Y_5 on the way out.  Products take bf16 operands and accumulate
+// in fp32.
+//
+// Per step:
+//   1. A (symmetric): wave w takes the 64 x 32 block of rows 64 (w / 4)..,
+//      columns 32 (w % 4)..; the two blocks below the diagonal (waves 4, 5)
+//      are not computed.  Every tile is stored transposed (8-byte stores),
+//      which for a symmetric result is the tile at the mirrored position;
+//      waves 2 and 3 (blocks above the diagonal) also store their tiles in
+//      place (2-byte stores), so all of A is written.
+//   2. A A the same way, then (after every read of A) B' = p A + q A A over
+//      A, with A read back from the wave's own transposed tiles.
+//   3. Y <- Y + B' Y: wave w owns columns [w COLS/8, (w+1) COLS/8) and forms
+//      their tiles of (B' Y)^T = Y^T B' (B' symmetric): lane (c, g) holds
+//      Y[16 nt + c][col0 + 16 mt + 4 g + i], four consecutive columns of one
+//      row, so global loads/stores and the bf16 copy to sX are 16 / 8-byte
+//      vectors.  The Y^T fragments are transpose reads of sX.
+// LDS rows are split into 16-byte chunks whose index is XORed with a function
+// of the row, so that 16-byte fragment reads (16 rows, one chunk column),
+// 8-byte tile stores and transpose reads (4 rows x 2 chunks per 16-lane group)
+// fall in distinct bank groups.
+__device__ __forceinline__ int nsr_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+template <int W>
+__device__ __forceinline__ int nsr_off(int r, int col) {
+  return r * W + ((((col >> 3) ^ nsr_swz(r))) << 3) + (col & 7);
+}
+
+// An opaque copy of a lane index: address arithmetic derived from it is
+// redone where it is used instead of being hoisted out of the step loop and
+// kept alive (one register per distinct swizzled address) across all steps.
+__device__ __forceinline__ int nsr_opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// acc[x][y] = sum over k < K of M[16 (x0 + x) + .][k] M[16 (y0 + y) + .][k]
+// for the row-major array s [.][W] (x < 4, y < 2).
+template <int W, int K>
+__device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, int gq, f32x4 (&acc)[4][2]) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16* bx = s + (16 * x0 + c) * W;
+  const bf16* by = s + (16 * y0 + c) * W;
+  const int sw = nsr_swz(c);
+  bf16x8 fx[4], fy[2];
+#define LACT_NSR_LOAD(K0, FX, FY)                                                   \
+  {                                                                                 \
+    const int ch = ((((K0) >> 3) + gq) ^ sw) << 3;                                  \
+    _Pragma("unroll") for (int x = 0; x < 4; ++x) FX[x] = ld8(bx + 16 * x * W + ch); \
+    _Pragma("unroll") for (int y = 0; y < 2; ++y) FY[y] = ld8(by + 16 * y * W + ch); \
+  }
+  LACT_NSR_LOAD(0, fx, fy);
+#pragma unroll 1
+  for (int k = 0; k < K; k += 32) {
+    bf16x8 nx[4], ny[2];
+    const int kn = k + 32 < K ? k + 32 : k;  // last slab: harmless re-read
+    LACT_NSR_LOAD(kn, nx, ny);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) mma(acc[x][y], fx[x], fy[y]);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) fx[x] = nx[x];
+#pragma unroll
+    for (int y = 0; y < 2; ++y) fy[y] = ny[y];
+  }
+#undef LACT_NSR_LOAD
+}
+
+// Stores the block's tiles v[x][y] (values of M[16 (x0+x) + 4 g + i][16 (y0+y) + c]
+// of a symmetric 128 x 128 matrix) transposed and, with DIRECT, also in place.
+__device__ __forceinline__ void nsr_store(bf16* s, int x0, int y0, int c, int gq, bool direct,
+                                          const f32x4 (&v)[4][2]) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int tx = x0 + x, ty = y0 + y;
+      bf16x4 b;
+      b[0] = (bf16)v[x][y][0]; b[1] = (bf16)v[x][y][1];
+      b[2] = (bf16)v[x][y][2]; b[3] = (bf16)v[x][y][3];
+      *reinterpret_cast<bf16x4*>(s + nsr_off<128>(16 * ty + c, 16 * tx + 4 * gq)) = b;
+      if (direct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[nsr_off<128>(16 * tx + 4 * gq + i, 16 * ty + c)] = b[i];
+      }
+    }
+}
+
+template <int COLS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_ns_r128(const float* g, float* u, float eps) {
+  constexpr int R = 128, NW = 8;
+  constexpr int CW = COLS / NW;  // columns per wave
+  constexpr int NMT = CW / 16;   // column tiles per wave
+  constexpr int NRT = R / 16;    // row tiles
+  static_assert(CW % 16 == 0, "shape");
+  extern __shared__ __attribute__((aligned(16))) bf16 lds_r[];
+  bf16* sX = lds_r;
+  bf16* sA = lds_r + R * COLS;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, gq = lane >> 4;
+  const int col0 = w * CW;
+  const int bx0 = 4 * (w >> 2), by0 = 2 * (w & 3);  // this wave's block of A
+  const bool active = !(w == 4 || w == 5);          // blocks below the diagonal: mirrored
+  const bool direct = (w == 2 || w == 3);           // blocks above it
+  const float* G = g + (int64_t)blockIdx.x * R * COLS;
+  float* U = u + (int64_t)blockIdx.x * R * COLS;
+
+  // ---- load G: whole rows, coalesced, staged through LDS (fp32, 16-byte
+  // chunks XORed with the row) into the accumulator layout ----
+  // rows per staging pass: fp32 rows must fit the LDS allocation (sX + sA)
+  constexpr int LDSB = (R * COLS + R * R) * 2;
+  constexpr int SR = R * COLS * 4 <= LDSB ? R : 64 * COLS * 4 <= LDSB ? 64 : 32;
+  static_assert(SR * COLS * 4 <= LDSB && (SR * COLS / 4) % (NW * 64) == 0, "staging");
+  constexpr int SV = SR * COLS / 4 / (NW * 64);           // float4 per thread per pass
+  float* stg = reinterpret_cast<float*>(lds_r);
+  auto soff = [](int r, int col) { return r * COLS + ((((col >> 2) ^ (r & 15))) << 2) + (col & 3); };
+  f32x4 yv[NMT][NRT];
+#pragma unroll
+  for (int p0 = 0; p0 < R; p0 += SR) {
+    if (p0) __syncthreads();  // previous pass fully read
+#pragma unroll
+    for (int v = 0; v < SV; ++v) {
+      const int q = tid + v * NW * 64, r = q / (COLS / 4), cq = 4 * (q % (COLS / 4));
+      *reinterpret_cast<f32x4*>(stg + soff(r, cq)) =
+          *reinterpret_cast<const f32x4*>(G + (int64_t)(p0 + r) * COLS + cq);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = p0 / 16; nt < (p0 + SR) / 16; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        yv[mt][nt] = *reinterpret_cast<const f32x4*>(stg + soff(16 * nt + c - p0, col0 + 16 * mt + 4 * gq));
+  }
+  // Frobenius norm (fixed order)
+  float ss = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NRT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss += yv[mt][nt][i] * yv[mt][nt][i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  __syncthreads();  // staging fully read
+  float* red = reinterpret_cast<float*>(sA);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) tot += red[x];
+  const float scale = 1.0f / (sqrtf(tot) + eps);
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NRT; ++nt) yv[mt][nt] = yv[mt][nt] * scale;
+
+  // operand copy: lane (c, g) writes 4 consecutive columns of row 16 nt + c
+#define LACT_NSR_PUT_X()                                                                 \
+  {                                                                                      \
+    const int c_ = nsr_opaque(c), g_ = nsr_opaque(gq);                                   \
+    _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt)                                   \
+    _Pragma("unroll") for (int nt = 0; nt < NRT; ++nt)                                   \
+      st4(sX + nsr_off<COLS>(16 * nt + c_, col0 + 16 * mt + 4 * g_), yv[mt][nt][0],      \
+          yv[mt][nt][1], yv[mt][nt][2], yv[mt][nt][3]);                                  \
+  }
+  LACT_NSR_PUT_X();
+
+  float P = 1.0f;
+#pragma unroll 1
+  for (int it = 0; it < 5; ++it) {
+    const float ca = kNsCoef[it][0], cb = kNsCoef[it][1], cc = kNsCoef[it][2];
+    __syncthreads();  // sX complete; last step's reads of sA done
+    // ---- 1. A = P^2 Y Y^T ----
+    if (active) {
+      const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
+      f32x4 t[4][2];
+      nsr_gram<COLS, COLS>(sX, bx0, by0, c, gq, t);
+      const float s2 = P * P;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) t[x][y] = t[x][y] * s2;
+      nsr_store(sA, bx0, by0, c, gq, direct, t);
+    }
+    __syncthreads();
+    // ---- 2. B' = (b A + c A A) / a, over A ----
+    f32x4 t[4][2];
+    if (active) nsr_gram<128, 128>(sA, bx0, by0, nsr_opaque(c), nsr_opaque(gq), t);
+    __syncthreads();  // every read of A as an operand is done
+    if (active) {
+      const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
+      const float p = cb / ca, q = cc / ca;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const bf16x4 a = *reinterpret_cast<const bf16x4*>(
+              sA + nsr_off<128>(16 * (by0 + y) + c, 16 * (bx0 + x) + 4 * gq));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[x][y][i] = p * (float)a[i] + q * t[x][y][i];
+        }
+      nsr_store(sA, bx0, by0, c, gq, direct, t);
+    }
+    __syncthreads();  // B' complete
+    // ---- 3. Y <- Y + B' Y on this wave's columns: (Y^T B') tiles ----
+    {
+      const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
+#pragma unroll 1
+      for (int ks = 0; ks < R / 32; ++ks) {
+        bf16x8 bf[NRT], af[NMT];
+#pragma unroll
+        for (int nt = 0; nt < NRT; ++nt) bf[nt] = ld8(sA + nsr_off<128>(16 * nt + c, 32 * ks + 8 * gq));
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          // lane (c, g): Y[32 ks + 8 g + 0..7][col0 + 16 mt + c]
+          const int r0 = 32 * ks + 8 * gq + (c >> 2), cl = col0 + 16 * mt + 4 * (c & 3);
+          af[mt] = cat8(ld_tr4(sX + nsr_off<COLS>(r0, cl)), ld_tr4(sX + nsr_off<COLS>(r0 + 4, cl)));
+        }
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NRT; ++nt) mma(yv[mt][nt], af[mt], bf[nt]);
+      }
+    }
+    P *= ca;
+    // own columns only: no other wave reads them before the next barrier
+    if (it < 4) LACT_NSR_PUT_X();
+  }
+#undef LACT_NSR_PUT_X
+  // ---- X_5 = P_5 Y_5, staged through LDS into whole rows ----
+#pragma unroll
+  for (int p0 = 0; p0 < R; p0 += SR) {
+    __syncthreads();  // every read of sX / sA (or of the previous pass) done
+    const int cf = nsr_opaque(c), gf = nsr_opaque(gq);
+#pragma unroll
+    for (int nt = p0 / 16; nt < (p0 + SR) / 16; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        *reinterpret_cast<f32x4*>(stg + soff(16 * nt + cf - p0, col0 + 16 * mt + 4 * gf)) = yv[mt][nt] * P;
+    __syncthreads();
+    const int tf = nsr_opaque(tid);
+#pragma unroll
+    for (int v = 0; v < SV; ++v) {
+      const int q = tf + v * NW * 64, r = q / (COLS / 4), cq = 4 * (q % (COLS / 4));
+      *reinterpret_cast<f32x4*>(U + (int64_t)(p0 + r) * COLS + cq) =
+          *reinterpret_cast<const f32x4*>(stg + soff(r, cq));
+    }
+  }
+}
+
+template <int COLS>
+static hipError_t run_ns_r128(int count, const float* g, float* u, float eps, hipStream_t s) {
+  const size_t lds = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ns_r128<COLS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_ns_r128<COLS>), dim3(count), dim3(512), lds, s, g, u, eps);
+  return hipGetLastError();
+}
+
 template <int ROWS, int COLS, int NW, bool XG>
 static hipError_t run_ns_fused(int count, const float* g, float* u, float eps, hipStream_t s) {
   const size_t lds = (size_t)ns_lds_elems(ROWS, COLS) * sizeof(bf16);
@@ -286,8 +566,8 @@ static hipError_t run_ns_fused(int count, const float* g, float* u, float eps, h
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, const float* g, float* u,
                            float eps, hipStream_t s) {
   if (dtype != 1) return hipErrorNotSupported;
-  if (rows == 128 && cols == 512) return run_ns_fused<128, 512, 8, false>(count, g, u, eps, s);
-  if (rows == 128 && cols == 256) return run_ns_fused<128, 256, 16, false>(count, g, u, eps, s);
+  if (rows == 128 && cols == 512) return run_ns_r128<512>(count, g, u, eps, s);
+  if (rows == 128 && cols == 256) return run_ns_r128<256>(count, g, u, eps, s);
   if (rows == 64 && cols == 256) return run_ns_fused<64, 256, 16, false>(count, g, u, eps, s);
   if (rows == 64 && cols == 512) return run_ns_fused<64, 512, 16, true>(count, g, u, eps, s);
   return hipErrorNotSupported;
