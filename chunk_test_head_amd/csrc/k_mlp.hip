@@ -27,7 +27,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
   constexpr int IT = D / 16;             // output feature tiles
   constexpr int V = 16 / sizeof(T);      // elements per 16-byte vector
   constexpr int P1 = D + V;              // LDS pitch of W1/W3 block rows
-  constexpr int P2 = HB + 4;             // LDS pitch of W2 block rows
+  // W2 block rows: the 32 hidden values of a row stored in kappa order (runs
+  // of four: 0-3, 16-19, 4-7, 20-23, ...), so that the A fragment of lane
+  // group g (hidden 4g..4g+3, 16+4g..16+4g+3) is one 16-byte read; the pitch
+  // (bf16: 80 bytes) puts 16 consecutive rows in distinct bank groups.
+  constexpr int P2 = sizeof(T) == 2 ? HB + 8 : HB + 4;
   constexpr int STAGE = 2 * HB * P1 + D * P2;
   constexpr int NV1 = HB * D / V / NTH;  // 16-byte vectors per thread (W1 / W3)
   constexpr int NV2 = D * HB / V / NTH;  // (W2)
@@ -103,9 +107,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
       const int vi = tid + x * NTH;                                                 \
       const int row = vi / (HB / V), col = (vi % (HB / V)) * V;                     \
       if constexpr (sizeof(T) == 2) {                                               \
-        uint2* dst = reinterpret_cast<uint2*>(s2_ + row * P2 + col);                \
-        dst[0] = uint2{r2[x].x, r2[x].y};                                           \
-        dst[1] = uint2{r2[x].z, r2[x].w};                                           \
+        /* hidden col..col+7 = runs 2q, 2q+1 (q = col / 8) -> slots kpos */         \
+        const int r0_ = col >> 2, r1_ = r0_ + 1;                                    \
+        const int k0_ = 2 * (r0_ & 3) + (r0_ >> 2), k1_ = 2 * (r1_ & 3) + (r1_ >> 2); \
+        *reinterpret_cast<uint2*>(s2_ + row * P2 + 4 * k0_) = uint2{r2[x].x, r2[x].y}; \
+        *reinterpret_cast<uint2*>(s2_ + row * P2 + 4 * k1_) = uint2{r2[x].z, r2[x].w}; \
       } else {                                                                      \
         *reinterpret_cast<uint4*>(s2_ + row * P2 + col) = r2[x];                    \
       }                                                                             \
@@ -159,7 +165,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const T* row = s2 + (16 * it + c) * P2;
-      const frag_t<T> a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
+      frag_t<T> a2;
+      if constexpr (sizeof(T) == 2) a2 = ld8(row + 8 * g);
+      else a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
     }
@@ -373,17 +381,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
 // k / v rows (K = d); the gradient contractions read k^T / v^T fragments
 // (K = tokens) from the same tiles with LDS transpose reads.
 // Tile layout: row r (token), 16-byte chunk q of the row stored at chunk
-// q ^ s(r), s(r) = 2 (r % 4) + (r / 4) % 2 (within each 128-byte window).
-// Eight consecutive rows then put one chunk in eight distinct bank groups
-// (row reads of the forward contractions), and four consecutive rows put two
-// adjacent chunks in eight distinct bank groups (transpose reads).
+// q ^ s(r).  For D >= 128 (rows of 16 or more chunks)
+//   s(r) = 2 (r % 4) + 8 ((r / 4) % 2) + (r / 8) % 2,
+// so 16 consecutive rows put one chunk in 16 distinct bank groups (16-byte
+// row reads of the forward contractions), and rows 4g .. 4g+3 of the lane
+// groups g = 0, 1 put two adjacent chunks in 16 distinct bank groups (the
+// 8-byte transpose reads).  D = 64 rows are 8 chunks: s(r) = 2 (r % 4) +
+// (r / 4) % 2 stays inside the row.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  return D >= 128 ? ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1)
+                  : ((r & 3) << 1) | ((r >> 2) & 1);
+}
 template <int D>
 __device__ __forceinline__ int swz(int r, int col) {
-  const int s = ((r & 3) << 1) | ((r >> 2) & 1);
-  return r * D + (((col >> 3) ^ s) << 3) + (col & 7);
+  return r * D + (((col >> 3) ^ swz_key<D>(r)) << 3) + (col & 7);
 }
 
-template <int D, int WAVES, bool PIPE>
+template <int D, int WAVES, int HT, bool PIPE>
 __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int NTH = WAVES * 64;
   constexpr int NT = 32;
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int hblocks = (a.dh + WAVES * 16 - 1) / (WAVES * 16);
+  const int hblocks = (a.dh + WAVES * 16 * HT - 1) / (WAVES * 16 * HT);
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int hb = lid % hblocks;
   const int rest = lid / hblocks;
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   if (head >= a.bh) return;
   const int64_t s0 = (int64_t)split * a.split_len;
   const int64_t s1 = (s0 + a.split_len < a.n_tok) ? s0 + a.split_len : a.n_tok;
-  const int j0 = hb * WAVES * 16 + wave * 16;
+  const int j0 = (hb * WAVES + wave) * 16 * HT;  // dh % 64 == 0: all HT tiles valid or none
   const bool active = j0 < a.dh;
 
   const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (int64_t)head * a.k_sbh;
@@ -420,24 +435,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
   const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
 
-  // W B fragments: lane holds W[j0 + c][32 ks + 8 g ..]
-  bf16x8 b1[KS], b3[KS], b2[KS];
-  {
-    const int64_t row = (int64_t)(active ? j0 + c : c) * D + 8 * g;
+  // W B fragments: lane holds W[j0 + 16 h + c][32 ks + 8 g ..]
+  bf16x8 b1[HT][KS], b3[HT][KS], b2[HT][KS];
+#pragma unroll
+  for (int h = 0; h < HT; ++h) {
+    const int64_t row = (int64_t)(active ? j0 + 16 * h + c : c) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      b1[ks] = ld8(sb + a.sh.off_w1 + row + 32 * ks);
-      b3[ks] = ld8(sb + a.sh.off_w3 + row + 32 * ks);
-      b2[ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
+      b1[h][ks] = ld8(sb + a.sh.off_w1 + row + 32 * ks);
+      b3[h][ks] = ld8(sb + a.sh.off_w3 + row + 32 * ks);
+      b2[h][ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
     }
   }
-  f32x4 G1[IT], G3[IT], G2[IT];
+  f32x4 G1[HT][IT], G3[HT][IT], G2[HT][IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    G1[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G3[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G2[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int h = 0; h < HT; ++h)
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      G1[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      G3[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      G2[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   // staging: thread tid moves 16-byte vectors vi = tid + x NTH of the k and v
   // tiles (row vi / (D/8), chunk vi % (D/8)) and, for tid < 3 NT, one eta
@@ -482,18 +500,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   {                                                                                 \
     const bf16* sK_ = sKV[BUF];                                                     \
     const bf16* sV_ = sK_ + TILE;                                                   \
-    _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                              \
-      P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                            \
-      U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                            \
-      E[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                            \
-    }                                                                               \
+    _Pragma("unroll") for (int h = 0; h < HT; ++h)                                  \
+      _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                            \
+        P[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
+        U[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
+        E[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
+      }                                                                             \
     _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
       _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                            \
         const bf16x8 ak = ld8(sK_ + swz<D>(16 * tt + c, 32 * ks + 8 * g));           \
         const bf16x8 av = ld8(sV_ + swz<D>(16 * tt + c, 32 * ks + 8 * g));           \
-        mma(P[tt], ak, b1[ks]);                                                     \
-        mma(U[tt], ak, b3[ks]);                                                     \
-        mma(E[tt], av, b2[ks]);                                                     \
+        _Pragma("unroll") for (int h = 0; h < HT; ++h) {                            \
+          mma(P[h][tt], ak, b1[h][ks]);                                             \
+          mma(U[h][tt], ak, b3[h][ks]);                                             \
+          mma(E[h][tt], av, b2[h][ks]);                                             \
+        }                                                                           \
       }                                                                             \
   }
   // SwiGLU backward + eta, packed as B operands (K = 32 tokens, kappa order)
@@ -503,14 +524,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[BUF][0][16 * tt + 4 * g]); \
       const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[BUF][1][16 * tt + 4 * g]); \
       const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[BUF][2][16 * tt + 4 * g]); \
+      _Pragma("unroll") for (int h = 0; h < HT; ++h)                                \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                               \
-        const float p = P[tt][i], u = U[tt][i], e = E[tt][i];                       \
+        const float p = P[h][tt][i], u = U[h][tt][i], e = E[h][tt][i];              \
         const float sg = sigmoid_fast(p);                                           \
         const float sl = p * sg;                                                    \
         const float dsl = sg * __builtin_fmaf(p, 1.f - sg, 1.f);                    \
-        fh[4 * tt + i] = (bf16)(n2[i] * sl * u);                                    \
-        fu[4 * tt + i] = (bf16)(n3[i] * e * sl);                                    \
-        fg[4 * tt + i] = (bf16)(n1[i] * e * u * dsl);                               \
+        fh[h][4 * tt + i] = (bf16)(n2[i] * sl * u);                                 \
+        fu[h][4 * tt + i] = (bf16)(n3[i] * e * sl);                                 \
+        fg[h][4 * tt + i] = (bf16)(n1[i] * e * u * dsl);                            \
       }                                                                             \
     }                                                                               \
   }
@@ -526,15 +548,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       const int fc = 16 * it + 4 * (c & 3);                                         \
       const bf16x8 akt = cat8(ld_tr4(sK_ + swz<D>(tr, fc)), ld_tr4(sK_ + swz<D>(tr + 16, fc))); \
       const bf16x8 avt = cat8(ld_tr4(sV_ + swz<D>(tr, fc)), ld_tr4(sV_ + swz<D>(tr + 16, fc))); \
-      mma(G1[it], akt, fg);                                                         \
-      mma(G3[it], akt, fu);                                                         \
-      mma(G2[it], avt, fh);                                                         \
+      _Pragma("unroll") for (int h = 0; h < HT; ++h) {                              \
+        mma(G1[h][it], akt, fg[h]);                                                 \
+        mma(G3[h][it], akt, fu[h]);                                                 \
+        mma(G2[h][it], avt, fh[h]);                                                 \
+      }                                                                             \
     }                                                                               \
   }
 
   const int ntile = s0 < s1 ? (int)((s1 - s0 + NT - 1) / NT) : 0;
-  f32x4 P[2], U[2], E[2];
-  bf16x8 fh, fu, fg;
+  f32x4 P[HT][2], U[HT][2], E[HT][2];
+  bf16x8 fh[HT], fu[HT], fg[HT];
   if (ntile > 0) {
     LACT_GRAD_GLOAD(s0);
     LACT_GRAD_LSTORE(0);
@@ -581,11 +605,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   const int64_t mat = (int64_t)a.dh * D;
   float* out = a.partial + ((int64_t)split * a.bh + head) * 3 * mat + (int64_t)(j0 + c) * D + 4 * g;
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    st4(out + 16 * it, G1[it][0], G1[it][1], G1[it][2], G1[it][3]);
-    st4(out + mat + 16 * it, G3[it][0], G3[it][1], G3[it][2], G3[it][3]);
-    st4(out + 2 * mat + 16 * it, G2[it][0], G2[it][1], G2[it][2], G2[it][3]);
-  }
+  for (int h = 0; h < HT; ++h)
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float* o = out + 16 * h * D + 16 * it;
+      st4(o, G1[h][it][0], G1[h][it][1], G1[h][it][2], G1[h][it][3]);
+      st4(o + mat, G3[h][it][0], G3[h][it][1], G3[h][it][2], G3[h][it][3]);
+      st4(o + 2 * mat, G2[h][it][0], G2[h][it][1], G2[h][it][2], G2[h][it][3]);
+    }
 }
 
 // --------------------------------------------------------------- launch --
@@ -615,16 +642,16 @@ hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
 }
 
 int grad_hidden_per_block(int dtype, int d) {
-  if (dtype == 1) return 16 * (d == 256 ? 4 : 8);   // k_grad_bf16: WAVES x 16
+  if (dtype == 1) return d == 256 ? 4 * 16 : 128;   // k_grad_bf16: WAVES x 16 x HT (d = 64, 128: 8 x 16)
   return 4 * (d == 64 ? 32 : 16);
 }
 
-template <int D, int WAVES, bool PIPE>
+template <int D, int WAVES, int HT, bool PIPE>
 static hipError_t run_grad_bf16(const GradArgs& a, hipStream_t s) {
-  const int hblocks = (a.dh + WAVES * 16 - 1) / (WAVES * 16);
+  const int hblocks = (a.dh + WAVES * 16 * HT - 1) / (WAVES * 16 * HT);
   const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_grad_bf16<D, WAVES, PIPE>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_grad_bf16<D, WAVES, HT, PIPE>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -640,9 +667,9 @@ static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
   if (dtype == 1) {
     switch (a.d) {
-      case 64: return run_grad_bf16<64, 8, false>(a, s);
-      case 128: return run_grad_bf16<128, 8, false>(a, s);
-      case 256: return run_grad_bf16<256, 4, true>(a, s);
+      case 64: return run_grad_bf16<64, 8, 1, false>(a, s);
+      case 128: return run_grad_bf16<128, 8, 1, false>(a, s);
+      case 256: return run_grad_bf16<256, 4, 1, true>(a, s);
     }
   } else {
     switch (a.d) {
