@@ -37,7 +37,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
   constexpr int NV2 = D * HB / V / NTH;  // (W2)
   static_assert(NV1 * V * NTH == HB * D && NV2 * V * NTH == D * HB, "stage split");
 
-  __shared__ __attribute__((aligned(16))) T lds[2 * STAGE];
+  // SUB hidden blocks per barrier (bf16, d <= 128: LDS allows two), double
+  // buffered: slots (stage % 2) SUB + sub
+  constexpr int SUB = (sizeof(T) == 2 && D <= 128) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) T lds[2 * SUB * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -119,12 +122,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
   }
 
   const int NB = dh / HB;
-  LACT_APPLY_GLOAD(0);
-  LACT_APPLY_LSTORE(0);
+  const int nst = (NB + SUB - 1) / SUB;
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb)
+    if (sb < NB) {
+      LACT_APPLY_GLOAD(sb);
+      LACT_APPLY_LSTORE(sb);
+    }
   __syncthreads();
-  for (int jb = 0; jb < NB; ++jb) {
-    const int buf = jb & 1;
-    if (jb + 1 < NB) LACT_APPLY_GLOAD(jb + 1);
+  for (int st = 0; st < nst; ++st)
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb) {
+    const int jb = st * SUB + sb, jn = jb + SUB;
+    const int buf = (st & 1) * SUB + sb, nbuf = ((st + 1) & 1) * SUB + sb;
+    if (jn < NB) LACT_APPLY_GLOAD(jn);
+    if (jb >= NB) continue;
     const T* s1 = lds + buf * STAGE;
     const T* s3 = s1 + HB * P1;
     const T* s2 = s3 + HB * P1;
@@ -171,8 +183,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
     }
-    if (jb + 1 < NB) LACT_APPLY_LSTORE(buf ^ 1);
-    __syncthreads();
+    if (jn < NB) LACT_APPLY_LSTORE(nbuf);
+    if (sb == SUB - 1) __syncthreads();
   }
 #undef LACT_APPLY_GLOAD
 #undef LACT_APPLY_LSTORE
@@ -409,10 +421,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int VPT = (NV + NTH - 1) / NTH;
   static_assert(NV % NTH == 0 || NTH % NV == 0, "tile split");
 
-  // PIPE: tiles n-1 (read), n (read), n+1 (written); else n (read), n+1 (written)
+  // PIPE: tiles n-1 (read), n (read), n+1 (written); else SUB tiles per
+  // barrier, double buffered (stage st read, stage st+1 written)
   constexpr int NBUF = PIPE ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF][2 * TILE];
-  __shared__ float sEta[NBUF][3][NT];
+  constexpr int SUB = PIPE ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF * SUB][2 * TILE];
+  __shared__ float sEta[NBUF * SUB][3][NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -559,41 +573,64 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   const int ntile = s0 < s1 ? (int)((s1 - s0 + NT - 1) / NT) : 0;
   f32x4 P[HT][2], U[HT][2], E[HT][2];
   bf16x8 fh[HT], fu[HT], fg[HT];
-  if (ntile > 0) {
-    LACT_GRAD_GLOAD(s0);
-    LACT_GRAD_LSTORE(0);
-  }
-  __syncthreads();
-  int n0 = 0;
-  if (PIPE && ntile > 0) {
-    // tile 0: forward + backward only
-    if (ntile > 1) LACT_GRAD_GLOAD(s0 + NT);
-    if (active) {
-      LACT_GRAD_FWD(0);
-      LACT_GRAD_EW(0);
-    }
-    if (ntile > 1) LACT_GRAD_LSTORE(1);
+  if constexpr (!PIPE) {
+    // SUB token tiles per barrier: stage st uses slots (st % 2) SUB + sub and
+    // stages the next stage's tiles, one tile at a time, into the other half
+    const int nst = (ntile + SUB - 1) / SUB;
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+      if (sb < ntile) {
+        LACT_GRAD_GLOAD(s0 + (int64_t)sb * NT);
+        LACT_GRAD_LSTORE(sb);
+      }
     __syncthreads();
-    n0 = 1;
-  }
-  for (int n = n0; n < ntile; ++n) {
-    const int cur = n % NBUF, prev = (n + NBUF - 1) % NBUF, nxt = (n + 1) % NBUF;
-    const bool more = n + 1 < ntile;
-    if (more) LACT_GRAD_GLOAD(s0 + (int64_t)(n + 1) * NT);
-    if (active) {
-      LACT_GRAD_FWD(cur);
-      if constexpr (PIPE) {
+    for (int st = 0; st < nst; ++st) {
+      const int cur = (st & 1) * SUB, nxt = ((st + 1) & 1) * SUB;
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        const int ti = st * SUB + sb, tn = ti + SUB;
+        if (tn < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)tn * NT);
+        if (active && ti < ntile) {
+          LACT_GRAD_FWD(cur + sb);
+          LACT_GRAD_EW(cur + sb);
+          LACT_GRAD_GG(cur + sb);
+        }
+        if (tn < ntile) LACT_GRAD_LSTORE(nxt + sb);
+      }
+      __syncthreads();
+    }
+  } else {
+    if (ntile > 0) {
+      LACT_GRAD_GLOAD(s0);
+      LACT_GRAD_LSTORE(0);
+    }
+    __syncthreads();
+    int n0 = 0;
+    if (ntile > 0) {
+      // tile 0: forward + backward only
+      if (ntile > 1) LACT_GRAD_GLOAD(s0 + NT);
+      if (active) {
+        LACT_GRAD_FWD(0);
+        LACT_GRAD_EW(0);
+      }
+      if (ntile > 1) LACT_GRAD_LSTORE(1);
+      __syncthreads();
+      n0 = 1;
+    }
+    for (int n = n0; n < ntile; ++n) {
+      const int cur = n % NBUF, prev = (n + NBUF - 1) % NBUF, nxt = (n + 1) % NBUF;
+      const bool more = n + 1 < ntile;
+      if (more) LACT_GRAD_GLOAD(s0 + (int64_t)(n + 1) * NT);
+      if (active) {
+        LACT_GRAD_FWD(cur);
         LACT_GRAD_GG(prev);   // reads fh/fu/fg of tile n-1 ...
         LACT_GRAD_EW(cur);    // ... before they are replaced by tile n's
-      } else {
-        LACT_GRAD_EW(cur);
-        LACT_GRAD_GG(cur);
       }
+      if (more) LACT_GRAD_LSTORE(nxt);  // slot of tile n-2, consumed last iteration
+      __syncthreads();
     }
-    if (more) LACT_GRAD_LSTORE(nxt);  // slot of tile n-2, consumed last iteration
-    __syncthreads();
+    if (ntile > 0 && active) LACT_GRAD_GG((ntile - 1) % NBUF);
   }
-  if (PIPE && ntile > 0 && active) LACT_GRAD_GG((ntile - 1) % NBUF);
 #undef LACT_GRAD_FWD
 #undef LACT_GRAD_EW
 #undef LACT_GRAD_GG

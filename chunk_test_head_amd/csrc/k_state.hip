@@ -1,5 +1,5 @@
-// State kernels: split reduction + momentum, momentum coefficient, Frobenius
-// normalisation, weight step + row renorm + operand copies, fill.
+// State kernels: split reduction + momentum, Frobenius normalisation, weight
+// step + row renorm + operand copies, fill.
 //
 // Momentum (LaCT rebuttal page, momentum block of block_causal_lact_swiglu):
 //   beta = mean over the written tokens of the per-token momentum,
@@ -18,6 +18,7 @@ namespace lact {
 // and write the wide [i][j] result.
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   __shared__ float tile[64][65];
+  __shared__ float bred[4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int jt = a.dh / 64, itn = a.d / 64;
   int id = blockIdx.x;
@@ -43,7 +44,25 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   __syncthreads();
   float* out = (mat == 0 ? a.out1 : mat == 1 ? a.out3 : a.out2) + (int64_t)head * msz;
   float* m = (mat == 0 ? a.m1 : mat == 1 ? a.m3 : a.m2);
-  const float beta = (m != nullptr) ? a.beta[head] : 0.f;
+  float beta = 0.f;
+  if (m != nullptr) {
+    // beta = mean of the head's per-token coefficients (fixed order; every
+    // workgroup of the head gets the same value)
+    const float* mc = a.mom + (int64_t)head * a.mom_sbh;
+    float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
+    for (int64_t t = tid; t < a.n_tok; t += 1024) {
+      q0 += mc[t];
+      if (t + 256 < a.n_tok) q1 += mc[t + 256];
+      if (t + 512 < a.n_tok) q2 += mc[t + 512];
+      if (t + 768 < a.n_tok) q3 += mc[t + 768];
+    }
+    float q = (q0 + q1) + (q2 + q3);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
+    if ((tid & 63) == 0) bred[tid >> 6] = q;
+    __syncthreads();
+    beta = a.n_tok > 0 ? ((bred[0] + bred[1]) + (bred[2] + bred[3])) / (float)a.n_tok : 0.f;
+  }
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int i = ty + 16 * rr;
@@ -66,27 +85,6 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.bh * 3 * (a.dh / 64) * (a.d / 64);
   hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------- beta -----
-__global__ __launch_bounds__(256) void k_beta(BetaArgs a) {
-  __shared__ float red[256];
-  const int head = blockIdx.x, tid = threadIdx.x;
-  const float* m = a.mom + (int64_t)head * a.sbh;
-  float s = 0.f;
-  for (int64_t t = tid; t < a.n_tok; t += 256) s += m[t];
-  red[tid] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) a.beta[head] = a.n_tok > 0 ? red[0] / (float)a.n_tok : 0.f;
-}
-
-hipError_t launch_beta(const BetaArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_beta, dim3(a.bh), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -121,161 +119,158 @@ hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s) {
 }
 
 // ------------------------------------------------------------- step -----
-// Tiles of 64 x 64 over the natural layout of each matrix:
-//   mat 0, 1 (W1, W3): rows = hidden j (dh), cols = feature i (d)
-//   mat 2    (W2)    : rows = feature i (d), cols = hidden j (dh)
-// U is wide ([i][j]) for all three, so W1/W3 tiles read it transposed.
-// Row partial sums of squares go to rowpart[head][mat][coltile][row].
-int64_t step_rowpart_elems(int bh, int d, int dh) {
-  // per head: W1, W3: (d/64) x dh ; W2: (dh/64) x d
-  return (int64_t)bh * (2 * (int64_t)(d / 64) * dh + (int64_t)(dh / 64) * d);
-}
-
-struct TileInfo {
-  int head, mat, tr, tc;  // tile row / col index in the natural layout
-  int rows, cols;         // natural dims of the matrix
-  int64_t rp_off;         // rowpart offset of this matrix for this head
-};
-
-__device__ __forceinline__ TileInfo tile_info(int id, int d, int dh) {
-  TileInfo t;
-  const int per = (dh / 64) * (d / 64);
-  t.head = id / (3 * per);
-  id -= t.head * 3 * per;
-  t.mat = id / per;
-  id -= t.mat * per;
-  if (t.mat < 2) { t.rows = dh; t.cols = d; } else { t.rows = d; t.cols = dh; }
-  const int ctn = t.cols / 64;
-  t.tr = id / ctn;
-  t.tc = id % ctn;
-  const int64_t per_head = 2 * (int64_t)(d / 64) * dh + (int64_t)(dh / 64) * d;
-  t.rp_off = (int64_t)t.head * per_head + (t.mat == 0 ? 0 : t.mat == 1 ? (int64_t)(d / 64) * dh : 2 * (int64_t)(d / 64) * dh);
-  return t;
-}
-
-// Pass 1: W <- W + U (written back when U is given), row partial sums.
-__global__ __launch_bounds__(256) void k_step_add(StepArgs a) {
-  __shared__ float tile[64][65];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const TileInfo t = tile_info(blockIdx.x, a.d, a.dh);
-  const int64_t msz = (int64_t)a.d * a.dh;
-  float* W = (t.mat == 0 ? a.w1 : t.mat == 1 ? a.w3 : a.w2) + (int64_t)t.head * msz;
-  const float* U = (t.mat == 0 ? a.u1 : t.mat == 1 ? a.u3 : a.u2);
-  const int r0 = t.tr * 64, c0 = t.tc * 64;
-  if (U != nullptr) {
-    U += (int64_t)t.head * msz;
-    if (t.mat < 2) {
-      // U wide [i][j]: tile rows j (r0..), cols i (c0..) -> read U[c0 + .][r0 + .]
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = ty + 16 * rr;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(U + (int64_t)(c0 + i) * a.dh + r0 + 4 * tx);
-        tile[4 * tx + 0][i] = v[0];
-        tile[4 * tx + 1][i] = v[1];
-        tile[4 * tx + 2][i] = v[2];
-        tile[4 * tx + 3][i] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = ty + 16 * rr;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(U + (int64_t)(r0 + r) * a.dh + c0 + 4 * tx);
-        tile[r][4 * tx + 0] = v[0];
-        tile[r][4 * tx + 1] = v[1];
-        tile[r][4 * tx + 2] = v[2];
-        tile[r][4 * tx + 3] = v[3];
-      }
-    }
-    __syncthreads();
-  }
-  __shared__ float part[64][17];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = ty + 16 * rr;
-    float* wp = W + (int64_t)(r0 + r) * t.cols + c0 + 4 * tx;
-    f32x4 w = *reinterpret_cast<const f32x4*>(wp);
-    if (U != nullptr) {
-      w[0] += tile[r][4 * tx + 0];
-      w[1] += tile[r][4 * tx + 1];
-      w[2] += tile[r][4 * tx + 2];
-      w[3] += tile[r][4 * tx + 3];
-      if (a.write_w) *reinterpret_cast<f32x4*>(wp) = w;
-    }
-    part[r][tx] = w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float s = 0.f;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) s += part[tid][x];
-    a.rowpart[t.rp_off + (int64_t)t.tc * t.rows + r0 + tid] = s;
-  }
-}
-
-// Pass 2: per-row factor, W <- W * factor, operand copies.
+// One pass per matrix: W <- W + U, row <- row * n0[row] / (||row|| + eps),
+// operand copies.  Every workgroup owns whole rows, so the row norms need no
+// second pass over W.
+//   W1, W3 ([dh][d], rows = hidden j): 64 rows per workgroup; U is wide
+//     ([d][dh]), so its 64-column block is transposed through LDS first.
+//   W2 ([d][dh], rows = feature i): 8 rows per workgroup (two per wave);
+//     the W2^T copy ([dh][d]) is written from an LDS tile, 8 features of a
+//     hidden unit per 16-byte store.
 template <class T>
-__global__ __launch_bounds__(256) void k_step_scale(StepArgs a) {
-  __shared__ float fac[64];
-  __shared__ float tile[64][65];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const TileInfo t = tile_info(blockIdx.x, a.d, a.dh);
-  const int64_t msz = (int64_t)a.d * a.dh;
-  float* W = (t.mat == 0 ? a.w1 : t.mat == 1 ? a.w3 : a.w2) + (int64_t)t.head * msz;
-  float* N0 = (t.mat == 0 ? a.n1 : t.mat == 1 ? a.n3 : a.n2) + (int64_t)t.head * t.rows;
-  const int r0 = t.tr * 64, c0 = t.tc * 64;
-  if (tid < 64) {
-    float f = 1.f;
-    if (a.renorm) {
-      const int ctn = t.cols / 64;
-      float sq = 0.f;
-      for (int x = 0; x < ctn; ++x) sq += a.rowpart[t.rp_off + (int64_t)x * t.rows + r0 + tid];
-      f = N0[r0 + tid] / (sqrtf(sq) + a.eps);
+__global__ __launch_bounds__(256) void k_step_w13(StepArgs a) {
+  extern __shared__ float ut[];  // [64][d + 1]
+  const int tid = threadIdx.x;
+  const int d = a.d, dh = a.dh, pt = d + 1;
+  const int nb = dh / 64;
+  const int jb = blockIdx.x % nb, mat = (blockIdx.x / nb) % 2, head = blockIdx.x / (2 * nb);
+  const int64_t msz = (int64_t)d * dh;
+  const int j0 = 64 * jb;
+  float* W = (mat == 0 ? a.w1 : a.w3) + (int64_t)head * msz + (int64_t)j0 * d;
+  const float* U = mat == 0 ? a.u1 : a.u3;
+  // The 64 x d block of W is contiguous: thread tid takes float4 number
+  // tid + 256 k (row (tid + 256 k) / (d/4)); the d/4 threads of a row are
+  // consecutive lanes and combine their sums of squares by shuffles.  W is
+  // requested first so that its loads overlap the transpose of U.
+  const int q4 = d / 4, nk = 64 * q4 / 256, rstep = 256 / q4;
+  const int r0 = tid / q4, c4 = 4 * (tid % q4);
+  constexpr int KMAX = 16;  // d <= 256
+  f32x4 w[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (k < nk) w[k] = *reinterpret_cast<const f32x4*>(W + (int64_t)(r0 + rstep * k) * d + c4);
+  if (U != nullptr) {
+    U += (int64_t)head * msz + j0;
+    // U[i][j0 + 4q .. +3] -> ut[4q .. 4q+3][i]
+    for (int e = tid; e < d * 16; e += 256) {
+      const int i = e >> 4, q = e & 15;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(U + (int64_t)i * dh + 4 * q);
+      ut[(4 * q + 0) * pt + i] = v[0];
+      ut[(4 * q + 1) * pt + i] = v[1];
+      ut[(4 * q + 2) * pt + i] = v[2];
+      ut[(4 * q + 3) * pt + i] = v[3];
     }
-    fac[tid] = f;
+    __syncthreads();
+  }
+  float ss[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < nk) {
+      const int r = r0 + rstep * k;
+      if (U != nullptr) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[k][x] += ut[r * pt + c4 + x];
+      }
+      ss[k] = w[k][0] * w[k][0] + w[k][1] * w[k][1] + w[k][2] * w[k][2] + w[k][3] * w[k][3];
+      for (int o = 1; o < q4; o <<= 1) ss[k] += __shfl_xor(ss[k], o);
+    }
+  }
+  const bool write_w = U != nullptr || a.renorm;
+  const float* N0 = (mat == 0 ? a.n1 : a.n3) + (int64_t)head * dh + j0;
+  T* S = reinterpret_cast<T*>(a.sh.base) + (int64_t)head * a.sh.per_head +
+         (mat == 0 ? a.sh.off_w1 : a.sh.off_w3) + (int64_t)j0 * d;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < nk) {
+      const int r = r0 + rstep * k;
+      const float f = a.renorm ? N0[r] / (sqrtf(ss[k]) + a.eps) : 1.f;
+      const f32x4 v = w[k] * f;
+      if (write_w) *reinterpret_cast<f32x4*>(W + (int64_t)r * d + c4) = v;
+      st4(S + (int64_t)r * d + c4, v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void k_step_w2(StepArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char tl_raw[];
+  T* tl = reinterpret_cast<T*>(tl_raw);  // [8][dh] operand values of the 8 rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = a.d, dh = a.dh;
+  const int nb = d / 8;
+  const int ib = blockIdx.x % nb, head = blockIdx.x / nb;
+  const int64_t msz = (int64_t)d * dh;
+  const int i0 = 8 * ib;
+  const bool write_w = a.u2 != nullptr || a.renorm;
+  T* sb = reinterpret_cast<T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+  constexpr int KMAX = 16;  // dh <= 4096: float4 columns 4 lane + 256 k
+  const int nk = dh / 256, rem = dh % 256;
+#pragma unroll 1
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = wave + 4 * rr;  // 0..7
+    float* W = a.w2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh;
+    const float* U = a.u2 != nullptr ? a.u2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh : nullptr;
+    f32x4 w[KMAX + 1];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k <= KMAX; ++k) {
+      const int col = 4 * lane + 256 * k;
+      if (k < nk || (k == nk && 4 * lane < rem)) {
+        w[k] = *reinterpret_cast<const f32x4*>(W + col);
+        if (U != nullptr) w[k] += *reinterpret_cast<const f32x4*>(U + col);
+        ss += w[k][0] * w[k][0] + w[k][1] * w[k][1] + w[k][2] * w[k][2] + w[k][3] * w[k][3];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    float f = 1.f;
+    if (a.renorm) f = a.n2[(int64_t)head * d + i0 + row] / (sqrtf(ss) + a.eps);
+    T* S = sb + a.sh.off_w2 + (int64_t)(i0 + row) * dh;
+#pragma unroll
+    for (int k = 0; k <= KMAX; ++k) {
+      const int col = 4 * lane + 256 * k;
+      if (k < nk || (k == nk && 4 * lane < rem)) {
+        const f32x4 v = w[k] * f;
+        if (write_w) *reinterpret_cast<f32x4*>(W + col) = v;
+        st4(S + col, v[0], v[1], v[2], v[3]);
+        st4(tl + row * dh + col, v[0], v[1], v[2], v[3]);
+      }
+    }
   }
   __syncthreads();
-  T* sb = reinterpret_cast<T*>(a.sh.base) + (int64_t)t.head * a.sh.per_head;
-  T* S = sb + (t.mat == 0 ? a.sh.off_w1 : t.mat == 1 ? a.sh.off_w3 : a.sh.off_w2);
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = ty + 16 * rr;
-    float* wp = W + (int64_t)(r0 + r) * t.cols + c0 + 4 * tx;
-    f32x4 w = *reinterpret_cast<const f32x4*>(wp);
-    w = w * fac[r];
-    if (a.renorm) *reinterpret_cast<f32x4*>(wp) = w;
-    st4(S + (int64_t)(r0 + r) * t.cols + c0 + 4 * tx, w[0], w[1], w[2], w[3]);
-    if (t.mat == 2) {
-      tile[r][4 * tx + 0] = w[0];
-      tile[r][4 * tx + 1] = w[1];
-      tile[r][4 * tx + 2] = w[2];
-      tile[r][4 * tx + 3] = w[3];
-    }
+  // W2^T[j][i0 .. i0 + 7]
+  T* St = sb + a.sh.off_w2t;
+  for (int j = tid; j < dh; j += 256) {
+    T* dst = St + (int64_t)j * d + i0;
+    st4(dst, (float)tl[0 * dh + j], (float)tl[1 * dh + j], (float)tl[2 * dh + j], (float)tl[3 * dh + j]);
+    st4(dst + 4, (float)tl[4 * dh + j], (float)tl[5 * dh + j], (float)tl[6 * dh + j], (float)tl[7 * dh + j]);
   }
-  if (t.mat == 2) {
-    // W2^T copy: [dh][d]; tile rows i (r0..), cols j (c0..)
-    __syncthreads();
-    T* St = sb + a.sh.off_w2t;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int j = ty + 16 * rr;
-      st4(St + (int64_t)(c0 + j) * a.d + r0 + 4 * tx, tile[4 * tx + 0][j], tile[4 * tx + 1][j],
-          tile[4 * tx + 2][j], tile[4 * tx + 3][j]);
-    }
+}
+
+template <class T>
+static hipError_t run_step(const StepArgs& a, hipStream_t s) {
+  const size_t l13 = (size_t)64 * (a.d + 1) * sizeof(float);
+  const size_t l2 = (size_t)8 * a.dh * sizeof(T);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step_w13<T>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 257 * 4);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step_w2<T>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * 4096 * sizeof(T)));
+    if (e != hipSuccess) return e;
+    attr = true;
   }
+  hipLaunchKernelGGL(k_step_w13<T>, dim3((unsigned)(a.bh * 2 * (a.dh / 64))), dim3(256),
+                     a.u1 != nullptr ? l13 : 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_step_w2<T>, dim3((unsigned)(a.bh * (a.d / 8))), dim3(256), l2, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.bh * 3 * (a.dh / 64) * (a.d / 64);
-  if (a.u1 != nullptr || a.renorm) {
-    hipLaunchKernelGGL(k_step_add, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_step_scale<bf16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_step_scale<float>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return dtype == 1 ? run_step<bf16>(a, s) : run_step<float>(a, s);
 }
 
 // -------------------------------------------------------- row norms -----

@@ -122,14 +122,12 @@ static int choose_nsplit(const lact_shape* sh, int64_t n_tok) {
 }
 
 struct Workspace {
-  float* beta;
   float* partial;
   float* g;       // 3 wide matrices per head: [3][bh][d][dh]
   float* xa;      // Newton-Schulz buffers
   float* xb;
   float* amat;    // [3 bh][d][d]
   float* bmat;
-  float* rowpart;
   int64_t bytes;
 };
 
@@ -142,7 +140,6 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
     off += align256(nfloat * 4);
     return p;
   };
-  w.beta = take(sh->bh);
   w.partial = take((int64_t)nsplit * sh->bh * 3 * msz);
   w.g = take((int64_t)3 * sh->bh * msz);
   if (muon) {
@@ -153,7 +150,6 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
   } else {
     w.xa = w.xb = w.amat = w.bmat = nullptr;
   }
-  w.rowpart = take(step_rowpart_elems(sh->bh, sh->d, sh->dh));
   w.bytes = off;
   return w;
 }
@@ -220,7 +216,7 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
                            lact_layout kl, const void* v, lact_layout vl, const float* e1,
                            const float* e3, const float* e2, int64_t esbh, int64_t n_tok,
                            const Workspace& w, int nsplit, float* o1, float* o3, float* o2,
-                           float* m1, float* m3, float* m2, hipStream_t s) {
+                           float* m1, float* m3, float* m2, const float* mom, hipStream_t s) {
   GradArgs a;
   a.k = k; a.k_sbh = kl.stride_bh; a.k_st = kl.stride_tok;
   a.v = v; a.v_sbh = vl.stride_bh; a.v_st = vl.stride_tok;
@@ -238,7 +234,7 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
     e = launch_grad(sh->dtype, a, s);
   }
   if (e != hipSuccess) return hip_fail(e);
-  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
+  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, mom, esbh, n_tok};
   {
     ProfScope p(LACT_PROF_REDUCE, s);
     e = launch_reduce(r, s);
@@ -248,15 +244,14 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
 
 static lact_status do_step(const lact_shape* sh, const lact_state* st, const float* u1,
                            const float* u3, const float* u2, int renorm, float eps,
-                           float* rowpart, hipStream_t s) {
+                           hipStream_t s) {
   StepArgs a;
   a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
   a.u1 = u1; a.u3 = u3; a.u2 = u2;
   a.n1 = st->n1; a.n3 = st->n3; a.n2 = st->n2;
-  a.rowpart = rowpart;
   a.sh = make_shadow(st->shadow, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
-  a.renorm = renorm; a.eps = eps; a.write_w = 1;
+  a.renorm = renorm; a.eps = eps;
   hipError_t e;
   {
     ProfScope p(LACT_PROF_STEP, s);
@@ -277,14 +272,9 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   float* g1 = w.g;
   float* g3 = w.g + mall;
   float* g2 = w.g + 2 * mall;
-  if (op->use_momentum) {
-    BetaArgs b{mom, esbh, n_tok, sh->bh, w.beta};
-    hipError_t e = launch_beta(b, s);
-    if (e != hipSuccess) return hip_fail(e);
-  }
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit, g1, g3, g2,
                           op->use_momentum ? st->m1 : nullptr, op->use_momentum ? st->m3 : nullptr,
-                          op->use_momentum ? st->m2 : nullptr, s);
+                          op->use_momentum ? st->m2 : nullptr, op->use_momentum ? mom : nullptr, s);
   if (r != LACT_OK) return r;
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
@@ -293,7 +283,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                           w.amat, w.bmat, s);
     if (e != hipSuccess) return hip_fail(e);
   }
-  return do_step(sh, st, g1, g3, g2, op->renorm ? 1 : 0, op->renorm_eps, w.rowpart, s);
+  return do_step(sh, st, g1, g3, g2, op->renorm ? 1 : 0, op->renorm_eps, s);
 }
 
 static lact_status check_update_args(const lact_shape* sh, const lact_state* st, const void* k,
@@ -397,7 +387,7 @@ lact_status lact_gradient(const lact_shape* sh, const lact_state* st, const void
   const int nsplit = choose_nsplit(sh, n_tok);
   Workspace w = layout_ws(sh, nsplit, false, reinterpret_cast<char*>(ws));
   return do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit, g1, g3, g2, nullptr,
-                 nullptr, nullptr, (hipStream_t)stream);
+                 nullptr, nullptr, nullptr, (hipStream_t)stream);
 }
 
 lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_t dtype,
@@ -434,8 +424,7 @@ lact_status lact_step_renorm(const lact_shape* sh, const lact_state* st, const f
   }
   if (ws == nullptr || ws_bytes < lact_workspace_bytes(sh, 0, op)) return LACT_ERR_WORKSPACE;
   if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps,
-                 reinterpret_cast<float*>(ws), (hipStream_t)stream);
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, (hipStream_t)stream);
 }
 
 lact_status lact_update(const lact_shape* sh, const lact_state* st, const void* k,

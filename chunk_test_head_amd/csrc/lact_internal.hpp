@@ -42,12 +42,11 @@ struct ReduceArgs {
   int bh, d, dh;
   float* out1; float* out3; float* out2;  // [bh][d][dh] each
   float* m1; float* m3; float* m2;        // momentum (NULL = off)
-  const float* beta;                      // [bh]
+  // per-token momentum coefficients of the n_tok written tokens ([bh] x
+  // stride mom_sbh); their mean is the coefficient of M
+  const float* mom; int64_t mom_sbh; int64_t n_tok;
 };
 
-struct BetaArgs {
-  const float* mom; int64_t sbh; int64_t n_tok; int bh; float* beta;
-};
 
 // Batched C = alpha * A B + beta * Dm, fp32 storage, MFMA operands in T.
 // A is [M][K] (K contiguous).  B is [N][K] (b_kn = 0) or [K][N] (b_kn = 1).
@@ -69,19 +68,16 @@ struct StepArgs {
   float* w1; float* w3; float* w2;
   const float* u1; const float* u3; const float* u2;  // wide [bh][d][dh]; NULL = no add
   float* n1; float* n3; float* n2;                    // renorm targets
-  float* rowpart;   // workspace: row partial sums
   Shadow sh;
   int bh, d, dh;
   int renorm;  // 0: factor 1 (copies only), 1: n0 / (||row|| + eps)
   float eps;
-  int write_w;
 };
 
 hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
 int grad_hidden_per_block(int dtype, int d);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
-hipError_t launch_beta(const BetaArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, const float* g, float* u,
                            float eps, hipStream_t s);
@@ -89,6 +85,5 @@ hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
 hipError_t launch_row_norms(const StepArgs& a, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
-int64_t step_rowpart_elems(int bh, int d, int dh);
 
 }  // namespace lact
