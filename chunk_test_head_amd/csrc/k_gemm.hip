@@ -101,4 +101,187 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path for matrices too large for one workgroup (d = 256): the iterate
+// X stays fp32 in global memory (for the exact a X term) and a bf16 copy is
+// the MFMA operand of the next products.
+//
+//   C = alpha A B + beta D, A bf16 [M][K] (row pitch lda), B bf16 [N][K]
+//   (BKN = false, pitch ldb) or [K][N] (BKN = true); D fp32 [M][N]; outputs
+//   fp32 C and / or bf16 Ch, [M][N].
+// One workgroup = one 64 x 64 tile, 4 waves of 32 x 32; K in slabs of 128,
+// double buffered through LDS (rows padded by 8 elements: 16 consecutive rows
+// of one 16-byte column fall in distinct bank groups); with BKN the B
+// fragments (K per lane) are transpose reads of the [k][n] tile.  The result
+// tile goes through LDS so that D, C and Ch move as whole 16-byte row pieces.
+namespace {
+constexpr int NSG_T = 64, NSG_K = 128;
+constexpr int NSG_PA = NSG_K + 8;                     // [m][k] / [n][k] tiles
+constexpr int NSG_PB = NSG_T + 8;                     // [k][n] tile
+constexpr int NSG_SA = NSG_T * NSG_PA;                // elements per A stage
+constexpr int NSG_SB = NSG_T * NSG_PA > NSG_K * NSG_PB ? NSG_T * NSG_PA : NSG_K * NSG_PB;
+constexpr int NSG_PC = NSG_T + 4;                     // fp32 result tile pitch
+}
+
+template <bool BKN>
+__global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 lds_g[2 * NSG_SA + 2 * NSG_SB];
+  static_assert(NSG_T * NSG_PC * 4 <= (2 * NSG_SA + 2 * NSG_SB) * 2, "result tile");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tn = a.N / NSG_T;
+  const int m0 = (blockIdx.x / tn) * NSG_T, n0 = (blockIdx.x % tn) * NSG_T;
+  const int64_t bidx = blockIdx.y;
+  const bf16* A = a.A + bidx * a.a_bs;
+  const bf16* B = a.B + bidx * a.b_bs;
+
+  // staging: 16-byte vectors vi = tid + 256 x; A: row vi / 16, chunk vi % 16
+  // ([m][k]); B: [n][k] likewise, or ([k][n]) row vi / 8, chunk vi % 8
+  uint4 ra[4], rb[4];
+// (K is a multiple of 64: the second half of a last, partial slab reads as 0)
+#define LACT_NSG_GLOAD(K0)                                                                   \
+  {                                                                                          \
+    _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                          \
+      const int vi = tid + 256 * x;                                                          \
+      const int ka = (K0) + 8 * (vi & 15), kb = BKN ? (K0) + (vi >> 3) : ka;                \
+      ra[x] = uint4{0u, 0u, 0u, 0u};                                                         \
+      rb[x] = uint4{0u, 0u, 0u, 0u};                                                         \
+      if (ka < a.K) ra[x] = *reinterpret_cast<const uint4*>(A + (int64_t)(m0 + (vi >> 4)) * a.lda + ka); \
+      if (kb < a.K)                                                                          \
+        rb[x] = BKN ? *reinterpret_cast<const uint4*>(B + (int64_t)kb * a.ldb + n0 + 8 * (vi & 7)) \
+                    : *reinterpret_cast<const uint4*>(B + (int64_t)(n0 + (vi >> 4)) * a.ldb + kb); \
+    }                                                                                        \
+  }
+#define LACT_NSG_LSTORE(BUF)                                                                 \
+  {                                                                                          \
+    bf16* sa_ = lds_g + (BUF) * NSG_SA;                                                      \
+    bf16* sb_ = lds_g + 2 * NSG_SA + (BUF) * NSG_SB;                                         \
+    _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                          \
+      const int vi = tid + 256 * x;                                                          \
+      *reinterpret_cast<uint4*>(sa_ + (vi >> 4) * NSG_PA + 8 * (vi & 15)) = ra[x];           \
+      if (BKN) *reinterpret_cast<uint4*>(sb_ + (vi >> 3) * NSG_PB + 8 * (vi & 7)) = rb[x];   \
+      else *reinterpret_cast<uint4*>(sb_ + (vi >> 4) * NSG_PA + 8 * (vi & 15)) = rb[x];      \
+    }                                                                                        \
+  }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  LACT_NSG_GLOAD(0);
+  LACT_NSG_LSTORE(0);
+  __syncthreads();
+  for (int k0 = 0; k0 < a.K; k0 += NSG_K) {
+    const int buf = (k0 / NSG_K) & 1;
+    const bool more = k0 + NSG_K < a.K;
+    if (more) LACT_NSG_GLOAD(k0 + NSG_K);
+    const bf16* sa = lds_g + buf * NSG_SA;
+    const bf16* sb = lds_g + 2 * NSG_SA + buf * NSG_SB;
+#pragma unroll
+    for (int s = 0; s < NSG_K / 32; ++s) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) fa[x] = ld8(sa + (32 * wm + 16 * x + c) * NSG_PA + 32 * s + 8 * g);
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        if constexpr (BKN) {
+          const bf16* p = sb + (32 * s + 8 * g + (c >> 2)) * NSG_PB + 32 * wn + 16 * y + 4 * (c & 3);
+          fb[y] = cat8(ld_tr4(p), ld_tr4(p + 4 * NSG_PB));
+        } else {
+          fb[y] = ld8(sb + (32 * wn + 16 * y + c) * NSG_PA + 32 * s + 8 * g);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) mma(acc[x][y], fa[x], fb[y]);
+    }
+    if (more) LACT_NSG_LSTORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef LACT_NSG_GLOAD
+#undef LACT_NSG_LSTORE
+  // result tile through LDS (every read of the operand tiles is done)
+  float* sc = reinterpret_cast<float*>(lds_g);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sc[(32 * wm + 16 * x + 4 * g + i) * NSG_PC + 32 * wn + 16 * y + c] = acc[x][y][i];
+  __syncthreads();
+  const float* D = a.D ? a.D + bidx * a.d_bs : nullptr;
+  float* C = a.C ? a.C + bidx * a.c_bs : nullptr;
+  bf16* Ch = a.Ch ? a.Ch + bidx * a.c_bs : nullptr;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
+    const int64_t o = (int64_t)(m0 + r) * a.N + n0 + c4;
+    f32x4 v = *reinterpret_cast<const f32x4*>(sc + r * NSG_PC + c4) * a.alpha;
+    if (D) v += *reinterpret_cast<const f32x4*>(D + o) * a.beta;
+    if (C) *reinterpret_cast<f32x4*>(C + o) = v;
+    if (Ch) st4(Ch + o, v[0], v[1], v[2], v[3]);
+  }
+}
+
+hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s) {
+  const dim3 grid((unsigned)((a.M / NSG_T) * (a.N / NSG_T)), (unsigned)batch);
+  if (b_kn)
+    hipLaunchKernelGGL(k_nsgemm<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_nsgemm<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Frobenius normalisation in two deterministic passes over NSN_B blocks per
+// matrix: partial sums of squares, then X = G / (||G|| + eps) as fp32 and bf16.
+namespace {
+constexpr int NSN_B = 32;
+}
+
+__global__ __launch_bounds__(256) void k_nsn_part(const float* g, float* part, int64_t n) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t per = n / NSN_B;
+  const float* p = g + (int64_t)blockIdx.y * n + (int64_t)blockIdx.x * per;
+  float s = 0.f;
+  for (int64_t e = 4 * tid; e < per; e += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p + e);
+    s += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) part[blockIdx.y * NSN_B + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void k_nsn_scale(const float* g, const float* part, float* x,
+                                                   bf16* xh, int64_t n, float eps) {
+  const int tid = threadIdx.x;
+  float tot = 0.f;
+  for (int b = 0; b < NSN_B; ++b) tot += part[blockIdx.y * NSN_B + b];
+  const float scale = 1.0f / (sqrtf(tot) + eps);
+  const int64_t per = n / NSN_B;
+  const int64_t base = (int64_t)blockIdx.y * n + (int64_t)blockIdx.x * per;
+  for (int64_t e = 4 * tid; e < per; e += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(g + base + e) * scale;
+    *reinterpret_cast<f32x4*>(x + base + e) = v;
+    st4(xh + base + e, v[0], v[1], v[2], v[3]);
+  }
+}
+
+hipError_t launch_nsn(const float* g, float* part, float* x, bf16* xh, int count, int64_t n, float eps,
+                      hipStream_t s) {
+  if (n % (4 * NSN_B) != 0) return hipErrorInvalidValue;
+  const dim3 grid(NSN_B, (unsigned)count);
+  hipLaunchKernelGGL(k_nsn_part, grid, dim3(256), 0, s, g, part, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_nsn_scale, grid, dim3(256), 0, s, g, part, x, xh, n, eps);
+  return hipGetLastError();
+}
+
 }  // namespace lact

@@ -11,6 +11,7 @@
 
 #include "../../include/lact.h"
 #include "lact_internal.hpp"
+#include <utility>
 
 namespace lact {
 
@@ -126,6 +127,7 @@ struct Workspace {
   float* g;       // 3 wide matrices per head: [3][bh][d][dh]
   float* xa;      // Newton-Schulz buffers
   float* xb;
+  float* xh;
   float* amat;    // [3 bh][d][d]
   float* bmat;
   int64_t bytes;
@@ -145,10 +147,11 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
   if (muon) {
     w.xa = take((int64_t)3 * sh->bh * msz);
     w.xb = take((int64_t)3 * sh->bh * msz);
+    w.xh = take((int64_t)3 * sh->bh * msz);
     w.amat = take((int64_t)3 * sh->bh * sh->d * sh->d);
     w.bmat = take((int64_t)3 * sh->bh * sh->d * sh->d);
   } else {
-    w.xa = w.xb = w.amat = w.bmat = nullptr;
+    w.xa = w.xb = w.xh = w.amat = w.bmat = nullptr;
   }
   w.bytes = off;
   return w;
@@ -159,16 +162,51 @@ static const float kNS[5][3] = {
     {4.0848f, -6.8946f, 2.9270f}, {3.9505f, -6.3029f, 2.6377f}, {3.7418f, -5.5913f, 2.3037f},
     {2.8769f, -3.1427f, 1.2046f}, {2.8366f, -3.0525f, 1.2012f}};
 
+// Newton-Schulz workspace: X fp32 twice, the bf16 copies of X (two, in one
+// fp32-sized region), A / B bf16 (one region) and A fp32.
 static int64_t ns_ws_bytes(int count, int rows, int cols) {
   const int64_t m = (int64_t)rows * cols;
-  return 2 * align256((int64_t)count * m * 4) + 2 * align256((int64_t)count * rows * rows * 4);
+  return 3 * align256((int64_t)count * m * 4) + 2 * align256((int64_t)count * rows * rows * 4);
 }
 
 static hipError_t run_ns(int dtype, int count, int rows, int cols, const float* g, float* u,
-                         float eps, float* xa, float* xb, float* am, float* bm, hipStream_t s) {
+                         float eps, float* xa, float* xb, float* xh, float* am, float* bm,
+                         hipStream_t s) {
   const int64_t m = (int64_t)rows * cols;
   hipError_t e = launch_ns_fused(dtype, count, rows, cols, g, u, eps, s);
   if (e != hipErrorNotSupported) return e;
+  if (dtype == LACT_BF16) {
+    // X fp32 in xa / xb, its bf16 copy in the two halves of xh; A fp32 in bm,
+    // A and B bf16 in am
+    typedef __bf16 bf16;
+    bf16* xh0 = reinterpret_cast<bf16*>(xh);
+    bf16* xh1 = xh0 + (int64_t)count * m;
+    bf16* ah = reinterpret_cast<bf16*>(am);
+    bf16* bh = ah + (int64_t)count * rows * rows;
+    const int64_t rr = (int64_t)rows * rows;
+    if ((e = launch_nsn(g, bm, xa, xh0, count, m, eps, s)) != hipSuccess) return e;
+    float* x = xa;
+    float* y = xb;
+    bf16* xc = xh0;
+    bf16* yc = xh1;
+    for (int it = 0; it < 5; ++it) {
+      const float ca = kNS[it][0], cb = kNS[it][1], cc = kNS[it][2];
+      // A = X X^T (fp32 for the b A term, bf16 operand)
+      NsGemmArgs ga{xc, m, cols, xc, m, cols, nullptr, 0, bm, ah, rr, rows, rows, cols, 1.f, 0.f};
+      if ((e = launch_nsgemm(false, ga, count, s)) != hipSuccess) return e;
+      // B = c A A + b A (A symmetric: its rows are the B operand)
+      NsGemmArgs gb{ah, rr, rows, ah, rr, rows, bm, rr, nullptr, bh, rr, rows, rows, rows, cc, cb};
+      if ((e = launch_nsgemm(false, gb, count, s)) != hipSuccess) return e;
+      // X' = B X + a X
+      const bool last = it == 4;
+      NsGemmArgs gx{bh, rr, rows, xc, m, cols, x, m, last ? u : y, last ? nullptr : yc, m,
+                    rows, cols, rows, 1.f, ca};
+      if ((e = launch_nsgemm(true, gx, count, s)) != hipSuccess) return e;
+      std::swap(x, y);
+      std::swap(xc, yc);
+    }
+    return hipSuccess;
+  }
   NsNormArgs na{g, xa, count, m, eps};
   e = launch_ns_norm(na, s);
   if (e != hipSuccess) return e;
@@ -279,8 +317,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
     hipError_t e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, w.g, w.g,
-                          op->ns_eps, w.xa, w.xb,
-                          w.amat, w.bmat, s);
+                          op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   return do_step(sh, st, g1, g3, g2, op->renorm ? 1 : 0, op->renorm_eps, s);
@@ -405,9 +442,10 @@ lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_
   const int64_t am = align256((int64_t)count * rows * rows * 4);
   float* xa = reinterpret_cast<float*>(b);
   float* xb = reinterpret_cast<float*>(b + xm);
-  float* a_ = reinterpret_cast<float*>(b + 2 * xm);
-  float* b_ = reinterpret_cast<float*>(b + 2 * xm + am);
-  hipError_t e = run_ns(dtype, count, rows, cols, g, u, eps, xa, xb, a_, b_, (hipStream_t)stream);
+  float* xh = reinterpret_cast<float*>(b + 2 * xm);
+  float* a_ = reinterpret_cast<float*>(b + 3 * xm);
+  float* b_ = reinterpret_cast<float*>(b + 3 * xm + am);
+  hipError_t e = run_ns(dtype, count, rows, cols, g, u, eps, xa, xb, xh, a_, b_, (hipStream_t)stream);
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 

@@ -59,6 +59,16 @@ struct GemmArgs {
   float alpha, beta;
 };
 
+// bf16-operand GEMM of the large-matrix Newton-Schulz path (k_gemm.hip).
+struct NsGemmArgs {
+  const __bf16* A; int64_t a_bs; int lda;
+  const __bf16* B; int64_t b_bs; int ldb;
+  const float* D; int64_t d_bs;
+  float* C; __bf16* Ch; int64_t c_bs;
+  int M, N, K;
+  float alpha, beta;
+};
+
 struct NsNormArgs {
   const float* g; float* x; int64_t count, n; float eps;
 };
@@ -82,6 +92,9 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, const float* g, float* u,
                            float eps, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
+hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s);
+hipError_t launch_nsn(const float* g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,
+                      hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
 hipError_t launch_row_norms(const StepArgs& a, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
