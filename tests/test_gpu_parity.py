@@ -101,7 +101,7 @@ def test_gradient_distinct_etas(device):
 
 
 @pytest.mark.parametrize("dtype,tol", [(L.BF16, 2e-2), (L.F32, 1e-4)])
-@pytest.mark.parametrize("rows,cols", [(128, 512), (128, 256), (256, 1024), (64, 128)])
+@pytest.mark.parametrize("rows,cols", [(128, 512), (128, 256), (256, 1024), (64, 128), (128, 192), (192, 320)])
 def test_newton_schulz(device, dtype, tol, rows, cols):
     import torch
     # a gradient-like input: oracle chunk gradient of a random head
@@ -123,24 +123,44 @@ def test_newton_schulz(device, dtype, tol, rows, cols):
         assert H.rel(got[i], ref) < tol, (i, H.rel(got[i], ref))
 
 
+@pytest.mark.parametrize("renorm", [True, False])
 @pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
-def test_step_renorm(device, wi):
+def test_step_renorm(device, wi, renorm):
+    """W <- W + U (+ row renorm) on the masters, then a read through the
+    operand copies the step rewrote (W1, W3, W2 and W2^T) against the oracle's
+    read with the new weights."""
     import torch
     w = small(wi, 64, 64, subset=(0, 64))
-    W, _ = inputs(w)
+    W, inp = inputs(w)
     fw = H.make_state(w, W, device)
     rng = np.random.default_rng(wi)
     U = [rng.standard_normal((w.bh, w.d, w.dh)).astype(np.float32) * 0.05 for _ in range(3)]
     u = [torch.from_numpy(x).to(device) for x in U]
     ws = H.workspace(w, 0, device)
-    L.lact_step_renorm(fw.shape, fw, u[0], u[1], u[2], H.opts_of(w), ws)
+    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=renorm)
+    L.lact_step_renorm(fw.shape, fw, u[0], u[1], u[2], o, ws)
+    q = H.act_to_dev(w, inp, "q", device)
+    out = H.out_buffer(w, w.T, device)
+    L.lact_apply(fw.shape, fw, q, out)
     torch.cuda.synchronize()
     W1, W3, W2 = H.to64(fw.w1), H.to64(fw.w3), H.to64(fw.w2)
+    got = H.to64(out)
+    tol_o = 2e-2 if w.dtype == "bf16" else 1e-4
     for b in range(w.bh):
-        n1, n3, n2 = O.row_norms(W[0][b]), O.row_norms(W[1][b]), O.row_norms(W[2][b])
-        assert H.rel(W1[b], O.step_renorm(W[0][b], U[0][b].T, n1)) < 1e-5
-        assert H.rel(W3[b], O.step_renorm(W[1][b], U[1][b].T, n3)) < 1e-5
-        assert H.rel(W2[b], O.step_renorm(W[2][b], U[2][b], n2)) < 1e-5
+        if renorm:
+            n1, n3, n2 = O.row_norms(W[0][b]), O.row_norms(W[1][b]), O.row_norms(W[2][b])
+            e1 = O.step_renorm(W[0][b], U[0][b].T, n1)
+            e3 = O.step_renorm(W[1][b], U[1][b].T, n3)
+            e2 = O.step_renorm(W[2][b], U[2][b], n2)
+        else:
+            e1 = W[0][b].astype(np.float64) + U[0][b].T
+            e3 = W[1][b].astype(np.float64) + U[1][b].T
+            e2 = W[2][b].astype(np.float64) + U[2][b]
+        assert H.rel(W1[b], e1) < 1e-5
+        assert H.rel(W3[b], e3) < 1e-5
+        assert H.rel(W2[b], e2) < 1e-5
+        ref = O.apply(e1, e3, e2, WL.token_values(inp, "q", b, 0, w.T))
+        assert H.rel(got[b], ref) < tol_o, (b, H.rel(got[b], ref))
     assert H.rel(H.to64(fw.n1), np.stack([O.row_norms(x) for x in W[0]])) < 1e-6
 
 
