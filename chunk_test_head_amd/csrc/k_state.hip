@@ -122,29 +122,29 @@ hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s) {
 // One pass per matrix: W <- W + U, row <- row * n0[row] / (||row|| + eps),
 // operand copies.  Every workgroup owns whole rows, so the row norms need no
 // second pass over W.
-//   W1, W3 ([dh][d], rows = hidden j): 64 rows per workgroup; U is wide
-//     ([d][dh]), so its 64-column block is transposed through LDS first.
+//   W1, W3 ([dh][d], rows = hidden j): 32 rows per workgroup; U is wide
+//     ([d][dh]), so its 32-column block is transposed through LDS first.
 //   W2 ([d][dh], rows = feature i): 8 rows per workgroup (two per wave);
 //     the W2^T copy ([dh][d]) is written from an LDS tile, 8 features of a
 //     hidden unit per 16-byte store.
 template <class T>
-__global__ __launch_bounds__(256) void k_step_w13(StepArgs a) {
-  extern __shared__ float ut[];  // [64][d + 1]
+__device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) {
+  constexpr int RB = 32;  // rows per workgroup; ut: [RB][d + 1]
   const int tid = threadIdx.x;
   const int d = a.d, dh = a.dh, pt = d + 1;
-  const int nb = dh / 64;
-  const int jb = blockIdx.x % nb, mat = (blockIdx.x / nb) % 2, head = blockIdx.x / (2 * nb);
+  const int nb = dh / RB;
+  const int jb = blk % nb, mat = (blk / nb) % 2, head = blk / (2 * nb);
   const int64_t msz = (int64_t)d * dh;
-  const int j0 = 64 * jb;
+  const int j0 = RB * jb;
   float* W = (mat == 0 ? a.w1 : a.w3) + (int64_t)head * msz + (int64_t)j0 * d;
   const float* U = mat == 0 ? a.u1 : a.u3;
-  // The 64 x d block of W is contiguous: thread tid takes float4 number
+  // The RB x d block of W is contiguous: thread tid takes float4 number
   // tid + 256 k (row (tid + 256 k) / (d/4)); the d/4 threads of a row are
   // consecutive lanes and combine their sums of squares by shuffles.  W is
   // requested first so that its loads overlap the transpose of U.
-  const int q4 = d / 4, nk = 64 * q4 / 256, rstep = 256 / q4;
+  const int q4 = d / 4, nk = RB * q4 / 256, rstep = 256 / q4;
   const int r0 = tid / q4, c4 = 4 * (tid % q4);
-  constexpr int KMAX = 16;  // d <= 256
+  constexpr int KMAX = RB / 4;  // d <= 256
   f32x4 w[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(256) void k_step_w13(StepArgs a) {
   if (U != nullptr) {
     U += (int64_t)head * msz + j0;
     // U[i][j0 + 4q .. +3] -> ut[4q .. 4q+3][i]
-    for (int e = tid; e < d * 16; e += 256) {
-      const int i = e >> 4, q = e & 15;
+    for (int e = tid; e < d * (RB / 4); e += 256) {
+      const int i = e / (RB / 4), q = e % (RB / 4);
       const f32x4 v = *reinterpret_cast<const f32x4*>(U + (int64_t)i * dh + 4 * q);
       ut[(4 * q + 0) * pt + i] = v[0];
       ut[(4 * q + 1) * pt + i] = v[1];
@@ -191,21 +191,20 @@ __global__ __launch_bounds__(256) void k_step_w13(StepArgs a) {
   }
 }
 
-template <class T>
-__global__ __launch_bounds__(256) void k_step_w2(StepArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char tl_raw[];
-  T* tl = reinterpret_cast<T*>(tl_raw);  // [8][dh] operand values of the 8 rows
+template <class T, int KMAX>
+__device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
+  // tl: [8][dh] operand values of the 8 rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = a.d, dh = a.dh;
   const int nb = d / 8;
-  const int ib = blockIdx.x % nb, head = blockIdx.x / nb;
+  const int ib = blk % nb, head = blk / nb;
   const int64_t msz = (int64_t)d * dh;
   const int i0 = 8 * ib;
   const bool write_w = a.u2 != nullptr || a.renorm;
   T* sb = reinterpret_cast<T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
-  constexpr int KMAX = 16;  // dh <= 4096: float4 columns 4 lane + 256 k
+  // float4 columns 4 lane + 256 k, k <= KMAX (dh <= 256 (KMAX + 1))
   const int nk = dh / 256, rem = dh % 256;
-#pragma unroll 1
+#pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const int row = wave + 4 * rr;  // 0..7
     float* W = a.w2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh;
@@ -247,30 +246,35 @@ __global__ __launch_bounds__(256) void k_step_w2(StepArgs a) {
   }
 }
 
-template <class T>
+// One launch for all three matrices: workgroups [0, n13) take W1 / W3 row
+// blocks, the rest W2 row blocks.
+template <class T, int KMAX>
+__global__ __launch_bounds__(256) void k_step(StepArgs a, int n13) {
+  extern __shared__ __attribute__((aligned(16))) float step_lds[];
+  if ((int)blockIdx.x < n13) step_w13<T>(a, blockIdx.x, step_lds);
+  else step_w2<T, KMAX>(a, blockIdx.x - n13, reinterpret_cast<T*>(step_lds));
+}
+
+template <class T, int KMAX>
 static hipError_t run_step(const StepArgs& a, hipStream_t s) {
-  const size_t l13 = (size_t)64 * (a.d + 1) * sizeof(float);
+  const size_t l13 = (size_t)32 * (a.d + 1) * sizeof(float);
   const size_t l2 = (size_t)8 * a.dh * sizeof(T);
+  const size_t lds = l13 > l2 ? l13 : l2;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step_w13<T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 257 * 4);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step_w2<T>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * 4096 * sizeof(T)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step<T, KMAX>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * 4096 * sizeof(T)));
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(k_step_w13<T>, dim3((unsigned)(a.bh * 2 * (a.dh / 64))), dim3(256),
-                     a.u1 != nullptr ? l13 : 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_step_w2<T>, dim3((unsigned)(a.bh * (a.d / 8))), dim3(256), l2, s, a);
+  const int n13 = a.bh * 2 * (a.dh / 32), n2 = a.bh * (a.d / 8);
+  hipLaunchKernelGGL((k_step<T, KMAX>), dim3((unsigned)(n13 + n2)), dim3(256), lds, s, a, n13);
   return hipGetLastError();
 }
 
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s) {
-  return dtype == 1 ? run_step<bf16>(a, s) : run_step<float>(a, s);
+  if (dtype == 1) return a.dh <= 1024 ? run_step<bf16, 3>(a, s) : run_step<bf16, 15>(a, s);
+  return a.dh <= 1024 ? run_step<float, 3>(a, s) : run_step<float, 15>(a, s);
 }
 
 // -------------------------------------------------------- row norms -----
