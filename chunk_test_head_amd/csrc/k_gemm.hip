@@ -241,11 +241,11 @@ namespace {
 constexpr int NSN_B = 32;
 }
 
-__global__ __launch_bounds__(256) void k_nsn_part(const float* g, float* part, int64_t n) {
+__global__ __launch_bounds__(256) void k_nsn_part(NsIn g, float* part, int64_t n) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t per = n / NSN_B;
-  const float* p = g + (int64_t)blockIdx.y * n + (int64_t)blockIdx.x * per;
+  const float* p = g.at(blockIdx.y, n) + (int64_t)blockIdx.x * per;
   float s = 0.f;
   for (int64_t e = 4 * tid; e < per; e += 1024) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(p + e);
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void k_nsn_part(const float* g, float* part, i
   if (tid == 0) part[blockIdx.y * NSN_B + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__global__ __launch_bounds__(256) void k_nsn_scale(const float* g, const float* part, float* x,
+__global__ __launch_bounds__(256) void k_nsn_scale(NsIn g, const float* part, float* x,
                                                    bf16* xh, int64_t n, float eps) {
   const int tid = threadIdx.x;
   float tot = 0.f;
@@ -266,14 +266,15 @@ __global__ __launch_bounds__(256) void k_nsn_scale(const float* g, const float* 
   const float scale = 1.0f / (sqrtf(tot) + eps);
   const int64_t per = n / NSN_B;
   const int64_t base = (int64_t)blockIdx.y * n + (int64_t)blockIdx.x * per;
+  const float* gp = g.at(blockIdx.y, n) + (int64_t)blockIdx.x * per;
   for (int64_t e = 4 * tid; e < per; e += 1024) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(g + base + e) * scale;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(gp + e) * scale;
     *reinterpret_cast<f32x4*>(x + base + e) = v;
     st4(xh + base + e, v[0], v[1], v[2], v[3]);
   }
 }
 
-hipError_t launch_nsn(const float* g, float* part, float* x, bf16* xh, int count, int64_t n, float eps,
+hipError_t launch_nsn(NsIn g, float* part, float* x, bf16* xh, int count, int64_t n, float eps,
                       hipStream_t s) {
   if (n % (4 * NSN_B) != 0) return hipErrorInvalidValue;
   const dim3 grid(NSN_B, (unsigned)count);

@@ -36,7 +36,7 @@ constexpr int ns_lds_elems(int rows, int cols) {
 // only its own columns, L2-resident) instead of in registers, for shapes
 // whose register copy would not fit.
 template <int ROWS, int COLS, int NW, bool XG>
-__global__ __launch_bounds__(NW * 64) void k_ns_fused(const float* g, float* u, float eps) {
+__global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float eps) {
   constexpr int NRT = ROWS / 16;          // row tiles of X
   constexpr int CW = COLS / NW;           // columns per wave
   constexpr int NCT = CW / 16;            // column tiles per wave
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(const float* g, float* u, 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, gq = lane >> 4;
   const int col0 = w * CW;
-  const float* G = g + (int64_t)blockIdx.x * ROWS * COLS;
+  const float* G = g.at(blockIdx.x, (int64_t)ROWS * COLS);
   float* Uo = u + (int64_t)blockIdx.x * ROWS * COLS;
 
   // ---- Frobenius norm (fixed order), then this wave's columns (C layout) ----
@@ -372,7 +372,7 @@ __device__ __forceinline__ void nsr_store(bf16* s, int x0, int y0, int c, int gq
 
 template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_ns_r128(const float* g, float* u, float eps) {
+void k_ns_r128(NsIn g, float* u, float eps) {
   constexpr int R = 128, NW = 8;
   constexpr int CW = COLS / NW;  // columns per wave
   constexpr int NMT = CW / 16;   // column tiles per wave
@@ -388,7 +388,7 @@ void k_ns_r128(const float* g, float* u, float eps) {
   const int bx0 = 4 * (w >> 2), by0 = 2 * (w & 3);  // this wave's block of A
   const bool active = !(w == 4 || w == 5);          // blocks below the diagonal: mirrored
   const bool direct = (w == 2 || w == 3);           // blocks above it
-  const float* G = g + (int64_t)blockIdx.x * R * COLS;
+  const float* G = g.at(blockIdx.x, (int64_t)R * COLS);
   float* U = u + (int64_t)blockIdx.x * R * COLS;
 
   // ---- load G: whole rows, coalesced, staged through LDS (fp32, 16-byte
@@ -535,7 +535,7 @@ void k_ns_r128(const float* g, float* u, float eps) {
 }
 
 template <int COLS>
-static hipError_t run_ns_r128(int count, const float* g, float* u, float eps, hipStream_t s) {
+static hipError_t run_ns_r128(int count, NsIn g, float* u, float eps, hipStream_t s) {
   const size_t lds = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
   static bool attr = false;
   if (!attr) {
@@ -549,7 +549,7 @@ static hipError_t run_ns_r128(int count, const float* g, float* u, float eps, hi
 }
 
 template <int ROWS, int COLS, int NW, bool XG>
-static hipError_t run_ns_fused(int count, const float* g, float* u, float eps, hipStream_t s) {
+static hipError_t run_ns_fused(int count, NsIn g, float* u, float eps, hipStream_t s) {
   const size_t lds = (size_t)ns_lds_elems(ROWS, COLS) * sizeof(bf16);
   static bool attr = false;
   if (!attr) {
@@ -563,7 +563,7 @@ static hipError_t run_ns_fused(int count, const float* g, float* u, float eps, h
 }
 
 // Returns hipErrorNotSupported when no fused variant covers the shape.
-hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, const float* g, float* u,
+hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
                            float eps, hipStream_t s) {
   if (dtype != 1) return hipErrorNotSupported;
   if (rows == 128 && cols == 512) return run_ns_r128<512>(count, g, u, eps, s);

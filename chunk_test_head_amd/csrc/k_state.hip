@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     tile[j][4 * tx + 3] = s[3];
   }
   __syncthreads();
-  float* out = (mat == 0 ? a.out1 : mat == 1 ? a.out3 : a.out2) + (int64_t)head * msz;
+  float* out = mat == 0 ? a.out1 : mat == 1 ? a.out3 : a.out2;
+  if (out != nullptr) out += (int64_t)head * msz;
   float* m = (mat == 0 ? a.m1 : mat == 1 ? a.m3 : a.m2);
   float beta = 0.f;
   if (m != nullptr) {
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
       v = v + beta * mo;
       *reinterpret_cast<f32x4*>(mp) = v;
     }
-    *reinterpret_cast<f32x4*>(out + off) = v;
+    if (out != nullptr) *reinterpret_cast<f32x4*>(out + off) = v;
   }
 }
 
@@ -93,7 +94,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
 __global__ __launch_bounds__(256) void k_ns_norm(NsNormArgs a) {
   __shared__ float red[256];
   const int tid = threadIdx.x;
-  const float* g = a.g + (int64_t)blockIdx.x * a.n;
+  const float* g = a.g.at(blockIdx.x, a.n);
   float* x = a.x + (int64_t)blockIdx.x * a.n;
   float s = 0.f;
   for (int64_t e = (int64_t)tid * 4; e < a.n; e += 1024) {

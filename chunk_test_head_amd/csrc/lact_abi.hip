@@ -169,7 +169,7 @@ static int64_t ns_ws_bytes(int count, int rows, int cols) {
   return 3 * align256((int64_t)count * m * 4) + 2 * align256((int64_t)count * rows * rows * 4);
 }
 
-static hipError_t run_ns(int dtype, int count, int rows, int cols, const float* g, float* u,
+static hipError_t run_ns(int dtype, int count, int rows, int cols, NsIn g, float* u,
                          float eps, float* xa, float* xb, float* xh, float* am, float* bm,
                          hipStream_t s) {
   const int64_t m = (int64_t)rows * cols;
@@ -310,17 +310,25 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   float* g1 = w.g;
   float* g3 = w.g + mall;
   float* g2 = w.g + 2 * mall;
-  lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit, g1, g3, g2,
-                          op->use_momentum ? st->m1 : nullptr, op->use_momentum ? st->m3 : nullptr,
-                          op->use_momentum ? st->m2 : nullptr, op->use_momentum ? mom : nullptr, s);
+  // with momentum the reduced gradient lives in M only (M <- G + beta M)
+  const bool mo = op->use_momentum != 0;
+  lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
+                          mo ? nullptr : g1, mo ? nullptr : g3, mo ? nullptr : g2,
+                          mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr,
+                          mo ? mom : nullptr, s);
   if (r != LACT_OK) return r;
+  const float* u1 = mo ? st->m1 : g1;
+  const float* u3 = mo ? st->m3 : g3;
+  const float* u2 = mo ? st->m2 : g2;
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
-    hipError_t e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, w.g, w.g,
+    const NsIn in{{u1, u3, u2}, sh->bh};
+    hipError_t e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,
                           op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
     if (e != hipSuccess) return hip_fail(e);
+    u1 = g1; u3 = g3; u2 = g2;
   }
-  return do_step(sh, st, g1, g3, g2, op->renorm ? 1 : 0, op->renorm_eps, s);
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, s);
 }
 
 static lact_status check_update_args(const lact_shape* sh, const lact_state* st, const void* k,
@@ -445,7 +453,8 @@ lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_
   float* xh = reinterpret_cast<float*>(b + 2 * xm);
   float* a_ = reinterpret_cast<float*>(b + 3 * xm);
   float* b_ = reinterpret_cast<float*>(b + 3 * xm + am);
-  hipError_t e = run_ns(dtype, count, rows, cols, g, u, eps, xa, xb, xh, a_, b_, (hipStream_t)stream);
+  const NsIn in{{g, g, g}, count};
+  hipError_t e = run_ns(dtype, count, rows, cols, in, u, eps, xa, xb, xh, a_, b_, (hipStream_t)stream);
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 

@@ -40,7 +40,7 @@ struct ReduceArgs {
   const float* partial;  // [nsplit][bh][3][dh][d]
   int nsplit;
   int bh, d, dh;
-  float* out1; float* out3; float* out2;  // [bh][d][dh] each
+  float* out1; float* out3; float* out2;  // [bh][d][dh] each (NULL: only M holds the result)
   float* m1; float* m3; float* m2;        // momentum (NULL = off)
   // per-token momentum coefficients of the n_tok written tokens ([bh] x
   // stride mom_sbh); their mean is the coefficient of M
@@ -69,8 +69,19 @@ struct NsGemmArgs {
   float alpha, beta;
 };
 
+// Input matrices of a Newton-Schulz batch: matrix m is p[m / per] +
+// (m % per) * size (three separately allocated blocks, e.g. the momentum
+// buffers of W1, W3, W2, or one contiguous block with per = count).
+struct NsIn {
+  const float* p[3];
+  int per;
+  __host__ __device__ const float* at(int m, int64_t size) const {
+    return p[m / per] + (int64_t)(m % per) * size;
+  }
+};
+
 struct NsNormArgs {
-  const float* g; float* x; int64_t count, n; float eps;
+  NsIn g; float* x; int64_t count, n; float eps;
 };
 
 // Step: W <- W + U (wide U), per-row partial sums of squares.
@@ -89,11 +100,11 @@ hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
 int grad_hidden_per_block(int dtype, int d);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, const float* g, float* u,
+hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
                            float eps, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s);
-hipError_t launch_nsn(const float* g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,
+hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,
                       hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
 hipError_t launch_row_norms(const StepArgs& a, hipStream_t s);
