@@ -145,8 +145,10 @@ def main():
     torch.cuda.synchronize()
 
     # timed region; the dominant kernel (k_grad) is bracketed by HIP events on
-    # the same stream to give its average launch duration
-    n_grad = len(writes) * args.steps
+    # the same stream to give its average launch duration.  Only the launches
+    # of the first timed step are bracketed: each event record costs a few us
+    # of queue bubble, which would otherwise be charged to every step.
+    n_grad = len(writes)
     L.lact_prof_begin(L.PROF_GRAD, max(1, n_grad))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -109,17 +109,48 @@ static lact_status check_opts(const lact_update_opts* o) {
 // ------------------------------------------------------------ workspace --
 static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
+// Token splits of the gradient launch.  Its bf16 workgroups run one per
+// compute unit, in rounds of 256; a split costs its 32-token tiles in every
+// round and one more partial set (written, then read by the reduction).
+// The split count minimises
+//     rounds * tiles per split * t_tile + splits * t_partial
+// with t_tile = 12 d hpb flop per token x 32 tokens at ~2.8 TFLOP/s per CU and
+// t_partial = 2 x 3 d dh bh x 4 bytes at ~5 TB/s, over at most two rounds
+// (so the workspace bound below holds for every token count).
+static int nsplit_bound(const lact_shape* sh, int64_t n_tok) {
+  const int hpb = grad_hidden_per_block(sh->dtype, sh->d);
+  const int64_t base = (int64_t)sh->bh * ((sh->dh + hpb - 1) / hpb);
+  int64_t ns = (512 + base - 1) / base;
+  const int64_t tiles = (n_tok + 31) / 32;
+  if (ns > tiles) ns = tiles;
+  if (ns > 64) ns = 64;
+  return ns < 1 ? 1 : (int)ns;
+}
+
 static int choose_nsplit(const lact_shape* sh, int64_t n_tok) {
   const int hpb = grad_hidden_per_block(sh->dtype, sh->d);
-  const int64_t hblocks = (sh->dh + hpb - 1) / hpb;
-  const int64_t base = (int64_t)sh->bh * hblocks;
-  // one resident workgroup per CU: aim at 256 workgroups in all
-  int64_t ns = (256 + base - 1) / base;
-  const int64_t cap = (n_tok + 255) / 256;
-  if (ns > cap) ns = cap;
-  if (ns < 1) ns = 1;
-  if (ns > 64) ns = 64;
-  return (int)ns;
+  const int64_t base = (int64_t)sh->bh * ((sh->dh + hpb - 1) / hpb);
+  if (sh->dtype != LACT_BF16) {
+    // fp32: several workgroups per CU; at least 256 tokens per split
+    int64_t ns = (256 + base - 1) / base;
+    const int64_t cap = (n_tok + 255) / 256;
+    if (ns > cap) ns = cap;
+    if (ns > 64) ns = 64;
+    return ns < 1 ? 1 : (int)ns;
+  }
+  const int lim = nsplit_bound(sh, n_tok);
+  const int64_t tiles = (n_tok + 31) / 32;
+  const double t_tile = 32.0 * 12.0 * sh->d * hpb / 2.8e12;
+  const double t_part = 2.0 * 3.0 * sh->d * sh->dh * (double)sh->bh * 4.0 / 5e12;
+  int best = 1;
+  double best_t = 0.0;
+  for (int ns = 1; ns <= lim; ++ns) {
+    const int64_t rounds = (base * ns + 255) / 256;
+    const int64_t per = (tiles + ns - 1) / ns;
+    const double t = (double)(rounds * per) * t_tile + (ns > 1 ? ns * t_part : 0.0);
+    if (ns == 1 || t < best_t) { best = ns; best_t = t; }
+  }
+  return best;
 }
 
 struct Workspace {
@@ -368,7 +399,8 @@ size_t lact_workspace_bytes(const lact_shape* sh, int64_t max_update_tokens,
                             const lact_update_opts* opts) {
   if (check_shape(sh) != LACT_OK || max_update_tokens < 0) return 0;
   const bool muon = opts != nullptr && opts->use_muon != 0;
-  const int ns = choose_nsplit(sh, max_update_tokens);
+  const int ns = sh->dtype == LACT_BF16 ? nsplit_bound(sh, max_update_tokens)
+                                         : choose_nsplit(sh, max_update_tokens);
   return (size_t)layout_ws(sh, ns, muon, nullptr).bytes;
 }
 
@@ -561,7 +593,9 @@ lact_status lact_prof_begin(int32_t kind, int32_t max_launches) {
   if (g_prof.kind != 0) return LACT_ERR_INVALID_ARG;
   g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
   for (auto& e : g_prof.ev) {
-    hipError_t r = hipEventCreate(&e);
+    // timing only: no system-scope fence (no cache writeback between the
+    // bracketed launch and its neighbours)
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (r != hipSuccess) {
       for (auto& x : g_prof.ev)
         if (x) hipEventDestroy(x);
