@@ -13,6 +13,38 @@
 
 namespace lact {
 
+// ------------------------------------------------------------ LDS layout --
+// gfx950 LDS banks, as measured with the bank-conflict counter: the banks
+// repeat every 256 bytes for reads; a 16-byte read (ds_read_b128) is served
+// in four passes of 16 lanes, lanes 32 h + 4 j .. +3 (j = 0..7) going to pass
+// (h, parity of j); an 8-byte read (plain or transposing) in two passes of 32
+// lanes; a 16-byte write in eight passes of 8 lanes over 128 bytes.  A pass
+// is conflict-free when its lanes touch distinct bank words.
+//
+// Token (or weight) rows of D bf16 are stored unpadded with the 16-byte chunk
+// q of row r at chunk q ^ s(r):
+//   D >= 128:  s(r) = 2 (r % 8)        D = 64:  s(r) = 2 ((r / 2) % 4).
+// With it the three access patterns of the MFMA operands are conflict-free:
+// 16-byte row reads (lane (c, g) = (lane % 16, lane / 16) reads row c, chunk
+// 4 ks + g), 8-byte transposing reads (row 4 g + c / 4, columns
+// 16 it + 4 (c % 4) ..) and 16-byte staging writes of consecutive chunks.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  return D >= 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1;
+}
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * D + (((col >> 3) ^ swz_key<D>(r)) << 3) + (col & 7);
+}
+// Rows of 32 bf16 (64 bytes: a W2 block row, the block's hidden units in the
+// kappa run order): the 8-byte slot k stored at chunk (k / 2) ^ t(r), half
+// k % 2, with t(r) = (r / 2) % 2 + 2 ((r / 8) % 2) - conflict-free for the
+// 16-byte A-fragment reads (lane (c, g): row c, slots 2g, 2g+1) and for the
+// 8-byte staging writes (4 lanes per row).
+__device__ __forceinline__ int swz32(int r, int k) {
+  return r * 32 + ((((k >> 1) ^ (((r >> 1) & 1) | (((r >> 3) & 1) << 1)))) << 3) + 4 * (k & 1);
+}
+
 // ----------------------------------------------------------------- apply --
 // One workgroup = WAVES waves x NTW tokens of one head.  The hidden dim is
 // streamed in blocks of 32 rows: W1/W3 rows and W2 columns of the block are
@@ -26,12 +58,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
   constexpr int KS = D / 32;             // K slabs over d
   constexpr int IT = D / 16;             // output feature tiles
   constexpr int V = 16 / sizeof(T);      // elements per 16-byte vector
-  constexpr int P1 = D + V;              // LDS pitch of W1/W3 block rows
+  // bf16: W1/W3 block rows unpadded and swizzled (swz); fp32: padded rows
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int P1 = BF ? D : D + V;     // LDS pitch of W1/W3 block rows
   // W2 block rows: the 32 hidden values of a row stored in kappa order (runs
   // of four: 0-3, 16-19, 4-7, 20-23, ...), so that the A fragment of lane
-  // group g (hidden 4g..4g+3, 16+4g..16+4g+3) is one 16-byte read; the pitch
-  // (bf16: 80 bytes) puts 16 consecutive rows in distinct bank groups.
-  constexpr int P2 = sizeof(T) == 2 ? HB + 8 : HB + 4;
+  // group g (hidden 4g..4g+3, 16+4g..16+4g+3) is one 16-byte read (bf16:
+  // swz32 rows; fp32: padded rows)
+  constexpr int P2 = BF ? HB : HB + 4;
   constexpr int STAGE = 2 * HB * P1 + D * P2;
   constexpr int NV1 = HB * D / V / NTH;  // 16-byte vectors per thread (W1 / W3)
   constexpr int NV2 = D * HB / V / NTH;  // (W2)
@@ -103,8 +137,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
     _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
       const int row = vi / (D / V), col = (vi % (D / V)) * V;                       \
-      *reinterpret_cast<uint4*>(s1_ + row * P1 + col) = r1[x];                      \
-      *reinterpret_cast<uint4*>(s3_ + row * P1 + col) = r3[x];                      \
+      const int o_ = BF ? swz<D>(row, col) : row * P1 + col;                        \
+      *reinterpret_cast<uint4*>(s1_ + o_) = r1[x];                                  \
+      *reinterpret_cast<uint4*>(s3_ + o_) = r3[x];                                  \
     }                                                                               \
     _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
@@ -113,8 +148,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
         /* hidden col..col+7 = runs 2q, 2q+1 (q = col / 8) -> slots kpos */         \
         const int r0_ = col >> 2, r1_ = r0_ + 1;                                    \
         const int k0_ = 2 * (r0_ & 3) + (r0_ >> 2), k1_ = 2 * (r1_ & 3) + (r1_ >> 2); \
-        *reinterpret_cast<uint2*>(s2_ + row * P2 + 4 * k0_) = uint2{r2[x].x, r2[x].y}; \
-        *reinterpret_cast<uint2*>(s2_ + row * P2 + 4 * k1_) = uint2{r2[x].z, r2[x].w}; \
+        *reinterpret_cast<uint2*>(s2_ + swz32(row, k0_)) = uint2{r2[x].x, r2[x].y};   \
+        *reinterpret_cast<uint2*>(s2_ + swz32(row, k1_)) = uint2{r2[x].z, r2[x].w};   \
       } else {                                                                      \
         *reinterpret_cast<uint4*>(s2_ + row * P2 + col) = r2[x];                    \
       }                                                                             \
@@ -154,8 +189,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
-        const frag_t<T> a1 = ld8(s1 + (16 * jt + c) * P1 + 32 * ks + 8 * g);
-        const frag_t<T> a3 = ld8(s3 + (16 * jt + c) * P1 + 32 * ks + 8 * g);
+        const int o1 = BF ? swz<D>(16 * jt + c, 32 * ks + 8 * g) : (16 * jt + c) * P1 + 32 * ks + 8 * g;
+        const frag_t<T> a1 = ld8(s1 + o1);
+        const frag_t<T> a3 = ld8(s3 + o1);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
           mma(P[jt][tt], a1, qf[tt][ks]);
@@ -176,10 +212,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
     // o^T[feature][token] += W2[:, block] h^T
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const T* row = s2 + (16 * it + c) * P2;
       frag_t<T> a2;
-      if constexpr (sizeof(T) == 2) a2 = ld8(row + 8 * g);
-      else a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
+      if constexpr (BF) {
+        a2 = ld8(s2 + swz32(16 * it + c, 2 * g));
+      } else {
+        const T* row = s2 + (16 * it + c) * P2;
+        a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
+      }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
     }
@@ -196,6 +235,193 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
 #pragma unroll
       for (int it = 0; it < IT; ++it)
         st4(o + t * a.o_st + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
+            acc[it][tt][3]);
+    }
+  }
+}
+
+// ------------------------------------------------------ apply, d = 256 --
+// Wave pairs, as the d = 256 gradient kernel: the two waves of a pair read
+// the same 32 tokens and split the features.  Wave (p, h) keeps the q
+// fragments and the o^T accumulators of features [128 h, 128 h + 128).  Per
+// block of 32 hidden units:
+//   1. half-K partials of the gate / up pre-activations (W1, W3 block rows
+//      over its 128 features),
+//   2. exchanged through LDS and summed in a fixed order (half 0 + half 1),
+//   3. h = silu(g) u (identical in both waves), o^T rows of its features
+//      += W2[features, block] h^T.
+// One workgroup = 8 waves = 4 pairs = 128 tokens; two waves per SIMD.  LDS:
+// two stages of the W blocks (unpadded, 16-byte chunks XOR-swizzled) and the
+// exchange slots, 160 KiB.
+template <int D>
+__global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
+  constexpr int NTH = 512, HB = 32, DH2 = D / 2;
+  constexpr int KS = DH2 / 32;   // K slabs (own half)
+  constexpr int IT = DH2 / 16;   // own output feature tiles
+  constexpr int S1 = HB * D;     // one W1 / W3 block, [HB][D]
+  constexpr int S2 = D * HB;     // W2 block, [D][HB] (kappa slot order)
+  constexpr int STAGE = 2 * S1 + S2;
+  constexpr int NV1 = S1 / 8 / NTH, NV2 = S2 / 8 / NTH;
+  static_assert(NV1 * 8 * NTH == S1 && NV2 * 8 * NTH == S2, "stage split");
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * STAGE];
+  __shared__ f32x4 sX[8][8][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int pair = wave >> 1, half = wave & 1;
+  const int tiles = (int)((a.n_tok + 127) / 128);
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int head = lid / tiles, tile = lid % tiles;
+  if (head >= a.bh) return;
+  const int dh = a.dh;
+  const int d0 = half * DH2;
+  const int64_t tok0 = (int64_t)tile * 128 + 32 * pair;
+
+  const bf16* q = reinterpret_cast<const bf16*>(a.q) + (int64_t)head * a.q_sbh;
+  bf16* o = reinterpret_cast<bf16*>(a.o) + (int64_t)head * a.o_sbh;
+  const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+  const bf16* w1 = sb + a.sh.off_w1;
+  const bf16* w3 = sb + a.sh.off_w3;
+  const bf16* w2 = sb + a.sh.off_w2;
+
+  // q^T fragments of the own feature half (B operand, K = features)
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (t < a.n_tok) {
+        qf[tt][ks] = ld8(q + t * a.q_st + d0 + 32 * ks + 8 * g);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) qf[tt][ks][m] = (bf16)0.f;
+      }
+    }
+  }
+  f32x4 acc[IT][2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // W2 block rows (features) of HB = 32 hidden units in kappa slot order (swz32)
+#define LACT_AP_GLOAD(JB)                                                              \
+  {                                                                                    \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
+      const int vi = tid + x * NTH;                                                    \
+      r1[x] = ld8(w1 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
+      r3[x] = ld8(w3 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
+    }                                                                                  \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
+      const int vi = tid + x * NTH;                                                    \
+      r2[x] = ld8(w2 + (int64_t)(vi >> 2) * dh + (JB) * HB + (vi & 3) * 8);          \
+    }                                                                                  \
+  }
+#define LACT_AP_LSTORE(BUF)                                                            \
+  {                                                                                    \
+    bf16* s1_ = lds + (BUF) * STAGE;                                                   \
+    bf16* s3_ = s1_ + S1;                                                              \
+    bf16* s2_ = s3_ + S1;                                                              \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
+      const int vi = tid + x * NTH;                                                    \
+      const int o_ = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                         \
+      *reinterpret_cast<bf16x8*>(s1_ + o_) = r1[x];                                    \
+      *reinterpret_cast<bf16x8*>(s3_ + o_) = r3[x];                                    \
+    }                                                                                  \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
+      const int vi = tid + x * NTH;                                                    \
+      const int row = vi >> 2, ru0 = 2 * (vi & 3), ru1 = ru0 + 1;                      \
+      *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru0 & 3) + (ru0 >> 2))) = __builtin_shufflevector(r2[x], r2[x], 0, 1, 2, 3); \
+      *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru1 & 3) + (ru1 >> 2))) = __builtin_shufflevector(r2[x], r2[x], 4, 5, 6, 7); \
+    }                                                                                  \
+  }
+
+  const int NB = dh / HB;
+  {
+    bf16x8 r1[NV1], r3[NV1], r2[NV2];
+    LACT_AP_GLOAD(0);
+    LACT_AP_LSTORE(0);
+  }
+  __syncthreads();
+  for (int jb = 0; jb < NB; ++jb) {
+    const int buf = jb & 1;
+    // the next block (the last one again at the end: branch-free, so the
+    // staging registers stay registers; the spare copy lands in the idle
+    // buffer)
+    bf16x8 r1[NV1], r3[NV1], r2[NV2];
+    LACT_AP_GLOAD(min(jb + 1, NB - 1));
+    const bf16* s1 = lds + buf * STAGE;
+    const bf16* s3 = s1 + S1;
+    const bf16* s2 = s3 + S1;
+    // 1. half-K partials, transposed: P^T[hidden][token]
+    f32x4 P[2][2], U[2][2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const bf16x8 a1 = ld8(s1 + swz<D>(16 * jt + c, d0 + 32 * ks + 8 * g));
+        const bf16x8 a3 = ld8(s3 + swz<D>(16 * jt + c, d0 + 32 * ks + 8 * g));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          mma(P[jt][tt], a1, qf[tt][ks]);
+          mma(U[jt][tt], a3, qf[tt][ks]);
+        }
+      }
+    // 2. exchange, fixed-order sum
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sX[wave][2 * jt + tt][lane] = P[jt][tt];
+        sX[wave][4 + 2 * jt + tt][lane] = U[jt][tt];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 op = sX[wave ^ 1][2 * jt + tt][lane], ou = sX[wave ^ 1][4 + 2 * jt + tt][lane];
+        P[jt][tt] = half == 0 ? P[jt][tt] + op : op + P[jt][tt];
+        U[jt][tt] = half == 0 ? U[jt][tt] + ou : ou + U[jt][tt];
+      }
+    // 3. h = silu(P) U as the B operand (K = the 32 hidden units, kappa order)
+    bf16x8 hf[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = P[0][tt][i], p1 = P[1][tt][i];
+        hf[tt][i] = (bf16)(p0 * sigmoid_fast(p0) * U[0][tt][i]);
+        hf[tt][4 + i] = (bf16)(p1 * sigmoid_fast(p1) * U[1][tt][i]);
+      }
+    //    o^T[own features][token] += W2[own features, block] h^T
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const bf16x8 a2 = ld8(s2 + swz32(d0 + 16 * it + c, 2 * g));
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) mma(acc[it][tt], a2, hf[tt]);
+    }
+    LACT_AP_LSTORE(buf ^ 1);
+    __syncthreads();  // stage and exchange slots free
+  }
+#undef LACT_AP_GLOAD
+#undef LACT_AP_LSTORE
+
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+    if (t < a.n_tok) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+        st4(o + t * a.o_st + d0 + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
             acc[it][tt][3]);
     }
   }
@@ -392,213 +618,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
 // flight while the current one is computed).  The forward contractions read
 // k / v rows (K = d); the gradient contractions read k^T / v^T fragments
 // (K = tokens) from the same tiles with LDS transpose reads.
-// Tile layout: row r (token), 16-byte chunk q of the row stored at chunk
-// q ^ s(r).  For D >= 128 (rows of 16 or more chunks)
-//   s(r) = 2 (r % 4) + 8 ((r / 4) % 2) + (r / 8) % 2,
-// so 16 consecutive rows put one chunk in 16 distinct bank groups (16-byte
-// row reads of the forward contractions), and rows 4g .. 4g+3 of the lane
-// groups g = 0, 1 put two adjacent chunks in 16 distinct bank groups (the
-// 8-byte transpose reads).  D = 64 rows are 8 chunks: s(r) = 2 (r % 4) +
-// (r / 4) % 2 stays inside the row.
-template <int D>
-__device__ __forceinline__ int swz_key(int r) {
-  return D >= 128 ? ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1)
-                  : ((r & 3) << 1) | ((r >> 2) & 1);
-}
-template <int D>
-__device__ __forceinline__ int swz(int r, int col) {
-  return r * D + (((col >> 3) ^ swz_key<D>(r)) << 3) + (col & 7);
-}
-
-// ------------------------------------------------------ apply, d = 256 --
-// Wave pairs, as the d = 256 gradient kernel: the two waves of a pair read
-// the same 32 tokens and split the features.  Wave (p, h) keeps the q
-// fragments and the o^T accumulators of features [128 h, 128 h + 128).  Per
-// block of 32 hidden units:
-//   1. half-K partials of the gate / up pre-activations (W1, W3 block rows
-//      over its 128 features),
-//   2. exchanged through LDS and summed in a fixed order (half 0 + half 1),
-//   3. h = silu(g) u (identical in both waves), o^T rows of its features
-//      += W2[features, block] h^T.
-// One workgroup = 8 waves = 4 pairs = 128 tokens; two waves per SIMD.  LDS:
-// two stages of the W blocks (unpadded, 16-byte chunks XOR-swizzled) and the
-// exchange slots, 160 KiB.
-template <int D>
-__global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
-  constexpr int NTH = 512, HB = 32, DH2 = D / 2;
-  constexpr int KS = DH2 / 32;   // K slabs (own half)
-  constexpr int IT = DH2 / 16;   // own output feature tiles
-  constexpr int S1 = HB * D;     // one W1 / W3 block, [HB][D]
-  constexpr int S2 = D * HB;     // W2 block, [D][HB] (kappa slot order)
-  constexpr int STAGE = 2 * S1 + S2;
-  constexpr int NV1 = S1 / 8 / NTH, NV2 = S2 / 8 / NTH;
-  static_assert(NV1 * 8 * NTH == S1 && NV2 * 8 * NTH == S2, "stage split");
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * STAGE];
-  __shared__ f32x4 sX[8][8][64];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int pair = wave >> 1, half = wave & 1;
-  const int tiles = (int)((a.n_tok + 127) / 128);
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int head = lid / tiles, tile = lid % tiles;
-  if (head >= a.bh) return;
-  const int dh = a.dh;
-  const int d0 = half * DH2;
-  const int64_t tok0 = (int64_t)tile * 128 + 32 * pair;
-
-  const bf16* q = reinterpret_cast<const bf16*>(a.q) + (int64_t)head * a.q_sbh;
-  bf16* o = reinterpret_cast<bf16*>(a.o) + (int64_t)head * a.o_sbh;
-  const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
-  const bf16* w1 = sb + a.sh.off_w1;
-  const bf16* w3 = sb + a.sh.off_w3;
-  const bf16* w2 = sb + a.sh.off_w2;
-
-  // q^T fragments of the own feature half (B operand, K = features)
-  bf16x8 qf[2][KS];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int64_t t = tok0 + 16 * tt + c;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (t < a.n_tok) {
-        qf[tt][ks] = ld8(q + t * a.q_st + d0 + 32 * ks + 8 * g);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) qf[tt][ks][m] = (bf16)0.f;
-      }
-    }
-  }
-  f32x4 acc[IT][2];
-#pragma unroll
-  for (int it = 0; it < IT; ++it)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // W2 block row r (a feature), 8-byte slot k (hidden run order kappa):
-  // 16-byte chunk k / 2 of the row stored at chunk (k / 2) ^ ((r / 4) % 4)
-  auto w2off = [](int r, int k) { return r * HB + ((((k >> 1) ^ ((r >> 2) & 3))) << 3) + 4 * (k & 1); };
-#define LACT_AP_GLOAD(JB)                                                              \
-  {                                                                                    \
-    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      r1[x] = ld8(w1 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
-      r3[x] = ld8(w3 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
-    }                                                                                  \
-    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      r2[x] = ld8(w2 + (int64_t)(vi >> 2) * dh + (JB) * HB + (vi & 3) * 8);          \
-    }                                                                                  \
-  }
-#define LACT_AP_LSTORE(BUF)                                                            \
-  {                                                                                    \
-    bf16* s1_ = lds + (BUF) * STAGE;                                                   \
-    bf16* s3_ = s1_ + S1;                                                              \
-    bf16* s2_ = s3_ + S1;                                                              \
-    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      const int o_ = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                         \
-      *reinterpret_cast<bf16x8*>(s1_ + o_) = r1[x];                                    \
-      *reinterpret_cast<bf16x8*>(s3_ + o_) = r3[x];                                    \
-    }                                                                                  \
-    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      const int row = vi >> 2, ru0 = 2 * (vi & 3), ru1 = ru0 + 1;                      \
-      *reinterpret_cast<bf16x4*>(s2_ + w2off(row, 2 * (ru0 & 3) + (ru0 >> 2))) = __builtin_shufflevector(r2[x], r2[x], 0, 1, 2, 3); \
-      *reinterpret_cast<bf16x4*>(s2_ + w2off(row, 2 * (ru1 & 3) + (ru1 >> 2))) = __builtin_shufflevector(r2[x], r2[x], 4, 5, 6, 7); \
-    }                                                                                  \
-  }
-
-  const int NB = dh / HB;
-  {
-    bf16x8 r1[NV1], r3[NV1], r2[NV2];
-    LACT_AP_GLOAD(0);
-    LACT_AP_LSTORE(0);
-  }
-  __syncthreads();
-  for (int jb = 0; jb < NB; ++jb) {
-    const int buf = jb & 1;
-    // the next block (the last one again at the end: branch-free, so the
-    // staging registers stay registers; the spare copy lands in the idle
-    // buffer)
-    bf16x8 r1[NV1], r3[NV1], r2[NV2];
-    LACT_AP_GLOAD(min(jb + 1, NB - 1));
-    const bf16* s1 = lds + buf * STAGE;
-    const bf16* s3 = s1 + S1;
-    const bf16* s2 = s3 + S1;
-    // 1. half-K partials, transposed: P^T[hidden][token]
-    f32x4 P[2][2], U[2][2];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const bf16x8 a1 = ld8(s1 + swz<D>(16 * jt + c, d0 + 32 * ks + 8 * g));
-        const bf16x8 a3 = ld8(s3 + swz<D>(16 * jt + c, d0 + 32 * ks + 8 * g));
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          mma(P[jt][tt], a1, qf[tt][ks]);
-          mma(U[jt][tt], a3, qf[tt][ks]);
-        }
-      }
-    // 2. exchange, fixed-order sum
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sX[wave][2 * jt + tt][lane] = P[jt][tt];
-        sX[wave][4 + 2 * jt + tt][lane] = U[jt][tt];
-      }
-    __syncthreads();
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 op = sX[wave ^ 1][2 * jt + tt][lane], ou = sX[wave ^ 1][4 + 2 * jt + tt][lane];
-        P[jt][tt] = half == 0 ? P[jt][tt] + op : op + P[jt][tt];
-        U[jt][tt] = half == 0 ? U[jt][tt] + ou : ou + U[jt][tt];
-      }
-    // 3. h = silu(P) U as the B operand (K = the 32 hidden units, kappa order)
-    bf16x8 hf[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = P[0][tt][i], p1 = P[1][tt][i];
-        hf[tt][i] = (bf16)(p0 * sigmoid_fast(p0) * U[0][tt][i]);
-        hf[tt][4 + i] = (bf16)(p1 * sigmoid_fast(p1) * U[1][tt][i]);
-      }
-    //    o^T[own features][token] += W2[own features, block] h^T
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const bf16x8 a2 = ld8(s2 + w2off(d0 + 16 * it + c, 2 * g));
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) mma(acc[it][tt], a2, hf[tt]);
-    }
-    LACT_AP_LSTORE(buf ^ 1);
-    __syncthreads();  // stage and exchange slots free
-  }
-#undef LACT_AP_GLOAD
-#undef LACT_AP_LSTORE
-
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int64_t t = tok0 + 16 * tt + c;
-    if (t < a.n_tok) {
-#pragma unroll
-      for (int it = 0; it < IT; ++it)
-        st4(o + t * a.o_st + d0 + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
-            acc[it][tt][3]);
-    }
-  }
-}
-
+// Tile layout: rows of D bf16, 16-byte chunks XOR-swizzled (swz).
 template <int D, int WAVES, int HT, bool PIPE>
 __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int NTH = WAVES * 64;
