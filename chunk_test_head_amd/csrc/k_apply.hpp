@@ -1,0 +1,249 @@
+// Read (apply) workgroup body and the LDS layouts of the MFMA operand tiles.
+//
+// Read (LaCT rebuttal page, apply step of both pseudocode functions):
+//   o_t = W2 (silu(W1 q_t) * (W3 q_t)).
+#pragma once
+#include "lact_internal.hpp"
+#include "mfma.hpp"
+
+namespace lact {
+
+// ------------------------------------------------------------ LDS layout --
+// gfx950 LDS banks, as measured with the bank-conflict counter: the banks
+// repeat every 256 bytes for reads; a 16-byte read (ds_read_b128) is served
+// in four passes of 16 lanes, lanes 32 h + 4 j .. +3 (j = 0..7) going to pass
+// (h, parity of j); an 8-byte read (plain or transposing) in two passes of 32
+// lanes; a 16-byte write in eight passes of 8 lanes over 128 bytes.  A pass
+// is conflict-free when its lanes touch distinct bank words.
+//
+// Token (or weight) rows of D bf16 are stored unpadded with the 16-byte chunk
+// q of row r at chunk q ^ s(r):
+//   D >= 128:  s(r) = 2 (r % 8)        D = 64:  s(r) = 2 ((r / 2) % 4).
+// With it the three access patterns of the MFMA operands are conflict-free:
+// 16-byte row reads (lane (c, g) = (lane % 16, lane / 16) reads row c, chunk
+// 4 ks + g), 8-byte transposing reads (row 4 g + c / 4, columns
+// 16 it + 4 (c % 4) ..) and 16-byte staging writes of consecutive chunks.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  return D >= 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1;
+}
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * D + (((col >> 3) ^ swz_key<D>(r)) << 3) + (col & 7);
+}
+// Rows of 32 bf16 (64 bytes: a W2 block row, the block's hidden units in the
+// kappa run order): the 8-byte slot k stored at chunk (k / 2) ^ t(r), half
+// k % 2, with t(r) = (r / 2) % 2 + 2 ((r / 8) % 2) - conflict-free for the
+// 16-byte A-fragment reads (lane (c, g): row c, slots 2g, 2g+1) and for the
+// 8-byte staging writes (4 lanes per row).
+__device__ __forceinline__ int swz32(int r, int k) {
+  return r * 32 + ((((k >> 1) ^ (((r >> 1) & 1) | (((r >> 3) & 1) << 1)))) << 3) + 4 * (k & 1);
+}
+
+// ----------------------------------------------------------------- apply --
+// One workgroup = WAVES waves x NTW tokens of one head.  The hidden dim is
+// streamed in blocks of 32 rows: W1/W3 rows and W2 columns of the block are
+// staged in LDS (double buffered) and shared by all waves; each wave keeps its
+// q fragments and its output accumulators (o^T, d x NTW) in registers.
+template <class T, int D>
+struct ApplyLds {
+  static constexpr int HB = 32, V = 16 / sizeof(T);
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int P1 = BF ? D : D + V, P2 = BF ? HB : HB + 4;
+  static constexpr int STAGE = 2 * HB * P1 + D * P2;
+  static constexpr int SUB = (BF && D <= 128) ? 2 : 1;
+  static constexpr int ELEMS = 2 * SUB * STAGE;
+};
+
+// Body of one workgroup: logical block lid (head-major tiles), LDS of
+// ApplyLds<T, D>::ELEMS elements.
+template <class T, int D, int NTW, int WAVES>
+__device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds) {
+  constexpr int NTH = WAVES * 64;
+  constexpr int HB = 32;                 // hidden rows per stage
+  constexpr int NT = NTW / 16;           // 16-token tiles per wave
+  constexpr int KS = D / 32;             // K slabs over d
+  constexpr int IT = D / 16;             // output feature tiles
+  constexpr int V = 16 / sizeof(T);      // elements per 16-byte vector
+  // bf16: W1/W3 block rows unpadded and swizzled (swz); fp32: padded rows
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int P1 = BF ? D : D + V;     // LDS pitch of W1/W3 block rows
+  // W2 block rows: the 32 hidden values of a row stored in kappa order (runs
+  // of four: 0-3, 16-19, 4-7, 20-23, ...), so that the A fragment of lane
+  // group g (hidden 4g..4g+3, 16+4g..16+4g+3) is one 16-byte read (bf16:
+  // swz32 rows; fp32: padded rows)
+  constexpr int P2 = BF ? HB : HB + 4;
+  constexpr int STAGE = 2 * HB * P1 + D * P2;
+  constexpr int NV1 = HB * D / V / NTH;  // 16-byte vectors per thread (W1 / W3)
+  constexpr int NV2 = D * HB / V / NTH;  // (W2)
+  static_assert(NV1 * V * NTH == HB * D && NV2 * V * NTH == D * HB, "stage split");
+
+  // SUB hidden blocks per barrier (bf16, d <= 128: LDS allows two), double
+  // buffered: slots (stage % 2) SUB + sub
+  constexpr int SUB = ApplyLds<T, D>::SUB;
+  static_assert(ApplyLds<T, D>::STAGE == STAGE, "layout");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int tiles = (int)((a.n_tok + (int64_t)WAVES * NTW - 1) / ((int64_t)WAVES * NTW));
+  const int head = lid / tiles, tile = lid % tiles;
+  if (head >= a.bh) return;
+  const int dh = a.dh;
+  const int64_t tok0 = (int64_t)tile * WAVES * NTW + (int64_t)wave * NTW;
+
+  const T* q = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.q_sbh;
+  T* o = reinterpret_cast<T*>(a.o) + (int64_t)head * a.o_sbh;
+  const T* sb = reinterpret_cast<const T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+  const T* w1 = sb + a.sh.off_w1;
+  const T* w3 = sb + a.sh.off_w3;
+  const T* w2 = sb + a.sh.off_w2;
+
+  // q^T fragments (B operand, K = d): lane holds q[token 16tt + c][32ks + 8g ..]
+  frag_t<T> qf[NT][KS];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (t < a.n_tok) {
+        qf[tt][ks] = ld8(q + t * a.q_st + 32 * ks + 8 * g);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) qf[tt][ks][m] = to_t<T>(0.f);
+      }
+    }
+  }
+
+  f32x4 acc[IT][NT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 r1[NV1], r3[NV1], r2[NV2];
+  // stage jb: W1 / W3 rows [jb HB, +HB) (contiguous) and W2 columns (rows of
+  // HB elements at pitch dh), as 16-byte vectors
+#define LACT_APPLY_GLOAD(JB)                                                        \
+  {                                                                                 \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      r1[x] = *reinterpret_cast<const uint4*>(w1 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
+      r3[x] = *reinterpret_cast<const uint4*>(w3 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
+    }                                                                               \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      r2[x] = *reinterpret_cast<const uint4*>(w2 + (int64_t)(vi / (HB / V)) * dh + (JB) * HB + (vi % (HB / V)) * V); \
+    }                                                                               \
+  }
+#define LACT_APPLY_LSTORE(BUF)                                                      \
+  {                                                                                 \
+    T* s1_ = lds + (BUF) * STAGE;                                                   \
+    T* s3_ = s1_ + HB * P1;                                                         \
+    T* s2_ = s3_ + HB * P1;                                                         \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      const int row = vi / (D / V), col = (vi % (D / V)) * V;                       \
+      const int o_ = BF ? swz<D>(row, col) : row * P1 + col;                        \
+      *reinterpret_cast<uint4*>(s1_ + o_) = r1[x];                                  \
+      *reinterpret_cast<uint4*>(s3_ + o_) = r3[x];                                  \
+    }                                                                               \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
+      const int vi = tid + x * NTH;                                                 \
+      const int row = vi / (HB / V), col = (vi % (HB / V)) * V;                     \
+      if constexpr (sizeof(T) == 2) {                                               \
+        /* hidden col..col+7 = runs 2q, 2q+1 (q = col / 8) -> slots kpos */         \
+        const int r0_ = col >> 2, r1_ = r0_ + 1;                                    \
+        const int k0_ = 2 * (r0_ & 3) + (r0_ >> 2), k1_ = 2 * (r1_ & 3) + (r1_ >> 2); \
+        *reinterpret_cast<uint2*>(s2_ + swz32(row, k0_)) = uint2{r2[x].x, r2[x].y};   \
+        *reinterpret_cast<uint2*>(s2_ + swz32(row, k1_)) = uint2{r2[x].z, r2[x].w};   \
+      } else {                                                                      \
+        *reinterpret_cast<uint4*>(s2_ + row * P2 + col) = r2[x];                    \
+      }                                                                             \
+    }                                                                               \
+  }
+
+  const int NB = dh / HB;
+  const int nst = (NB + SUB - 1) / SUB;
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb)
+    if (sb < NB) {
+      LACT_APPLY_GLOAD(sb);
+      LACT_APPLY_LSTORE(sb);
+    }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st)
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb) {
+    const int jb = st * SUB + sb, jn = jb + SUB;
+    const int buf = (st & 1) * SUB + sb, nbuf = ((st + 1) & 1) * SUB + sb;
+    if (jn < NB) LACT_APPLY_GLOAD(jn);
+    if (jb >= NB) continue;
+    const T* s1 = lds + buf * STAGE;
+    const T* s3 = s1 + HB * P1;
+    const T* s2 = s3 + HB * P1;
+
+    // gate / up pre-activations, transposed: P^T[hidden][token]
+    f32x4 P[2][NT], U[2][NT];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const int o1 = BF ? swz<D>(16 * jt + c, 32 * ks + 8 * g) : (16 * jt + c) * P1 + 32 * ks + 8 * g;
+        const frag_t<T> a1 = ld8(s1 + o1);
+        const frag_t<T> a3 = ld8(s3 + o1);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          mma(P[jt][tt], a1, qf[tt][ks]);
+          mma(U[jt][tt], a3, qf[tt][ks]);
+        }
+      }
+    }
+    // h = silu(P) * U, packed as the B operand (K = the 32 hidden rows).
+    frag_t<T> hf[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = P[0][tt][i], p1 = P[1][tt][i];
+        hf[tt][i] = to_t<T>(p0 * sigmoid_fast(p0) * U[0][tt][i]);
+        hf[tt][4 + i] = to_t<T>(p1 * sigmoid_fast(p1) * U[1][tt][i]);
+      }
+    // o^T[feature][token] += W2[:, block] h^T
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      frag_t<T> a2;
+      if constexpr (BF) {
+        a2 = ld8(s2 + swz32(16 * it + c, 2 * g));
+      } else {
+        const T* row = s2 + (16 * it + c) * P2;
+        a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
+    }
+    if (jn < NB) LACT_APPLY_LSTORE(nbuf);
+    if (sb == SUB - 1) __syncthreads();
+  }
+#undef LACT_APPLY_GLOAD
+#undef LACT_APPLY_LSTORE
+
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+    if (t < a.n_tok) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+        st4(o + t * a.o_st + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
+            acc[it][tt][3]);
+    }
+  }
+}
+
+}  // namespace lact

@@ -20,6 +20,7 @@
 //      X (B operand, K = rows) and rows of B from LDS; X = a X + B X in fp32.
 #include "lact_internal.hpp"
 #include "mfma.hpp"
+#include "k_apply.hpp"
 
 namespace lact {
 
@@ -296,14 +297,23 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
 //      Y[16 nt + c][col0 + 16 mt + 4 g + i], four consecutive columns of one
 //      row, so global loads/stores and the bf16 copy to sX are 16 / 8-byte
 //      vectors.  The Y^T fragments are transpose reads of sX.
-// LDS rows are split into 16-byte chunks whose index is XORed with a function
-// of the row, so that 16-byte fragment reads (16 rows, one chunk column),
-// 8-byte tile stores and transpose reads (4 rows x 2 chunks per 16-lane group)
-// fall in distinct bank groups.
-__device__ __forceinline__ int nsr_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+// LDS rows are split into 16-byte chunks whose index is XORed with a linear
+// function of the row bits r0..r3, chosen with the measured gfx950 bank
+// model (16-byte reads in 16-lane passes by lane-quad parity, 8-byte reads
+// in 32-lane passes, 8-byte writes in 16-lane passes over 128 bytes):
+//   sX (rows of COLS):  s(r) = 2 r0 ^ 4 r1 ^ 9 r3 - fragment reads (16 rows,
+//     one chunk column) and transpose reads (rows 8 g + 0..3) conflict-free,
+//     operand-copy stores (16 rows, one column) two-way, the least possible;
+//   sA (rows of 128):   s(r) = r mod 16 - fragment reads and the 8-byte reads
+//     of B' conflict-free, transposed tile stores two-way.
+template <int W>
+__device__ __forceinline__ int nsr_swz(int r) {
+  if constexpr (W == 128) return r & 15;
+  return ((r & 1) << 1) ^ (((r >> 1) & 1) << 2) ^ (((r >> 3) & 1) * 9);
+}
 template <int W>
 __device__ __forceinline__ int nsr_off(int r, int col) {
-  return r * W + ((((col >> 3) ^ nsr_swz(r))) << 3) + (col & 7);
+  return r * W + ((((col >> 3) ^ nsr_swz<W>(r))) << 3) + (col & 7);
 }
 
 // An opaque copy of a lane index: address arithmetic derived from it is
@@ -324,7 +334,7 @@ __device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, i
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16* bx = s + (16 * x0 + c) * W;
   const bf16* by = s + (16 * y0 + c) * W;
-  const int sw = nsr_swz(c);
+  const int sw = nsr_swz<W>(c);
   bf16x8 fx[4], fy[2];
 #define LACT_NSR_LOAD(K0, FX, FY)                                                   \
   {                                                                                 \
@@ -371,14 +381,13 @@ __device__ __forceinline__ void nsr_store(bf16* s, int x0, int y0, int c, int gq
 }
 
 template <int COLS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_ns_r128(NsIn g, float* u, float eps) {
+__device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps, int m,
+                                              bf16* lds_r) {
   constexpr int R = 128, NW = 8;
   constexpr int CW = COLS / NW;  // columns per wave
   constexpr int NMT = CW / 16;   // column tiles per wave
   constexpr int NRT = R / 16;    // row tiles
   static_assert(CW % 16 == 0, "shape");
-  extern __shared__ __attribute__((aligned(16))) bf16 lds_r[];
   bf16* sX = lds_r;
   bf16* sA = lds_r + R * COLS;
 
@@ -388,8 +397,8 @@ void k_ns_r128(NsIn g, float* u, float eps) {
   const int bx0 = 4 * (w >> 2), by0 = 2 * (w & 3);  // this wave's block of A
   const bool active = !(w == 4 || w == 5);          // blocks below the diagonal: mirrored
   const bool direct = (w == 2 || w == 3);           // blocks above it
-  const float* G = g.at(blockIdx.x, (int64_t)R * COLS);
-  float* U = u + (int64_t)blockIdx.x * R * COLS;
+  const float* G = g.at(m, (int64_t)R * COLS);
+  float* U = u + (int64_t)m * R * COLS;
 
   // ---- load G: whole rows, coalesced, staged through LDS (fp32, 16-byte
   // chunks XORed with the row) into the accumulator layout ----
@@ -535,6 +544,47 @@ void k_ns_r128(NsIn g, float* u, float eps) {
 }
 
 template <int COLS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_ns_r128(NsIn g, float* u, float eps) {
+  extern __shared__ __attribute__((aligned(16))) bf16 lds_r[];
+  ns_r128_block<COLS>(g, u, eps, blockIdx.x, lds_r);
+}
+
+// Newton-Schulz of the write and a read that uses the weights this write
+// replaces, in one launch: workgroups [0, count) run the matrices, the rest
+// the read's tiles (d = 128).  Workgroups start in index order, so the
+// matrices get their compute units first and the read fills the others -
+// the Newton-Schulz launch alone holds one workgroup per matrix and leaves
+// most compute units idle.
+template <int COLS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_ns_apply(NsIn g, float* u, float eps, int count, ApplyArgs a) {
+  extern __shared__ __attribute__((aligned(16))) bf16 lds_f[];
+  const int b = blockIdx.x;
+  if (b < count) ns_r128_block<COLS>(g, u, eps, b, lds_f);
+  else apply_block<bf16, 128, 32, 8>(a, xcd_logical_id(b - count, (int)gridDim.x - count), lds_f);
+}
+
+template <int COLS>
+static hipError_t run_ns_apply(int count, NsIn g, float* u, float eps, const ApplyArgs& a,
+                               hipStream_t s) {
+  const size_t lns = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
+  const size_t lap = (size_t)ApplyLds<bf16, 128>::ELEMS * sizeof(bf16);
+  const size_t lds = lns > lap ? lns : lap;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ns_apply<COLS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t napply = (a.n_tok + 255) / 256 * a.bh;
+  hipLaunchKernelGGL((k_ns_apply<COLS>), dim3((unsigned)(count + napply)), dim3(512), lds, s, g, u,
+                     eps, count, a);
+  return hipGetLastError();
+}
+
+template <int COLS>
 static hipError_t run_ns_r128(int count, NsIn g, float* u, float eps, hipStream_t s) {
   const size_t lds = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
   static bool attr = false;
@@ -563,6 +613,14 @@ static hipError_t run_ns_fused(int count, NsIn g, float* u, float eps, hipStream
 }
 
 // Returns hipErrorNotSupported when no fused variant covers the shape.
+hipError_t launch_ns_apply(int count, int rows, int cols, NsIn g, float* u, float eps,
+                           const ApplyArgs& a, hipStream_t s) {
+  if (rows != 128 || a.d != 128 || a.n_tok <= 0) return hipErrorNotSupported;
+  if (cols == 512) return run_ns_apply<512>(count, g, u, eps, a, s);
+  if (cols == 256) return run_ns_apply<256>(count, g, u, eps, a, s);
+  return hipErrorNotSupported;
+}
+
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
                            float eps, hipStream_t s) {
   if (dtype != 1) return hipErrorNotSupported;

@@ -264,15 +264,33 @@ static hipError_t run_ns(int dtype, int count, int rows, int cols, NsIn g, float
 }
 
 // -------------------------------------------------------------- pieces --
-static lact_status do_apply(const lact_shape* sh, const lact_state* st, const void* q,
-                            lact_layout ql, void* o, lact_layout ol, int64_t n_tok,
-                            hipStream_t s) {
-  if (n_tok == 0) return LACT_OK;
+// A read (apply) that the drivers may hand to the next write: within one
+// chunk step the read and the write gradient both use the current weights and
+// only the step kernel replaces them, so the read can share the
+// Newton-Schulz launch (which alone leaves most compute units idle).
+struct ApplyJob {
+  const void* q;
+  lact_layout ql;
+  void* o;
+  lact_layout ol;
+  int64_t n_tok;
+};
+
+static ApplyArgs apply_args(const lact_shape* sh, const lact_state* st, const void* q,
+                            lact_layout ql, void* o, lact_layout ol, int64_t n_tok) {
   ApplyArgs a;
   a.q = q; a.q_sbh = ql.stride_bh; a.q_st = ql.stride_tok;
   a.o = o; a.o_sbh = ol.stride_bh; a.o_st = ol.stride_tok;
   a.sh = make_shadow(st->shadow, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh; a.n_tok = n_tok;
+  return a;
+}
+
+static lact_status do_apply(const lact_shape* sh, const lact_state* st, const void* q,
+                            lact_layout ql, void* o, lact_layout ol, int64_t n_tok,
+                            hipStream_t s) {
+  if (n_tok == 0) return LACT_OK;
+  const ApplyArgs a = apply_args(sh, st, q, ql, o, ol, n_tok);
   hipError_t e;
   {
     ProfScope p(LACT_PROF_APPLY, s);
@@ -333,7 +351,15 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                              lact_layout kl, const void* v, lact_layout vl, const float* e1,
                              const float* e3, const float* e2, const float* mom, int64_t esbh,
                              int64_t n_tok, const lact_update_opts* op, void* ws,
-                             hipStream_t s) {
+                             hipStream_t s, const ApplyJob* job = nullptr) {
+  // job: a read with the weights this write replaces; it shares the
+  // Newton-Schulz launch where that kernel supports it, else runs first
+  const bool fuse = job != nullptr && job->n_tok > 0 && op->use_muon && !op->ns_fp32 &&
+                    sh->dtype == LACT_BF16 && sh->d == 128 && (sh->dh == 256 || sh->dh == 512);
+  if (job != nullptr && !fuse) {
+    lact_status r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, s);
+    if (r != LACT_OK) return r;
+  }
   const int nsplit = choose_nsplit(sh, n_tok);
   Workspace w = layout_ws(sh, nsplit, op->use_muon != 0, reinterpret_cast<char*>(ws));
   const int64_t msz = (int64_t)sh->d * sh->dh;
@@ -354,8 +380,14 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
     const NsIn in{{u1, u3, u2}, sh->bh};
-    hipError_t e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,
-                          op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
+    hipError_t e;
+    if (fuse) {
+      const ApplyArgs aa = apply_args(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok);
+      e = launch_ns_apply(3 * sh->bh, sh->d, sh->dh, in, w.g, op->ns_eps, aa, s);
+    } else {
+      e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,
+                 op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
+    }
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
   }
@@ -532,9 +564,9 @@ lact_status lact_chunk_step(const lact_shape* sh, const lact_state* st, const vo
   if ((r = check_act(sh, o, ol, n_tok)) != LACT_OK) return r;
   if (n_tok > 0 && q == o) return LACT_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if ((r = do_apply(sh, st, q, ql, o, ol, n_tok, s)) != LACT_OK) return r;
   if (n_tok == 0) return LACT_OK;
-  return do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s);
+  const ApplyJob job{q, ql, o, ol, n_tok};
+  return do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s, &job);
 }
 
 lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void* q,
@@ -566,6 +598,8 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
   auto at = [&](const void* base, lact_layout l, int64_t t) {
     return reinterpret_cast<const char*>(base) + t * l.stride_tok * es;
   };
+  ApplyJob pending{};
+  bool have_pending = false;
   for (int64_t s0 = 0; s0 < T; s0 += chunk) {
     const int64_t e0 = s0 + chunk < T ? s0 + chunk : T;
     const bool last = e0 == T;
@@ -574,17 +608,31 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
       a0 = s0 + sub_off;
       a1 = a0 + sub_len < e0 ? a0 + sub_len : e0;
     }
-    const bool write = (order == LACT_UPDATE_THEN_APPLY) || !last || update_last;
-    auto upd = [&]() -> lact_status {
-      if (!write || a1 <= a0) return LACT_OK;
-      return do_update(sh, st, at(k, kl, a0), kl, at(v, vl, a0), vl, e1 + a0, e3 + a0, e2 + a0,
-                       mom ? mom + a0 : nullptr, esbh, a1 - a0, op, ws, s);
-    };
-    if (order == LACT_UPDATE_THEN_APPLY && (r = upd()) != LACT_OK) return r;
-    r = do_apply(sh, st, at(q, ql, s0), ql, const_cast<char*>(at(o, ol, s0)), ol, e0 - s0, s);
-    if (r != LACT_OK) return r;
-    if (order == LACT_APPLY_THEN_UPDATE && (r = upd()) != LACT_OK) return r;
+    const bool write = ((order == LACT_UPDATE_THEN_APPLY) || !last || update_last) && a1 > a0;
+    const ApplyJob job{at(q, ql, s0), ql, const_cast<char*>(at(o, ol, s0)), ol, e0 - s0};
+    // the read of a chunk goes with the next write after the weights it uses
+    // (this chunk's write when reading first, the next chunk's otherwise)
+    if (order == LACT_APPLY_THEN_UPDATE) {
+      if (write)
+        r = do_update(sh, st, at(k, kl, a0), kl, at(v, vl, a0), vl, e1 + a0, e3 + a0, e2 + a0,
+                      mom ? mom + a0 : nullptr, esbh, a1 - a0, op, ws, s, &job);
+      else
+        r = do_apply(sh, st, job.q, job.ql, job.o, job.ol, job.n_tok, s);
+      if (r != LACT_OK) return r;
+    } else {
+      if (write)
+        r = do_update(sh, st, at(k, kl, a0), kl, at(v, vl, a0), vl, e1 + a0, e3 + a0, e2 + a0,
+                      mom ? mom + a0 : nullptr, esbh, a1 - a0, op, ws, s,
+                      have_pending ? &pending : nullptr);
+      else if (have_pending)
+        r = do_apply(sh, st, pending.q, pending.ql, pending.o, pending.ol, pending.n_tok, s);
+      if (r != LACT_OK) return r;
+      pending = job;
+      have_pending = true;
+    }
   }
+  if (have_pending)
+    return do_apply(sh, st, pending.q, pending.ql, pending.o, pending.ol, pending.n_tok, s);
   return LACT_OK;
 }
 

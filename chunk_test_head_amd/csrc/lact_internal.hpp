@@ -102,6 +102,10 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
                            float eps, hipStream_t s);
+// Newton-Schulz (bf16, 128 rows, 256 or 512 columns) and a d = 128 bf16 read
+// in one launch; hipErrorNotSupported for other shapes.
+hipError_t launch_ns_apply(int count, int rows, int cols, NsIn g, float* u, float eps,
+                           const ApplyArgs& a, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s);
 hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,

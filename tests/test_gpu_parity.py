@@ -200,6 +200,39 @@ def test_update_twice(device, wi):
             sts[b] = st
 
 
+@pytest.mark.parametrize("wi", [0, 1, 3, 4])
+def test_chunk_step(device, wi):
+    """One chunk step (read with W_c, then write): with Newton-Schulz on and
+    d = 128 the read shares the Newton-Schulz launch (its workgroups after
+    the matrices'), otherwise it runs first.  Both results against the oracle."""
+    import torch
+    n = 320
+    w = small(wi, n, n, subset=(0, n))
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    q = H.act_to_dev(w, inp, "q", device)
+    k = H.act_to_dev(w, inp, "k", device)
+    v = H.act_to_dev(w, inp, "v", device)
+    out = H.out_buffer(w, n, device)
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    mom = torch.from_numpy(inp["mom"]).to(device) if inp["mom"] is not None else None
+    ws = H.workspace(w, n, device)
+    print(f"chunk_step wl={wi} n={n}", flush=True)
+    L.lact_chunk_step(fw.shape, fw, q, k, v, out, eta, eta, eta, mom, H.opts_of(w), ws)
+    torch.cuda.synchronize()
+    got = H.to64(out)
+    W1, W3, W2, M1, M3, M2 = H.state64(fw)
+    for b in range(w.bh):
+        ref_o = O.apply(W[0][b], W[1][b], W[2][b], WL.token_values(inp, "q", b, 0, n))
+        assert H.rel(got[b], ref_o) < H.TOL[w.dtype], (b, H.rel(got[b], ref_o))
+        e = inp["eta"][b]
+        m = None if inp["mom"] is None else inp["mom"][b]
+        ref = O.update(O.HeadState(W[0][b], W[1][b], W[2][b]), inp["k"][b], inp["v"][b], e, e, e,
+                       mom=m, use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+        for name, x, y in (("W1", W1[b], ref.W1), ("W3", W3[b], ref.W3), ("W2", W2[b], ref.W2)):
+            assert H.rel(x, y) < H.TOL[w.dtype], (name, b, H.rel(x, y))
+
+
 SEQ_CASES = {
     # workload: (T, chunk, subset)
     0: (1024, 256, None),
