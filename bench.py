@@ -31,7 +31,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="lm-causal")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=8, help="heads of the oracle sample")
+    p.add_argument("--cpu-heads", type=int, default=32, help="heads of the oracle sample (10-30 s of host work)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES (counter calibration)")
     return p.parse_args()
