@@ -31,6 +31,14 @@ template <int D>
 __device__ __forceinline__ int swz(int r, int col) {
   return r * D + (((col >> 3) ^ swz_key<D>(r)) << 3) + (col & 7);
 }
+// Padded alternative for token tiles: rows of D bf16 stored at a pitch of
+// D + 16 elements (32 bytes of padding) are conflict-free for the same three
+// patterns, and every fragment address is a per-lane base plus a
+// compile-time offset (no per-fragment XOR, no address registers per tile).
+template <int D>
+__device__ __forceinline__ int tpad(int r, int col) {
+  return r * (D + 16) + col;
+}
 // Rows of 32 bf16 (64 bytes: a W2 block row, the block's hidden units in the
 // kappa run order): the 8-byte slot k stored at chunk (k / 2) ^ t(r), half
 // k % 2, with t(r) = (r / 2) % 2 + 2 ((r / 8) % 2) - conflict-free for the

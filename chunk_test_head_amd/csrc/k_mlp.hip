@@ -408,14 +408,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int NT = 32;
   constexpr int KS = D / 32;
   constexpr int IT = D / 16;
-  constexpr int TILE = NT * D;             // one k or v tile (no padding: swizzled)
+  constexpr int TILE = NT * (D + 16);      // one k or v tile (rows padded: tpad)
   constexpr int NV = NT * D / 8;           // 16-byte vectors per tile
   constexpr int VPT = (NV + NTH - 1) / NTH;
   static_assert(NV % NTH == 0 || NTH % NV == 0, "tile split");
 
   // PIPE: tiles n-1 (read), n (read), n+1 (written); else SUB tiles per
-  // barrier, double buffered (stage st read, stage st+1 written)
-  constexpr int NBUF = PIPE ? 3 : 2;
+  // barrier, three stage buffers (stage st read, st+1 written, st-1 still
+  // read by the waves that defer their last gradient contraction)
+  constexpr int NBUF = 3;
   constexpr int SUB = PIPE ? 1 : 2;
   __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF * SUB][2 * TILE];
   __shared__ float sEta[NBUF * SUB][3][NT];
@@ -439,6 +440,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh;
   const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh;
   const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
+  // one learning rate for all three matrices (the pages' usual case): the
+  // SwiGLU backward shares its eta products
+  const bool same_eta = a.eta1 == a.eta3 && a.eta3 == a.eta2;
   const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
 
   // W B fragments: lane holds W[j0 + 16 h + c][32 ks + 8 g ..]
@@ -489,7 +493,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
     _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
       if (vi < NV) {                                                                \
-        const int o = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                     \
+        const int o = tpad<D>(vi / (D / 8), (vi % (D / 8)) * 8);                     \
         *reinterpret_cast<uint4*>(sK_ + o) = rk[x];                                 \
         *reinterpret_cast<uint4*>(sK_ + TILE + o) = rv[x];                          \
       }                                                                             \
@@ -514,8 +518,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       }                                                                             \
     _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
       _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                            \
-        const bf16x8 ak = ld8(sK_ + swz<D>(16 * tt + c, 32 * ks + 8 * g));           \
-        const bf16x8 av = ld8(sV_ + swz<D>(16 * tt + c, 32 * ks + 8 * g));           \
+        const bf16x8 ak = ld8(sK_ + tpad<D>(16 * tt + c, 32 * ks + 8 * g));           \
+        const bf16x8 av = ld8(sV_ + tpad<D>(16 * tt + c, 32 * ks + 8 * g));           \
         _Pragma("unroll") for (int h = 0; h < HT; ++h) {                            \
           mma(P[h][tt], ak, b1[h][ks]);                                             \
           mma(U[h][tt], ak, b3[h][ks]);                                             \
@@ -530,15 +534,29 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[BUF][0][16 * tt + 4 * g]); \
       const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[BUF][1][16 * tt + 4 * g]); \
       const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[BUF][2][16 * tt + 4 * g]); \
-      _Pragma("unroll") for (int h = 0; h < HT; ++h)                                \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                               \
-        const float p = P[h][tt][i], u = U[h][tt][i], e = E[h][tt][i];              \
-        const float sg = sigmoid_fast(p);                                           \
-        const float sl = p * sg;                                                    \
-        const float dsl = sg * __builtin_fmaf(p, 1.f - sg, 1.f);                    \
-        fh[h][4 * tt + i] = (bf16)(n2[i] * sl * u);                                 \
-        fu[h][4 * tt + i] = (bf16)(n3[i] * e * sl);                                 \
-        fg[h][4 * tt + i] = (bf16)(n1[i] * e * u * dsl);                            \
+      if (same_eta) {                                                               \
+        _Pragma("unroll") for (int h = 0; h < HT; ++h)                              \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                             \
+          const float p = P[h][tt][i], u = U[h][tt][i], e = E[h][tt][i];            \
+          const float sg = sigmoid_fast(p);                                         \
+          const float sl = p * sg;                                                  \
+          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);                       \
+          const float sn = n1[i] * sl;                                              \
+          fh[h][4 * tt + i] = (bf16)(sn * u);                                       \
+          fu[h][4 * tt + i] = (bf16)(sn * e);                                       \
+          fg[h][4 * tt + i] = (bf16)((n1[i] * dsl) * (e * u));                      \
+        }                                                                           \
+      } else {                                                                      \
+        _Pragma("unroll") for (int h = 0; h < HT; ++h)                              \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                             \
+          const float p = P[h][tt][i], u = U[h][tt][i], e = E[h][tt][i];            \
+          const float sg = sigmoid_fast(p);                                         \
+          const float sl = p * sg;                                                  \
+          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);                       \
+          fh[h][4 * tt + i] = (bf16)((n2[i] * sl) * u);                             \
+          fu[h][4 * tt + i] = (bf16)((n3[i] * sl) * e);                             \
+          fg[h][4 * tt + i] = (bf16)((n1[i] * dsl) * (e * u));                      \
+        }                                                                           \
       }                                                                             \
     }                                                                               \
   }
@@ -549,11 +567,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   {                                                                                 \
     const bf16* sK_ = sKV[BUF];                                                     \
     const bf16* sV_ = sK_ + TILE;                                                   \
-    const int tr = 4 * g + (c >> 2);                                                \
+    const int cq_ = opaque(c), gq_ = opaque(g);                                     \
+    const int tr = 4 * gq_ + (cq_ >> 2);                                            \
     _Pragma("unroll") for (int it = 0; it < IT; ++it) {                             \
-      const int fc = 16 * it + 4 * (c & 3);                                         \
-      const bf16x8 akt = cat8(ld_tr4(sK_ + swz<D>(tr, fc)), ld_tr4(sK_ + swz<D>(tr + 16, fc))); \
-      const bf16x8 avt = cat8(ld_tr4(sV_ + swz<D>(tr, fc)), ld_tr4(sV_ + swz<D>(tr + 16, fc))); \
+      const int fc = 16 * it + 4 * (cq_ & 3);                                       \
+      const bf16x8 akt = cat8(ld_tr4(sK_ + tpad<D>(tr, fc)), ld_tr4(sK_ + tpad<D>(tr + 16, fc))); \
+      const bf16x8 avt = cat8(ld_tr4(sV_ + tpad<D>(tr, fc)), ld_tr4(sV_ + tpad<D>(tr + 16, fc))); \
       _Pragma("unroll") for (int h = 0; h < HT; ++h) {                              \
         mma(G1[h][it], akt, fg[h]);                                                 \
         mma(G3[h][it], akt, fu[h]);                                                 \
@@ -566,8 +585,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   f32x4 P[HT][2], U[HT][2], E[HT][2];
   bf16x8 fh[HT], fu[HT], fg[HT];
   if constexpr (!PIPE) {
-    // SUB token tiles per barrier: stage st uses slots (st % 2) SUB + sub and
-    // stages the next stage's tiles, one tile at a time, into the other half
+    // Two token tiles per barrier: stage st reads slots (st % 3) SUB + 0, 1
+    // and stages the next stage's tiles into ((st + 1) % 3) SUB + 0, 1.
+    // Waves WAVES/2.. (which share their SIMDs with waves 0..WAVES/2-1) run
+    // the gradient contractions of their second tile at the start of the
+    // next stage, so the two waves of a SIMD are out of phase: one wave's
+    // SwiGLU backward (VALU) overlaps the other's MFMA phases.
+    static_assert(SUB == 2, "stage = two tiles");
+    const bool late = wave >= WAVES / 2;
     const int nst = (ntile + SUB - 1) / SUB;
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
@@ -577,20 +602,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       }
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
-      const int cur = (st & 1) * SUB, nxt = ((st + 1) & 1) * SUB;
-#pragma unroll
-      for (int sb = 0; sb < SUB; ++sb) {
-        const int ti = st * SUB + sb, tn = ti + SUB;
-        if (tn < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)tn * NT);
-        if (active && ti < ntile) {
-          LACT_GRAD_FWD(cur + sb);
-          LACT_GRAD_EW(cur + sb);
-          LACT_GRAD_GG(cur + sb);
-        }
-        if (tn < ntile) LACT_GRAD_LSTORE(nxt + sb);
+      const int cur = (st % 3) * SUB, nxt = ((st + 1) % 3) * SUB, prv = ((st + 2) % 3) * SUB;
+      const int ta = st * SUB, tb = ta + 1;
+      if (late && active && st > 0) LACT_GRAD_GG(prv + 1);  // deferred tile
+      if (ta + SUB < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)(ta + SUB) * NT);
+      if (active) {
+        LACT_GRAD_FWD(cur);
+        LACT_GRAD_EW(cur);
+        LACT_GRAD_GG(cur);
       }
+      if (ta + SUB < ntile) LACT_GRAD_LSTORE(nxt);
+      if (tb + SUB < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)(tb + SUB) * NT);
+      if (active && tb < ntile) {
+        LACT_GRAD_FWD(cur + 1);
+        LACT_GRAD_EW(cur + 1);
+        if (!late) LACT_GRAD_GG(cur + 1);
+      }
+      if (tb + SUB < ntile) LACT_GRAD_LSTORE(nxt + 1);
       __syncthreads();
     }
+    // the last stage's second tile (late waves), if it exists
+    if (late && active && nst > 0 && (nst - 1) * SUB + 1 < ntile)
+      LACT_GRAD_GG(((nst - 1) % 3) * SUB + 1);
   } else {
     if (ntile > 0) {
       LACT_GRAD_GLOAD(s0);

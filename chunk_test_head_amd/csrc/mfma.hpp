@@ -110,6 +110,14 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// An opaque copy of a value: address arithmetic derived from it is redone
+// where it is used instead of being hoisted out of a loop and kept live in
+// registers (one per distinct swizzled address).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8).  Renumber them so
 // that each XCD runs one contiguous range of logical ids: neighbouring tiles
 // (same head, same weights) then share that XCD's L2.
