@@ -57,7 +57,7 @@ template <class T, int D>
 struct ApplyLds {
   static constexpr int HB = 32, V = 16 / sizeof(T);
   static constexpr bool BF = sizeof(T) == 2;
-  static constexpr int P1 = BF ? D : D + V, P2 = BF ? HB : HB + 4;
+  static constexpr int P1 = BF ? D + 16 : D + V, P2 = BF ? HB : HB + 4;
   static constexpr int STAGE = 2 * HB * P1 + D * P2;
   static constexpr int SUB = (BF && D <= 128) ? 2 : 1;
   static constexpr int ELEMS = 2 * SUB * STAGE;
@@ -73,9 +73,9 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
   constexpr int KS = D / 32;             // K slabs over d
   constexpr int IT = D / 16;             // output feature tiles
   constexpr int V = 16 / sizeof(T);      // elements per 16-byte vector
-  // bf16: W1/W3 block rows unpadded and swizzled (swz); fp32: padded rows
+  // W1/W3 block rows at a padded pitch (bf16: tpad, conflict-free)
   constexpr bool BF = sizeof(T) == 2;
-  constexpr int P1 = BF ? D : D + V;     // LDS pitch of W1/W3 block rows
+  constexpr int P1 = BF ? D + 16 : D + V;  // LDS pitch of W1/W3 block rows
   // W2 block rows: the 32 hidden values of a row stored in kappa order (runs
   // of four: 0-3, 16-19, 4-7, 20-23, ...), so that the A fragment of lane
   // group g (hidden 4g..4g+3, 16+4g..16+4g+3) is one 16-byte read (bf16:
@@ -151,7 +151,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
     _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
       const int row = vi / (D / V), col = (vi % (D / V)) * V;                       \
-      const int o_ = BF ? swz<D>(row, col) : row * P1 + col;                        \
+      const int o_ = row * P1 + col;                                                \
       *reinterpret_cast<uint4*>(s1_ + o_) = r1[x];                                  \
       *reinterpret_cast<uint4*>(s3_ + o_) = r3[x];                                  \
     }                                                                               \
@@ -203,7 +203,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
-        const int o1 = BF ? swz<D>(16 * jt + c, 32 * ks + 8 * g) : (16 * jt + c) * P1 + 32 * ks + 8 * g;
+        const int o1 = (16 * jt + c) * P1 + 32 * ks + 8 * g;
         const frag_t<T> a1 = ld8(s1 + o1);
         const frag_t<T> a3 = ld8(s3 + o1);
 #pragma unroll

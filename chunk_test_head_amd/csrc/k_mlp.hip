@@ -696,7 +696,7 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
   constexpr int DH2 = D / 2;           // features per wave
   constexpr int KS = DH2 / 32;         // K slabs of the forward contractions
   constexpr int IT = DH2 / 16;         // feature tiles of the gradient
-  constexpr int TILE = NT * D;
+  constexpr int TILE = NT * (D + 16);   // rows at a padded pitch (tpad)
   constexpr int NV = NT * D / 8;       // 16-byte vectors per tile
   constexpr int VPT = NV / NTH;
   static_assert(NV % NTH == 0, "tile split");
@@ -724,6 +724,7 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
   const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh;
   const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh;
   const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
+  const bool same_eta = a.eta1 == a.eta3 && a.eta3 == a.eta2;
   const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
 
   // W B fragments of the own feature half: lane holds W[j0 + c][d0 + 32 ks + 8 g ..]
@@ -770,7 +771,7 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
     bf16* sK_ = sKV[BUF];                                                           \
     _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
-      const int o = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                       \
+      const int o = tpad<D>(vi / (D / 8), (vi % (D / 8)) * 8);                       \
       *reinterpret_cast<uint4*>(sK_ + o) = rk[x];                                   \
       *reinterpret_cast<uint4*>(sK_ + TILE + o) = rv[x];                            \
     }                                                                               \
@@ -801,8 +802,8 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 ak = ld8(sK + swz<D>(16 * tt + c, d0 + 32 * ks + 8 * g));
-        const bf16x8 av = ld8(sV + swz<D>(16 * tt + c, d0 + 32 * ks + 8 * g));
+        const bf16x8 ak = ld8(sK + tpad<D>(16 * tt + c, d0 + 32 * ks + 8 * g));
+        const bf16x8 av = ld8(sV + tpad<D>(16 * tt + c, d0 + 32 * ks + 8 * g));
         mma(P[tt], ak, b1[ks]);
         mma(U[tt], ak, b3[ks]);
         mma(E[tt], av, b2[ks]);
@@ -826,15 +827,29 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
       const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[cur][0][16 * tt + 4 * g]);
       const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[cur][1][16 * tt + 4 * g]);
       const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[cur][2][16 * tt + 4 * g]);
+      if (same_eta) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
-        const float sg = sigmoid_fast(p);
-        const float sl = p * sg;
-        const float dsl = sg * __builtin_fmaf(p, 1.f - sg, 1.f);
-        fh[4 * tt + i] = (bf16)(n2[i] * sl * u);
-        fu[4 * tt + i] = (bf16)(n3[i] * e * sl);
-        fg[4 * tt + i] = (bf16)(n1[i] * e * u * dsl);
+        for (int i = 0; i < 4; ++i) {
+          const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
+          const float sg = sigmoid_fast(p);
+          const float sl = p * sg;
+          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);
+          const float sn = n1[i] * sl;
+          fh[4 * tt + i] = (bf16)(sn * u);
+          fu[4 * tt + i] = (bf16)(sn * e);
+          fg[4 * tt + i] = (bf16)((n1[i] * dsl) * (e * u));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
+          const float sg = sigmoid_fast(p);
+          const float sl = p * sg;
+          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);
+          fh[4 * tt + i] = (bf16)((n2[i] * sl) * u);
+          fu[4 * tt + i] = (bf16)((n3[i] * sl) * e);
+          fg[4 * tt + i] = (bf16)((n1[i] * dsl) * (e * u));
+        }
       }
     }
     //    gradient contractions of the own feature rows
@@ -843,8 +858,8 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int fc = d0 + 16 * it + 4 * (c & 3);
-        const bf16x8 akt = cat8(ld_tr4(sK + swz<D>(tr, fc)), ld_tr4(sK + swz<D>(tr + 16, fc)));
-        const bf16x8 avt = cat8(ld_tr4(sV + swz<D>(tr, fc)), ld_tr4(sV + swz<D>(tr + 16, fc)));
+        const bf16x8 akt = cat8(ld_tr4(sK + tpad<D>(tr, fc)), ld_tr4(sK + tpad<D>(tr + 16, fc)));
+        const bf16x8 avt = cat8(ld_tr4(sV + tpad<D>(tr, fc)), ld_tr4(sV + tpad<D>(tr + 16, fc)));
         mma(G1[it], akt, fg);
         mma(G3[it], akt, fu);
         mma(G2[it], avt, fh);
