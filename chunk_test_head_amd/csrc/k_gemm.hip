@@ -109,15 +109,19 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s) {
 //   C = alpha A B + beta D, A bf16 [M][K] (row pitch lda), B bf16 [N][K]
 //   (BKN = false, pitch ldb) or [K][N] (BKN = true); D fp32 [M][N]; outputs
 //   fp32 C and / or bf16 Ch, [M][N].
-// One workgroup = one 64 x 64 tile, 4 waves of 32 x 32; K in slabs of 128,
-// double buffered through LDS (rows padded by 8 elements: 16 consecutive rows
-// of one 16-byte column fall in distinct bank groups); with BKN the B
-// fragments (K per lane) are transpose reads of the [k][n] tile.  The result
-// tile goes through LDS so that D, C and Ch move as whole 16-byte row pieces.
+// One workgroup = one 64 x 64 tile, 4 waves of 32 x 32; K in slabs of 64,
+// double buffered through LDS (rows padded by 16 elements: conflict-free
+// fragment and transpose reads); with BKN the B fragments (K per lane) are
+// transpose reads of the [k][n] tile.  The result tile goes through LDS so
+// that D, C and Ch move as whole 16-byte row pieces.  The small slabs keep
+// the LDS at 40 KiB, four workgroups per CU: the loop is bound by the
+// latency of each slab's loads, so more workgroups in flight is what counts.
 namespace {
-constexpr int NSG_T = 64, NSG_K = 128;
-constexpr int NSG_PA = NSG_K + 8;                     // [m][k] / [n][k] tiles
-constexpr int NSG_PB = NSG_T + 8;                     // [k][n] tile
+constexpr int NSG_T = 64, NSG_K = 64;
+constexpr int NSG_PA = NSG_K + 16;                    // [m][k] / [n][k] tiles
+constexpr int NSG_PB = NSG_T + 16;                    // [k][n] tile
+constexpr int NSG_VA = NSG_T * NSG_K / 8 / 256;       // 16-byte vectors per thread and operand
+constexpr int NSG_RA = NSG_K / 8;                     // vectors per [m][k] row
 constexpr int NSG_SA = NSG_T * NSG_PA;                // elements per A stage
 constexpr int NSG_SB = NSG_T * NSG_PA > NSG_K * NSG_PB ? NSG_T * NSG_PA : NSG_K * NSG_PB;
 constexpr int NSG_PC = NSG_T + 4;                     // fp32 result tile pitch
@@ -138,30 +142,27 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
 
   // staging: 16-byte vectors vi = tid + 256 x; A: row vi / 16, chunk vi % 16
   // ([m][k]); B: [n][k] likewise, or ([k][n]) row vi / 8, chunk vi % 8
-  uint4 ra[4], rb[4];
-// (K is a multiple of 64: the second half of a last, partial slab reads as 0)
+  bf16x8 ra[NSG_VA], rb[NSG_VA];
+  // (K is a multiple of 64)
 #define LACT_NSG_GLOAD(K0)                                                                   \
   {                                                                                          \
-    _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                          \
+    _Pragma("unroll") for (int x = 0; x < NSG_VA; ++x) {                                     \
       const int vi = tid + 256 * x;                                                          \
-      const int ka = (K0) + 8 * (vi & 15), kb = BKN ? (K0) + (vi >> 3) : ka;                \
-      ra[x] = uint4{0u, 0u, 0u, 0u};                                                         \
-      rb[x] = uint4{0u, 0u, 0u, 0u};                                                         \
-      if (ka < a.K) ra[x] = *reinterpret_cast<const uint4*>(A + (int64_t)(m0 + (vi >> 4)) * a.lda + ka); \
-      if (kb < a.K)                                                                          \
-        rb[x] = BKN ? *reinterpret_cast<const uint4*>(B + (int64_t)kb * a.ldb + n0 + 8 * (vi & 7)) \
-                    : *reinterpret_cast<const uint4*>(B + (int64_t)(n0 + (vi >> 4)) * a.ldb + kb); \
+      const int ka = (K0) + 8 * (vi % NSG_RA), kb = BKN ? (K0) + (vi >> 3) : ka;             \
+      ra[x] = ld8(A + (int64_t)(m0 + vi / NSG_RA) * a.lda + ka);                              \
+      rb[x] = BKN ? ld8(B + (int64_t)kb * a.ldb + n0 + 8 * (vi & 7))                           \
+                  : ld8(B + (int64_t)(n0 + vi / NSG_RA) * a.ldb + kb);                         \
     }                                                                                        \
   }
 #define LACT_NSG_LSTORE(BUF)                                                                 \
   {                                                                                          \
     bf16* sa_ = lds_g + (BUF) * NSG_SA;                                                      \
     bf16* sb_ = lds_g + 2 * NSG_SA + (BUF) * NSG_SB;                                         \
-    _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                          \
+    _Pragma("unroll") for (int x = 0; x < NSG_VA; ++x) {                                     \
       const int vi = tid + 256 * x;                                                          \
-      *reinterpret_cast<uint4*>(sa_ + (vi >> 4) * NSG_PA + 8 * (vi & 15)) = ra[x];           \
-      if (BKN) *reinterpret_cast<uint4*>(sb_ + (vi >> 3) * NSG_PB + 8 * (vi & 7)) = rb[x];   \
-      else *reinterpret_cast<uint4*>(sb_ + (vi >> 4) * NSG_PA + 8 * (vi & 15)) = rb[x];      \
+      *reinterpret_cast<bf16x8*>(sa_ + (vi / NSG_RA) * NSG_PA + 8 * (vi % NSG_RA)) = ra[x]; \
+      if (BKN) *reinterpret_cast<bf16x8*>(sb_ + (vi >> 3) * NSG_PB + 8 * (vi & 7)) = rb[x]; \
+      else *reinterpret_cast<bf16x8*>(sb_ + (vi / NSG_RA) * NSG_PA + 8 * (vi % NSG_RA)) = rb[x]; \
     }                                                                                        \
   }
   f32x4 acc[2][2];
