@@ -128,19 +128,23 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 r1[NV1], r3[NV1], r2[NV2];
+  // 16-byte staging vectors as native vector types (register-allocated;
+  // a struct type would be copied through a stack slot)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x4 r1[NV1], r3[NV1], r2[NV2];
   // stage jb: W1 / W3 rows [jb HB, +HB) (contiguous) and W2 columns (rows of
   // HB elements at pitch dh), as 16-byte vectors
 #define LACT_APPLY_GLOAD(JB)                                                        \
   {                                                                                 \
     _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
-      r1[x] = *reinterpret_cast<const uint4*>(w1 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
-      r3[x] = *reinterpret_cast<const uint4*>(w3 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
+      r1[x] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
+      r3[x] = *reinterpret_cast<const u32x4*>(w3 + (int64_t)(JB) * HB * D + (int64_t)vi * V); \
     }                                                                               \
     _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
-      r2[x] = *reinterpret_cast<const uint4*>(w2 + (int64_t)(vi / (HB / V)) * dh + (JB) * HB + (vi % (HB / V)) * V); \
+      r2[x] = *reinterpret_cast<const u32x4*>(w2 + (int64_t)(vi / (HB / V)) * dh + (JB) * HB + (vi % (HB / V)) * V); \
     }                                                                               \
   }
 #define LACT_APPLY_LSTORE(BUF)                                                      \
@@ -152,8 +156,8 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
       const int vi = tid + x * NTH;                                                 \
       const int row = vi / (D / V), col = (vi % (D / V)) * V;                       \
       const int o_ = row * P1 + col;                                                \
-      *reinterpret_cast<uint4*>(s1_ + o_) = r1[x];                                  \
-      *reinterpret_cast<uint4*>(s3_ + o_) = r3[x];                                  \
+      *reinterpret_cast<u32x4*>(s1_ + o_) = r1[x];                                  \
+      *reinterpret_cast<u32x4*>(s3_ + o_) = r3[x];                                  \
     }                                                                               \
     _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                               \
       const int vi = tid + x * NTH;                                                 \
@@ -162,10 +166,10 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
         /* hidden col..col+7 = runs 2q, 2q+1 (q = col / 8) -> slots kpos */         \
         const int r0_ = col >> 2, r1_ = r0_ + 1;                                    \
         const int k0_ = 2 * (r0_ & 3) + (r0_ >> 2), k1_ = 2 * (r1_ & 3) + (r1_ >> 2); \
-        *reinterpret_cast<uint2*>(s2_ + swz32(row, k0_)) = uint2{r2[x].x, r2[x].y};   \
-        *reinterpret_cast<uint2*>(s2_ + swz32(row, k1_)) = uint2{r2[x].z, r2[x].w};   \
+        *reinterpret_cast<u32x2*>(s2_ + swz32(row, k0_)) = r2[x].xy;                  \
+        *reinterpret_cast<u32x2*>(s2_ + swz32(row, k1_)) = r2[x].zw;                  \
       } else {                                                                      \
-        *reinterpret_cast<uint4*>(s2_ + row * P2 + col) = r2[x];                    \
+        *reinterpret_cast<u32x4*>(s2_ + row * P2 + col) = r2[x];                    \
       }                                                                             \
     }                                                                               \
   }
