@@ -376,6 +376,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
     }  // active
     __syncthreads();
   }
+  // momentum: the head's mean coefficient, once per head
+  if (a.mom != nullptr && hb == 0 && split == 0)
+    block_mean<NTH>(a.mom + (int64_t)head * a.mom_sbh, a.n_tok, a.beta + head);
   if (!active) return;
 
   // ---- partials, [split][head][3][dh][d]: lane holds 4 consecutive d ----
@@ -661,6 +664,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
 #undef LACT_GRAD_GG
 #undef LACT_GRAD_GLOAD
 #undef LACT_GRAD_LSTORE
+  // momentum: the head's mean coefficient, once per head
+  if (a.mom != nullptr && hb == 0 && split == 0)
+    block_mean<NTH>(a.mom + (int64_t)head * a.mom_sbh, a.n_tok, a.beta + head);
   if (!active) return;
 
   // ---- partials, [split][head][3][dh][d]: lane holds 4 consecutive d ----
@@ -870,6 +876,9 @@ __global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
   }
 #undef LACT_GP_GLOAD
 #undef LACT_GP_LSTORE
+  // momentum: the head's mean coefficient, once per head
+  if (a.mom != nullptr && hb == 0 && split == 0)
+    block_mean<NTH>(a.mom + (int64_t)head * a.mom_sbh, a.n_tok, a.beta + head);
 
   // ---- partials, [split][head][3][dh][d]: lane holds 4 consecutive d ----
   const int64_t mat = (int64_t)a.dh * D;

@@ -18,7 +18,6 @@ namespace lact {
 // and write the wide [i][j] result.
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   __shared__ float tile[64][65];
-  __shared__ float bred[4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int jt = a.dh / 64, itn = a.d / 64;
   int id = blockIdx.x;
@@ -30,40 +29,48 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   const int64_t pstride = (int64_t)a.bh * 3 * msz;  // between splits
   const float* p = a.partial + ((int64_t)head * 3 + mat) * msz;
   const int j0 = tj * 64, i0 = ti * 64;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int j = ty + 16 * rr;
-    const int64_t off = (int64_t)(j0 + j) * a.d + i0 + 4 * tx;
-    f32x4 s = *reinterpret_cast<const f32x4*>(p + off);
-    for (int sp = 1; sp < a.nsplit; ++sp) s += *reinterpret_cast<const f32x4*>(p + sp * pstride + off);
-    tile[j][4 * tx + 0] = s[0];
-    tile[j][4 * tx + 1] = s[1];
-    tile[j][4 * tx + 2] = s[2];
-    tile[j][4 * tx + 3] = s[3];
-  }
-  __syncthreads();
   float* out = mat == 0 ? a.out1 : mat == 1 ? a.out3 : a.out2;
   if (out != nullptr) out += (int64_t)head * msz;
   float* m = (mat == 0 ? a.m1 : mat == 1 ? a.m3 : a.m2);
-  float beta = 0.f;
+  if (m != nullptr) m += (int64_t)head * msz;
+  // the old momentum rows first (independent of the sum)
+  f32x4 mo[4];
   if (m != nullptr) {
-    // beta = mean of the head's per-token coefficients (fixed order; every
-    // workgroup of the head gets the same value)
-    const float* mc = a.mom + (int64_t)head * a.mom_sbh;
-    float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
-    for (int64_t t = tid; t < a.n_tok; t += 1024) {
-      q0 += mc[t];
-      if (t + 256 < a.n_tok) q1 += mc[t + 256];
-      if (t + 512 < a.n_tok) q2 += mc[t + 512];
-      if (t + 768 < a.n_tok) q3 += mc[t + 768];
-    }
-    float q = (q0 + q1) + (q2 + q3);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
-    if ((tid & 63) == 0) bred[tid >> 6] = q;
-    __syncthreads();
-    beta = a.n_tok > 0 ? ((bred[0] + bred[1]) + (bred[2] + bred[3])) / (float)a.n_tok : 0.f;
+    for (int rr = 0; rr < 4; ++rr)
+      mo[rr] = *reinterpret_cast<const f32x4*>(m + (int64_t)(i0 + ty + 16 * rr) * a.dh + j0 + 4 * tx);
   }
+  // split partials, up to four splits' loads in flight per row, summed in
+  // split order
+  f32x4 acc[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) acc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < a.nsplit; sp0 += 4) {
+    f32x4 v[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t off = (int64_t)(j0 + ty + 16 * rr) * a.d + i0 + 4 * tx;
+        v[q][rr] = sp0 + q < a.nsplit ? *reinterpret_cast<const f32x4*>(p + (sp0 + q) * pstride + off)
+                                      : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (sp0 + q < a.nsplit) acc[rr] = (sp0 + q == 0) ? v[q][rr] : acc[rr] + v[q][rr];
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int j = ty + 16 * rr;
+    tile[j][4 * tx + 0] = acc[rr][0];
+    tile[j][4 * tx + 1] = acc[rr][1];
+    tile[j][4 * tx + 2] = acc[rr][2];
+    tile[j][4 * tx + 3] = acc[rr][3];
+  }
+  __syncthreads();
+  const float beta = m != nullptr ? a.beta[head] : 0.f;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int i = ty + 16 * rr;
@@ -74,10 +81,8 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     v[2] = tile[4 * tx + 2][i];
     v[3] = tile[4 * tx + 3][i];
     if (m != nullptr) {
-      float* mp = m + (int64_t)head * msz + off;
-      const f32x4 mo = *reinterpret_cast<const f32x4*>(mp);
-      v = v + beta * mo;
-      *reinterpret_cast<f32x4*>(mp) = v;
+      v = v + beta * mo[rr];
+      *reinterpret_cast<f32x4*>(m + off) = v;
     }
     if (out != nullptr) *reinterpret_cast<f32x4*>(out + off) = v;
   }

@@ -155,6 +155,7 @@ static int choose_nsplit(const lact_shape* sh, int64_t n_tok) {
 
 struct Workspace {
   float* partial;
+  float* beta;    // [bh] momentum coefficient of the write
   float* g;       // 3 wide matrices per head: [3][bh][d][dh]
   float* xa;      // Newton-Schulz buffers
   float* xb;
@@ -174,6 +175,7 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
     return p;
   };
   w.partial = take((int64_t)nsplit * sh->bh * 3 * msz);
+  w.beta = take(sh->bh);
   w.g = take((int64_t)3 * sh->bh * msz);
   if (muon) {
     w.xa = take((int64_t)3 * sh->bh * msz);
@@ -315,13 +317,14 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
   sl = (sl + 31) / 32 * 32;
   a.split_len = sl > 0 ? sl : 32;
   a.partial = w.partial;
+  a.mom = mom; a.mom_sbh = esbh; a.beta = w.beta;
   hipError_t e;
   {
     ProfScope p(LACT_PROF_GRAD, s);
     e = launch_grad(sh->dtype, a, s);
   }
   if (e != hipSuccess) return hip_fail(e);
-  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, mom, esbh, n_tok};
+  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
   {
     ProfScope p(LACT_PROF_REDUCE, s);
     e = launch_reduce(r, s);

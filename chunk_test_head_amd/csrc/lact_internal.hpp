@@ -33,6 +33,9 @@ struct GradArgs {
   int nsplit;
   int64_t split_len;
   float* partial;  // [nsplit][bh][3][dh][d] fp32
+  // momentum (else mom = NULL): one workgroup per head writes beta[head], the
+  // mean of the head's per-token coefficients mom[head * mom_sbh + t], t < n_tok
+  const float* mom; int64_t mom_sbh; float* beta;
 };
 
 // Sum of split partials, transpose to the wide orientation, momentum.
@@ -42,9 +45,7 @@ struct ReduceArgs {
   int bh, d, dh;
   float* out1; float* out3; float* out2;  // [bh][d][dh] each (NULL: only M holds the result)
   float* m1; float* m3; float* m2;        // momentum (NULL = off)
-  // per-token momentum coefficients of the n_tok written tokens ([bh] x
-  // stride mom_sbh); their mean is the coefficient of M
-  const float* mom; int64_t mom_sbh; int64_t n_tok;
+  const float* beta;                      // [bh] coefficient of M (from the gradient launch)
 };
 
 

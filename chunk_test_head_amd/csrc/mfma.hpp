@@ -118,6 +118,36 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Mean of x[0 .. n) by the whole workgroup in a fixed order (thread-strided
+// partial sums, wave butterflies, waves in index order); every thread must
+// call it.  Thread 0 writes the result to *out.
+template <int NTH>
+__device__ __forceinline__ void block_mean(const float* x, int64_t n, float* out) {
+  __shared__ float red_bm[NTH / 64];
+  const int tid = threadIdx.x;
+  float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
+  int64_t t = tid;
+  for (; t + 3 * NTH < n; t += 4 * NTH) {
+    q0 += x[t];
+    q1 += x[t + NTH];
+    q2 += x[t + 2 * NTH];
+    q3 += x[t + 3 * NTH];
+  }
+  for (; t < n; t += NTH) q0 += x[t];
+  float q = (q0 + q1) + (q2 + q3);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
+  __syncthreads();
+  if ((tid & 63) == 0) red_bm[tid >> 6] = q;
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NTH / 64; ++w) tot += red_bm[w];
+    *out = n > 0 ? tot / (float)n : 0.f;
+  }
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8).  Renumber them so
 // that each XCD runs one contiguous range of logical ids: neighbouring tiles
 // (same head, same weights) then share that XCD's L2.
