@@ -400,12 +400,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
 // column tile), over one token split of one head.  Per wave, for the whole
 // token loop: its W1 / W3 / W2^T rows as B fragments (K = d) and the fp32
 // accumulators of G1^T, G3^T, G2 (d x 16).  Token tiles of 32 are staged once
-// in LDS, row-major and double buffered (the next tile's global loads are in
-// flight while the current one is computed).  The forward contractions read
+// in LDS, row-major, two per barrier in three stage buffers (the next stage's
+// global loads are in flight while the current one is computed).  The
+// forward contractions read
 // k / v rows (K = d); the gradient contractions read k^T / v^T fragments
 // (K = tokens) from the same tiles with LDS transpose reads.
-// Tile layout: rows of D bf16, 16-byte chunks XOR-swizzled (swz).
-template <int D, int WAVES, int HT, bool PIPE>
+// Tile layout: rows of D bf16 at the padded pitch of tpad.
+template <int D, int WAVES, int HT>
 __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int NTH = WAVES * 64;
   constexpr int NT = 32;
@@ -416,11 +417,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   constexpr int VPT = (NV + NTH - 1) / NTH;
   static_assert(NV % NTH == 0 || NTH % NV == 0, "tile split");
 
-  // PIPE: tiles n-1 (read), n (read), n+1 (written); else SUB tiles per
-  // barrier, three stage buffers (stage st read, st+1 written, st-1 still
-  // read by the waves that defer their last gradient contraction)
+  // SUB tiles per barrier, three stage buffers (stage st read, st+1 written,
+  // st-1 still read by the waves that defer their last gradient contraction)
   constexpr int NBUF = 3;
-  constexpr int SUB = PIPE ? 1 : 2;
+  constexpr int SUB = 2;
   __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF * SUB][2 * TILE];
   __shared__ float sEta[NBUF * SUB][3][NT];
 
@@ -504,11 +504,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
     if (tid < 3 * NT) sEta[BUF][tid / NT][er] = re;                                 \
   }
 
-  // PIPE: software pipeline over token tiles: iteration n runs the forward
-  // contractions of tile n and the gradient contractions of tile n-1 (both
-  // MFMA, independent of each other), and the SwiGLU backward of tile n (VALU)
-  // can issue while those MFMAs run.  It needs more live registers, so it is
-  // used where it pays (d = 256).
+  // forward contractions of one tile: P = W1 k, U = W3 k, E = W2^T v
 #define LACT_GRAD_FWD(BUF)                                                          \
   {                                                                                 \
     const bf16* sK_ = sKV[BUF];                                                     \
@@ -587,78 +583,45 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   const int ntile = s0 < s1 ? (int)((s1 - s0 + NT - 1) / NT) : 0;
   f32x4 P[HT][2], U[HT][2], E[HT][2];
   bf16x8 fh[HT], fu[HT], fg[HT];
-  if constexpr (!PIPE) {
-    // Two token tiles per barrier: stage st reads slots (st % 3) SUB + 0, 1
-    // and stages the next stage's tiles into ((st + 1) % 3) SUB + 0, 1.
-    // Waves WAVES/2.. (which share their SIMDs with waves 0..WAVES/2-1) run
-    // the gradient contractions of their second tile at the start of the
-    // next stage, so the two waves of a SIMD are out of phase: one wave's
-    // SwiGLU backward (VALU) overlaps the other's MFMA phases.
-    static_assert(SUB == 2, "stage = two tiles");
-    const bool late = wave >= WAVES / 2;
-    const int nst = (ntile + SUB - 1) / SUB;
+  // Two token tiles per barrier: stage st reads slots (st % 3) SUB + 0, 1
+  // and stages the next stage's tiles into ((st + 1) % 3) SUB + 0, 1.
+  // Waves WAVES/2.. (which share their SIMDs with waves 0..WAVES/2-1) run
+  // the gradient contractions of their second tile at the start of the
+  // next stage, so the two waves of a SIMD are out of phase: one wave's
+  // SwiGLU backward (VALU) overlaps the other's MFMA phases.
+  static_assert(SUB == 2, "stage = two tiles");
+  const bool late = wave >= WAVES / 2;
+  const int nst = (ntile + SUB - 1) / SUB;
 #pragma unroll
-    for (int sb = 0; sb < SUB; ++sb)
-      if (sb < ntile) {
-        LACT_GRAD_GLOAD(s0 + (int64_t)sb * NT);
-        LACT_GRAD_LSTORE(sb);
-      }
+  for (int sb = 0; sb < SUB; ++sb)
+    if (sb < ntile) {
+      LACT_GRAD_GLOAD(s0 + (int64_t)sb * NT);
+      LACT_GRAD_LSTORE(sb);
+    }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = (st % 3) * SUB, nxt = ((st + 1) % 3) * SUB, prv = ((st + 2) % 3) * SUB;
+    const int ta = st * SUB, tb = ta + 1;
+    if (late && active && st > 0) LACT_GRAD_GG(prv + 1);  // deferred tile
+    if (ta + SUB < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)(ta + SUB) * NT);
+    if (active) {
+      LACT_GRAD_FWD(cur);
+      LACT_GRAD_EW(cur);
+      LACT_GRAD_GG(cur);
+    }
+    if (ta + SUB < ntile) LACT_GRAD_LSTORE(nxt);
+    if (tb + SUB < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)(tb + SUB) * NT);
+    if (active && tb < ntile) {
+      LACT_GRAD_FWD(cur + 1);
+      LACT_GRAD_EW(cur + 1);
+      if (!late) LACT_GRAD_GG(cur + 1);
+    }
+    if (tb + SUB < ntile) LACT_GRAD_LSTORE(nxt + 1);
     __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-      const int cur = (st % 3) * SUB, nxt = ((st + 1) % 3) * SUB, prv = ((st + 2) % 3) * SUB;
-      const int ta = st * SUB, tb = ta + 1;
-      if (late && active && st > 0) LACT_GRAD_GG(prv + 1);  // deferred tile
-      if (ta + SUB < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)(ta + SUB) * NT);
-      if (active) {
-        LACT_GRAD_FWD(cur);
-        LACT_GRAD_EW(cur);
-        LACT_GRAD_GG(cur);
-      }
-      if (ta + SUB < ntile) LACT_GRAD_LSTORE(nxt);
-      if (tb + SUB < ntile) LACT_GRAD_GLOAD(s0 + (int64_t)(tb + SUB) * NT);
-      if (active && tb < ntile) {
-        LACT_GRAD_FWD(cur + 1);
-        LACT_GRAD_EW(cur + 1);
-        if (!late) LACT_GRAD_GG(cur + 1);
-      }
-      if (tb + SUB < ntile) LACT_GRAD_LSTORE(nxt + 1);
-      __syncthreads();
-    }
-    // the last stage's second tile (late waves), if it exists
-    if (late && active && nst > 0 && (nst - 1) * SUB + 1 < ntile)
-      LACT_GRAD_GG(((nst - 1) % 3) * SUB + 1);
-  } else {
-    if (ntile > 0) {
-      LACT_GRAD_GLOAD(s0);
-      LACT_GRAD_LSTORE(0);
-    }
-    __syncthreads();
-    int n0 = 0;
-    if (ntile > 0) {
-      // tile 0: forward + backward only
-      if (ntile > 1) LACT_GRAD_GLOAD(s0 + NT);
-      if (active) {
-        LACT_GRAD_FWD(0);
-        LACT_GRAD_EW(0);
-      }
-      if (ntile > 1) LACT_GRAD_LSTORE(1);
-      __syncthreads();
-      n0 = 1;
-    }
-    for (int n = n0; n < ntile; ++n) {
-      const int cur = n % NBUF, prev = (n + NBUF - 1) % NBUF, nxt = (n + 1) % NBUF;
-      const bool more = n + 1 < ntile;
-      if (more) LACT_GRAD_GLOAD(s0 + (int64_t)(n + 1) * NT);
-      if (active) {
-        LACT_GRAD_FWD(cur);
-        LACT_GRAD_GG(prev);   // reads fh/fu/fg of tile n-1 ...
-        LACT_GRAD_EW(cur);    // ... before they are replaced by tile n's
-      }
-      if (more) LACT_GRAD_LSTORE(nxt);  // slot of tile n-2, consumed last iteration
-      __syncthreads();
-    }
-    if (ntile > 0 && active) LACT_GRAD_GG((ntile - 1) % NBUF);
   }
+  // the last stage's second tile (late waves), if it exists
+  if (late && active && nst > 0 && (nst - 1) * SUB + 1 < ntile)
+    LACT_GRAD_GG(((nst - 1) % 3) * SUB + 1);
 #undef LACT_GRAD_FWD
 #undef LACT_GRAD_EW
 #undef LACT_GRAD_GG
@@ -929,12 +892,12 @@ int grad_hidden_per_block(int dtype, int d) {
   return 4 * (d == 64 ? 32 : 16);
 }
 
-template <int D, int WAVES, int HT, bool PIPE>
+template <int D, int WAVES, int HT>
 static hipError_t run_grad_bf16(const GradArgs& a, hipStream_t s) {
   const int hblocks = (a.dh + WAVES * 16 * HT - 1) / (WAVES * 16 * HT);
   const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_grad_bf16<D, WAVES, HT, PIPE>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_grad_bf16<D, WAVES, HT>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -957,8 +920,8 @@ static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
   if (dtype == 1) {
     switch (a.d) {
-      case 64: return run_grad_bf16<64, 8, 1, false>(a, s);
-      case 128: return run_grad_bf16<128, 8, 1, false>(a, s);
+      case 64: return run_grad_bf16<64, 8, 1>(a, s);
+      case 128: return run_grad_bf16<128, 8, 1>(a, s);
       case 256: return run_grad_pair(a, s);
     }
   } else {
