@@ -60,7 +60,10 @@ struct ApplyLds {
   static constexpr int P1 = BF ? D + 16 : D + V, P2 = BF ? HB : HB + 4;
   static constexpr int STAGE = 2 * HB * P1 + D * P2;
   static constexpr int SUB = (BF && D <= 128) ? 2 : 1;
-  static constexpr int ELEMS = 2 * SUB * STAGE;
+  // three stage buffers where the waves of a SIMD run out of phase (the W2
+  // block of a deferred product must outlive the next stage's staging)
+  static constexpr int NBUF = (BF && D == 128) ? 3 : 2;
+  static constexpr int ELEMS = NBUF * SUB * STAGE;
 };
 
 // Body of one workgroup: logical block lid (head-major tiles), LDS of
@@ -174,8 +177,31 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
     }                                                                               \
   }
 
+  // Three stage buffers (d = 128, 8 waves): waves WAVES/2.. (sharing their
+  // SIMDs with waves 0..WAVES/2-1) run the output product of a stage's second
+  // block at the start of the next stage, so the two waves of a SIMD are out
+  // of phase (one's SiLU, VALU, overlaps the other's MFMA phases).
+  constexpr int NBUF = ApplyLds<T, D>::NBUF;
+  constexpr bool SKEW = NBUF == 3 && SUB == 2 && WAVES == 8;
+  const bool late = SKEW && wave >= WAVES / 2;
   const int NB = dh / HB;
   const int nst = (NB + SUB - 1) / SUB;
+  frag_t<T> hf[NT];
+  // o^T[feature][token] += W2[:, block] h^T, W2 block of slot BUF
+#define LACT_APPLY_OPROD(BUF)                                                       \
+  {                                                                                 \
+    const T* s2_ = lds + (BUF) * STAGE + 2 * HB * P1;                               \
+    _Pragma("unroll") for (int it = 0; it < IT; ++it) {                             \
+      frag_t<T> a2;                                                                 \
+      if constexpr (BF) {                                                           \
+        a2 = ld8(s2_ + swz32(16 * it + c, 2 * g));                                  \
+      } else {                                                                      \
+        const T* row = s2_ + (16 * it + c) * P2;                                    \
+        a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);                                  \
+      }                                                                             \
+      _Pragma("unroll") for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]); \
+    }                                                                               \
+  }
 #pragma unroll
   for (int sb = 0; sb < SUB; ++sb)
     if (sb < NB) {
@@ -183,66 +209,57 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
       LACT_APPLY_LSTORE(sb);
     }
   __syncthreads();
-  for (int st = 0; st < nst; ++st)
+  for (int st = 0; st < nst; ++st) {
+    if (late && st > 0) LACT_APPLY_OPROD(((st + NBUF - 1) % NBUF) * SUB + SUB - 1);  // deferred
 #pragma unroll
-  for (int sb = 0; sb < SUB; ++sb) {
-    const int jb = st * SUB + sb, jn = jb + SUB;
-    const int buf = (st & 1) * SUB + sb, nbuf = ((st + 1) & 1) * SUB + sb;
-    if (jn < NB) LACT_APPLY_GLOAD(jn);
-    if (jb >= NB) continue;
-    const T* s1 = lds + buf * STAGE;
-    const T* s3 = s1 + HB * P1;
-    const T* s2 = s3 + HB * P1;
-
-    // gate / up pre-activations, transposed: P^T[hidden][token]
-    f32x4 P[2][NT], U[2][NT];
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int jb = st * SUB + sb, jn = jb + SUB;
+      const int buf = (st % NBUF) * SUB + sb, nbuf = ((st + 1) % NBUF) * SUB + sb;
+      if (jn < NB) LACT_APPLY_GLOAD(jn);
+      if (jb < NB) {
+        const T* s1 = lds + buf * STAGE;
+        const T* s3 = s1 + HB * P1;
+        // gate / up pre-activations, transposed: P^T[hidden][token]
+        f32x4 P[2][NT], U[2][NT];
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+          for (int tt = 0; tt < NT; ++tt) {
+            P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const int o1 = (16 * jt + c) * P1 + 32 * ks + 8 * g;
-        const frag_t<T> a1 = ld8(s1 + o1);
-        const frag_t<T> a3 = ld8(s3 + o1);
+          for (int jt = 0; jt < 2; ++jt) {
+            const int o1 = (16 * jt + c) * P1 + 32 * ks + 8 * g;
+            const frag_t<T> a1 = ld8(s1 + o1);
+            const frag_t<T> a3 = ld8(s3 + o1);
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          mma(P[jt][tt], a1, qf[tt][ks]);
-          mma(U[jt][tt], a3, qf[tt][ks]);
+            for (int tt = 0; tt < NT; ++tt) {
+              mma(P[jt][tt], a1, qf[tt][ks]);
+              mma(U[jt][tt], a3, qf[tt][ks]);
+            }
+          }
         }
+        // h = silu(P) * U, packed as the B operand (K = the 32 hidden rows).
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = P[0][tt][i], p1 = P[1][tt][i];
+            hf[tt][i] = to_t<T>(p0 * sigmoid_fast(p0) * U[0][tt][i]);
+            hf[tt][4 + i] = to_t<T>(p1 * sigmoid_fast(p1) * U[1][tt][i]);
+          }
+        if (!(late && sb == SUB - 1)) LACT_APPLY_OPROD(buf);
       }
+      if (jn < NB) LACT_APPLY_LSTORE(nbuf);
     }
-    // h = silu(P) * U, packed as the B operand (K = the 32 hidden rows).
-    frag_t<T> hf[NT];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = P[0][tt][i], p1 = P[1][tt][i];
-        hf[tt][i] = to_t<T>(p0 * sigmoid_fast(p0) * U[0][tt][i]);
-        hf[tt][4 + i] = to_t<T>(p1 * sigmoid_fast(p1) * U[1][tt][i]);
-      }
-    // o^T[feature][token] += W2[:, block] h^T
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      frag_t<T> a2;
-      if constexpr (BF) {
-        a2 = ld8(s2 + swz32(16 * it + c, 2 * g));
-      } else {
-        const T* row = s2 + (16 * it + c) * P2;
-        a2 = ld4x2(row + 4 * g, row + 16 + 4 * g);
-      }
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) mma(acc[it][tt], a2, hf[tt]);
-    }
-    if (jn < NB) LACT_APPLY_LSTORE(nbuf);
-    if (sb == SUB - 1) __syncthreads();
+    __syncthreads();
   }
+  // the last stage's second block (late waves), if it exists
+  if (late && nst > 0 && (nst - 1) * SUB + SUB - 1 < NB) LACT_APPLY_OPROD(((nst - 1) % NBUF) * SUB + SUB - 1);
+#undef LACT_APPLY_OPROD
 #undef LACT_APPLY_GLOAD
 #undef LACT_APPLY_LSTORE
 
