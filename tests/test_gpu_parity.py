@@ -200,13 +200,13 @@ def test_update_twice(device, wi):
             sts[b] = st
 
 
-@pytest.mark.parametrize("wi", [0, 1, 3, 4])
-def test_chunk_step(device, wi):
+@pytest.mark.parametrize("wi,n", [(0, 320), (1, 320), (1, 1), (3, 320), (3, 17), (4, 320)])
+def test_chunk_step(device, wi, n):
     """One chunk step (read with W_c, then write): with Newton-Schulz on and
     d = 128 the read shares the Newton-Schulz launch (its workgroups after
-    the matrices'), otherwise it runs first.  Both results against the oracle."""
+    the matrices'), otherwise it runs first.  Both results against the oracle
+    (also a one-token and a 17-token chunk)."""
     import torch
-    n = 320
     w = small(wi, n, n, subset=(0, n))
     W, inp = inputs(w)
     fw = H.make_state(w, W, device)
