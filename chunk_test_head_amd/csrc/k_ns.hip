@@ -380,9 +380,14 @@ __device__ __forceinline__ void nsr_store(bf16* s, int x0, int y0, int c, int gq
     }
 }
 
-template <int COLS>
+template <int COLS, int NMT, int NRT>
+__device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], float P, int m,
+                                                 const NsStep& st, float* stg);
+
+// STEP: instead of writing U, add it to the weights (ns_step_epilogue).
+template <int COLS, bool STEP>
 __device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps, int m,
-                                              bf16* lds_r) {
+                                              bf16* lds_r, const NsStep& st) {
   constexpr int R = 128, NW = 8;
   constexpr int CW = COLS / NW;  // columns per wave
   constexpr int NMT = CW / 16;   // column tiles per wave
@@ -522,6 +527,10 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps
     if (it < 4) LACT_NSR_PUT_X();
   }
 #undef LACT_NSR_PUT_X
+  if constexpr (STEP) {
+    ns_step_epilogue<COLS>(yv, P, m, st, stg);
+    return;
+  }
   // ---- X_5 = P_5 Y_5, staged through LDS into whole rows ----
 #pragma unroll
   for (int p0 = 0; p0 < R; p0 += SR) {
@@ -547,7 +556,162 @@ template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_ns_r128(NsIn g, float* u, float eps) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds_r[];
-  ns_r128_block<COLS>(g, u, eps, blockIdx.x, lds_r);
+  ns_r128_block<COLS, false>(g, u, eps, blockIdx.x, lds_r, NsStep{});
+}
+
+// ---- step epilogue ----
+// The result X5 = P Y (this wave's columns col0 .. col0 + COLS / 8 of the
+// 128 x COLS wide matrix, accumulator layout) is added to the fp32 weights,
+// each row rescaled to n0 / (||row|| + eps) (renorm; else left as is), and
+// the weights and their bf16 operand copies written.  Part of X5 at a time is
+// staged in LDS (fp32) and each W row goes to 8 consecutive lanes (128-byte
+// segments, 16 float4 per lane), so a row norm is three shuffles.  W loads
+// are issued after the staging stores, when those registers of X5 are free.
+//   W1, W3 ([COLS][128], row j = column j of X5): every wave steps the rows of
+//     its own columns, 32 per pass, through its own 16 KiB of LDS (no
+//     barrier after the first).
+//   W2 ([128][COLS], the orientation of X5): 64 (COLS 512) or 128 (COLS 256)
+//     rows per pass, staged by all waves; the final rows go back into the
+//     tile, whose columns then give the W2^T copy (8 features of a hidden unit
+//     per 16-byte store).
+// LDS keys (measured bank model: 16-byte reads in 16-lane passes by lane-quad
+// parity, 16-byte writes in 8-lane passes): every staging store and every
+// read below touches 64 distinct banks.
+template <int COLS, int NMT, int NRT>
+__device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], float P, int m,
+                                                 const NsStep& st, float* stg) {
+  constexpr int CW = COLS / 8;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col0 = w * CW;
+  const int mat = m / st.bh, head = m - mat * st.bh;
+  const int64_t msz = (int64_t)128 * COLS;
+  bf16* sb = reinterpret_cast<bf16*>(st.sh.base) + (int64_t)head * st.sh.per_head;
+  __syncthreads();  // every Newton-Schulz read of LDS done
+  if (mat < 2) {
+    float* W = (mat == 0 ? st.w1 : st.w3) + head * msz;
+    const float* N0 = (mat == 0 ? st.n1 : st.n3) + (int64_t)head * COLS;
+    bf16* S = sb + (mat == 0 ? st.sh.off_w1 : st.sh.off_w3);
+    float* ws = stg + w * 32 * 128;  // this wave's [32][128] block
+    // element (row t, feature i) of the block
+    auto off = [](int t, int i) {
+      return t * 128 + (((i >> 2) ^ (4 * (((t >> 2) ^ t) & 3))) << 2) + (i & 3);
+    };
+#pragma unroll
+    for (int p = 0; p < NMT / 2; ++p) {
+      // rows col0 + 32 p + 8 v + lr, features 4 (lk + 8 kk) .. + 3; lane
+      // indices laundered per pass so that no address outlives its pass
+      const int c = opaque(lane & 15), gq = opaque(lane >> 4);
+      const int lr = opaque(lane >> 3), lk = lane & 7;
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+        for (int nt = 0; nt < NRT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ws[off(16 * mh + 4 * gq + e, 16 * nt + c)] = yv[2 * p + mh][nt][e] * P;
+      asm volatile("" ::: "memory");  // loads stay after the stores (register pressure)
+      f32x4 x[4][4];
+      float n0[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = col0 + 32 * p + 8 * v + lr;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          x[v][kk] = *reinterpret_cast<const f32x4*>(W + (int64_t)j * 128 + 4 * (lk + 8 * kk));
+        n0[v] = st.renorm ? N0[j] : 1.f;
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 8 * v + lr;
+        float ss = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          x[v][kk] += *reinterpret_cast<const f32x4*>(ws + off(t, 4 * (lk + 8 * kk)));
+          ss += x[v][kk][0] * x[v][kk][0] + x[v][kk][1] * x[v][kk][1] +
+                x[v][kk][2] * x[v][kk][2] + x[v][kk][3] * x[v][kk][3];
+        }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        const float f = st.renorm ? n0[v] / (sqrtf(ss) + st.eps) : 1.f;
+        const int64_t row = (int64_t)(col0 + 32 * p + t) * 128;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const f32x4 y = x[v][kk] * f;
+          *reinterpret_cast<f32x4*>(W + row + 4 * (lk + 8 * kk)) = y;
+          st4(S + row + 4 * (lk + 8 * kk), y[0], y[1], y[2], y[3]);
+        }
+      }
+    }
+  } else {
+    constexpr int KK = COLS / 32;  // float4 per lane per row
+    constexpr int V = 16 / KK;     // rows per lane per pass
+    constexpr int SR = 64 * V;     // rows per pass
+    float* W = st.w2 + head * msz;
+    const float* N0 = st.n2 + (int64_t)head * 128;
+    bf16* S = sb + st.sh.off_w2;
+    bf16* St = sb + st.sh.off_w2t;
+    auto off = [](int r, int j) {
+      return r * COLS + (((j >> 2) ^ ((4 * (r & 3)) | ((r >> 2) & 1))) << 2) + (j & 3);
+    };
+#pragma unroll
+    for (int p0 = 0; p0 < 128; p0 += SR) {
+      if (p0) __syncthreads();  // the previous pass's tile fully read
+      const int c = opaque(lane & 15), gq = opaque(lane >> 4);
+      const int lr = opaque(lane >> 3), lk = lane & 7;
+#pragma unroll
+      for (int nt = p0 / 16; nt < (p0 + SR) / 16; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+          *reinterpret_cast<f32x4*>(stg + off(16 * nt + c - p0, col0 + 16 * mt + 4 * gq)) = yv[mt][nt] * P;
+      asm volatile("" ::: "memory");  // loads stay after the stores (register pressure)
+      f32x4 x[V][KK];
+      float n0[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int r = 64 * v + 8 * w + lr;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          x[v][kk] = *reinterpret_cast<const f32x4*>(W + (int64_t)(p0 + r) * COLS + 4 * (lk + 8 * kk));
+        n0[v] = st.renorm ? N0[p0 + r] : 1.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int r = 64 * v + 8 * w + lr;
+        float ss = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          x[v][kk] += *reinterpret_cast<const f32x4*>(stg + off(r, 4 * (lk + 8 * kk)));
+          ss += x[v][kk][0] * x[v][kk][0] + x[v][kk][1] * x[v][kk][1] +
+                x[v][kk][2] * x[v][kk][2] + x[v][kk][3] * x[v][kk][3];
+        }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        const float f = st.renorm ? n0[v] / (sqrtf(ss) + st.eps) : 1.f;
+        const int64_t row = (int64_t)(p0 + r) * COLS;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const f32x4 y = x[v][kk] * f;
+          *reinterpret_cast<f32x4*>(W + row + 4 * (lk + 8 * kk)) = y;
+          st4(S + row + 4 * (lk + 8 * kk), y[0], y[1], y[2], y[3]);
+          *reinterpret_cast<f32x4*>(stg + off(r, 4 * (lk + 8 * kk))) = y;  // own slot
+        }
+      }
+      __syncthreads();
+      // W2^T[j][p0 + 8 s .. + 7]: eight 16-byte stores per thread
+      const int j = opaque(tid) % COLS, s0 = (tid / COLS) * 8;
+#pragma unroll 1
+      for (int q = 0; q < 8; ++q) {
+        const int r0 = 8 * (s0 + q);
+        bf16x8 b;
+#pragma unroll
+        for (int x8 = 0; x8 < 8; ++x8) b[x8] = (bf16)stg[off(r0 + x8, j)];
+        *reinterpret_cast<bf16x8*>(St + (int64_t)j * 128 + p0 + r0) = b;
+      }
+    }
+  }
 }
 
 // Newton-Schulz of the write and a read that uses the weights this write
@@ -558,15 +722,15 @@ void k_ns_r128(NsIn g, float* u, float eps) {
 // most compute units idle.
 template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_ns_apply(NsIn g, float* u, float eps, int count, ApplyArgs a) {
+void k_ns_apply(NsIn g, float eps, int count, NsStep st, ApplyArgs a) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds_f[];
   const int b = blockIdx.x;
-  if (b < count) ns_r128_block<COLS>(g, u, eps, b, lds_f);
+  if (b < count) ns_r128_block<COLS, true>(g, nullptr, eps, b, lds_f, st);
   else apply_block<bf16, 128, 32, 8>(a, xcd_logical_id(b - count, (int)gridDim.x - count), lds_f);
 }
 
 template <int COLS>
-static hipError_t run_ns_apply(int count, NsIn g, float* u, float eps, const ApplyArgs& a,
+static hipError_t run_ns_apply(int count, NsIn g, float eps, const NsStep& st, const ApplyArgs& a,
                                hipStream_t s) {
   const size_t lns = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
   const size_t lap = (size_t)ApplyLds<bf16, 128>::ELEMS * sizeof(bf16);
@@ -578,9 +742,9 @@ static hipError_t run_ns_apply(int count, NsIn g, float* u, float eps, const App
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int64_t napply = (a.n_tok + 255) / 256 * a.bh;
-  hipLaunchKernelGGL((k_ns_apply<COLS>), dim3((unsigned)(count + napply)), dim3(512), lds, s, g, u,
-                     eps, count, a);
+  const int64_t napply = a.n_tok > 0 ? (a.n_tok + 255) / 256 * a.bh : 0;
+  hipLaunchKernelGGL((k_ns_apply<COLS>), dim3((unsigned)(count + napply)), dim3(512), lds, s, g,
+                     eps, count, st, a);
   return hipGetLastError();
 }
 
@@ -613,12 +777,25 @@ static hipError_t run_ns_fused(int count, NsIn g, float* u, float eps, hipStream
 }
 
 // Returns hipErrorNotSupported when no fused variant covers the shape.
-hipError_t launch_ns_apply(int count, int rows, int cols, NsIn g, float* u, float eps,
-                           const ApplyArgs& a, hipStream_t s) {
-  if (rows != 128 || a.d != 128 || a.n_tok <= 0) return hipErrorNotSupported;
-  if (cols == 512) return run_ns_apply<512>(count, g, u, eps, a, s);
-  if (cols == 256) return run_ns_apply<256>(count, g, u, eps, a, s);
+hipError_t launch_ns_step_apply(int count, int rows, int cols, NsIn g, float eps,
+                                const NsStep& st, const ApplyArgs& a, hipStream_t s) {
+  if (rows != 128 || (a.n_tok > 0 && a.d != 128) || count != 3 * st.bh) return hipErrorNotSupported;
+  if (cols == 512) return run_ns_apply<512>(count, g, eps, st, a, s);
+  if (cols == 256) return run_ns_apply<256>(count, g, eps, st, a, s);
   return hipErrorNotSupported;
+}
+
+__global__ void k_copy16(f32x4* __restrict__ dst, const f32x4* __restrict__ src, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+hipError_t launch_copy16(void* dst, const void* src, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 16;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<f32x4*>(dst), reinterpret_cast<const f32x4*>(src), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,

@@ -162,10 +162,19 @@ struct Workspace {
   float* xh;
   float* amat;    // [3 bh][d][d]
   float* bmat;
+  void* shadow2;  // second operand copy of the weights (ns_step_fused shapes)
   int64_t bytes;
 };
 
-static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* base) {
+// Shapes whose Newton-Schulz workgroups also take the weight step (and can
+// share their launch with a read, which then needs a second shadow).
+static bool ns_step_fused(const lact_shape* sh, const lact_update_opts* op) {
+  return op != nullptr && op->use_muon && !op->ns_fp32 && sh->dtype == LACT_BF16 && sh->d == 128 &&
+         (sh->dh == 256 || sh->dh == 512);
+}
+
+static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* base,
+                           bool shadow2 = false) {
   Workspace w;
   const int64_t msz = (int64_t)sh->d * sh->dh;
   int64_t off = 0;
@@ -174,6 +183,9 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
     off += align256(nfloat * 4);
     return p;
   };
+  // first, so that its place does not depend on the split count: operand
+  // copies, 4 d dh bf16 per head
+  w.shadow2 = shadow2 ? take((int64_t)sh->bh * 2 * msz) : nullptr;
   w.partial = take((int64_t)nsplit * sh->bh * 3 * msz);
   w.beta = take(sh->bh);
   w.g = take((int64_t)3 * sh->bh * msz);
@@ -334,12 +346,12 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
 
 static lact_status do_step(const lact_shape* sh, const lact_state* st, const float* u1,
                            const float* u3, const float* u2, int renorm, float eps,
-                           hipStream_t s) {
+                           void* shadow_out, hipStream_t s) {
   StepArgs a;
   a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
   a.u1 = u1; a.u3 = u3; a.u2 = u2;
   a.n1 = st->n1; a.n3 = st->n3; a.n2 = st->n2;
-  a.sh = make_shadow(st->shadow, sh->d, sh->dh);
+  a.sh = make_shadow(shadow_out, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
   a.renorm = renorm; a.eps = eps;
   hipError_t e;
@@ -350,21 +362,25 @@ static lact_status do_step(const lact_shape* sh, const lact_state* st, const flo
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
+// One write.  The weights are read through st->shadow and their new operand
+// copies go to shadow_out (NULL: st->shadow, in place).  job: a read with the
+// weights this write replaces; it shares the Newton-Schulz launch where that
+// kernel supports it and shadow_out is another buffer, else it runs first.
 static lact_status do_update(const lact_shape* sh, const lact_state* st, const void* k,
                              lact_layout kl, const void* v, lact_layout vl, const float* e1,
                              const float* e3, const float* e2, const float* mom, int64_t esbh,
                              int64_t n_tok, const lact_update_opts* op, void* ws,
-                             hipStream_t s, const ApplyJob* job = nullptr) {
-  // job: a read with the weights this write replaces; it shares the
-  // Newton-Schulz launch where that kernel supports it, else runs first
-  const bool fuse = job != nullptr && job->n_tok > 0 && op->use_muon && !op->ns_fp32 &&
-                    sh->dtype == LACT_BF16 && sh->d == 128 && (sh->dh == 256 || sh->dh == 512);
+                             hipStream_t s, const ApplyJob* job = nullptr,
+                             void* shadow_out = nullptr) {
+  if (shadow_out == nullptr) shadow_out = st->shadow;
+  const bool nsstep = ns_step_fused(sh, op);
+  const bool fuse = nsstep && job != nullptr && job->n_tok > 0 && shadow_out != st->shadow;
   if (job != nullptr && !fuse) {
     lact_status r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, s);
     if (r != LACT_OK) return r;
   }
   const int nsplit = choose_nsplit(sh, n_tok);
-  Workspace w = layout_ws(sh, nsplit, op->use_muon != 0, reinterpret_cast<char*>(ws));
+  Workspace w = layout_ws(sh, nsplit, op->use_muon != 0, reinterpret_cast<char*>(ws), nsstep);
   const int64_t msz = (int64_t)sh->d * sh->dh;
   const int64_t mall = (int64_t)sh->bh * msz;
   float* g1 = w.g;
@@ -384,17 +400,28 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
     ProfScope p(LACT_PROF_NS, s);
     const NsIn in{{u1, u3, u2}, sh->bh};
     hipError_t e;
-    if (fuse) {
-      const ApplyArgs aa = apply_args(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok);
-      e = launch_ns_apply(3 * sh->bh, sh->d, sh->dh, in, w.g, op->ns_eps, aa, s);
-    } else {
-      e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,
-                 op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
+    if (nsstep) {
+      // Newton-Schulz workgroups take the step; the read (if fused) fills the
+      // other compute units
+      ApplyArgs aa;
+      if (fuse) {
+        aa = apply_args(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok);
+      } else {
+        memset(&aa, 0, sizeof(aa));
+        aa.n_tok = 0;
+      }
+      const NsStep ns{st->w1, st->w3, st->w2, st->n1, st->n3, st->n2,
+                      make_shadow(shadow_out, sh->d, sh->dh), sh->bh, op->renorm ? 1 : 0,
+                      op->renorm_eps};
+      e = launch_ns_step_apply(3 * sh->bh, sh->d, sh->dh, in, op->ns_eps, ns, aa, s);
+      return e == hipSuccess ? LACT_OK : hip_fail(e);
     }
+    e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,
+               op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
   }
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, s);
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, shadow_out, s);
 }
 
 static lact_status check_update_args(const lact_shape* sh, const lact_state* st, const void* k,
@@ -419,6 +446,12 @@ static lact_status check_update_args(const lact_shape* sh, const lact_state* st,
   return LACT_OK;
 }
 
+// The workspace's second shadow (NULL when the shape does not use one).
+static void* second_shadow(const lact_shape* sh, const lact_update_opts* op, void* ws) {
+  if (!ns_step_fused(sh, op)) return nullptr;
+  return layout_ws(sh, 1, op->use_muon != 0, reinterpret_cast<char*>(ws), true).shadow2;
+}
+
 }  // namespace lact
 
 using namespace lact;
@@ -436,7 +469,7 @@ size_t lact_workspace_bytes(const lact_shape* sh, int64_t max_update_tokens,
   const bool muon = opts != nullptr && opts->use_muon != 0;
   const int ns = sh->dtype == LACT_BF16 ? nsplit_bound(sh, max_update_tokens)
                                          : choose_nsplit(sh, max_update_tokens);
-  return (size_t)layout_ws(sh, ns, muon, nullptr).bytes;
+  return (size_t)layout_ws(sh, ns, muon, nullptr, ns_step_fused(sh, opts)).bytes;
 }
 
 size_t lact_ns_workspace_bytes(int32_t count, int32_t rows, int32_t cols) {
@@ -538,7 +571,8 @@ lact_status lact_step_renorm(const lact_shape* sh, const lact_state* st, const f
   }
   if (ws == nullptr || ws_bytes < lact_workspace_bytes(sh, 0, op)) return LACT_ERR_WORKSPACE;
   if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, (hipStream_t)stream);
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, st->shadow,
+                 (hipStream_t)stream);
 }
 
 lact_status lact_update(const lact_shape* sh, const lact_state* st, const void* k,
@@ -569,7 +603,13 @@ lact_status lact_chunk_step(const lact_shape* sh, const lact_state* st, const vo
   hipStream_t s = (hipStream_t)stream;
   if (n_tok == 0) return LACT_OK;
   const ApplyJob job{q, ql, o, ol, n_tok};
-  return do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s, &job);
+  // with the read in the Newton-Schulz launch, the new operand copies go to
+  // the workspace shadow and are copied back
+  void* alt = second_shadow(sh, op, ws);
+  r = do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s, &job, alt);
+  if (r != LACT_OK || alt == nullptr) return r;
+  const hipError_t e = launch_copy16(st->shadow, alt, (int64_t)lact_shadow_bytes(sh), s);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
 lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void* q,
@@ -603,6 +643,19 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
   };
   ApplyJob pending{};
   bool have_pending = false;
+  // Operand copies: a write whose read shares its Newton-Schulz launch puts
+  // the new copies in the other of (state shadow, workspace shadow); cs reads
+  // from the current one.  The state's own shadow holds them at the end.
+  lact_state cs = *st;
+  void* const alt = second_shadow(sh, op, ws);
+  auto write = [&](const void* kp, const void* vp, int64_t a0, int64_t n, const ApplyJob* job) {
+    void* out = cs.shadow;
+    if (alt != nullptr && job != nullptr && job->n_tok > 0) out = cs.shadow == st->shadow ? alt : st->shadow;
+    const lact_status rr = do_update(sh, &cs, kp, kl, vp, vl, e1 + a0, e3 + a0, e2 + a0,
+                                     mom ? mom + a0 : nullptr, esbh, n, op, ws, s, job, out);
+    if (rr == LACT_OK) cs.shadow = out;
+    return rr;
+  };
   for (int64_t s0 = 0; s0 < T; s0 += chunk) {
     const int64_t e0 = s0 + chunk < T ? s0 + chunk : T;
     const bool last = e0 == T;
@@ -611,31 +664,34 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
       a0 = s0 + sub_off;
       a1 = a0 + sub_len < e0 ? a0 + sub_len : e0;
     }
-    const bool write = ((order == LACT_UPDATE_THEN_APPLY) || !last || update_last) && a1 > a0;
+    const bool do_write = ((order == LACT_UPDATE_THEN_APPLY) || !last || update_last) && a1 > a0;
     const ApplyJob job{at(q, ql, s0), ql, const_cast<char*>(at(o, ol, s0)), ol, e0 - s0};
     // the read of a chunk goes with the next write after the weights it uses
     // (this chunk's write when reading first, the next chunk's otherwise)
     if (order == LACT_APPLY_THEN_UPDATE) {
-      if (write)
-        r = do_update(sh, st, at(k, kl, a0), kl, at(v, vl, a0), vl, e1 + a0, e3 + a0, e2 + a0,
-                      mom ? mom + a0 : nullptr, esbh, a1 - a0, op, ws, s, &job);
+      if (do_write)
+        r = write(at(k, kl, a0), at(v, vl, a0), a0, a1 - a0, &job);
       else
-        r = do_apply(sh, st, job.q, job.ql, job.o, job.ol, job.n_tok, s);
+        r = do_apply(sh, &cs, job.q, job.ql, job.o, job.ol, job.n_tok, s);
       if (r != LACT_OK) return r;
     } else {
-      if (write)
-        r = do_update(sh, st, at(k, kl, a0), kl, at(v, vl, a0), vl, e1 + a0, e3 + a0, e2 + a0,
-                      mom ? mom + a0 : nullptr, esbh, a1 - a0, op, ws, s,
-                      have_pending ? &pending : nullptr);
+      if (do_write)
+        r = write(at(k, kl, a0), at(v, vl, a0), a0, a1 - a0, have_pending ? &pending : nullptr);
       else if (have_pending)
-        r = do_apply(sh, st, pending.q, pending.ql, pending.o, pending.ol, pending.n_tok, s);
+        r = do_apply(sh, &cs, pending.q, pending.ql, pending.o, pending.ol, pending.n_tok, s);
       if (r != LACT_OK) return r;
       pending = job;
       have_pending = true;
     }
   }
-  if (have_pending)
-    return do_apply(sh, st, pending.q, pending.ql, pending.o, pending.ol, pending.n_tok, s);
+  if (have_pending) {
+    r = do_apply(sh, &cs, pending.q, pending.ql, pending.o, pending.ol, pending.n_tok, s);
+    if (r != LACT_OK) return r;
+  }
+  if (cs.shadow != st->shadow) {
+    const hipError_t e = launch_copy16(st->shadow, cs.shadow, (int64_t)lact_shadow_bytes(sh), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return LACT_OK;
 }
 

@@ -103,10 +103,25 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
                            float eps, hipStream_t s);
-// Newton-Schulz (bf16, 128 rows, 256 or 512 columns) and a d = 128 bf16 read
-// in one launch; hipErrorNotSupported for other shapes.
-hipError_t launch_ns_apply(int count, int rows, int cols, NsIn g, float* u, float eps,
-                           const ApplyArgs& a, hipStream_t s);
+// Weight step done by the Newton-Schulz workgroups themselves: matrix
+// m = mat * bh + head (mat 0: W1, 1: W3, 2: W2) adds its result U (wide
+// orientation) to W, rescales the rows (renorm) and writes the operand copies
+// into `sh`, which may differ from the shadow a read in the same launch uses.
+struct NsStep {
+  float* w1; float* w3; float* w2;
+  const float* n1; const float* n3; const float* n2;
+  Shadow sh;
+  int bh;
+  int renorm;
+  float eps;
+};
+// Newton-Schulz + step (bf16, 128 rows, 256 or 512 columns), with the tiles
+// of a d = 128 bf16 read (a.n_tok > 0) in the same launch;
+// hipErrorNotSupported for other shapes.
+hipError_t launch_ns_step_apply(int count, int rows, int cols, NsIn g, float eps,
+                                const NsStep& st, const ApplyArgs& a, hipStream_t s);
+// Device copy of `bytes` (a multiple of 16, 16-byte aligned pointers).
+hipError_t launch_copy16(void* dst, const void* src, int64_t bytes, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s);
 hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,

@@ -91,6 +91,21 @@ def state64(fw):
     return W1, W3, W2, M1, M3, M2
 
 
+def check_shadow(fw):
+    """The operand copies must be the fp32 weights rounded to the operand type
+    (round to nearest even), bit for bit: W1, W3 [dh][d], W2 [d][dh] and W2^T
+    [dh][d] per head."""
+    import torch
+    sh = fw.shape
+    dt = torch.bfloat16 if sh.dtype == L.BF16 else torch.float32
+    m = sh.d * sh.dh
+    s = fw.shadow.view(dt).view(sh.bh, 4, m)
+    want = (fw.w1.reshape(sh.bh, m), fw.w3.reshape(sh.bh, m), fw.w2.reshape(sh.bh, m),
+            fw.w2.transpose(1, 2).reshape(sh.bh, m))
+    for x, (name, ref) in enumerate(zip(("W1", "W3", "W2", "W2T"), want)):
+        assert torch.equal(s[:, x], ref.to(dt)), f"shadow {name} differs from the weights"
+
+
 def oracle_state(O, W1, W3, W2, n1=None, n3=None, n2=None, M=None):
     """An oracle HeadState with the given weights (and norms / momentum)."""
     st = O.HeadState(W1, W3, W2)

@@ -162,6 +162,7 @@ def test_step_renorm(device, wi, renorm):
         ref = O.apply(e1, e3, e2, WL.token_values(inp, "q", b, 0, w.T))
         assert H.rel(got[b], ref) < tol_o, (b, H.rel(got[b], ref))
     assert H.rel(H.to64(fw.n1), np.stack([O.row_norms(x) for x in W[0]])) < 1e-6
+    H.check_shadow(fw)
 
 
 @pytest.mark.parametrize("wi", [0, 1, 3, 4])
@@ -198,6 +199,7 @@ def test_update_twice(device, wi):
             st = H.oracle_state(O, W1[b], W3[b], W2[b], sts[b].n1, sts[b].n3, sts[b].n2,
                                 None if M1 is None else (M1[b], M3[b], M2[b]))
             sts[b] = st
+        H.check_shadow(fw)
 
 
 @pytest.mark.parametrize("wi,n", [(0, 320), (1, 320), (1, 1), (3, 320), (3, 17), (4, 320)])
@@ -231,6 +233,7 @@ def test_chunk_step(device, wi, n):
                        mom=m, use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
         for name, x, y in (("W1", W1[b], ref.W1), ("W3", W3[b], ref.W3), ("W2", W2[b], ref.W2)):
             assert H.rel(x, y) < H.TOL[w.dtype], (name, b, H.rel(x, y))
+    H.check_shadow(fw)
 
 
 SEQ_CASES = {
@@ -262,3 +265,4 @@ def test_sequence_end_to_end(device, wi):
         assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
         assert H.rel(W1[b], st.W1) < H.TOL[w.dtype]
         assert H.rel(W2[b], st.W2) < H.TOL[w.dtype]
+    H.check_shadow(fw)
