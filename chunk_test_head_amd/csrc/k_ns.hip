@@ -384,10 +384,15 @@ template <int COLS, int NMT, int NRT>
 __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], float P, int m,
                                                  const NsStep& st, float* stg);
 
-// STEP: instead of writing U, add it to the weights (ns_step_epilogue).
+template <int COLS, int NMT, int NRT>
+__device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const NsGrad& gr,
+                                             float* stg);
+
+// STEP: G from the split partials (ns_load_grad) instead of g, and instead of
+// writing U, add it to the weights (ns_step_epilogue).
 template <int COLS, bool STEP>
-__device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps, int m,
-                                              bf16* lds_r, const NsStep& st) {
+__device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, float* u, float eps,
+                                              int m, bf16* lds_r, const NsStep& st) {
   constexpr int R = 128, NW = 8;
   constexpr int CW = COLS / NW;  // columns per wave
   constexpr int NMT = CW / 16;   // column tiles per wave
@@ -402,9 +407,6 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps
   const int bx0 = 4 * (w >> 2), by0 = 2 * (w & 3);  // this wave's block of A
   const bool active = !(w == 4 || w == 5);          // blocks below the diagonal: mirrored
   const bool direct = (w == 2 || w == 3);           // blocks above it
-  const float* G = g.at(m, (int64_t)R * COLS);
-  float* U = u + (int64_t)m * R * COLS;
-
   // ---- load G: whole rows, coalesced, staged through LDS (fp32, 16-byte
   // chunks XORed with the row) into the accumulator layout ----
   // rows per staging pass: fp32 rows must fit the LDS allocation (sX + sA)
@@ -415,6 +417,9 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps
   float* stg = reinterpret_cast<float*>(lds_r);
   auto soff = [](int r, int col) { return r * COLS + ((((col >> 2) ^ (r & 15))) << 2) + (col & 3); };
   f32x4 yv[NMT][NRT];
+  if constexpr (STEP) ns_load_grad<COLS>(yv, m, gr, stg);
+  else {
+  const float* G = g.at(m, (int64_t)R * COLS);
 #pragma unroll
   for (int p0 = 0; p0 < R; p0 += SR) {
     if (p0) __syncthreads();  // previous pass fully read
@@ -430,6 +435,7 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
         yv[mt][nt] = *reinterpret_cast<const f32x4*>(stg + soff(16 * nt + c - p0, col0 + 16 * mt + 4 * gq));
+  }
   }
   // Frobenius norm (fixed order)
   float ss = 0.f;
@@ -531,6 +537,7 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, float* u, float eps
     ns_step_epilogue<COLS>(yv, P, m, st, stg);
     return;
   }
+  float* U = u + (int64_t)m * R * COLS;
   // ---- X_5 = P_5 Y_5, staged through LDS into whole rows ----
 #pragma unroll
   for (int p0 = 0; p0 < R; p0 += SR) {
@@ -556,7 +563,103 @@ template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_ns_r128(NsIn g, float* u, float eps) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds_r[];
-  ns_r128_block<COLS, false>(g, u, eps, blockIdx.x, lds_r, NsStep{});
+  ns_r128_block<COLS, false>(g, NsGrad{}, u, eps, blockIdx.x, lds_r, NsStep{});
+}
+
+// ---- gradient prologue ----
+// G in the accumulator layout (lane (c, g): row 16 nt + c, columns col0 +
+// 16 mt + 4 g .. + 3) from the split partials, which hold G^T ([dh][128]):
+// every wave sums the partial rows of its own columns, 32 per pass, 8 lanes
+// per row (128-byte segments), in split order, stores the sums in its own
+// 16 KiB of LDS and reads them back transposed; then the momentum
+// G <- G + beta M (M loaded in the accumulator layout, 16 bytes per lane) and
+// M <- G.  The LDS key is the one of the W1 step below (every store and read
+// on 64 distinct banks); no barrier: each wave touches only its own block.
+template <int COLS, int NMT, int NRT>
+__device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const NsGrad& gr,
+                                             float* stg) {
+  constexpr int CW = COLS / 8;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col0 = w * CW;
+  const int mat = m / gr.bh, head = m - mat * gr.bh;
+  const int64_t msz = (int64_t)128 * COLS;
+  const float* P0 = gr.partial + ((int64_t)head * 3 + mat) * msz;
+  const int64_t pstr = (int64_t)gr.bh * 3 * msz;  // between splits
+  float* M = gr.m[mat] != nullptr ? gr.m[mat] + head * msz : nullptr;
+  const float beta = M != nullptr ? gr.beta[head] : 0.f;
+  float* ws = stg + w * 32 * 128;
+  auto off = [](int t, int i) {
+    return t * 128 + (((i >> 2) ^ (4 * (((t >> 2) ^ t) & 3))) << 2) + (i & 3);
+  };
+  // Load schedule (registers): pass 0 issues its partial rows and its old
+  // momentum together; later passes hold the earlier passes' results, so their
+  // momentum loads follow the partial sums.  Three round trips for COLS 512.
+  auto load_mo = [&](int p, f32x4 (&mo)[2][NRT]) {
+    const int c = opaque(lane & 15), gq = opaque(lane >> 4);
+    const float* mrow = M + (int64_t)c * COLS + col0 + 32 * p + 4 * gq;
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int nt = 0; nt < NRT; ++nt)
+        mo[mh][nt] = *reinterpret_cast<const f32x4*>(mrow + (int64_t)16 * nt * COLS + 16 * mh);
+  };
+#pragma unroll
+  for (int p = 0; p < NMT / 2; ++p) {
+    asm volatile("" ::: "memory");  // no load of this pass above the last one (registers)
+    f32x4 mo[2][NRT];
+    if (p == 0 && M != nullptr) load_mo(0, mo);
+    const int c = opaque(lane & 15), gq = opaque(lane >> 4);
+    const int lr = opaque(lane >> 3), lk = lane & 7;
+    // partial rows col0 + 32 p + 8 v + lr, features 4 (lk + 8 kk) .. + 3
+    const float* pp = P0 + (int64_t)(col0 + 32 * p + lr) * 128 + 4 * lk;
+    f32x4 x[4][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) x[v][kk] = *reinterpret_cast<const f32x4*>(pp + 8 * v * 128 + 32 * kk);
+    for (int sp = 1; sp < gr.nsplit; ++sp) {
+      const float* q = pp + sp * pstr;
+      f32x4 y[4][4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) y[v][kk] = *reinterpret_cast<const f32x4*>(q + 8 * v * 128 + 32 * kk);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) x[v][kk] += y[v][kk];
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        *reinterpret_cast<f32x4*>(ws + off(8 * v + lr, 4 * (lk + 8 * kk))) = x[v][kk];
+    // transposed read-back: G[16 nt + c][col0 + 16 (2p + mh) + 4 gq + e]
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int nt = 0; nt < NRT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yv[2 * p + mh][nt][e] = ws[off(16 * mh + 4 * gq + e, 16 * nt + c)];
+    if (M != nullptr) {
+      // M <- G + beta M (later passes: one 16-column tile at a time)
+      float* mrow = M + (int64_t)c * COLS + col0 + 32 * p + 4 * gq;
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh) {
+        if (p > 0) {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int nt = 0; nt < NRT; ++nt)
+            mo[mh][nt] = *reinterpret_cast<const f32x4*>(mrow + (int64_t)16 * nt * COLS + 16 * mh);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NRT; ++nt) {
+          yv[2 * p + mh][nt] = yv[2 * p + mh][nt] + beta * mo[mh][nt];
+          *reinterpret_cast<f32x4*>(mrow + (int64_t)16 * nt * COLS + 16 * mh) = yv[2 * p + mh][nt];
+        }
+      }
+    }
+  }
 }
 
 // ---- step epilogue ----
@@ -722,16 +825,16 @@ __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], fl
 // most compute units idle.
 template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_ns_apply(NsIn g, float eps, int count, NsStep st, ApplyArgs a) {
+void k_ns_apply(NsGrad gr, float eps, int count, NsStep st, ApplyArgs a) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds_f[];
   const int b = blockIdx.x;
-  if (b < count) ns_r128_block<COLS, true>(g, nullptr, eps, b, lds_f, st);
+  if (b < count) ns_r128_block<COLS, true>(NsIn{}, gr, nullptr, eps, b, lds_f, st);
   else apply_block<bf16, 128, 32, 8>(a, xcd_logical_id(b - count, (int)gridDim.x - count), lds_f);
 }
 
 template <int COLS>
-static hipError_t run_ns_apply(int count, NsIn g, float eps, const NsStep& st, const ApplyArgs& a,
-                               hipStream_t s) {
+static hipError_t run_ns_apply(int count, const NsGrad& g, float eps, const NsStep& st,
+                               const ApplyArgs& a, hipStream_t s) {
   const size_t lns = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
   const size_t lap = (size_t)ApplyLds<bf16, 128>::ELEMS * sizeof(bf16);
   const size_t lds = lns > lap ? lns : lap;
@@ -777,9 +880,11 @@ static hipError_t run_ns_fused(int count, NsIn g, float* u, float eps, hipStream
 }
 
 // Returns hipErrorNotSupported when no fused variant covers the shape.
-hipError_t launch_ns_step_apply(int count, int rows, int cols, NsIn g, float eps,
+hipError_t launch_ns_step_apply(int count, int rows, int cols, const NsGrad& g, float eps,
                                 const NsStep& st, const ApplyArgs& a, hipStream_t s) {
-  if (rows != 128 || (a.n_tok > 0 && a.d != 128) || count != 3 * st.bh) return hipErrorNotSupported;
+  if (rows != 128 || (a.n_tok > 0 && a.d != 128) || count != 3 * st.bh || g.bh != st.bh ||
+      g.nsplit < 1)
+    return hipErrorNotSupported;
   if (cols == 512) return run_ns_apply<512>(count, g, eps, st, a, s);
   if (cols == 256) return run_ns_apply<256>(count, g, eps, st, a, s);
   return hipErrorNotSupported;

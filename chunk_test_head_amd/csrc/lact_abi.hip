@@ -317,7 +317,8 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
                            lact_layout kl, const void* v, lact_layout vl, const float* e1,
                            const float* e3, const float* e2, int64_t esbh, int64_t n_tok,
                            const Workspace& w, int nsplit, float* o1, float* o3, float* o2,
-                           float* m1, float* m3, float* m2, const float* mom, hipStream_t s) {
+                           float* m1, float* m3, float* m2, const float* mom, hipStream_t s,
+                           bool reduce = true) {
   GradArgs a;
   a.k = k; a.k_sbh = kl.stride_bh; a.k_st = kl.stride_tok;
   a.v = v; a.v_sbh = vl.stride_bh; a.v_st = vl.stride_tok;
@@ -336,6 +337,7 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
     e = launch_grad(sh->dtype, a, s);
   }
   if (e != hipSuccess) return hip_fail(e);
+  if (!reduce) return LACT_OK;  // the consumer sums the partials itself
   ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
   {
     ProfScope p(LACT_PROF_REDUCE, s);
@@ -391,7 +393,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
                           mo ? nullptr : g1, mo ? nullptr : g3, mo ? nullptr : g2,
                           mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr,
-                          mo ? mom : nullptr, s);
+                          mo ? mom : nullptr, s, !nsstep);
   if (r != LACT_OK) return r;
   const float* u1 = mo ? st->m1 : g1;
   const float* u3 = mo ? st->m3 : g3;
@@ -401,8 +403,8 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
     const NsIn in{{u1, u3, u2}, sh->bh};
     hipError_t e;
     if (nsstep) {
-      // Newton-Schulz workgroups take the step; the read (if fused) fills the
-      // other compute units
+      // Newton-Schulz workgroups sum the split partials (+ momentum) and take
+      // the step; the read (if fused) fills the other compute units
       ApplyArgs aa;
       if (fuse) {
         aa = apply_args(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok);
@@ -413,7 +415,10 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
       const NsStep ns{st->w1, st->w3, st->w2, st->n1, st->n3, st->n2,
                       make_shadow(shadow_out, sh->d, sh->dh), sh->bh, op->renorm ? 1 : 0,
                       op->renorm_eps};
-      e = launch_ns_step_apply(3 * sh->bh, sh->d, sh->dh, in, op->ns_eps, ns, aa, s);
+      const NsGrad gr{w.partial, nsplit, sh->bh,
+                      {mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr},
+                      w.beta};
+      e = launch_ns_step_apply(3 * sh->bh, sh->d, sh->dh, gr, op->ns_eps, ns, aa, s);
       return e == hipSuccess ? LACT_OK : hip_fail(e);
     }
     e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,

@@ -115,10 +115,20 @@ struct NsStep {
   int renorm;
   float eps;
 };
-// Newton-Schulz + step (bf16, 128 rows, 256 or 512 columns), with the tiles
-// of a d = 128 bf16 read (a.n_tok > 0) in the same launch;
-// hipErrorNotSupported for other shapes.
-hipError_t launch_ns_step_apply(int count, int rows, int cols, NsIn g, float eps,
+// Input of a Newton-Schulz launch that also finishes the gradient: matrix
+// m = mat * bh + head starts from G = the sum over splits s (in split order)
+// of partial[s][head][mat]^T; with momentum (m[mat] != NULL)
+// G <- G + beta[head] M and M <- G.
+struct NsGrad {
+  const float* partial;  // [nsplit][bh][3][dh][d]
+  int nsplit, bh;
+  float* m[3];           // wide [bh][d][dh] each, or NULL
+  const float* beta;     // [bh]
+};
+// Gradient reduction + Newton-Schulz + step (bf16, 128 rows, 256 or 512
+// columns), with the tiles of a d = 128 bf16 read (a.n_tok > 0) in the same
+// launch; hipErrorNotSupported for other shapes.
+hipError_t launch_ns_step_apply(int count, int rows, int cols, const NsGrad& gr, float eps,
                                 const NsStep& st, const ApplyArgs& a, hipStream_t s);
 // Device copy of `bytes` (a multiple of 16, 16-byte aligned pointers).
 hipError_t launch_copy16(void* dst, const void* src, int64_t bytes, hipStream_t s);
