@@ -24,8 +24,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
 }
 
 // ------------------------------------------------------ apply, d = 256 --
-// Wave pairs, as the d = 256 gradient kernel: the two waves of a pair read
-// the same 32 tokens and split the features.  Wave (p, h) keeps the q
+// Wave pairs: the two waves of a pair read the same 32 tokens and split the
+// features.  Wave (p, h) keeps the q
 // fragments and the o^T accumulators of features [128 h, 128 h + 128).  Per
 // block of 32 hidden units:
 //   1. half-K partials of the gate / up pre-activations (W1, W3 block rows
@@ -646,219 +646,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
     }
 }
 
-// ---------------------------------------------- gradient, bf16, d = 256 --
-// Wave pairs.  A wave holding 16 hidden units over all 256 features needs
-// 96 registers of W fragments and 192 of gradient accumulators, which allows
-// only one wave per SIMD.  Here the two waves of a pair share 16 hidden units
-// and split the features: wave (p, h) keeps the W fragments and the G1^T,
-// G3^T, G2 rows of features [128 h, 128 h + 128).  Per 32-token tile:
-//   1. each wave forms its half-K partial of the forward contractions
-//      (g, u, e over its 128 features);
-//   2. the partials are exchanged through LDS and summed in a fixed order
-//      (half 0 + half 1), so both waves hold the same g, u, e;
-//   3. both run the SwiGLU backward (identical values) and the gradient
-//      contractions of their own feature rows.
-// One workgroup = 8 waves = 4 pairs = 64 hidden units; two waves per SIMD.
-template <int D>
-__global__ __launch_bounds__(512) void k_grad_pair(GradArgs a) {
-  constexpr int WAVES = 8, NTH = 512, NT = 32;
-  constexpr int DH2 = D / 2;           // features per wave
-  constexpr int KS = DH2 / 32;         // K slabs of the forward contractions
-  constexpr int IT = DH2 / 16;         // feature tiles of the gradient
-  constexpr int TILE = NT * (D + 16);   // rows at a padded pitch (tpad)
-  constexpr int NV = NT * D / 8;       // 16-byte vectors per tile
-  constexpr int VPT = NV / NTH;
-  static_assert(NV % NTH == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) bf16 sKV[2][2 * TILE];
-  __shared__ float sEta[2][3][NT];
-  __shared__ f32x4 sX[WAVES][6][64];   // forward partials, C layout
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int pair = wave >> 1, half = wave & 1;
-  const int hblocks = a.dh / 64;
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int hb = lid % hblocks;
-  const int rest = lid / hblocks;
-  const int split = rest % a.nsplit;
-  const int head = rest / a.nsplit;
-  if (head >= a.bh) return;
-  const int64_t s0 = (int64_t)split * a.split_len;
-  const int64_t s1 = (s0 + a.split_len < a.n_tok) ? s0 + a.split_len : a.n_tok;
-  const int j0 = (hb * 4 + pair) * 16;
-  const int d0 = half * DH2;
-
-  const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (int64_t)head * a.k_sbh;
-  const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (int64_t)head * a.v_sbh;
-  const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh;
-  const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh;
-  const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
-  const bool same_eta = a.eta1 == a.eta3 && a.eta3 == a.eta2;
-  const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
-
-  // W B fragments of the own feature half: lane holds W[j0 + c][d0 + 32 ks + 8 g ..]
-  bf16x8 b1[KS], b3[KS], b2[KS];
-  {
-    const int64_t row = (int64_t)(j0 + c) * D + d0 + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      b1[ks] = ld8(sb + a.sh.off_w1 + row + 32 * ks);
-      b3[ks] = ld8(sb + a.sh.off_w3 + row + 32 * ks);
-      b2[ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
-    }
-  }
-  f32x4 G1[IT], G3[IT], G2[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    G1[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G3[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G2[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // staging (as k_grad_bf16): 16-byte vectors vi = tid + x NTH of the k and v
-  // tiles, and for tid < 3 NT one eta
-  const float* ep = tid < NT ? e1 : (tid < 2 * NT ? e3 : e2);
-  const int er = tid % NT;
-  uint4 rk[VPT], rv[VPT];
-  float re = 0.f;
-#define LACT_GP_GLOAD(T0)                                                           \
-  {                                                                                 \
-    _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
-      const int vi = tid + x * NTH;                                                 \
-      const int64_t t = (T0) + vi / (D / 8);                                        \
-      rk[x] = uint4{0u, 0u, 0u, 0u};                                                \
-      rv[x] = uint4{0u, 0u, 0u, 0u};                                                \
-      if (t < s1) {                                                                 \
-        rk[x] = *reinterpret_cast<const uint4*>(kp + t * a.k_st + (vi % (D / 8)) * 8); \
-        rv[x] = *reinterpret_cast<const uint4*>(vp + t * a.v_st + (vi % (D / 8)) * 8); \
-      }                                                                             \
-    }                                                                               \
-    if (tid < 3 * NT) re = ((T0) + er < s1) ? ep[(T0) + er] : 0.f;                  \
-  }
-#define LACT_GP_LSTORE(BUF)                                                         \
-  {                                                                                 \
-    bf16* sK_ = sKV[BUF];                                                           \
-    _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
-      const int vi = tid + x * NTH;                                                 \
-      const int o = tpad<D>(vi / (D / 8), (vi % (D / 8)) * 8);                       \
-      *reinterpret_cast<uint4*>(sK_ + o) = rk[x];                                   \
-      *reinterpret_cast<uint4*>(sK_ + TILE + o) = rv[x];                            \
-    }                                                                               \
-    if (tid < 3 * NT) sEta[BUF][tid / NT][er] = re;                                 \
-  }
-
-  const int ntile = s0 < s1 ? (int)((s1 - s0 + NT - 1) / NT) : 0;
-  if (ntile > 0) {
-    LACT_GP_GLOAD(s0);
-    LACT_GP_LSTORE(0);
-  }
-  __syncthreads();
-  for (int n = 0; n < ntile; ++n) {
-    const int cur = n & 1;
-    const bool more = n + 1 < ntile;
-    if (more) LACT_GP_GLOAD(s0 + (int64_t)(n + 1) * NT);
-    const bf16* sK = sKV[cur];
-    const bf16* sV = sK + TILE;
-    // 1. half-K forward partials
-    f32x4 P[2], U[2], E[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      E[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 ak = ld8(sK + tpad<D>(16 * tt + c, d0 + 32 * ks + 8 * g));
-        const bf16x8 av = ld8(sV + tpad<D>(16 * tt + c, d0 + 32 * ks + 8 * g));
-        mma(P[tt], ak, b1[ks]);
-        mma(U[tt], ak, b3[ks]);
-        mma(E[tt], av, b2[ks]);
-      }
-    // 2. exchange, fixed-order sum
-    sX[wave][0][lane] = P[0]; sX[wave][1][lane] = P[1];
-    sX[wave][2][lane] = U[0]; sX[wave][3][lane] = U[1];
-    sX[wave][4][lane] = E[0]; sX[wave][5][lane] = E[1];
-    __syncthreads();
-    {
-      const int o = wave ^ 1;
-#define LACT_GP_SUM(X, Q) X = half == 0 ? X + sX[o][Q][lane] : sX[o][Q][lane] + X;
-      LACT_GP_SUM(P[0], 0) LACT_GP_SUM(P[1], 1) LACT_GP_SUM(U[0], 2)
-      LACT_GP_SUM(U[1], 3) LACT_GP_SUM(E[0], 4) LACT_GP_SUM(E[1], 5)
-#undef LACT_GP_SUM
-    }
-    // 3. SwiGLU backward + eta (B operands, K = 32 tokens in kappa order)
-    bf16x8 fh, fu, fg;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const f32x4 n1 = *reinterpret_cast<const f32x4*>(&sEta[cur][0][16 * tt + 4 * g]);
-      const f32x4 n3 = *reinterpret_cast<const f32x4*>(&sEta[cur][1][16 * tt + 4 * g]);
-      const f32x4 n2 = *reinterpret_cast<const f32x4*>(&sEta[cur][2][16 * tt + 4 * g]);
-      if (same_eta) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
-          const float sg = sigmoid_fast(p);
-          const float sl = p * sg;
-          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);
-          const float sn = n1[i] * sl;
-          fh[4 * tt + i] = (bf16)(sn * u);
-          fu[4 * tt + i] = (bf16)(sn * e);
-          fg[4 * tt + i] = (bf16)((n1[i] * dsl) * (e * u));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = P[tt][i], u = U[tt][i], e = E[tt][i];
-          const float sg = sigmoid_fast(p);
-          const float sl = p * sg;
-          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);
-          fh[4 * tt + i] = (bf16)((n2[i] * sl) * u);
-          fu[4 * tt + i] = (bf16)((n3[i] * sl) * e);
-          fg[4 * tt + i] = (bf16)((n1[i] * dsl) * (e * u));
-        }
-      }
-    }
-    //    gradient contractions of the own feature rows
-    {
-      const int tr = 4 * g + (c >> 2);
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int fc = d0 + 16 * it + 4 * (c & 3);
-        const bf16x8 akt = cat8(ld_tr4(sK + tpad<D>(tr, fc)), ld_tr4(sK + tpad<D>(tr + 16, fc)));
-        const bf16x8 avt = cat8(ld_tr4(sV + tpad<D>(tr, fc)), ld_tr4(sV + tpad<D>(tr + 16, fc)));
-        mma(G1[it], akt, fg);
-        mma(G3[it], akt, fu);
-        mma(G2[it], avt, fh);
-      }
-    }
-    if (more) LACT_GP_LSTORE(cur ^ 1);
-    __syncthreads();  // tile and exchange slots free for the next tile
-  }
-#undef LACT_GP_GLOAD
-#undef LACT_GP_LSTORE
-  // momentum: the head's mean coefficient, once per head
-  if (a.mom != nullptr && hb == 0 && split == 0)
-    block_mean<NTH>(a.mom + (int64_t)head * a.mom_sbh, a.n_tok, a.beta + head);
-
-  // ---- partials, [split][head][3][dh][d]: lane holds 4 consecutive d ----
-  const int64_t mat = (int64_t)a.dh * D;
-  float* out = a.partial + ((int64_t)split * a.bh + head) * 3 * mat + (int64_t)(j0 + c) * D + d0 + 4 * g;
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    st4(out + 16 * it, G1[it][0], G1[it][1], G1[it][2], G1[it][3]);
-    st4(out + mat + 16 * it, G3[it][0], G3[it][1], G3[it][2], G3[it][3]);
-    st4(out + 2 * mat + 16 * it, G2[it][0], G2[it][1], G2[it][2], G2[it][3]);
-  }
-}
-
 // -------------------------------------------- gradient, bf16, d = 256, solo --
 // One wave per SIMD holding 16 hidden units over all 256 features: its W
 // fragments (96 registers) and G1^T, G3^T, G2 accumulators (192) take a whole
-// SIMD's register file (VGPRs + AGPRs), so no partial exchange and no
-// duplicated SwiGLU backward as in k_grad_pair.  4 waves = 64 hidden units
+// SIMD's register file (VGPRs + AGPRs).  (Two waves per SIMD would have to
+// split the features, exchange the forward partials through LDS and both
+// run the SwiGLU backward: measured 20-30 % slower.)  4 waves = 64 hidden units
 // share the staged k / v tiles.  Software pipeline over 32-token tiles, three
 // stage buffers: iteration n runs the SwiGLU backward of tile n (VALU) next to
 // the forward contractions of tile n + 1 (MFMA), then the gradient
@@ -1143,13 +936,6 @@ static hipError_t run_grad_bf16(const GradArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_grad_bf16<D, WAVES, HT>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
-  return hipGetLastError();
-}
-
-static hipError_t run_grad_pair(const GradArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)(a.dh / 64) * a.nsplit * a.bh;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_grad_pair<256>), dim3((unsigned)blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
