@@ -646,17 +646,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
     }
 }
 
-// -------------------------------------------- gradient, bf16, d = 256, solo --
-// One wave per SIMD holding 16 hidden units over all 256 features: its W
-// fragments (96 registers) and G1^T, G3^T, G2 accumulators (192) take a whole
-// SIMD's register file (VGPRs + AGPRs).  (Two waves per SIMD would have to
-// split the features, exchange the forward partials through LDS and both
-// run the SwiGLU backward: measured 20-30 % slower.)  4 waves = 64 hidden units
-// share the staged k / v tiles.  Software pipeline over 32-token tiles, three
-// stage buffers: iteration n runs the SwiGLU backward of tile n (VALU) next to
-// the forward contractions of tile n + 1 (MFMA), then the gradient
-// contractions of tile n, while tile n + 2 is loaded; one barrier per tile.
-template <int D>
+// ------------------------------------------------- gradient, bf16, solo --
+// One wave per SIMD holding 16 HW hidden units over all D features: its W
+// fragments (3 HW D / 8 registers) and G1^T, G3^T, G2 accumulators
+// (6 HW D / 4, in AGPRs) take a whole SIMD's register file; D = 256: HW = 1,
+// D = 128: HW = 2 (every k / v fragment then feeds two hidden tiles, half
+// the LDS reads of one 16-unit tile per wave).  (For d = 256, two waves per
+// SIMD would have to split the features, exchange the forward partials
+// through LDS and both run the SwiGLU backward: measured 20-30 % slower.)
+// 4 waves = 64 HW hidden units share the staged k / v tiles.  Software
+// pipeline over 32-token tiles, three stage buffers, one barrier per tile:
+// iteration n runs the forward contractions of tile n + 1 with the SwiGLU
+// backward of tile n spread between them, then the gradient contractions
+// of tile n with the staging stores of tile n + 2 between them; fragment
+// reads two steps ahead of their MFMAs, the order held by scheduling fences.
+template <int D, int HW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_grad_solo(GradArgs a) {
   constexpr int NTH = 256, NT = 32;
@@ -666,13 +670,17 @@ void k_grad_solo(GradArgs a) {
   constexpr int NV = NT * D / 8;       // 16-byte vectors per tile
   constexpr int VPT = NV / NTH;
   constexpr int NBUF = 3;
-  static_assert(NV % NTH == 0, "tile split");
+  constexpr int NST = 2 * KS;          // forward steps (K slab, token half)
+  constexpr int EPS_ = 8 * HW / NST;   // backward elements per forward step
+  constexpr int EVERY = NST / (8 * HW) > 0 ? NST / (8 * HW) : 1;  // steps per element
+  static_assert(NV % NTH == 0 && VPT <= IT - 4, "tile split");
+  static_assert(EPS_ * NST == 8 * HW || EVERY * 8 * HW == NST, "backward spread");
   __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF][2 * TILE];
   __shared__ float sEta[NBUF][3][NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int hblocks = a.dh / 64;
+  const int hblocks = a.dh / (64 * HW);
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int hb = lid % hblocks;
   const int rest = lid / hblocks;
@@ -681,7 +689,7 @@ void k_grad_solo(GradArgs a) {
   if (head >= a.bh) return;
   const int64_t s0 = (int64_t)split * a.split_len;
   const int64_t s1 = (s0 + a.split_len < a.n_tok) ? s0 + a.split_len : a.n_tok;
-  const int j0 = (hb * 4 + wave) * 16;
+  const int j0 = (hb * 4 + wave) * 16 * HW;
 
   const bf16* kp = reinterpret_cast<const bf16*>(a.k) + (int64_t)head * a.k_sbh;
   const bf16* vp = reinterpret_cast<const bf16*>(a.v) + (int64_t)head * a.v_sbh;
@@ -690,24 +698,27 @@ void k_grad_solo(GradArgs a) {
   const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
   const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
 
-  // W B fragments: lane holds W[j0 + c][32 ks + 8 g ..]
-  bf16x8 b1[KS], b3[KS], b2[KS];
-  {
-    const int64_t row = (int64_t)(j0 + c) * D + 8 * g;
+  // W B fragments: lane holds W[j0 + 16 h + c][32 ks + 8 g ..]
+  bf16x8 b1[HW][KS], b3[HW][KS], b2[HW][KS];
+#pragma unroll
+  for (int h = 0; h < HW; ++h) {
+    const int64_t row = (int64_t)(j0 + 16 * h + c) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      b1[ks] = ld8(sb + a.sh.off_w1 + row + 32 * ks);
-      b3[ks] = ld8(sb + a.sh.off_w3 + row + 32 * ks);
-      b2[ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
+      b1[h][ks] = ld8(sb + a.sh.off_w1 + row + 32 * ks);
+      b3[h][ks] = ld8(sb + a.sh.off_w3 + row + 32 * ks);
+      b2[h][ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
     }
   }
-  f32x4 G1[IT], G3[IT], G2[IT];
+  f32x4 G1[HW][IT], G3[HW][IT], G2[HW][IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    G1[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G3[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G2[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int h = 0; h < HW; ++h)
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      G1[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      G3[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      G2[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   // staging: 16-byte vectors vi = tid + x NTH of the k and v tiles, and for
   // tid < 3 NT one eta (zero past the split: no contribution)
@@ -740,25 +751,6 @@ void k_grad_solo(GradArgs a) {
     }                                                                               \
     if (tid < 3 * NT) sEta[BUF][tid / NT][er] = re;                                 \
   }
-  // forward contractions of the tile in buffer BUF: gate, up (k rows) and
-  // W2^T v (v rows), tokens 16 tt + 4 g + i, hidden c
-#define LACT_GS_FWD(BUF, P_, U_, E_)                                                \
-  {                                                                                 \
-    const bf16* pk_ = sKV[BUF] + fo;                                                \
-    _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                              \
-      P_[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                           \
-      U_[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                           \
-      E_[tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                           \
-    }                                                                               \
-    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
-    _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                              \
-      const bf16x8 ak = ld8(pk_ + 16 * tt * (D + 16) + 32 * ks);                    \
-      const bf16x8 av = ld8(pk_ + TILE + 16 * tt * (D + 16) + 32 * ks);             \
-      mma(P_[tt], ak, b1[ks]);                                                      \
-      mma(U_[tt], ak, b3[ks]);                                                      \
-      mma(E_[tt], av, b2[ks]);                                                      \
-    }                                                                               \
-  }
 
   // per-lane element offsets in a tile (laundered: the stage buffer is a
   // runtime choice, and every read should be this base + an immediate):
@@ -766,6 +758,74 @@ void k_grad_solo(GradArgs a) {
   // 4 g + c / 4, features 4 (c % 4) ..)
   const int fo = opaque(tpad<D>(c, 8 * g));
   const int to = opaque(tpad<D>(4 * g + (c >> 2), 4 * (c & 3)));
+  // forward contractions of the tile in buffer BUF (gate, up from k rows,
+  // W2^T v from v rows): tokens 16 tt + 4 g + i, hidden 16 h + c.  With
+  // BW, the SwiGLU backward of the previous tile runs between the steps.
+  f32x4 P[HW][2], U[HW][2], E[HW][2];
+  bf16x8 fh[HW], fu[HW], fg[HW];
+  auto forward = [&](int buf, f32x4 (&Pn)[HW][2], f32x4 (&Un)[HW][2], f32x4 (&En)[HW][2],
+                     bool bw, int eb, const f32x4 (&Pc)[HW][2], const f32x4 (&Uc)[HW][2],
+                     const f32x4 (&Ec)[HW][2]) {
+    f32x4 n1[2], n2[2], n3[2];
+    if (bw) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        n1[tt] = *reinterpret_cast<const f32x4*>(&sEta[eb][0][16 * tt + 4 * g]);
+        n3[tt] = *reinterpret_cast<const f32x4*>(&sEta[eb][1][16 * tt + 4 * g]);
+        n2[tt] = *reinterpret_cast<const f32x4*>(&sEta[eb][2][16 * tt + 4 * g]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < HW; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        Pn[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Un[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        En[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    const bf16* pk = sKV[buf] + fo;
+    bf16x8 rk_[3], rv_[3];
+    // step s = KS tt + ks reads row block tt, K slab ks: token half 0 first,
+    // as the backward below, so that the two tiles' halves overlap in
+    // registers instead of the whole of both
+#define LACT_GS_FRAG(S)                                                             \
+  {                                                                                 \
+    rk_[(S) % 3] = ld8(pk + 16 * ((S) / KS) * (D + 16) + 32 * ((S) % KS));          \
+    rv_[(S) % 3] = ld8(pk + TILE + 16 * ((S) / KS) * (D + 16) + 32 * ((S) % KS));   \
+  }
+    LACT_GS_FRAG(0);
+    LACT_GS_FRAG(1);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + 2 < NST) LACT_GS_FRAG(st + 2);
+      const int tt = st / KS, ks = st % KS;
+#pragma unroll
+      for (int h = 0; h < HW; ++h) {
+        mma(Pn[h][tt], rk_[st % 3], b1[h][ks]);
+        mma(Un[h][tt], rk_[st % 3], b3[h][ks]);
+        mma(En[h][tt], rv_[st % 3], b2[h][ks]);
+      }
+      if (bw) {
+#pragma unroll
+        for (int q = 0; q < EPS_ + (EPS_ == 0 ? 1 : 0); ++q) {
+          if (EPS_ == 0 && (st % EVERY) != EVERY - 1) continue;
+          // backward element e8 = (token half te, h, row ie)
+          const int e8 = EPS_ > 0 ? st * EPS_ + q : st / EVERY;
+          const int te = e8 / (4 * HW), h = (e8 >> 2) % HW, ie = e8 & 3;
+          const float p = Pc[h][te][ie], u = Uc[h][te][ie], e = Ec[h][te][ie];
+          const float sg = sigmoid_fast(p);
+          const float sl = p * sg;
+          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);
+          fh[h][4 * te + ie] = (bf16)((n2[te][ie] * sl) * u);
+          fu[h][4 * te + ie] = (bf16)((n3[te][ie] * sl) * e);
+          fg[h][4 * te + ie] = (bf16)((n1[te][ie] * dsl) * (e * u));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#undef LACT_GS_FRAG
+  };
+
   const int ntile = s0 < s1 ? (int)((s1 - s0 + NT - 1) / NT) : 0;
   if (ntile > 0) {
     LACT_GS_GLOAD(s0);
@@ -776,8 +836,7 @@ void k_grad_solo(GradArgs a) {
     LACT_GS_LSTORE(1);
   }
   __syncthreads();
-  f32x4 P[2], U[2], E[2];
-  LACT_GS_FWD(0, P, U, E);  // (unused when there is no tile)
+  forward(0, P, U, E, false, 0, P, U, E);  // (unused when there is no tile)
   for (int n = 0; n < ntile; ++n) {
     const int cb = n % NBUF, nb = (n + 1) % NBUF, lb = (n + 2) % NBUF;
     // tile n + 2 (rows past the split read as zeros; past the last tile the
@@ -785,56 +844,9 @@ void k_grad_solo(GradArgs a) {
     LACT_GS_GLOAD(s0 + (int64_t)(n + 2) * NT);
     __builtin_amdgcn_sched_barrier(0);
     // ---- region 1: forward contractions of tile n + 1 (past the last
-    // tile: stale buffer, results unused) with the SwiGLU backward + eta of
-    // tile n spread between them; fragment reads two steps ahead ----
-    f32x4 n1[2], n2[2], n3[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      n1[tt] = *reinterpret_cast<const f32x4*>(&sEta[cb][0][16 * tt + 4 * g]);
-      n3[tt] = *reinterpret_cast<const f32x4*>(&sEta[cb][1][16 * tt + 4 * g]);
-      n2[tt] = *reinterpret_cast<const f32x4*>(&sEta[cb][2][16 * tt + 4 * g]);
-    }
-    f32x4 Pn[2], Un[2], En[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      Pn[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Un[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      En[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    bf16x8 fh, fu, fg;
-    {
-      const bf16* pk = sKV[nb] + fo;
-      bf16x8 rk_[3], rv_[3];
-      // step s = 2 ks + tt reads row block tt, K slab ks
-#define LACT_GS_FRAG(S)                                                             \
-  {                                                                                 \
-    rk_[(S) % 3] = ld8(pk + 16 * ((S) & 1) * (D + 16) + 32 * ((S) >> 1));           \
-    rv_[(S) % 3] = ld8(pk + TILE + 16 * ((S) & 1) * (D + 16) + 32 * ((S) >> 1));    \
-  }
-      LACT_GS_FRAG(0);
-      LACT_GS_FRAG(1);
-#pragma unroll
-      for (int st = 0; st < 2 * KS; ++st) {
-        if (st + 2 < 2 * KS) LACT_GS_FRAG(st + 2);
-        const int tt = st & 1, ks = st >> 1;
-        mma(Pn[tt], rk_[st % 3], b1[ks]);
-        mma(Un[tt], rk_[st % 3], b3[ks]);
-        mma(En[tt], rv_[st % 3], b2[ks]);
-        if (st & 1) {
-          // one backward element per two steps: token 16 te + 4 g + ie
-          const int e8 = st >> 1, te = e8 >> 2, ie = e8 & 3;
-          const float p = P[te][ie], u = U[te][ie], e = E[te][ie];
-          const float sg = sigmoid_fast(p);
-          const float sl = p * sg;
-          const float dsl = __builtin_fmaf(sl, 1.f - sg, sg);
-          fh[4 * te + ie] = (bf16)((n2[te][ie] * sl) * u);
-          fu[4 * te + ie] = (bf16)((n3[te][ie] * sl) * e);
-          fg[4 * te + ie] = (bf16)((n1[te][ie] * dsl) * (e * u));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#undef LACT_GS_FRAG
-    }
+    // tile: stale buffer, results unused) with the backward of tile n ----
+    f32x4 Pn[HW][2], Un[HW][2], En[HW][2];
+    forward(nb, Pn, Un, En, true, cb, P, U, E);
     // ---- region 2: gradient contractions of tile n, transpose reads two
     // steps ahead, the staging stores of tile n + 2 between them ----
     {
@@ -852,9 +864,12 @@ void k_grad_solo(GradArgs a) {
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         if (it + 2 < IT) LACT_GS_TFRAG(it + 2);
-        mma(G1[it], tk_[it % 3], fg);
-        mma(G3[it], tk_[it % 3], fu);
-        mma(G2[it], tv_[it % 3], fh);
+#pragma unroll
+        for (int h = 0; h < HW; ++h) {
+          mma(G1[h][it], tk_[it % 3], fg[h]);
+          mma(G3[h][it], tk_[it % 3], fu[h]);
+          mma(G2[h][it], tv_[it % 3], fh[h]);
+        }
         if (it >= 4 && it < 4 + VPT) {
           const int x = it - 4, vi = tid + x * NTH;
           const int o = tpad<D>(vi / (D / 8), (vi % (D / 8)) * 8);
@@ -868,15 +883,16 @@ void k_grad_solo(GradArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      P[tt] = Pn[tt];
-      U[tt] = Un[tt];
-      E[tt] = En[tt];
-    }
+    for (int h = 0; h < HW; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        P[h][tt] = Pn[h][tt];
+        U[h][tt] = Un[h][tt];
+        E[h][tt] = En[h][tt];
+      }
   }
 #undef LACT_GS_GLOAD
 #undef LACT_GS_LSTORE
-#undef LACT_GS_FWD
   // momentum: the head's mean coefficient, once per head
   if (a.mom != nullptr && hb == 0 && split == 0)
     block_mean<NTH>(a.mom + (int64_t)head * a.mom_sbh, a.n_tok, a.beta + head);
@@ -885,11 +901,14 @@ void k_grad_solo(GradArgs a) {
   const int64_t mat = (int64_t)a.dh * D;
   float* out = a.partial + ((int64_t)split * a.bh + head) * 3 * mat + (int64_t)(j0 + c) * D + 4 * g;
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    st4(out + 16 * it, G1[it][0], G1[it][1], G1[it][2], G1[it][3]);
-    st4(out + mat + 16 * it, G3[it][0], G3[it][1], G3[it][2], G3[it][3]);
-    st4(out + 2 * mat + 16 * it, G2[it][0], G2[it][1], G2[it][2], G2[it][3]);
-  }
+  for (int h = 0; h < HW; ++h)
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float* o = out + 16 * h * D + 16 * it;
+      st4(o, G1[h][it][0], G1[h][it][1], G1[h][it][2], G1[h][it][3]);
+      st4(o + mat, G3[h][it][0], G3[h][it][1], G3[h][it][2], G3[h][it][3]);
+      st4(o + 2 * mat, G2[h][it][0], G2[h][it][1], G2[h][it][2], G2[h][it][3]);
+    }
 }
 
 // --------------------------------------------------------------- launch --
@@ -939,10 +958,11 @@ static hipError_t run_grad_bf16(const GradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int HW>
 static hipError_t run_grad_solo(const GradArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)(a.dh / 64) * a.nsplit * a.bh;
+  const int64_t blocks = (int64_t)(a.dh / (64 * HW)) * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_grad_solo<256>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_grad_solo<D, HW>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -960,7 +980,7 @@ hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
     switch (a.d) {
       case 64: return run_grad_bf16<64, 8, 1>(a, s);
       case 128: return run_grad_bf16<128, 8, 1>(a, s);
-      case 256: return run_grad_solo(a, s);
+      case 256: return run_grad_solo<256, 1>(a, s);
     }
   } else {
     switch (a.d) {
