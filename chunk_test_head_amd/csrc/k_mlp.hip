@@ -23,42 +23,40 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
   apply_block<T, D, NTW, WAVES>(a, xcd_logical_id(blockIdx.x, gridDim.x), lds);
 }
 
-// ------------------------------------------------------ apply, d = 256 --
-// Wave pairs: the two waves of a pair read the same 32 tokens and split the
-// features.  Wave (p, h) keeps the q
-// fragments and the o^T accumulators of features [128 h, 128 h + 128).  Per
-// block of 32 hidden units:
-//   1. half-K partials of the gate / up pre-activations (W1, W3 block rows
-//      over its 128 features),
-//   2. exchanged through LDS and summed in a fixed order (half 0 + half 1),
-//   3. h = silu(g) u (identical in both waves), o^T rows of its features
-//      += W2[features, block] h^T.
-// One workgroup = 8 waves = 4 pairs = 128 tokens; two waves per SIMD.  LDS:
-// two stages of the W blocks (unpadded, 16-byte chunks XOR-swizzled) and the
-// exchange slots, 160 KiB.
+// ------------------------------------------------ apply, d = 256, solo --
+// One wave per SIMD holding 32 tokens over all D features: q fragments
+// (D / 4 VGPRs) and the o^T accumulators (D / 2, in AGPRs) - no partial
+// exchange and no duplicated silu(g) u as when two waves per SIMD split the
+// features (measured 14-16 % slower).  4 waves = 128 tokens per workgroup.  The hidden dim is streamed in blocks of 32 through
+// three LDS stages (W1 / W3 block rows at swz<D>, the W2 block at swz32),
+// software-pipelined: iteration jb runs the gate / up contractions of block
+// jb + 1 with h = silu(g) u of block jb between them, then
+// o^T += W2[:, block jb] h^T with the staging stores of block jb + 2 between
+// those; fragment reads two steps ahead, the order held by scheduling fences.
 template <int D>
-__global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
-  constexpr int NTH = 512, HB = 32, DH2 = D / 2;
-  constexpr int KS = DH2 / 32;   // K slabs (own half)
-  constexpr int IT = DH2 / 16;   // own output feature tiles
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_apply_solo(ApplyArgs a) {
+  constexpr int NTH = 256, HB = 32;
+  constexpr int KS = D / 32;     // K slabs of the gate / up contractions
+  constexpr int IT = D / 16;     // output feature tiles
   constexpr int S1 = HB * D;     // one W1 / W3 block, [HB][D]
   constexpr int S2 = D * HB;     // W2 block, [D][HB] (kappa slot order)
   constexpr int STAGE = 2 * S1 + S2;
+  constexpr int NBUF = 3;
   constexpr int NV1 = S1 / 8 / NTH, NV2 = S2 / 8 / NTH;
+  constexpr int NST = 2 * KS;    // gate / up steps (K slab, hidden tile)
   static_assert(NV1 * 8 * NTH == S1 && NV2 * 8 * NTH == S2, "stage split");
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * STAGE];
-  __shared__ f32x4 sX[8][8][64];
+  static_assert(NST == 16 && 2 * NV1 + 2 * NV2 <= IT, "step plan");
+  __shared__ __attribute__((aligned(16))) bf16 lds[NBUF * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int pair = wave >> 1, half = wave & 1;
   const int tiles = (int)((a.n_tok + 127) / 128);
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int head = lid / tiles, tile = lid % tiles;
   if (head >= a.bh) return;
   const int dh = a.dh;
-  const int d0 = half * DH2;
-  const int64_t tok0 = (int64_t)tile * 128 + 32 * pair;
+  const int64_t tok0 = (int64_t)tile * 128 + 32 * wave;
 
   const bf16* q = reinterpret_cast<const bf16*>(a.q) + (int64_t)head * a.q_sbh;
   bf16* o = reinterpret_cast<bf16*>(a.o) + (int64_t)head * a.o_sbh;
@@ -67,7 +65,7 @@ __global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
   const bf16* w3 = sb + a.sh.off_w3;
   const bf16* w2 = sb + a.sh.off_w2;
 
-  // q^T fragments of the own feature half (B operand, K = features)
+  // q^T fragments (B operand, K = features): token 16 tt + c, features 32 ks + 8 g ..
   bf16x8 qf[2][KS];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -75,7 +73,7 @@ __global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (t < a.n_tok) {
-        qf[tt][ks] = ld8(q + t * a.q_st + d0 + 32 * ks + 8 * g);
+        qf[tt][ks] = ld8(q + t * a.q_st + 32 * ks + 8 * g);
       } else {
 #pragma unroll
         for (int m = 0; m < 8; ++m) qf[tt][ks][m] = (bf16)0.f;
@@ -88,8 +86,11 @@ __global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // W2 block rows (features) of HB = 32 hidden units in kappa slot order (swz32)
-#define LACT_AP_GLOAD(JB)                                                              \
+  const int NB = dh / HB;
+  bf16x8 r1[NV1], r3[NV1], r2[NV2];
+  // block JB of W1 / W3 rows and W2 columns (W2 rows of HB hidden units in
+  // kappa slot order, swz32)
+#define LACT_AS_GLOAD(JB)                                                              \
   {                                                                                    \
     _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
       const int vi = tid + x * NTH;                                                    \
@@ -101,102 +102,124 @@ __global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
       r2[x] = ld8(w2 + (int64_t)(vi >> 2) * dh + (JB) * HB + (vi & 3) * 8);          \
     }                                                                                  \
   }
-#define LACT_AP_LSTORE(BUF)                                                            \
+  // staging store number X of the block (X < 2 NV1 + 2 NV2)
+#define LACT_AS_LSTORE1(S_, X)                                                         \
   {                                                                                    \
-    bf16* s1_ = lds + (BUF) * STAGE;                                                   \
-    bf16* s3_ = s1_ + S1;                                                              \
-    bf16* s2_ = s3_ + S1;                                                              \
-    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
+    if ((X) < 2 * NV1) {                                                               \
+      const int x_ = (X) >> 1, vi = tid + x_ * NTH;                                    \
       const int o_ = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                         \
-      *reinterpret_cast<bf16x8*>(s1_ + o_) = r1[x];                                    \
-      *reinterpret_cast<bf16x8*>(s3_ + o_) = r3[x];                                    \
-    }                                                                                  \
-    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      const int row = vi >> 2, ru0 = 2 * (vi & 3), ru1 = ru0 + 1;                      \
-      *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru0 & 3) + (ru0 >> 2))) = __builtin_shufflevector(r2[x], r2[x], 0, 1, 2, 3); \
-      *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru1 & 3) + (ru1 >> 2))) = __builtin_shufflevector(r2[x], r2[x], 4, 5, 6, 7); \
+      if (((X) & 1) == 0) *reinterpret_cast<bf16x8*>((S_) + o_) = r1[x_];              \
+      else *reinterpret_cast<bf16x8*>((S_) + S1 + o_) = r3[x_];                        \
+    } else {                                                                           \
+      const int y_ = (X) - 2 * NV1, x_ = y_ >> 1, vi = tid + x_ * NTH;                 \
+      const int row = vi >> 2, ru = 2 * (vi & 3) + (y_ & 1);                           \
+      bf16* s2_ = (S_) + 2 * S1;                                                       \
+      if ((y_ & 1) == 0)                                                               \
+        *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru & 3) + (ru >> 2))) =       \
+            __builtin_shufflevector(r2[x_], r2[x_], 0, 1, 2, 3);                       \
+      else                                                                             \
+        *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru & 3) + (ru >> 2))) =       \
+            __builtin_shufflevector(r2[x_], r2[x_], 4, 5, 6, 7);                       \
     }                                                                                  \
   }
 
-  const int NB = dh / HB;
-  {
-    bf16x8 r1[NV1], r3[NV1], r2[NV2];
-    LACT_AP_GLOAD(0);
-    LACT_AP_LSTORE(0);
+  // per-lane offsets (laundered: the stage is a runtime choice, every read
+  // should be this base + an immediate): gate / up A fragments (row c,
+  // features 8 g ..) and W2 A fragments (row c, slots 2 g, 2 g + 1)
+  const int fo = opaque(c * D);
+  const int key = opaque(swz_key<D>(c));
+  const int wo = opaque(swz32(c, 2 * g));
+  f32x4 P[2][2], U[2][2];  // [hidden tile jt][token half tt]
+  bf16x8 hf[2];
+  // gate / up contractions of the block in stage BUF into Pn, Un; with BW,
+  // h = silu(g) u of the previous block (Pc, Uc) between the steps
+  auto forward = [&](int buf, f32x4 (&Pn)[2][2], f32x4 (&Un)[2][2], bool bw,
+                     const f32x4 (&Pc)[2][2], const f32x4 (&Uc)[2][2]) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        Pn[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Un[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    const bf16* s1 = lds + buf * STAGE + fo;
+    bf16x8 f1[3], f3[3];
+    // step s = 2 ks + jt: rows 16 jt + c, features 32 ks + 8 g .. (chunk
+    // 4 ks + g XOR the row key)
+#define LACT_AS_FRAG(S)                                                                \
+  {                                                                                    \
+    const int ch_ = ((4 * ((S) >> 1) + g) ^ key) << 3;                                 \
+    f1[(S) % 3] = ld8(s1 + 16 * ((S) & 1) * D + ch_);                                  \
+    f3[(S) % 3] = ld8(s1 + S1 + 16 * ((S) & 1) * D + ch_);                             \
   }
+    LACT_AS_FRAG(0);
+    LACT_AS_FRAG(1);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + 2 < NST) LACT_AS_FRAG(st + 2);
+      const int jt = st & 1, ks = st >> 1;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        mma(Pn[jt][tt], f1[st % 3], qf[tt][ks]);
+        mma(Un[jt][tt], f3[st % 3], qf[tt][ks]);
+      }
+      if (bw) {
+        // element (token half te, hidden tile je, row ie) of h: one per step
+        const int te = st >> 3, je = (st >> 2) & 1, ie = st & 3;
+        const float p = Pc[je][te][ie];
+        hf[te][4 * je + ie] = (bf16)(p * sigmoid_fast(p) * Uc[je][te][ie]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#undef LACT_AS_FRAG
+  };
+
+  LACT_AS_GLOAD(0);
+#pragma unroll
+  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds, x);
+  LACT_AS_GLOAD(min(1, NB - 1));
+#pragma unroll
+  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds + STAGE, x);
   __syncthreads();
+  forward(0, P, U, false, P, U);
   for (int jb = 0; jb < NB; ++jb) {
-    const int buf = jb & 1;
-    // the next block (the last one again at the end: branch-free, so the
-    // staging registers stay registers; the spare copy lands in the idle
-    // buffer)
-    bf16x8 r1[NV1], r3[NV1], r2[NV2];
-    LACT_AP_GLOAD(min(jb + 1, NB - 1));
-    const bf16* s1 = lds + buf * STAGE;
-    const bf16* s3 = s1 + S1;
-    const bf16* s2 = s3 + S1;
-    // 1. half-K partials, transposed: P^T[hidden][token]
-    f32x4 P[2][2], U[2][2];
+    const int cb = jb % NBUF, nb = (jb + 1) % NBUF, lb = (jb + 2) % NBUF;
+    // block jb + 2 (the last one again at the end: its copy lands in a free
+    // stage)
+    LACT_AS_GLOAD(min(jb + 2, NB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- region 1: gate / up of block jb + 1 (past the last block: stale
+    // stage, results unused) with h of block jb ----
+    f32x4 Pn[2][2], Un[2][2];
+    forward(nb, Pn, Un, true, P, U);
+    // ---- region 2: o^T += W2[:, block jb] h^T, W2 reads two steps ahead,
+    // the staging stores of block jb + 2 between them ----
+    {
+      const bf16* s2 = lds + cb * STAGE + 2 * S1 + wo;
+      bf16* sl = lds + lb * STAGE;
+      bf16x8 f2[3];
+      f2[0] = ld8(s2);
+      f2[1] = ld8(s2 + 16 * HB);
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+      for (int it = 0; it < IT; ++it) {
+        if (it + 2 < IT) f2[(it + 2) % 3] = ld8(s2 + 16 * HB * (it + 2));
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        P[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        U[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 2; ++tt) mma(acc[it][tt], f2[it % 3], hf[tt]);
+        if (it < 2 * NV1 + 2 * NV2) LACT_AS_LSTORE1(sl, it);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const bf16x8 a1 = ld8(s1 + swz<D>(16 * jt + c, d0 + 32 * ks + 8 * g));
-        const bf16x8 a3 = ld8(s3 + swz<D>(16 * jt + c, d0 + 32 * ks + 8 * g));
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          mma(P[jt][tt], a1, qf[tt][ks]);
-          mma(U[jt][tt], a3, qf[tt][ks]);
-        }
-      }
-    // 2. exchange, fixed-order sum
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sX[wave][2 * jt + tt][lane] = P[jt][tt];
-        sX[wave][4 + 2 * jt + tt][lane] = U[jt][tt];
-      }
+    }
     __syncthreads();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 op = sX[wave ^ 1][2 * jt + tt][lane], ou = sX[wave ^ 1][4 + 2 * jt + tt][lane];
-        P[jt][tt] = half == 0 ? P[jt][tt] + op : op + P[jt][tt];
-        U[jt][tt] = half == 0 ? U[jt][tt] + ou : ou + U[jt][tt];
+        P[jt][tt] = Pn[jt][tt];
+        U[jt][tt] = Un[jt][tt];
       }
-    // 3. h = silu(P) U as the B operand (K = the 32 hidden units, kappa order)
-    bf16x8 hf[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = P[0][tt][i], p1 = P[1][tt][i];
-        hf[tt][i] = (bf16)(p0 * sigmoid_fast(p0) * U[0][tt][i]);
-        hf[tt][4 + i] = (bf16)(p1 * sigmoid_fast(p1) * U[1][tt][i]);
-      }
-    //    o^T[own features][token] += W2[own features, block] h^T
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const bf16x8 a2 = ld8(s2 + swz32(d0 + 16 * it + c, 2 * g));
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) mma(acc[it][tt], a2, hf[tt]);
-    }
-    LACT_AP_LSTORE(buf ^ 1);
-    __syncthreads();  // stage and exchange slots free
   }
-#undef LACT_AP_GLOAD
-#undef LACT_AP_LSTORE
+#undef LACT_AS_GLOAD
+#undef LACT_AS_LSTORE1
 
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -204,7 +227,7 @@ __global__ __launch_bounds__(512) void k_apply_pair(ApplyArgs a) {
     if (t < a.n_tok) {
 #pragma unroll
       for (int it = 0; it < IT; ++it)
-        st4(o + t * a.o_st + d0 + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
+        st4(o + t * a.o_st + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
             acc[it][tt][3]);
     }
   }
@@ -912,10 +935,10 @@ void k_grad_solo(GradArgs a) {
 }
 
 // --------------------------------------------------------------- launch --
-static hipError_t run_apply_pair(const ApplyArgs& a, hipStream_t s) {
+static hipError_t run_apply_solo(const ApplyArgs& a, hipStream_t s) {
   const int64_t blocks = (a.n_tok + 127) / 128 * a.bh;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_apply_pair<256>), dim3((unsigned)blocks), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((k_apply_solo<256>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -933,7 +956,7 @@ hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
     switch (a.d) {
       case 64: return run_apply<bf16, 64, 64, 4>(a, s);
       case 128: return run_apply<bf16, 128, 32, 8>(a, s);
-      case 256: return run_apply_pair(a, s);
+      case 256: return run_apply_solo(a, s);
     }
   } else {
     switch (a.d) {
