@@ -275,4 +275,221 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
   }
 }
 
+// ------------------------------------------------ apply, d = 256, solo --
+// One wave per SIMD holding 32 tokens over all D features: q fragments
+// (D / 4 VGPRs) and the o^T accumulators (D / 2, in AGPRs) - no partial
+// exchange and no duplicated silu(g) u as when two waves per SIMD split the
+// features (measured 14-16 % slower).  4 waves = 128 tokens per workgroup.  The hidden dim is streamed in blocks of 32 through
+// three LDS stages (W1 / W3 block rows at swz<D>, the W2 block at swz32),
+// software-pipelined: iteration jb runs the gate / up contractions of block
+// jb + 1 with h = silu(g) u of block jb between them, then
+// o^T += W2[:, block jb] h^T with the staging stores of block jb + 2 between
+// those; fragment reads two steps ahead, the order held by scheduling fences.
+template <int D>
+struct ApplySoloLds {
+  static constexpr int HB = 32;
+  static constexpr int STAGE = 2 * HB * D + D * HB;
+  static constexpr int ELEMS = 3 * STAGE;
+};
+
+// Body of one workgroup (256 threads, one wave per SIMD): logical block lid
+// (head-major tiles of 128 tokens), LDS of ApplySoloLds<D>::ELEMS elements.
+template <int D>
+__device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf16* lds) {
+  constexpr int NTH = 256, HB = 32;
+  constexpr int KS = D / 32;     // K slabs of the gate / up contractions
+  constexpr int IT = D / 16;     // output feature tiles
+  constexpr int S1 = HB * D;     // one W1 / W3 block, [HB][D]
+  constexpr int S2 = D * HB;     // W2 block, [D][HB] (kappa slot order)
+  constexpr int STAGE = 2 * S1 + S2;
+  constexpr int NBUF = 3;
+  constexpr int NV1 = S1 / 8 / NTH, NV2 = S2 / 8 / NTH;
+  constexpr int NST = 2 * KS;    // gate / up steps (K slab, hidden tile)
+  static_assert(NV1 * 8 * NTH == S1 && NV2 * 8 * NTH == S2, "stage split");
+  static_assert(NST == 16 && 2 * NV1 + 2 * NV2 <= IT, "step plan");
+  static_assert(ApplySoloLds<D>::STAGE == STAGE, "layout");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int tiles = (int)((a.n_tok + 127) / 128);
+  const int head = lid / tiles, tile = lid % tiles;
+  if (head >= a.bh) return;
+  const int dh = a.dh;
+  const int64_t tok0 = (int64_t)tile * 128 + 32 * wave;
+
+  const bf16* q = reinterpret_cast<const bf16*>(a.q) + (int64_t)head * a.q_sbh;
+  bf16* o = reinterpret_cast<bf16*>(a.o) + (int64_t)head * a.o_sbh;
+  const bf16* sb = reinterpret_cast<const bf16*>(a.sh.base) + (int64_t)head * a.sh.per_head;
+  const bf16* w1 = sb + a.sh.off_w1;
+  const bf16* w3 = sb + a.sh.off_w3;
+  const bf16* w2 = sb + a.sh.off_w2;
+
+  // q^T fragments (B operand, K = features): token 16 tt + c, features 32 ks + 8 g ..
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (t < a.n_tok) {
+        qf[tt][ks] = ld8(q + t * a.q_st + 32 * ks + 8 * g);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) qf[tt][ks][m] = (bf16)0.f;
+      }
+    }
+  }
+  f32x4 acc[IT][2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int NB = dh / HB;
+  bf16x8 r1[NV1], r3[NV1], r2[NV2];
+  // block JB of W1 / W3 rows and W2 columns (W2 rows of HB hidden units in
+  // kappa slot order, swz32)
+#define LACT_AS_GLOAD(JB)                                                              \
+  {                                                                                    \
+    _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
+      const int vi = tid + x * NTH;                                                    \
+      r1[x] = ld8(w1 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
+      r3[x] = ld8(w3 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
+    }                                                                                  \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
+      const int vi = tid + x * NTH;                                                    \
+      r2[x] = ld8(w2 + (int64_t)(vi >> 2) * dh + (JB) * HB + (vi & 3) * 8);          \
+    }                                                                                  \
+  }
+  // staging store number X of the block (X < 2 NV1 + 2 NV2)
+#define LACT_AS_LSTORE1(S_, X)                                                         \
+  {                                                                                    \
+    if ((X) < 2 * NV1) {                                                               \
+      const int x_ = (X) >> 1, vi = tid + x_ * NTH;                                    \
+      const int o_ = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                         \
+      if (((X) & 1) == 0) *reinterpret_cast<bf16x8*>((S_) + o_) = r1[x_];              \
+      else *reinterpret_cast<bf16x8*>((S_) + S1 + o_) = r3[x_];                        \
+    } else {                                                                           \
+      const int y_ = (X) - 2 * NV1, x_ = y_ >> 1, vi = tid + x_ * NTH;                 \
+      const int row = vi >> 2, ru = 2 * (vi & 3) + (y_ & 1);                           \
+      bf16* s2_ = (S_) + 2 * S1;                                                       \
+      if ((y_ & 1) == 0)                                                               \
+        *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru & 3) + (ru >> 2))) =       \
+            __builtin_shufflevector(r2[x_], r2[x_], 0, 1, 2, 3);                       \
+      else                                                                             \
+        *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru & 3) + (ru >> 2))) =       \
+            __builtin_shufflevector(r2[x_], r2[x_], 4, 5, 6, 7);                       \
+    }                                                                                  \
+  }
+
+  // per-lane offsets (laundered: the stage is a runtime choice, every read
+  // should be this base + an immediate): gate / up A fragments (row c,
+  // features 8 g ..) and W2 A fragments (row c, slots 2 g, 2 g + 1)
+  const int fo = opaque(c * D);
+  const int key = opaque(swz_key<D>(c));
+  const int wo = opaque(swz32(c, 2 * g));
+  f32x4 P[2][2], U[2][2];  // [hidden tile jt][token half tt]
+  bf16x8 hf[2];
+  // gate / up contractions of the block in stage BUF into Pn, Un; with BW,
+  // h = silu(g) u of the previous block (Pc, Uc) between the steps
+  auto forward = [&](int buf, f32x4 (&Pn)[2][2], f32x4 (&Un)[2][2], bool bw,
+                     const f32x4 (&Pc)[2][2], const f32x4 (&Uc)[2][2]) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        Pn[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Un[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    const bf16* s1 = lds + buf * STAGE + fo;
+    bf16x8 f1[3], f3[3];
+    // step s = 2 ks + jt: rows 16 jt + c, features 32 ks + 8 g .. (chunk
+    // 4 ks + g XOR the row key)
+#define LACT_AS_FRAG(S)                                                                \
+  {                                                                                    \
+    const int ch_ = ((4 * ((S) >> 1) + g) ^ key) << 3;                                 \
+    f1[(S) % 3] = ld8(s1 + 16 * ((S) & 1) * D + ch_);                                  \
+    f3[(S) % 3] = ld8(s1 + S1 + 16 * ((S) & 1) * D + ch_);                             \
+  }
+    LACT_AS_FRAG(0);
+    LACT_AS_FRAG(1);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + 2 < NST) LACT_AS_FRAG(st + 2);
+      const int jt = st & 1, ks = st >> 1;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        mma(Pn[jt][tt], f1[st % 3], qf[tt][ks]);
+        mma(Un[jt][tt], f3[st % 3], qf[tt][ks]);
+      }
+      if (bw) {
+        // element (token half te, hidden tile je, row ie) of h: one per step
+        const int te = st >> 3, je = (st >> 2) & 1, ie = st & 3;
+        const float p = Pc[je][te][ie];
+        hf[te][4 * je + ie] = (bf16)(p * sigmoid_fast(p) * Uc[je][te][ie]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#undef LACT_AS_FRAG
+  };
+
+  LACT_AS_GLOAD(0);
+#pragma unroll
+  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds, x);
+  LACT_AS_GLOAD(min(1, NB - 1));
+#pragma unroll
+  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds + STAGE, x);
+  __syncthreads();
+  forward(0, P, U, false, P, U);
+  for (int jb = 0; jb < NB; ++jb) {
+    const int cb = jb % NBUF, nb = (jb + 1) % NBUF, lb = (jb + 2) % NBUF;
+    // block jb + 2 (the last one again at the end: its copy lands in a free
+    // stage)
+    LACT_AS_GLOAD(min(jb + 2, NB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- region 1: gate / up of block jb + 1 (past the last block: stale
+    // stage, results unused) with h of block jb ----
+    f32x4 Pn[2][2], Un[2][2];
+    forward(nb, Pn, Un, true, P, U);
+    // ---- region 2: o^T += W2[:, block jb] h^T, W2 reads two steps ahead,
+    // the staging stores of block jb + 2 between them ----
+    {
+      const bf16* s2 = lds + cb * STAGE + 2 * S1 + wo;
+      bf16* sl = lds + lb * STAGE;
+      bf16x8 f2[3];
+      f2[0] = ld8(s2);
+      f2[1] = ld8(s2 + 16 * HB);
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        if (it + 2 < IT) f2[(it + 2) % 3] = ld8(s2 + 16 * HB * (it + 2));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) mma(acc[it][tt], f2[it % 3], hf[tt]);
+        if (it < 2 * NV1 + 2 * NV2) LACT_AS_LSTORE1(sl, it);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        P[jt][tt] = Pn[jt][tt];
+        U[jt][tt] = Un[jt][tt];
+      }
+  }
+#undef LACT_AS_GLOAD
+#undef LACT_AS_LSTORE1
+
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t t = tok0 + 16 * tt + c;
+    if (t < a.n_tok) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+        st4(o + t * a.o_st + 16 * it + 4 * g, acc[it][tt][0], acc[it][tt][1], acc[it][tt][2],
+            acc[it][tt][3]);
+    }
+  }
+}
+
 }  // namespace lact
