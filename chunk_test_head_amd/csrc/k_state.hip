@@ -182,7 +182,7 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
     }
   }
   const bool write_w = U != nullptr || a.renorm;
-  const float* N0 = (mat == 0 ? a.n1 : a.n3) + (int64_t)head * dh + j0;
+  float* N0 = (mat == 0 ? a.n1 : a.n3) + (int64_t)head * dh + j0;
   T* S = reinterpret_cast<T*>(a.sh.base) + (int64_t)head * a.sh.per_head +
          (mat == 0 ? a.sh.off_w1 : a.sh.off_w3) + (int64_t)j0 * d;
 #pragma unroll
@@ -190,6 +190,7 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
     if (k < nk) {
       const int r = r0 + rstep * k;
       const float f = a.renorm ? N0[r] / (sqrtf(ss[k]) + a.eps) : 1.f;
+      if (a.init && c4 == 0) N0[r] = sqrtf(ss[k]);  // sequence-start norm
       const f32x4 v = w[k] * f;
       if (write_w) *reinterpret_cast<f32x4*>(W + (int64_t)r * d + c4) = v;
       st4(S + (int64_t)r * d + c4, v[0], v[1], v[2], v[3]);
@@ -230,6 +231,7 @@ __device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     float f = 1.f;
     if (a.renorm) f = a.n2[(int64_t)head * d + i0 + row] / (sqrtf(ss) + a.eps);
+    if (a.init && lane == 0) a.n2[(int64_t)head * d + i0 + row] = sqrtf(ss);  // sequence-start norm
     T* S = sb + a.sh.off_w2 + (int64_t)(i0 + row) * dh;
 #pragma unroll
     for (int k = 0; k <= KMAX; ++k) {
@@ -252,11 +254,25 @@ __device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
   }
 }
 
+// Sequence start: workgroup blk of nblk zeroes its share of the momentum
+// buffers (as one concatenation of m1, m3, m2; NULL buffers skipped).
+__device__ __forceinline__ void zero_share(const StepArgs& a, int blk, int nblk) {
+  const int64_t per = (int64_t)a.bh * a.d * a.dh / 4;  // float4 per buffer
+  const int64_t tot = 3 * per, q = (tot + nblk - 1) / nblk;
+  const int64_t end = (int64_t)(blk + 1) * q < tot ? (int64_t)(blk + 1) * q : tot;
+  for (int64_t i = (int64_t)blk * q + threadIdx.x; i < end; i += 256) {
+    const int mb = (int)(i / per);
+    float* m = mb == 0 ? a.mz1 : (mb == 1 ? a.mz3 : a.mz2);
+    if (m != nullptr) reinterpret_cast<f32x4*>(m)[i - mb * per] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // One launch for all three matrices: workgroups [0, n13) take W1 / W3 row
 // blocks, the rest W2 row blocks.
 template <class T, int KMAX>
 __global__ __launch_bounds__(256) void k_step(StepArgs a, int n13) {
   extern __shared__ __attribute__((aligned(16))) float step_lds[];
+  if (a.init) zero_share(a, blockIdx.x, gridDim.x);
   if ((int)blockIdx.x < n13) step_w13<T>(a, blockIdx.x, step_lds);
   else step_w2<T, KMAX>(a, blockIdx.x - n13, reinterpret_cast<T*>(step_lds));
 }
@@ -281,35 +297,6 @@ static hipError_t run_step(const StepArgs& a, hipStream_t s) {
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s) {
   if (dtype == 1) return a.dh <= 1024 ? run_step<bf16, 3>(a, s) : run_step<bf16, 15>(a, s);
   return a.dh <= 1024 ? run_step<float, 3>(a, s) : run_step<float, 15>(a, s);
-}
-
-// -------------------------------------------------------- row norms -----
-// n0 <- L2 norm of every row, one wave per row (rows of W1, W3: d; W2: dh).
-__global__ __launch_bounds__(256) void k_row_norms(StepArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t per_head = 2 * (int64_t)a.dh + a.d;
-  if (row >= per_head * a.bh) return;
-  const int head = (int)(row / per_head);
-  int64_t r = row % per_head;
-  const int64_t msz = (int64_t)a.d * a.dh;
-  const float* W;
-  float* N;
-  int len;
-  if (r < a.dh) { W = a.w1 + head * msz + r * a.d; N = a.n1 + (int64_t)head * a.dh + r; len = a.d; }
-  else if (r < 2 * a.dh) { r -= a.dh; W = a.w3 + head * msz + r * a.d; N = a.n3 + (int64_t)head * a.dh + r; len = a.d; }
-  else { r -= 2 * a.dh; W = a.w2 + head * msz + r * a.dh; N = a.n2 + (int64_t)head * a.d + r; len = a.dh; }
-  float s = 0.f;
-  for (int x = lane; x < len; x += 64) s += W[x] * W[x];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) *N = sqrtf(s);
-}
-
-hipError_t launch_row_norms(const StepArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.bh * (2 * (int64_t)a.dh + a.d);
-  hipLaunchKernelGGL(k_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  return hipGetLastError();
 }
 
 // ------------------------------------------------------------- fill -----

@@ -350,6 +350,7 @@ static lact_status do_step(const lact_shape* sh, const lact_state* st, const flo
                            const float* u3, const float* u2, int renorm, float eps,
                            void* shadow_out, hipStream_t s) {
   StepArgs a;
+  memset(&a, 0, sizeof(a));
   a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
   a.u1 = u1; a.u3 = u3; a.u2 = u2;
   a.n1 = st->n1; a.n3 = st->n3; a.n2 = st->n2;
@@ -489,12 +490,7 @@ lact_status lact_init_state(const lact_shape* sh, const lact_state* st, void* st
   for (float* m : {st->m1, st->m3, st->m2})
     if (m != nullptr && !aligned16(m)) return LACT_ERR_ALIGNMENT;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t mall = (int64_t)sh->bh * sh->d * sh->dh;
-  for (float* m : {st->m1, st->m3, st->m2}) {
-    if (m == nullptr) continue;
-    hipError_t e = launch_fill(m, mall, 0.f, s);
-    if (e != hipSuccess) return hip_fail(e);
-  }
+  // one launch: row norms, operand copies, momentum buffers zeroed
   StepArgs a;
   memset(&a, 0, sizeof(a));
   a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
@@ -502,9 +498,9 @@ lact_status lact_init_state(const lact_shape* sh, const lact_state* st, void* st
   a.sh = make_shadow(st->shadow, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
   a.renorm = 0;
-  hipError_t e = launch_row_norms(a, s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = launch_step(sh->dtype, a, s);  // operand copies only
+  a.init = 1;
+  a.mz1 = st->m1; a.mz3 = st->m3; a.mz2 = st->m2;
+  const hipError_t e = launch_step(sh->dtype, a, s);
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 

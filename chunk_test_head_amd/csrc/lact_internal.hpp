@@ -94,6 +94,10 @@ struct StepArgs {
   int bh, d, dh;
   int renorm;  // 0: factor 1 (copies only), 1: n0 / (||row|| + eps)
   float eps;
+  // sequence start (init = 1, with renorm = 0 and no U): the row norms are
+  // written to n1, n3, n2 and the momentum buffers (non-NULL ones) zeroed
+  int init;
+  float* mz1; float* mz3; float* mz2;
 };
 
 hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
@@ -137,7 +141,6 @@ hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t 
 hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,
                       hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
-hipError_t launch_row_norms(const StepArgs& a, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 }  // namespace lact
