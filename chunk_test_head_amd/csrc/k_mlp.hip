@@ -289,6 +289,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       G3[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
       G2[h][it] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  // momentum folded in: split 0 starts from beta M_old (M wide: element
+  // (feature i, hidden j) at i dh + j), so that the split sum is G + beta M
+  // (loads in flight while the first tiles are staged and contracted)
+  if (a.mo1 != nullptr && split == 0) {
+    const float beta = block_mean_all<NTH>(a.mom + (int64_t)head * a.mom_sbh, a.n_tok);
+    if (active) {
+      const int64_t hm = (int64_t)head * a.dh * D;
+#pragma unroll
+      for (int h = 0; h < HT; ++h)
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t o = hm + (int64_t)(16 * it + 4 * g + e) * a.dh + j0 + 16 * h + c;
+            G1[h][it][e] = beta * a.mo1[o];
+            G3[h][it][e] = beta * a.mo3[o];
+            G2[h][it][e] = beta * a.mo2[o];
+          }
+    }
+  }
 
   // staging: thread tid moves 16-byte vectors vi = tid + x NTH of the k and v
   // tiles (row vi / (D/8), chunk vi % (D/8)) and, for tid < 3 NT, one eta
@@ -796,6 +816,8 @@ static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
+  // folding the old momentum in is a k_grad_bf16 feature
+  if (a.mo1 != nullptr && !(dtype == 1 && a.d <= 128 && a.mom != nullptr)) return hipErrorInvalidValue;
   if (dtype == 1) {
     switch (a.d) {
       case 64: return run_grad_bf16<64, 8, 1>(a, s);

@@ -571,10 +571,11 @@ void k_ns_r128(NsIn g, float* u, float eps) {
 // 16 mt + 4 g .. + 3) from the split partials, which hold G^T ([dh][128]):
 // every wave sums the partial rows of its own columns, 32 per pass, 8 lanes
 // per row (128-byte segments), in split order, stores the sums in its own
-// 16 KiB of LDS and reads them back transposed; then the momentum
-// G <- G + beta M (M loaded in the accumulator layout, 16 bytes per lane) and
-// M <- G.  The LDS key is the one of the W1 step below (every store and read
-// on 64 distinct banks); no barrier: each wave touches only its own block.
+// 16 KiB of LDS and reads them back transposed.  With momentum the gradient
+// launch has already put beta M_old into split 0, so the sum is the new M:
+// M <- G (stored from the accumulator layout, 16 bytes per lane).  The LDS
+// key is the one of the W1 step below (every store and read on 64 distinct
+// banks); no barrier: each wave touches only its own block.
 template <int COLS, int NMT, int NRT>
 __device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const NsGrad& gr,
                                              float* stg) {
@@ -586,28 +587,13 @@ __device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const
   const float* P0 = gr.partial + ((int64_t)head * 3 + mat) * msz;
   const int64_t pstr = (int64_t)gr.bh * 3 * msz;  // between splits
   float* M = gr.m[mat] != nullptr ? gr.m[mat] + head * msz : nullptr;
-  const float beta = M != nullptr ? gr.beta[head] : 0.f;
   float* ws = stg + w * 32 * 128;
   auto off = [](int t, int i) {
     return t * 128 + (((i >> 2) ^ (4 * (((t >> 2) ^ t) & 3))) << 2) + (i & 3);
   };
-  // Load schedule (registers): pass 0 issues its partial rows and its old
-  // momentum together; later passes hold the earlier passes' results, so their
-  // momentum loads follow the partial sums.  Three round trips for COLS 512.
-  auto load_mo = [&](int p, f32x4 (&mo)[2][NRT]) {
-    const int c = opaque(lane & 15), gq = opaque(lane >> 4);
-    const float* mrow = M + (int64_t)c * COLS + col0 + 32 * p + 4 * gq;
-#pragma unroll
-    for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-      for (int nt = 0; nt < NRT; ++nt)
-        mo[mh][nt] = *reinterpret_cast<const f32x4*>(mrow + (int64_t)16 * nt * COLS + 16 * mh);
-  };
 #pragma unroll
   for (int p = 0; p < NMT / 2; ++p) {
     asm volatile("" ::: "memory");  // no load of this pass above the last one (registers)
-    f32x4 mo[2][NRT];
-    if (p == 0 && M != nullptr) load_mo(0, mo);
     const int c = opaque(lane & 15), gq = opaque(lane >> 4);
     const int lr = opaque(lane >> 3), lk = lane & 7;
     // partial rows col0 + 32 p + 8 v + lr, features 4 (lk + 8 kk) .. + 3
@@ -642,22 +628,12 @@ __device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const
 #pragma unroll
         for (int e = 0; e < 4; ++e) yv[2 * p + mh][nt][e] = ws[off(16 * mh + 4 * gq + e, 16 * nt + c)];
     if (M != nullptr) {
-      // M <- G + beta M (later passes: one 16-column tile at a time)
       float* mrow = M + (int64_t)c * COLS + col0 + 32 * p + 4 * gq;
 #pragma unroll
-      for (int mh = 0; mh < 2; ++mh) {
-        if (p > 0) {
-          asm volatile("" ::: "memory");
+      for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-          for (int nt = 0; nt < NRT; ++nt)
-            mo[mh][nt] = *reinterpret_cast<const f32x4*>(mrow + (int64_t)16 * nt * COLS + 16 * mh);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NRT; ++nt) {
-          yv[2 * p + mh][nt] = yv[2 * p + mh][nt] + beta * mo[mh][nt];
+        for (int nt = 0; nt < NRT; ++nt)
           *reinterpret_cast<f32x4*>(mrow + (int64_t)16 * nt * COLS + 16 * mh) = yv[2 * p + mh][nt];
-        }
-      }
     }
   }
 }

@@ -331,6 +331,11 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
   a.split_len = sl > 0 ? sl : 32;
   a.partial = w.partial;
   a.mom = mom; a.mom_sbh = esbh; a.beta = w.beta;
+  // without the reduction launch, its consumer finishes the sum: the
+  // momentum is folded into split 0 here
+  a.mo1 = reduce ? nullptr : m1;
+  a.mo3 = reduce ? nullptr : m3;
+  a.mo2 = reduce ? nullptr : m2;
   hipError_t e;
   {
     ProfScope p(LACT_PROF_GRAD, s);
@@ -417,8 +422,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                       make_shadow(shadow_out, sh->d, sh->dh), sh->bh, op->renorm ? 1 : 0,
                       op->renorm_eps};
       const NsGrad gr{w.partial, nsplit, sh->bh,
-                      {mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr},
-                      w.beta};
+                      {mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr}};
       e = launch_ns_step_apply(3 * sh->bh, sh->d, sh->dh, gr, op->ns_eps, ns, aa, s);
       return e == hipSuccess ? LACT_OK : hip_fail(e);
     }

@@ -36,6 +36,10 @@ struct GradArgs {
   // momentum (else mom = NULL): one workgroup per head writes beta[head], the
   // mean of the head's per-token coefficients mom[head * mom_sbh + t], t < n_tok
   const float* mom; int64_t mom_sbh; float* beta;
+  // old momentum M1, M3, M2 (wide [bh][d][dh]) to fold in, or NULL: the
+  // workgroups of split 0 start from beta M instead of zero (bf16 d <= 128),
+  // so that the split sum is G + beta M
+  const float* mo1; const float* mo3; const float* mo2;
 };
 
 // Sum of split partials, transpose to the wide orientation, momentum.
@@ -121,13 +125,12 @@ struct NsStep {
 };
 // Input of a Newton-Schulz launch that also finishes the gradient: matrix
 // m = mat * bh + head starts from G = the sum over splits s (in split order)
-// of partial[s][head][mat]^T; with momentum (m[mat] != NULL)
-// G <- G + beta[head] M and M <- G.
+// of partial[s][head][mat]^T (with momentum, split 0 already holds beta M_old:
+// GradArgs::mo*), and M <- G when m[mat] != NULL.
 struct NsGrad {
   const float* partial;  // [nsplit][bh][3][dh][d]
   int nsplit, bh;
   float* m[3];           // wide [bh][d][dh] each, or NULL
-  const float* beta;     // [bh]
 };
 // Gradient reduction + Newton-Schulz + step (bf16, 128 rows, 256 or 512
 // columns), with the tiles of a d = 128 bf16 read (a.n_tok > 0) in the same

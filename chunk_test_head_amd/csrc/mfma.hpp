@@ -119,11 +119,11 @@ __device__ __forceinline__ int opaque(int x) {
 }
 
 // Mean of x[0 .. n) by the whole workgroup in a fixed order (thread-strided
-// partial sums, wave butterflies, waves in index order); every thread must
-// call it.  Thread 0 writes the result to *out.
+// partial sums, wave butterflies, waves in index order), returned to every
+// thread; every thread must call it.
 template <int NTH>
-__device__ __forceinline__ void block_mean(const float* x, int64_t n, float* out) {
-  __shared__ float red_bm[NTH / 64];
+__device__ __forceinline__ float block_mean_all(const float* x, int64_t n) {
+  __shared__ float red_bm[NTH / 64 + 1];
   const int tid = threadIdx.x;
   float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
   int64_t t = tid;
@@ -144,8 +144,17 @@ __device__ __forceinline__ void block_mean(const float* x, int64_t n, float* out
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < NTH / 64; ++w) tot += red_bm[w];
-    *out = n > 0 ? tot / (float)n : 0.f;
+    red_bm[NTH / 64] = n > 0 ? tot / (float)n : 0.f;
   }
+  __syncthreads();
+  return red_bm[NTH / 64];
+}
+
+// The same mean, written by thread 0 to *out.
+template <int NTH>
+__device__ __forceinline__ void block_mean(const float* x, int64_t n, float* out) {
+  const float m = block_mean_all<NTH>(x, n);
+  if (threadIdx.x == 0) *out = m;
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8).  Renumber them so
