@@ -299,16 +299,4 @@ hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s) {
   return a.dh <= 1024 ? run_step<float, 3>(a, s) : run_step<float, 15>(a, s);
 }
 
-// ------------------------------------------------------------- fill -----
-__global__ void k_fill(float* p, int64_t n, float v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
 }  // namespace lact

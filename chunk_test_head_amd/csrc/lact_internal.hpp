@@ -144,6 +144,5 @@ hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t 
 hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,
                       hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
-hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 }  // namespace lact
