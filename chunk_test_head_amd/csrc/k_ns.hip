@@ -284,12 +284,17 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
 // in fp32.
 //
 // Per step:
-//   1. A (symmetric): wave w takes the 64 x 32 block of rows 64 (w / 4)..,
-//      columns 32 (w % 4)..; the two blocks below the diagonal (waves 4, 5)
-//      are not computed.  Every tile is stored transposed (8-byte stores),
-//      which for a symmetric result is the tile at the mirrored position;
-//      waves 2 and 3 (blocks above the diagonal) also store their tiles in
-//      place (2-byte stores), so all of A is written.
+//   1. A (symmetric, 8 x 8 tiles of 16 x 16): six waves take a block of
+//      4 x 2 or 2 x 2 tiles that together cover the tiles on and above the
+//      diagonal (row tiles x, column tiles y):
+//        wave 0: x 0-3, y 2-3   wave 1: x 0-3, y 4-5   wave 4: x 0-1, y 0-1
+//        wave 2: x 0-3, y 6-7   wave 3: x 4-7, y 6-7   wave 5: x 4-5, y 4-5
+//      (waves 6, 7 idle).  Wave w runs on SIMD w mod 4, so the SIMDs carry
+//      12, 12, 8 and 8 tiles (two skipped 4 x 2 blocks would leave two SIMDs
+//      with 16, as many as all of A).  Every tile is stored transposed
+//      (8-byte stores), which for a symmetric result is the tile at the
+//      mirrored position; the 4 x 2 blocks also store their tiles in place
+//      (2-byte stores), so all of A is written.
 //   2. A A the same way, then (after every read of A) B' = p A + q A A over
 //      A, with A read back from the wave's own transposed tiles.
 //   3. Y <- Y + B' Y: wave w owns columns [w COLS/8, (w+1) COLS/8) and forms
@@ -325,11 +330,11 @@ __device__ __forceinline__ int nsr_opaque(int x) {
 }
 
 // acc[x][y] = sum over k < K of M[16 (x0 + x) + .][k] M[16 (y0 + y) + .][k]
-// for the row-major array s [.][W] (x < 4, y < 2).
-template <int W, int K>
+// for the row-major array s [.][W] (x < NX, y < 2).
+template <int W, int K, int NX>
 __device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, int gq, f32x4 (&acc)[4][2]) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < NX; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16* bx = s + (16 * x0 + c) * W;
@@ -339,7 +344,7 @@ __device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, i
 #define LACT_NSR_LOAD(K0, FX, FY)                                                   \
   {                                                                                 \
     const int ch = ((((K0) >> 3) + gq) ^ sw) << 3;                                  \
-    _Pragma("unroll") for (int x = 0; x < 4; ++x) FX[x] = ld8(bx + 16 * x * W + ch); \
+    _Pragma("unroll") for (int x = 0; x < NX; ++x) FX[x] = ld8(bx + 16 * x * W + ch); \
     _Pragma("unroll") for (int y = 0; y < 2; ++y) FY[y] = ld8(by + 16 * y * W + ch); \
   }
   LACT_NSR_LOAD(0, fx, fy);
@@ -349,11 +354,11 @@ __device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, i
     const int kn = k + 32 < K ? k + 32 : k;  // last slab: harmless re-read
     LACT_NSR_LOAD(kn, nx, ny);
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < NX; ++x)
 #pragma unroll
       for (int y = 0; y < 2; ++y) mma(acc[x][y], fx[x], fy[y]);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) fx[x] = nx[x];
+    for (int x = 0; x < NX; ++x) fx[x] = nx[x];
 #pragma unroll
     for (int y = 0; y < 2; ++y) fy[y] = ny[y];
   }
@@ -361,11 +366,13 @@ __device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, i
 }
 
 // Stores the block's tiles v[x][y] (values of M[16 (x0+x) + 4 g + i][16 (y0+y) + c]
-// of a symmetric 128 x 128 matrix) transposed and, with DIRECT, also in place.
+// of a symmetric 128 x 128 matrix, x < NX) transposed and, with DIRECT, also
+// in place.
+template <int NX>
 __device__ __forceinline__ void nsr_store(bf16* s, int x0, int y0, int c, int gq, bool direct,
                                           const f32x4 (&v)[4][2]) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < NX; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int tx = x0 + x, ty = y0 + y;
@@ -404,9 +411,12 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, gq = lane >> 4;
   const int col0 = w * CW;
-  const int bx0 = 4 * (w >> 2), by0 = 2 * (w & 3);  // this wave's block of A
-  const bool active = !(w == 4 || w == 5);          // blocks below the diagonal: mirrored
-  const bool direct = (w == 2 || w == 3);           // blocks above it
+  // this wave's block of A: row tiles bx0 .. bx0 + nx - 1, column tiles by0, by0 + 1
+  const int bx0 = (w == 3 || w == 5) ? 4 : 0;
+  const int by0 = w == 0 ? 2 : w == 1 ? 4 : (w == 2 || w == 3) ? 6 : w == 4 ? 0 : 4;
+  const int nx = w < 4 ? 4 : w < 6 ? 2 : 0;
+  const bool active = nx > 0;
+  const bool direct = nx == 4;  // 4 x 2 blocks also store in place
   // ---- load G: whole rows, coalesced, staged through LDS (fp32, 16-byte
   // chunks XORed with the row) into the accumulator layout ----
   // rows per staging pass: fp32 rows must fit the LDS allocation (sX + sA)
@@ -477,36 +487,41 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
     const float ca = kNsCoef[it][0], cb = kNsCoef[it][1], cc = kNsCoef[it][2];
     __syncthreads();  // sX complete; last step's reads of sA done
     // ---- 1. A = P^2 Y Y^T ----
-    if (active) {
-      const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
-      f32x4 t[4][2];
-      nsr_gram<COLS, COLS>(sX, bx0, by0, c, gq, t);
-      const float s2 = P * P;
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) t[x][y] = t[x][y] * s2;
-      nsr_store(sA, bx0, by0, c, gq, direct, t);
-    }
+    // (NX = 4 and NX = 2 blocks run separate instantiations; the branch is
+    // uniform per wave)
+#define LACT_NSR_A(NX)                                                                   \
+  {                                                                                      \
+    const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);                     \
+    f32x4 t[4][2];                                                                       \
+    nsr_gram<COLS, COLS, NX>(sX, bx0, by0, c, gq, t);                                    \
+    const float s2 = P * P;                                                              \
+    _Pragma("unroll") for (int x = 0; x < NX; ++x)                                       \
+      _Pragma("unroll") for (int y = 0; y < 2; ++y) t[x][y] = t[x][y] * s2;              \
+    nsr_store<NX>(sA, bx0, by0, c, gq, direct, t);                                       \
+  }
+    if (nx == 4) LACT_NSR_A(4) else if (nx == 2) LACT_NSR_A(2)
+#undef LACT_NSR_A
     __syncthreads();
     // ---- 2. B' = (b A + c A A) / a, over A ----
     f32x4 t[4][2];
-    if (active) nsr_gram<128, 128>(sA, bx0, by0, nsr_opaque(c), nsr_opaque(gq), t);
+    if (nx == 4) nsr_gram<128, 128, 4>(sA, bx0, by0, nsr_opaque(c), nsr_opaque(gq), t);
+    else if (nx == 2) nsr_gram<128, 128, 2>(sA, bx0, by0, nsr_opaque(c), nsr_opaque(gq), t);
     __syncthreads();  // every read of A as an operand is done
-    if (active) {
-      const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
-      const float p = cb / ca, q = cc / ca;
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const bf16x4 a = *reinterpret_cast<const bf16x4*>(
-              sA + nsr_off<128>(16 * (by0 + y) + c, 16 * (bx0 + x) + 4 * gq));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t[x][y][i] = p * (float)a[i] + q * t[x][y][i];
-        }
-      nsr_store(sA, bx0, by0, c, gq, direct, t);
-    }
+#define LACT_NSR_B(NX)                                                                   \
+  {                                                                                      \
+    const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);                     \
+    const float p = cb / ca, q = cc / ca;                                                \
+    _Pragma("unroll") for (int x = 0; x < NX; ++x)                                       \
+      _Pragma("unroll") for (int y = 0; y < 2; ++y) {                                    \
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(                               \
+            sA + nsr_off<128>(16 * (by0 + y) + c, 16 * (bx0 + x) + 4 * gq));             \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                    \
+          t[x][y][i] = p * (float)a[i] + q * t[x][y][i];                                 \
+      }                                                                                  \
+    nsr_store<NX>(sA, bx0, by0, c, gq, direct, t);                                       \
+  }
+    if (nx == 4) LACT_NSR_B(4) else if (nx == 2) LACT_NSR_B(2)
+#undef LACT_NSR_B
     __syncthreads();  // B' complete
     // ---- 3. Y <- Y + B' Y on this wave's columns: (Y^T B') tiles ----
     {
