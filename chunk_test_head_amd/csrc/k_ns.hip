@@ -284,17 +284,18 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
 // in fp32.
 //
 // Per step:
-//   1. A (symmetric, 8 x 8 tiles of 16 x 16): six waves take a block of
-//      4 x 2 or 2 x 2 tiles that together cover the tiles on and above the
-//      diagonal (row tiles x, column tiles y):
-//        wave 0: x 0-3, y 2-3   wave 1: x 0-3, y 4-5   wave 4: x 0-1, y 0-1
-//        wave 2: x 0-3, y 6-7   wave 3: x 4-7, y 6-7   wave 5: x 4-5, y 4-5
-//      (waves 6, 7 idle).  Wave w runs on SIMD w mod 4, so the SIMDs carry
-//      12, 12, 8 and 8 tiles (two skipped 4 x 2 blocks would leave two SIMDs
-//      with 16, as many as all of A).  Every tile is stored transposed
-//      (8-byte stores), which for a symmetric result is the tile at the
-//      mirrored position; the 4 x 2 blocks also store their tiles in place
-//      (2-byte stores), so all of A is written.
+//   1. A (symmetric, 8 x 8 tiles of 16 x 16): every wave forms a set of
+//      tiles on or above the diagonal (NsrSet): each diagonal 4 x 4 block
+//      is split into two sets of 5 tiles that share their operand reads (4
+//      and 3 row tiles per K slab), the block of row tiles 0-3 by column
+//      tiles 4-7 into four 2 x 2 blocks.  Wave w runs on SIMD w mod 4, so
+//      every SIMD forms 9 tiles and has two waves whose LDS reads and MFMAs
+//      interleave; fragment reads per K slab total 30 row tiles.  (Blocks of
+//      4 x 2 tiles with two of them skipped left two SIMDs with 16 tiles;
+//      unequal blocks left single waves on a SIMD waiting on their reads.)
+//      Every tile is stored transposed (8-byte stores), which for a
+//      symmetric result is the tile at the mirrored position; tiles off the
+//      diagonal also in place (2-byte stores), so all of A is written.
 //   2. A A the same way, then (after every read of A) B' = p A + q A A over
 //      A, with A read back from the wave's own transposed tiles.
 //   3. Y <- Y + B' Y: wave w owns columns [w COLS/8, (w+1) COLS/8) and forms
@@ -329,62 +330,78 @@ __device__ __forceinline__ int nsr_opaque(int x) {
   return x;
 }
 
-// acc[x][y] = sum over k < K of M[16 (x0 + x) + .][k] M[16 (y0 + y) + .][k]
-// for the row-major array s [.][W] (x < NX, y < 2).
-template <int W, int K, int NX>
-__device__ __forceinline__ void nsr_gram(const bf16* s, int x0, int y0, int c, int gq, f32x4 (&acc)[4][2]) {
+// Tile sets of a symmetric 128 x 128 product (8 x 8 tiles of 16 x 16), one
+// set per wave.  A set reads NF row tiles of the operand per K slab (row
+// tile nsr_row<SH>(f, a, b) for f < NF) and forms the NT tiles (row tile of
+// TI[t], row tile of TJ[t]), each on or above the diagonal.
+template <int SH> struct NsrSet;
+template <> struct NsrSet<0> {  // rows a..a+3: (a,a) (a,a+1) (a,a+2) (a,a+3) (a+1,a+1)
+  static constexpr int NF = 4, NT = 5;
+  static constexpr int TI[NT] = {0, 0, 0, 0, 1}, TJ[NT] = {0, 1, 2, 3, 1};
+};
+template <> struct NsrSet<1> {  // rows a..a+2: (a,a+1) (a,a+2) (a+1,a+1) (a+1,a+2) (a+2,a+2)
+  static constexpr int NF = 3, NT = 5;
+  static constexpr int TI[NT] = {0, 0, 1, 1, 2}, TJ[NT] = {1, 2, 1, 2, 2};
+};
+template <> struct NsrSet<2> {  // rows a, a+1 by rows b, b+1
+  static constexpr int NF = 4, NT = 4;
+  static constexpr int TI[NT] = {0, 0, 1, 1}, TJ[NT] = {2, 3, 2, 3};
+};
+template <int SH>
+__device__ __forceinline__ int nsr_row(int f, int a, int b) {
+  return SH == 2 ? (f < 2 ? a + f : b + f - 2) : a + f;
+}
+
+// acc[t] = sum over k < K of M[16 x + .][k] M[16 y + .][k] for the tiles
+// (x, y) of set SH of the row-major array s [.][W].
+template <int W, int K, int SH>
+__device__ __forceinline__ void nsr_gram(const bf16* s, int a, int b, int c, int gq, f32x4 (&acc)[8]) {
+  using S = NsrSet<SH>;
 #pragma unroll
-  for (int x = 0; x < NX; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16* bx = s + (16 * x0 + c) * W;
-  const bf16* by = s + (16 * y0 + c) * W;
+  for (int t = 0; t < S::NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16* ba = s + (16 * a + c) * W;
+  const bf16* bb = s + (16 * b + c) * W;
   const int sw = nsr_swz<W>(c);
-  bf16x8 fx[4], fy[2];
-#define LACT_NSR_LOAD(K0, FX, FY)                                                   \
-  {                                                                                 \
-    const int ch = ((((K0) >> 3) + gq) ^ sw) << 3;                                  \
-    _Pragma("unroll") for (int x = 0; x < NX; ++x) FX[x] = ld8(bx + 16 * x * W + ch); \
-    _Pragma("unroll") for (int y = 0; y < 2; ++y) FY[y] = ld8(by + 16 * y * W + ch); \
+  bf16x8 fr[S::NF];
+#define LACT_NSR_LOAD(K0, FR)                                                        \
+  {                                                                                  \
+    const int ch = ((((K0) >> 3) + gq) ^ sw) << 3;                                   \
+    _Pragma("unroll") for (int f = 0; f < S::NF; ++f)                                \
+      FR[f] = ld8((SH == 2 && f >= 2 ? bb + 16 * (f - 2) * W : ba + 16 * f * W) + ch); \
   }
-  LACT_NSR_LOAD(0, fx, fy);
+  LACT_NSR_LOAD(0, fr);
 #pragma unroll 1
   for (int k = 0; k < K; k += 32) {
-    bf16x8 nx[4], ny[2];
+    bf16x8 nf[S::NF];
     const int kn = k + 32 < K ? k + 32 : k;  // last slab: harmless re-read
-    LACT_NSR_LOAD(kn, nx, ny);
+    LACT_NSR_LOAD(kn, nf);
 #pragma unroll
-    for (int x = 0; x < NX; ++x)
+    for (int t = 0; t < S::NT; ++t) mma(acc[t], fr[S::TI[t]], fr[S::TJ[t]]);
 #pragma unroll
-      for (int y = 0; y < 2; ++y) mma(acc[x][y], fx[x], fy[y]);
-#pragma unroll
-    for (int x = 0; x < NX; ++x) fx[x] = nx[x];
-#pragma unroll
-    for (int y = 0; y < 2; ++y) fy[y] = ny[y];
+    for (int f = 0; f < S::NF; ++f) fr[f] = nf[f];
   }
 #undef LACT_NSR_LOAD
 }
 
-// Stores the block's tiles v[x][y] (values of M[16 (x0+x) + 4 g + i][16 (y0+y) + c]
-// of a symmetric 128 x 128 matrix, x < NX) transposed and, with DIRECT, also
-// in place.
-template <int NX>
-__device__ __forceinline__ void nsr_store(bf16* s, int x0, int y0, int c, int gq, bool direct,
-                                          const f32x4 (&v)[4][2]) {
+// Stores the set's tiles v[t] (values of M[16 x + 4 g + i][16 y + c] of a
+// symmetric 128 x 128 matrix) transposed, which for a symmetric result is
+// the tile at the mirrored position (y, x), and, off the diagonal, also in
+// place (x, y).
+template <int SH>
+__device__ __forceinline__ void nsr_store(bf16* s, int a, int b, int c, int gq, const f32x4 (&v)[8]) {
+  using S = NsrSet<SH>;
 #pragma unroll
-  for (int x = 0; x < NX; ++x)
+  for (int t = 0; t < S::NT; ++t) {
+    const int tx = nsr_row<SH>(S::TI[t], a, b), ty = nsr_row<SH>(S::TJ[t], a, b);
+    bf16x4 q;
+    q[0] = (bf16)v[t][0]; q[1] = (bf16)v[t][1];
+    q[2] = (bf16)v[t][2]; q[3] = (bf16)v[t][3];
+    *reinterpret_cast<bf16x4*>(s + nsr_off<128>(16 * ty + c, 16 * tx + 4 * gq)) = q;
+    if (S::TI[t] != S::TJ[t]) {
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int tx = x0 + x, ty = y0 + y;
-      bf16x4 b;
-      b[0] = (bf16)v[x][y][0]; b[1] = (bf16)v[x][y][1];
-      b[2] = (bf16)v[x][y][2]; b[3] = (bf16)v[x][y][3];
-      *reinterpret_cast<bf16x4*>(s + nsr_off<128>(16 * ty + c, 16 * tx + 4 * gq)) = b;
-      if (direct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[nsr_off<128>(16 * tx + 4 * gq + i, 16 * ty + c)] = b[i];
-      }
+      for (int i = 0; i < 4; ++i) s[nsr_off<128>(16 * tx + 4 * gq + i, 16 * ty + c)] = q[i];
     }
+  }
 }
 
 template <int COLS, int NMT, int NRT>
@@ -411,12 +428,13 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, gq = lane >> 4;
   const int col0 = w * CW;
-  // this wave's block of A: row tiles bx0 .. bx0 + nx - 1, column tiles by0, by0 + 1
-  const int bx0 = (w == 3 || w == 5) ? 4 : 0;
-  const int by0 = w == 0 ? 2 : w == 1 ? 4 : (w == 2 || w == 3) ? 6 : w == 4 ? 0 : 4;
-  const int nx = w < 4 ? 4 : w < 6 ? 2 : 0;
-  const bool active = nx > 0;
-  const bool direct = nx == 4;  // 4 x 2 blocks also store in place
+  // this wave's tile set of A and A A (NsrSet): the diagonal 4 x 4 blocks
+  // are split into sets 0 and 1 (waves 0, 1: rows 0-3; waves 2, 3: rows
+  // 4-7), the block of row tiles 0-3 by column tiles 4-7 into four 2 x 2
+  // sets (waves 4-7)
+  const int sh = w < 4 ? (w & 1) : 2;
+  const int sa = w < 4 ? 4 * (w >> 1) + (w & 1) : 2 * ((w - 4) >> 1);
+  const int sb = w < 4 ? 0 : 4 + 2 * (w & 1);
   // ---- load G: whole rows, coalesced, staged through LDS (fp32, 16-byte
   // chunks XORed with the row) into the accumulator layout ----
   // rows per staging pass: fp32 rows must fit the LDS allocation (sX + sA)
@@ -487,40 +505,39 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
     const float ca = kNsCoef[it][0], cb = kNsCoef[it][1], cc = kNsCoef[it][2];
     __syncthreads();  // sX complete; last step's reads of sA done
     // ---- 1. A = P^2 Y Y^T ----
-    // (NX = 4 and NX = 2 blocks run separate instantiations; the branch is
-    // uniform per wave)
-#define LACT_NSR_A(NX)                                                                   \
+    // (one instantiation per tile set; the branch is uniform per wave)
+#define LACT_NSR_A(SH)                                                                   \
   {                                                                                      \
     const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);                     \
-    f32x4 t[4][2];                                                                       \
-    nsr_gram<COLS, COLS, NX>(sX, bx0, by0, c, gq, t);                                    \
+    f32x4 t[8];                                                                          \
+    nsr_gram<COLS, COLS, SH>(sX, sa, sb, c, gq, t);                                      \
     const float s2 = P * P;                                                              \
-    _Pragma("unroll") for (int x = 0; x < NX; ++x)                                       \
-      _Pragma("unroll") for (int y = 0; y < 2; ++y) t[x][y] = t[x][y] * s2;              \
-    nsr_store<NX>(sA, bx0, by0, c, gq, direct, t);                                       \
+    _Pragma("unroll") for (int x = 0; x < NsrSet<SH>::NT; ++x) t[x] = t[x] * s2;         \
+    nsr_store<SH>(sA, sa, sb, c, gq, t);                                                 \
   }
-    if (nx == 4) LACT_NSR_A(4) else if (nx == 2) LACT_NSR_A(2)
+    if (sh == 0) LACT_NSR_A(0) else if (sh == 1) LACT_NSR_A(1) else LACT_NSR_A(2)
 #undef LACT_NSR_A
     __syncthreads();
     // ---- 2. B' = (b A + c A A) / a, over A ----
-    f32x4 t[4][2];
-    if (nx == 4) nsr_gram<128, 128, 4>(sA, bx0, by0, nsr_opaque(c), nsr_opaque(gq), t);
-    else if (nx == 2) nsr_gram<128, 128, 2>(sA, bx0, by0, nsr_opaque(c), nsr_opaque(gq), t);
+    f32x4 t[8];
+    if (sh == 0) nsr_gram<128, 128, 0>(sA, sa, sb, nsr_opaque(c), nsr_opaque(gq), t);
+    else if (sh == 1) nsr_gram<128, 128, 1>(sA, sa, sb, nsr_opaque(c), nsr_opaque(gq), t);
+    else nsr_gram<128, 128, 2>(sA, sa, sb, nsr_opaque(c), nsr_opaque(gq), t);
     __syncthreads();  // every read of A as an operand is done
-#define LACT_NSR_B(NX)                                                                   \
+#define LACT_NSR_B(SH)                                                                   \
   {                                                                                      \
     const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);                     \
     const float p = cb / ca, q = cc / ca;                                                \
-    _Pragma("unroll") for (int x = 0; x < NX; ++x)                                       \
-      _Pragma("unroll") for (int y = 0; y < 2; ++y) {                                    \
-        const bf16x4 a = *reinterpret_cast<const bf16x4*>(                               \
-            sA + nsr_off<128>(16 * (by0 + y) + c, 16 * (bx0 + x) + 4 * gq));             \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                    \
-          t[x][y][i] = p * (float)a[i] + q * t[x][y][i];                                 \
-      }                                                                                  \
-    nsr_store<NX>(sA, bx0, by0, c, gq, direct, t);                                       \
+    _Pragma("unroll") for (int x = 0; x < NsrSet<SH>::NT; ++x) {                         \
+      const int tx = nsr_row<SH>(NsrSet<SH>::TI[x], sa, sb);                             \
+      const int ty = nsr_row<SH>(NsrSet<SH>::TJ[x], sa, sb);                             \
+      const bf16x4 a = *reinterpret_cast<const bf16x4*>(                                 \
+          sA + nsr_off<128>(16 * ty + c, 16 * tx + 4 * gq));                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) t[x][i] = p * (float)a[i] + q * t[x][i]; \
+    }                                                                                    \
+    nsr_store<SH>(sA, sa, sb, c, gq, t);                                                 \
   }
-    if (nx == 4) LACT_NSR_B(4) else if (nx == 2) LACT_NSR_B(2)
+    if (sh == 0) LACT_NSR_B(0) else if (sh == 1) LACT_NSR_B(1) else LACT_NSR_B(2)
 #undef LACT_NSR_B
     __syncthreads();  // B' complete
     // ---- 3. Y <- Y + B' Y on this wave's columns: (Y^T B') tiles ----
