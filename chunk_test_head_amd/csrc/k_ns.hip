@@ -383,10 +383,31 @@ __device__ __forceinline__ void nsr_gram(const bf16* s, int a, int b, int c, int
 #undef LACT_NSR_LOAD
 }
 
+// 4 x 4 transpose of 16-bit values over the four lanes of a quad (lanes
+// 4k .. 4k + 3): value i of lane j becomes value j of lane i.  p[0] holds
+// values 0, 1 and p[1] values 2, 3 (lower half first).  Lane j first swaps a
+// dword with lane j ^ 2 (the one the partner needs), then each dword's
+// halves with lane j ^ 1 (DPP quad permutations and a byte permute; no LDS).
+__device__ __forceinline__ void quad_transpose16(uint32_t (&p)[2], int j) {
+  const bool b1 = (j & 2) != 0, b0 = (j & 1) != 0;
+  const uint32_t send = b1 ? p[0] : p[1];
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true);  // j ^ 2
+  p[0] = b1 ? recv : p[0];
+  p[1] = b1 ? p[1] : recv;
+  // even lane: (own low half, partner's low half); odd: (partner's high, own high)
+  const uint32_t sel = b0 ? 0x03020706u : 0x05040100u;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)p[x], 0xB1, 0xF, 0xF, true);  // j ^ 1
+    p[x] = __builtin_amdgcn_perm(r, p[x], sel);
+  }
+}
+
 // Stores the set's tiles v[t] (values of M[16 x + 4 g + i][16 y + c] of a
 // symmetric 128 x 128 matrix) transposed, which for a symmetric result is
 // the tile at the mirrored position (y, x), and, off the diagonal, also in
-// place (x, y).
+// place (x, y): after a transpose within lane quads, lane (c, g) holds row
+// 16 x + 4 g + c % 4, columns 16 y + 4 (c / 4) + 0..3 (8-byte stores).
 template <int SH>
 __device__ __forceinline__ void nsr_store(bf16* s, int a, int b, int c, int gq, const f32x4 (&v)[8]) {
   using S = NsrSet<SH>;
@@ -398,8 +419,11 @@ __device__ __forceinline__ void nsr_store(bf16* s, int a, int b, int c, int gq, 
     q[2] = (bf16)v[t][2]; q[3] = (bf16)v[t][3];
     *reinterpret_cast<bf16x4*>(s + nsr_off<128>(16 * ty + c, 16 * tx + 4 * gq)) = q;
     if (S::TI[t] != S::TJ[t]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[nsr_off<128>(16 * tx + 4 * gq + i, 16 * ty + c)] = q[i];
+      uint32_t p[2];
+      __builtin_memcpy(p, &q, sizeof(p));
+      quad_transpose16(p, c & 3);
+      *reinterpret_cast<uint2*>(s + nsr_off<128>(16 * tx + 4 * gq + (c & 3), 16 * ty + 4 * (c >> 2))) =
+          make_uint2(p[0], p[1]);
     }
   }
 }
