@@ -295,7 +295,8 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
 //      unequal blocks left single waves on a SIMD waiting on their reads.)
 //      Every tile is stored transposed (8-byte stores), which for a
 //      symmetric result is the tile at the mirrored position; tiles off the
-//      diagonal also in place (2-byte stores), so all of A is written.
+//      diagonal also in place (8-byte stores after a transpose within lane
+//      quads), so all of A is written.
 //   2. A A the same way, then (after every read of A) B' = p A + q A A over
 //      A, with A read back from the wave's own transposed tiles.
 //   3. Y <- Y + B' Y: wave w owns columns [w COLS/8, (w+1) COLS/8) and forms
