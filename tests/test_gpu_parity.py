@@ -123,6 +123,32 @@ def test_newton_schulz(device, dtype, tol, rows, cols):
         assert H.rel(got[i], ref) < tol, (i, H.rel(got[i], ref))
 
 
+@pytest.mark.parametrize("dtype,tol", [(L.BF16, 2e-2), (L.F32, 1e-4)])
+@pytest.mark.parametrize("rows,cols", [(128, 512), (128, 256)])
+def test_newton_schulz_degenerate(device, dtype, tol, rows, cols):
+    """Degenerate inputs (Muon orthogonalisation, quintic Newton-Schulz of the
+    LaCT pages): a zero gradient stays exactly zero (the norm guard eps keeps
+    the scale finite), a rank-one gradient, and one whose norm is far below
+    eps (its Gram products underflow; the iterate is then the scaled input
+    times the product of the a coefficients, as in the oracle)."""
+    import torch
+    rng = np.random.default_rng(7 + cols)
+    Gs = [np.zeros((rows, cols)),
+          np.outer(rng.standard_normal(rows), rng.standard_normal(cols)),
+          1e-30 * rng.standard_normal((rows, cols))]
+    g = torch.from_numpy(np.stack(Gs).astype(np.float32)).to(device)
+    u = torch.full_like(g, float("nan"))
+    ws = torch.empty(L.ns_workspace_bytes(3, rows, cols) // 4 + 1, device=device)
+    print(f"ns degenerate dtype={dtype} {rows}x{cols}", flush=True)
+    L.lact_newton_schulz(g, u, ws, dtype=dtype)
+    torch.cuda.synchronize()
+    got = H.to64(u)
+    assert np.all(got[0] == 0.0)
+    for i in (1, 2):
+        ref = O.newton_schulz5(g[i].cpu().numpy().astype(np.float64))
+        assert H.rel(got[i], ref) < tol, (i, H.rel(got[i], ref))
+
+
 @pytest.mark.parametrize("renorm", [True, False])
 @pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
 def test_step_renorm(device, wi, renorm):
