@@ -101,7 +101,8 @@ def test_gradient_distinct_etas(device):
 
 
 @pytest.mark.parametrize("dtype,tol", [(L.BF16, 2e-2), (L.F32, 1e-4)])
-@pytest.mark.parametrize("rows,cols", [(128, 512), (128, 256), (256, 1024), (64, 128), (128, 192), (192, 320)])
+@pytest.mark.parametrize("rows,cols", [(128, 512), (128, 256), (256, 1024), (64, 128), (64, 256), (64, 512),
+                                       (128, 192), (192, 320)])
 def test_newton_schulz(device, dtype, tol, rows, cols):
     import torch
     # a gradient-like input: oracle chunk gradient of a random head
