@@ -293,3 +293,29 @@ def test_sequence_end_to_end(device, wi):
         assert H.rel(W1[b], st.W1) < H.TOL[w.dtype]
         assert H.rel(W2[b], st.W2) < H.TOL[w.dtype]
     H.check_shadow(fw)
+
+
+@pytest.mark.parametrize("dh", [256, 512])
+def test_sequence_bf16_d64(device, dh):
+    """bf16 operands at d = 64 (a supported shape no workload uses): the
+    d = 64 read and gradient kernels, the one-launch Newton-Schulz of 64 x dh,
+    momentum and renorm, over a causal sequence with a ragged last chunk,
+    against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(WL.WORKLOADS[1], d=64, dh=dh, heads=2, batch=1, T=3 * 128 + 50, chunk=128,
+                            name=f"lm-causal-d64-dh{dh}")
+    W, inp = inputs(w)
+    print(f"sequence bf16 d=64 dh={dh} T={w.T} C={w.chunk}", flush=True)
+    got, fw = H.run_sequence(w, inp, W, device)
+    W1, W3, W2, *_ = H.state64(fw)
+    for b in range(w.bh):
+        m = None if inp["mom"] is None else inp["mom"][b]
+        e = inp["eta"][b]
+        ref, st = O.sequence(W[0][b], W[1][b], W[2][b], inp["q"][b], inp["k"][b], inp["v"][b], e, e, e,
+                             w.chunk, mom=m, order=w.order, subset=w.subset, update_last=w.update_last,
+                             use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+        assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
+        assert H.rel(W1[b], st.W1) < H.TOL[w.dtype]
+        assert H.rel(W2[b], st.W2) < H.TOL[w.dtype]
+    H.check_shadow(fw)
+
