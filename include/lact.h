@@ -27,7 +27,8 @@
  *    elements; the three eta pointers may alias.
  *
  * Supported shapes: d in {64, 128, 256}; dh a multiple of 64 with
- * d <= dh <= 4096; bh >= 1.  Anything else returns LACT_ERR_UNSUPPORTED.
+ * d <= dh <= 4096; bh >= 1; with LACT_F32 activations d <= 128.  Anything
+ * else returns LACT_ERR_UNSUPPORTED.
  */
 #ifndef LACT_H
 #define LACT_H

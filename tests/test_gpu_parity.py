@@ -319,3 +319,25 @@ def test_sequence_bf16_d64(device, dh):
         assert H.rel(W2[b], st.W2) < H.TOL[w.dtype]
     H.check_shadow(fw)
 
+
+def test_sequence_f32_d128(device):
+    """fp32 activations and operands at d = 128 (the fp32 read and gradient
+    kernels, Newton-Schulz with fp32 operands, momentum, renorm) over a
+    causal sequence with a ragged last chunk, against the oracle (bar 1e-4)."""
+    import dataclasses
+    w = dataclasses.replace(WL.WORKLOADS[1], dtype="f32", d=128, dh=256, heads=2, batch=1,
+                            T=3 * 128 + 50, chunk=128, name="lm-causal-f32-d128")
+    W, inp = inputs(w)
+    print(f"sequence f32 d=128 T={w.T} C={w.chunk}", flush=True)
+    got, fw = H.run_sequence(w, inp, W, device)
+    W1, W3, W2, *_ = H.state64(fw)
+    for b in range(w.bh):
+        m = None if inp["mom"] is None else inp["mom"][b]
+        e = inp["eta"][b]
+        ref, st = O.sequence(W[0][b], W[1][b], W[2][b], inp["q"][b], inp["k"][b], inp["v"][b], e, e, e,
+                             w.chunk, mom=m, order=w.order, subset=w.subset, update_last=w.update_last,
+                             use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+        assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
+        assert H.rel(W1[b], st.W1) < H.TOL[w.dtype], (b, H.rel(W1[b], st.W1))
+        assert H.rel(W2[b], st.W2) < H.TOL[w.dtype], (b, H.rel(W2[b], st.W2))
+
