@@ -341,3 +341,33 @@ def test_sequence_f32_d128(device):
         assert H.rel(W1[b], st.W1) < H.TOL[w.dtype], (b, H.rel(W1[b], st.W1))
         assert H.rel(W2[b], st.W2) < H.TOL[w.dtype], (b, H.rel(W2[b], st.W2))
 
+
+@pytest.mark.parametrize("wi", [1, 3])
+def test_zero_tokens_write_nothing(device, wi):
+    """Reads, writes and chunk steps of zero tokens return LACT_OK and leave
+    the state (weights, norms, momentum, operand copies) and the output
+    buffer bitwise unchanged."""
+    import torch
+    w = small(wi, 64, 64, subset=(0, 64))
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    q = H.act_to_dev(w, inp, "q", device)
+    k = H.act_to_dev(w, inp, "k", device)
+    v = H.act_to_dev(w, inp, "v", device)
+    out = H.out_buffer(w, 64, device)
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    mom = torch.from_numpy(inp["mom"]).to(device) if inp["mom"] is not None else None
+    ws = H.workspace(w, 64, device)
+    torch.cuda.synchronize()
+    bufs = [fw.w1, fw.w3, fw.w2, fw.n1, fw.n3, fw.n2, fw.shadow] + \
+        [m for m in (fw.m1, fw.m3, fw.m2) if m is not None]
+    before = [b.clone() for b in bufs]
+    print(f"zero tokens wl={wi}", flush=True)
+    L.lact_apply(fw.shape, fw, q, out, n_tok=0)
+    L.lact_update(fw.shape, fw, k, v, eta, eta, eta, mom, H.opts_of(w), ws, n_tok=0)
+    L.lact_chunk_step(fw.shape, fw, q, k, v, out, eta, eta, eta, mom, H.opts_of(w), ws, n_tok=0)
+    torch.cuda.synchronize()
+    for a, b in zip(bufs, before):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    assert torch.isnan(out.float()).all()
+
