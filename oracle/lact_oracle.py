@@ -20,15 +20,18 @@ Everything is the plain definition, in float64, one (batch, head) at a time:
   step of both functions).
 * write (update): descent direction of the associative loss
   L_j = -sum_t eta_{j,t} <f_W(k_t), v_t>, one eta per matrix j (rebuttal
-  page, "compute the gradient and update the fast weights" block; summary
-  page section 3.2 Eq. 4-5).  G_j = -dL_j/dW_j, summed over the tokens.
+  page, the gradient block inside the chunk loop of the block-causal
+  function; summary page section 3.2 Eq. 4-5).  G_j = -dL_j/dW_j, summed
+  over the tokens.
 * momentum: beta = mean over the written tokens of the per-token momentum,
   G <- G + beta M, M <- G, M = 0 at sequence start, before Muon
   (rebuttal page, momentum block of the block-causal function).
-* Muon: Newton-Schulz quintic iteration, 5 steps with 5 coefficient triples,
-  on the wide orientation, after Frobenius normalisation with eps 1e-7
-  (rebuttal page, ``zeropower_via_newtonschulz5``; summary page section 3.2
-  Eq. 9-10).
+* Muon: five quintic Newton-Schulz steps with five coefficient triples after
+  Frobenius normalisation with eps 1e-7 (rebuttal page,
+  ``zeropower_via_newtonschulz5``; summary page section 3.2 Eq. 9-10).  A
+  quintic step is an odd matrix polynomial, so it keeps the singular vectors
+  and maps each singular value through the scalar quintic; the oracle
+  computes exactly that from an SVD.
 * step + L2 row renorm: W <- W + G, then each row rescaled to its norm at
   sequence start, with eps 1e-5 added to the current norm (rebuttal page,
   end of the chunk loop; summary page section 3.2 Eq. 8).
@@ -47,8 +50,10 @@ Readings where the pages are silent or inconsistent are listed in the design doc
   that ends at T is read only.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
-(finite differences, linearity, SVD closed form of Newton-Schulz, norm and
-momentum closed forms, brute force, causality invariants).
+(finite differences, linearity, the matrix iteration of Newton-Schulz
+written in the other Gram orientation, its singular-value band and rank-one
+closed form, norm and momentum closed forms, the momentum buffer and the
+renorm targets across two writes, brute force, causality invariants).
 """
 from __future__ import annotations
 
@@ -146,20 +151,21 @@ def momentum_step(G, M, beta):
 def newton_schulz5(G, eps=NS_EPS, coeffs=NS_COEFFS):
     """Muon orthogonalisation of one matrix.
 
-    Work on the wide orientation (transpose when rows > cols), divide by the
-    Frobenius norm plus eps, then for each (a, b, c):
-    A = X X^T, B = b A + c A A, X <- a X + B X; transpose back.
+    The iterate starts at X0 = G / (||G||_F + eps).  One step with
+    coefficients (a, b, c) replaces X by a X + b (X X^T) X + c (X X^T)^2 X.
+    Writing X = U diag(s) V^T (thin SVD), (X X^T)^k X = U diag(s^(2k+1)) V^T,
+    so the step keeps U and V and sends every singular value s to
+    a s + b s^3 + c s^5.  Five steps therefore give U diag(phi(s0)) V^T, with
+    s0 the singular values of X0 and phi the five scalar quintics applied in
+    order.  (The page transposes tall matrices first; that only changes which
+    side the Gram matrix is formed on, not the result.)
     """
-    X = _f64(G)
-    tall = X.shape[0] > X.shape[1]
-    if tall:
-        X = X.T
-    X = X / (np.linalg.norm(X) + eps)
+    G = _f64(G)
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    s = S / (np.linalg.norm(G) + eps)
     for a, b, c in coeffs:
-        A = X @ X.T
-        B = b * A + c * (A @ A)
-        X = a * X + B @ X
-    return X.T.copy() if tall else X
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (U * s) @ Vt
 
 
 def step_renorm(W, U, n0, eps=RENORM_EPS):

@@ -3,9 +3,11 @@
 Each test checks one oracle function against something fixed by the pages or
 by mathematics: central finite differences of the associative loss, the
 linearity of the chunk gradient in its tokens, brute-force scalar loops, the
-SVD closed form of the Newton-Schulz polynomial, closed forms of the renorm
-and of momentum, the printed constants, and the causality structure of the
-orderings.  CPU only.
+Newton-Schulz matrix iteration written with the Gram matrix on the other
+side (the oracle uses the singular-value form), its singular-value band and
+rank-one closed form, closed forms of the renorm and of momentum, the
+momentum buffer and renorm targets over two writes, the printed constants,
+and the causality structure of the orderings.  CPU only.
 """
 import math
 import os
@@ -160,16 +162,40 @@ def test_ns_coefficients_are_the_pages():
     assert O.NS_EPS == 1e-7 and O.RENORM_EPS == 1e-5
 
 
-@pytest.mark.parametrize("shape", [(12, 30), (30, 12), (16, 16), (128, 512)])
-def test_ns_svd_closed_form(shape):
-    """NS(G) = U phi(S / (||G||_F + eps)) V^T with phi the scalar quintic chain."""
+def _ns_matrix_iteration(G):
+    """The five quintic steps as matrix products, written here with the Gram
+    matrix on the column side: X <- X (a I + b X^T X + c (X^T X)^2), which
+    equals a X + b (X X^T) X + c (X X^T)^2 X, in the orientation G has."""
+    X = np.array(G, dtype=np.float64)
+    X = X / (math.sqrt(float(np.sum(X * X))) + 1e-7)
+    eye = np.eye(X.shape[1])
+    for a, b, c in _golden_coeffs():
+        S = X.T @ X
+        X = X @ (a * eye + b * S + c * (S @ S))
+    return X
+
+
+@pytest.mark.parametrize("shape", [(12, 30), (30, 12), (16, 16), (128, 512), (1024, 256)])
+def test_ns_matches_matrix_iteration(shape):
+    """The oracle's singular-value form equals the matrix iteration."""
     rng = np.random.default_rng(6)
     G = rng.standard_normal(shape) * 3.0
-    U, S, Vt = np.linalg.svd(G, full_matrices=False)
-    ref = (U * _phi(S / (np.linalg.norm(G) + 1e-7))) @ Vt
+    ref = _ns_matrix_iteration(G)
     out = O.newton_schulz5(G)
     assert out.shape == G.shape
     assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_ns_zero_and_low_rank():
+    """A zero gradient gives a zero step; a rank-deficient one keeps its rank
+    (phi(0) = 0) and its row and column spaces."""
+    assert np.array_equal(O.newton_schulz5(np.zeros((8, 20))), np.zeros((8, 20)))
+    rng = np.random.default_rng(17)
+    G = rng.standard_normal((16, 3)) @ rng.standard_normal((3, 40))
+    out = O.newton_schulz5(G)
+    assert np.max(np.abs(out - _ns_matrix_iteration(G))) < 1e-12
+    sv = np.linalg.svd(out, compute_uv=False)
+    assert sv[3] < 1e-12 * sv[0]
 
 
 def test_ns_singular_values_approach_one():
@@ -252,6 +278,59 @@ def test_update_momentum_beta_is_chunk_mean():
     _, parts = O.update(st, K, V, eta, eta, eta, mom=mom, use_momentum=True, return_parts=True)
     raw1 = parts["raw"][0]
     assert np.max(np.abs(parts["pre_ns"][0] - (raw1 + mom.mean() * st.M1))) < 1e-15
+
+
+def test_momentum_buffer_holds_pre_muon_sum():
+    """Two writes with momentum and Muon: after the second write the buffer
+    is G2 + beta G1, both raw chunk gradients (before Newton-Schulz), G1 at
+    the initial weights and G2 at the weights after the first write."""
+    rng = np.random.default_rng(18)
+    d, dh, n = 6, 14, 11
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    st0 = O.HeadState(W1, W3, W2)
+    ks = [rng.standard_normal((n, d)) for _ in range(2)]
+    vs = [rng.standard_normal((n, d)) for _ in range(2)]
+    eta = np.full(n, 0.02)
+    mom = rng.uniform(0.6, 0.95, (2, n))
+    st1 = O.update(st0, ks[0], vs[0], eta, eta, eta, mom=mom[0], use_muon=True, use_momentum=True)
+    st2 = O.update(st1, ks[1], vs[1], eta, eta, eta, mom=mom[1], use_muon=True, use_momentum=True)
+    g1 = O.chunk_gradient(st0.W1, st0.W3, st0.W2, ks[0], vs[0], eta, eta, eta)
+    g2 = O.chunk_gradient(st1.W1, st1.W3, st1.W2, ks[1], vs[1], eta, eta, eta)
+    beta2 = float(np.mean(mom[1]))
+    for M, a, b in zip((st2.M1, st2.M3, st2.M2), g1, g2):
+        want = b + beta2 * a
+        assert np.max(np.abs(M - want)) < 1e-13 * np.max(np.abs(want))
+    # the buffer after the first write is the first raw gradient itself
+    for M, a in zip((st1.M1, st1.M3, st1.M2), g1):
+        assert np.max(np.abs(M - a)) < 1e-15 * np.max(np.abs(a)) + 1e-300
+
+
+@pytest.mark.parametrize("muon", [False, True])
+def test_renorm_targets_are_sequence_start_norms(muon):
+    """Over two writes every row ends at n0 ||r|| / (||r|| + 1e-5), with n0
+    the row norms of the initial weights (not of the weights before the
+    write) and r the row after the step.  The initial rows are made short
+    (norm ~1e-5) so that the two readings differ by a factor near two."""
+    rng = np.random.default_rng(19)
+    d, dh, n = 5, 9, 13
+    W1, W3, W2 = _rand_state(rng, d, dh, scale=1e-5 if not muon else None)
+    n0 = [np.sqrt((W * W).sum(1)) for W in (W1, W3, W2)]
+    st = O.HeadState(W1, W3, W2)
+    for c in range(2):
+        K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+        eta = np.full(n, 1e-9 if not muon else 0.01)
+        new, parts = O.update(st, K, V, eta, eta, eta, use_muon=muon, return_parts=True)
+        for W_prev, U, W_new, tgt in zip((st.W1, st.W3, st.W2), parts["step"], (new.W1, new.W3, new.W2), n0):
+            r = W_prev + U
+            nr = np.sqrt((r * r).sum(1))
+            got = np.sqrt((W_new * W_new).sum(1))
+            assert np.max(np.abs(got / (tgt * nr / (nr + 1e-5)) - 1.0)) < 1e-13, c
+            if not muon and c == 1:
+                # recomputing the targets from the weights before the write
+                # would give rows about half as long
+                prev = np.sqrt((W_prev * W_prev).sum(1))
+                assert np.min(np.abs(got - prev * nr / (nr + 1e-5)) / got) > 0.2
+        st = new
 
 
 # ---------------------------------------------------------- orderings ----
