@@ -18,8 +18,11 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "lact.h")
 
 F32, BF16 = 0, 1
 APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
+NS_BF16_SHIFTED, NS_BF16, NS_F32 = 0, 1, 2
+NS_PREC_NAMES = {NS_BF16_SHIFTED: "bf16-shifted", NS_BF16: "bf16", NS_F32: "f32"}
+OK, ERR_NONFINITE = 0, 6
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "alignment",
-          4: "workspace", 5: "HIP error"}
+          4: "workspace", 5: "HIP error", 6: "non-finite weights"}
 
 
 class Shape(ctypes.Structure):
@@ -38,7 +41,8 @@ class Layout(ctypes.Structure):
 class UpdateOpts(ctypes.Structure):
     _fields_ = [("use_muon", ctypes.c_int32), ("use_momentum", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("renorm_eps", ctypes.c_float),
-                ("ns_eps", ctypes.c_float), ("ns_fp32", ctypes.c_int32)]
+                ("ns_eps", ctypes.c_float), ("ns_prec", ctypes.c_int32),
+                ("nonfinite", ctypes.c_void_p)]
 
 
 class LactError(RuntimeError):
@@ -81,6 +85,7 @@ def load():
         "lact_prof_begin": (I32, [I32, I32]),
         "lact_prof_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(F), ctypes.POINTER(F),
                                 ctypes.POINTER(F)]),
+        "lact_check_finite": (I32, [P, P]),
         "lact_status_string": (ctypes.c_char_p, [I32]),
         "lact_last_hip_error": (ctypes.c_int, []),
     }
@@ -127,8 +132,11 @@ def layout_of(t):
     return Layout(t.stride(0), t.stride(1))
 
 
-def opts(use_muon=False, use_momentum=False, renorm=True, renorm_eps=1e-5, ns_eps=1e-7, ns_fp32=False):
-    return UpdateOpts(int(use_muon), int(use_momentum), int(renorm), renorm_eps, ns_eps, int(ns_fp32))
+def opts(use_muon=False, use_momentum=False, renorm=True, renorm_eps=1e-5, ns_eps=1e-7,
+         ns_prec=NS_BF16_SHIFTED, nonfinite=None):
+    """lact_update_opts; nonfinite: a device int32 tensor (or None)."""
+    return UpdateOpts(int(use_muon), int(use_momentum), int(renorm), renorm_eps, ns_eps, int(ns_prec),
+                      _ptr(nonfinite))
 
 
 def shadow_bytes(shape):
@@ -207,10 +215,18 @@ def lact_gradient(shape, fw, k, v, eta1, eta3, eta2, g1, g3, g2, ws, n_tok=None,
                                 ws.numel() * ws.element_size(), _stream(stream)), "lact_gradient")
 
 
-def lact_newton_schulz(g, u, ws, dtype=BF16, eps=1e-7, stream=None):
+def lact_newton_schulz(g, u, ws, prec=NS_BF16_SHIFTED, eps=1e-7, stream=None):
     count, rows, cols = g.shape
-    _check(load().lact_newton_schulz(count, rows, cols, dtype, _ptr(g), _ptr(u), eps, _ptr(ws),
+    _check(load().lact_newton_schulz(count, rows, cols, prec, _ptr(g), _ptr(u), eps, _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "lact_newton_schulz")
+
+
+def lact_check_finite(flag, stream=None):
+    """Waits for the stream; returns the status (OK or ERR_NONFINITE)."""
+    st = load().lact_check_finite(_ptr(flag), _stream(stream))
+    if st not in (OK, ERR_NONFINITE):
+        raise LactError(st, "lact_check_finite")
+    return st
 
 
 def lact_step_renorm(shape, fw, u1, u3, u2, o, ws, stream=None):

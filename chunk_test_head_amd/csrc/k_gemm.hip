@@ -106,14 +106,16 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s) {
 // X stays fp32 in global memory (for the exact a X term) and a bf16 copy is
 // the MFMA operand of the next products.
 //
-//   C = alpha A B + beta D, A bf16 [M][K] (row pitch lda), B bf16 [N][K]
+//   C = alpha A B + beta' D + diag' I, A bf16 [M][K] (row pitch lda), B bf16 [N][K]
 //   (BKN = false, pitch ldb) or [K][N] (BKN = true); D fp32 [M][N]; outputs
 //   fp32 C and / or bf16 Ch, [M][N].
 // One workgroup = one 64 x 64 tile, 4 waves of 32 x 32; K in slabs of 64,
 // double buffered through LDS (rows padded by 16 elements: conflict-free
 // fragment and transpose reads); with BKN the B fragments (K per lane) are
 // transpose reads of the [k][n] tile.  The result tile goes through LDS so
-// that D, C and Ch move as whole 16-byte row pieces.  The small slabs keep
+// that D, C and Ch move as whole 16-byte row pieces.  beta' and diag' take
+// the step's shift mu into account (NsGemmArgs), and the launch can leave the
+// sum of squares of every result tile for the next step's mu.  The small slabs keep
 // the LDS at 40 KiB, four workgroups per CU: the loop is bound by the
 // latency of each slab's loads, so more workgroups in flight is what counts.
 namespace {
@@ -216,14 +218,42 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
   const float* D = a.D ? a.D + bidx * a.d_bs : nullptr;
   float* C = a.C ? a.C + bidx * a.c_bs : nullptr;
   bf16* Ch = a.Ch ? a.Ch + bidx * a.c_bs : nullptr;
+  // shift of this step (the same mu in every workgroup of the matrix: the
+  // partial sums are added in a fixed order)
+  float mu = 0.f;
+  if (a.mu_part != nullptr) {
+    const float* mp = a.mu_part + bidx * a.mu_np;
+    float t = 0.f;
+    for (int q = lane; q < a.mu_np; q += 64) t += mp[q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+    mu = t / a.mu_div;
+  }
+  const float be = a.beta + (a.beta_mu + a.beta_mu2 * mu) * mu;
+  const float dg = a.diag_mu * mu;
+  float ss = 0.f;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
     const int64_t o = (int64_t)(m0 + r) * a.N + n0 + c4;
     f32x4 v = *reinterpret_cast<const f32x4*>(sc + r * NSG_PC + c4) * a.alpha;
-    if (D) v += *reinterpret_cast<const f32x4*>(D + o) * a.beta;
+    if (D) v += *reinterpret_cast<const f32x4*>(D + o) * be;
+    if (dg != 0.f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += (m0 + r == n0 + c4 + j) ? dg : 0.f;
+    }
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     if (C) *reinterpret_cast<f32x4*>(C + o) = v;
     if (Ch) st4(Ch + o, v[0], v[1], v[2], v[3]);
+  }
+  if (a.ss_part != nullptr) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    __syncthreads();  // every read of the result tile done
+    if (lane == 0) sc[wave] = ss;
+    __syncthreads();
+    if (tid == 0)
+      a.ss_part[bidx * gridDim.x + blockIdx.x] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
   }
 }
 

@@ -18,6 +18,17 @@
 //      transpose of its tiles, again as 8-byte stores.
 //   3. each wave computes its columns of B X from bf16 fragments of its own
 //      X (B operand, K = rows) and rows of B from LDS; X = a X + B X in fp32.
+//
+// Shifted steps (every step from `shift_from` on): once most singular values
+// are near one, A is near a multiple mu I of the identity and B near
+// (b mu + c mu^2) I, so rounding A, B and the X operand of B X to bf16 costs
+// about 2^-9 of X per step.  Those steps take mu = trace(A) / rows, store
+// A_s = A - mu I instead and form
+//   B_s = (b + 2 c mu) A_s + c A_s A_s      (= B - (b mu + c mu^2) I),
+//   X  <- (a + b mu + c mu^2) X + B_s X      (the same step in real numbers),
+// so the multiples of the identity stay in fp32 and only the remainders are
+// rounded.  mu is the mean eigenvalue of A, so a spectrum that has not yet
+// gathered near one is shifted by little.
 #include "lact_internal.hpp"
 #include "mfma.hpp"
 #include "k_apply.hpp"
@@ -37,7 +48,7 @@ constexpr int ns_lds_elems(int rows, int cols) {
 // only its own columns, L2-resident) instead of in registers, for shapes
 // whose register copy would not fit.
 template <int ROWS, int COLS, int NW, bool XG>
-__global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float eps) {
+__global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float eps, int shift_from) {
   constexpr int NRT = ROWS / 16;          // row tiles of X
   constexpr int CW = COLS / NW;           // columns per wave
   constexpr int NCT = CW / 16;            // column tiles per wave
@@ -113,6 +124,7 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
     bf16* sA = lds_ns + lb;
     bf16* sB = lds_ns + lb + ROWS * PA;
     const float ca = kNsCoef[it][0], cb = kNsCoef[it][1], cc = kNsCoef[it][2];
+    const bool shf = it >= shift_from;
     // ---- 1. X -> LDS row-major; A = X X^T ----
     __syncthreads();  // previous step's readers of sB are done
     // X^T row-major: lane (c, g) stores rows 4g .. 4g+3 of column col as 8 bytes
@@ -164,7 +176,35 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
     __syncthreads();  // all reads of sX done before A overwrites it
     // ---- 2. A -> LDS; A A; B = b A + c A A -> LDS ----
     // A symmetric: store the transposed tile, row (col of the tile) gets 4
-    // consecutive elements
+    // consecutive elements (shifted step: A - mu I, mu = trace(A) / ROWS,
+    // from the waves' partial traces in a fixed order)
+    float mu = 0.f;
+    if (shf) {
+      float pt = 0.f;
+#pragma unroll
+      for (int x = 0; x < BTM; ++x)
+#pragma unroll
+        for (int y = 0; y < BTN; ++y)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (BMS * bm + 16 * x + 4 * gq + i == BNS * bn + 16 * y + c) pt += acc[x][y][i];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) pt += __shfl_xor(pt, o);
+      if (lane == 0) red[w] = pt;
+      __syncthreads();
+      float tr = 0.f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) tr += red[x];
+      mu = tr * (1.0f / ROWS);
+      __syncthreads();  // every read of red done before the next step writes it
+#pragma unroll
+      for (int x = 0; x < BTM; ++x)
+#pragma unroll
+        for (int y = 0; y < BTN; ++y)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (BMS * bm + 16 * x + 4 * gq + i == BNS * bn + 16 * y + c) acc[x][y][i] -= mu;
+    }
 #pragma unroll
     for (int x = 0; x < BTM; ++x)
 #pragma unroll
@@ -196,7 +236,9 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
           for (int y = 0; y < BTH; ++y) mma(a2[x][y], fa[x], fb[y]);
       }
       // B = b A + c A A (symmetric): transposed tile, 8-byte stores; b A uses
-      // the bf16 A in LDS (its accumulators are dead by now)
+      // the bf16 A in LDS (its accumulators are dead by now); shifted step:
+      // B_s = (b + 2 c mu) A_s + c A_s A_s
+      const float cbs = cb + 2.f * cc * mu;
 #pragma unroll
       for (int x = 0; x < BTM; ++x)
 #pragma unroll
@@ -205,13 +247,15 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
           const bf16x4 av = *reinterpret_cast<const bf16x4*>(sA + o);
           bf16x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)(cb * (float)av[i] + cc * a2[x][y][i]);
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)(cbs * (float)av[i] + cc * a2[x][y][i]);
           *reinterpret_cast<bf16x4*>(sB + o) = v;
         }
     }
     __syncthreads();
     // ---- 3. X = a X + B X on this wave's columns, one column tile at a
-    // time (columns of B X only depend on the same columns of X) ----
+    // time (columns of B X only depend on the same columns of X); shifted
+    // step: X = (a + b mu + c mu^2) X + B_s X ----
+    const float cas = ca + cb * mu + cc * mu * mu;
     // (opaque to the optimiser: the bf16 copies made for step 1 must not be
     // kept alive until here)
     if constexpr (!XG) {
@@ -254,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void k_ns_fused(NsIn g, float* u, float ep
             mma(xo[rr], ld4x2(br + 4 * gq, br + 16 + 4 * gq), xf[ks]);
           }
 #pragma unroll
-        for (int rr = 0; rr < RH; ++rr) xv[r0 + rr][ct] = ca * xv[r0 + rr][ct] + xo[rr];
+        for (int rr = 0; rr < RH; ++rr) xv[r0 + rr][ct] = cas * xv[r0 + rr][ct] + xo[rr];
         if (last || XG) {
 #pragma unroll
           for (int rr = 0; rr < RH; ++rr)
@@ -441,7 +485,7 @@ __device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const
 // writing U, add it to the weights (ns_step_epilogue).
 template <int COLS, bool STEP>
 __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, float* u, float eps,
-                                              int m, bf16* lds_r, const NsStep& st) {
+                                              int shift_from, int m, bf16* lds_r, const NsStep& st) {
   constexpr int R = 128, NW = 8;
   constexpr int CW = COLS / NW;  // columns per wave
   constexpr int NMT = CW / 16;   // column tiles per wave
@@ -528,22 +572,55 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
 #pragma unroll 1
   for (int it = 0; it < 5; ++it) {
     const float ca = kNsCoef[it][0], cb = kNsCoef[it][1], cc = kNsCoef[it][2];
+    const bool shf = it >= shift_from;
     __syncthreads();  // sX complete; last step's reads of sA done
-    // ---- 1. A = P^2 Y Y^T ----
+    // ---- 1. A = P^2 Y Y^T (shifted step: A - mu I, mu = trace(A) / 128) ----
     // (one instantiation per tile set; the branch is uniform per wave)
-#define LACT_NSR_A(SH)                                                                   \
-  {                                                                                      \
-    const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);                     \
-    f32x4 t[8];                                                                          \
-    nsr_gram<COLS, COLS, SH>(sX, sa, sb, c, gq, t);                                      \
-    const float s2 = P * P;                                                              \
-    _Pragma("unroll") for (int x = 0; x < NsrSet<SH>::NT; ++x) t[x] = t[x] * s2;         \
-    nsr_store<SH>(sA, sa, sb, c, gq, t);                                                 \
-  }
-    if (sh == 0) LACT_NSR_A(0) else if (sh == 1) LACT_NSR_A(1) else LACT_NSR_A(2)
-#undef LACT_NSR_A
+    float mu = 0.f;
+    {
+      const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
+      f32x4 ta[8];
+      if (sh == 0) nsr_gram<COLS, COLS, 0>(sX, sa, sb, c, gq, ta);
+      else if (sh == 1) nsr_gram<COLS, COLS, 1>(sX, sa, sb, c, gq, ta);
+      else nsr_gram<COLS, COLS, 2>(sX, sa, sb, c, gq, ta);
+      const float s2 = P * P;
+#pragma unroll
+      for (int x = 0; x < 5; ++x) ta[x] = ta[x] * s2;
+      if (shf) {
+        // the diagonal tiles: set 0 holds (a, a) and (a+1, a+1) as tiles 0
+        // and 4, set 1 (a+1, a+1) and (a+2, a+2) as tiles 2 and 4; lane
+        // (c, g) holds element i of row 4 g + i, column c of a tile
+        const int x0 = sh == 0 ? 0 : 2;
+        float pt = 0.f;
+        if (sh < 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * gq + i == c) pt += ta[x0][i] + ta[4][i];
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) pt += __shfl_xor(pt, o);
+        // sA is free until the stores below: exchange the four partial traces
+        float* red = reinterpret_cast<float*>(sA);
+        if (lane == 0 && w < 4) red[w] = pt;
+        __syncthreads();
+        mu = ((red[0] + red[1]) + (red[2] + red[3])) * (1.0f / 128.0f);
+        __syncthreads();  // every read of red done before A overwrites it
+        if (sh < 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * gq + i == c) {
+              ta[x0][i] -= mu;
+              ta[4][i] -= mu;
+            }
+        }
+      }
+      if (sh == 0) nsr_store<0>(sA, sa, sb, c, gq, ta);
+      else if (sh == 1) nsr_store<1>(sA, sa, sb, c, gq, ta);
+      else nsr_store<2>(sA, sa, sb, c, gq, ta);
+    }
     __syncthreads();
-    // ---- 2. B' = (b A + c A A) / a, over A ----
+    // ---- 2. B' = (b A + c A A) / a, over A (shifted step: B'_s = ((b +
+    // 2 c mu) A_s + c A_s A_s) / a = B' - (b mu + c mu^2) / a I) ----
     f32x4 t[8];
     if (sh == 0) nsr_gram<128, 128, 0>(sA, sa, sb, nsr_opaque(c), nsr_opaque(gq), t);
     else if (sh == 1) nsr_gram<128, 128, 1>(sA, sa, sb, nsr_opaque(c), nsr_opaque(gq), t);
@@ -552,7 +629,7 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
 #define LACT_NSR_B(SH)                                                                   \
   {                                                                                      \
     const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);                     \
-    const float p = cb / ca, q = cc / ca;                                                \
+    const float p = (cb + 2.f * cc * mu) / ca, q = cc / ca;                              \
     _Pragma("unroll") for (int x = 0; x < NsrSet<SH>::NT; ++x) {                         \
       const int tx = nsr_row<SH>(NsrSet<SH>::TI[x], sa, sb);                             \
       const int ty = nsr_row<SH>(NsrSet<SH>::TJ[x], sa, sb);                             \
@@ -565,7 +642,15 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
     if (sh == 0) LACT_NSR_B(0) else if (sh == 1) LACT_NSR_B(1) else LACT_NSR_B(2)
 #undef LACT_NSR_B
     __syncthreads();  // B' complete
-    // ---- 3. Y <- Y + B' Y on this wave's columns: (Y^T B') tiles ----
+    // ---- 3. Y <- Y + B' Y on this wave's columns: (Y^T B') tiles (shifted
+    // step: Y <- (1 + (b mu + c mu^2) / a) Y + B'_s Y) ----
+    if (shf) {
+      const float f = 1.f + (cb * mu + cc * mu * mu) / ca;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NRT; ++nt) yv[mt][nt] = yv[mt][nt] * f;
+    }
     {
       const int c = nsr_opaque(lane & 15), gq = nsr_opaque(lane >> 4);
 #pragma unroll 1
@@ -618,9 +703,9 @@ __device__ __forceinline__ void ns_r128_block(const NsIn& g, const NsGrad& gr, f
 
 template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_ns_r128(NsIn g, float* u, float eps) {
+void k_ns_r128(NsIn g, float* u, float eps, int shift_from) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds_r[];
-  ns_r128_block<COLS, false>(g, NsGrad{}, u, eps, blockIdx.x, lds_r, NsStep{});
+  ns_r128_block<COLS, false>(g, NsGrad{}, u, eps, shift_from, blockIdx.x, lds_r, NsStep{});
 }
 
 // ---- gradient prologue ----
@@ -769,6 +854,7 @@ __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], fl
         ss += __shfl_xor(ss, 1);
         ss += __shfl_xor(ss, 2);
         ss += __shfl_xor(ss, 4);
+        if (st.nonfinite != nullptr && lk == 0 && !(ss <= 3.402823466e38f)) atomicOr(st.nonfinite, 1);
         const float f = st.renorm ? n0[v] / (sqrtf(ss) + st.eps) : 1.f;
         const int64_t row = (int64_t)(col0 + 32 * p + t) * 128;
 #pragma unroll
@@ -825,6 +911,7 @@ __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], fl
         ss += __shfl_xor(ss, 1);
         ss += __shfl_xor(ss, 2);
         ss += __shfl_xor(ss, 4);
+        if (st.nonfinite != nullptr && lk == 0 && !(ss <= 3.402823466e38f)) atomicOr(st.nonfinite, 1);
         const float f = st.renorm ? n0[v] / (sqrtf(ss) + st.eps) : 1.f;
         const int64_t row = (int64_t)(p0 + r) * COLS;
 #pragma unroll
@@ -858,68 +945,72 @@ __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], fl
 // most compute units idle.
 template <int COLS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_ns_apply(NsGrad gr, float eps, int count, NsStep st, ApplyArgs a) {
+void k_ns_apply(NsGrad gr, float eps, int shift_from, int count, NsStep st, ApplyArgs a) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds_f[];
   const int b = blockIdx.x;
-  if (b < count) ns_r128_block<COLS, true>(NsIn{}, gr, nullptr, eps, b, lds_f, st);
+  if (b < count) ns_r128_block<COLS, true>(NsIn{}, gr, nullptr, eps, shift_from, b, lds_f, st);
   else apply_block<bf16, 128, 32, 8>(a, xcd_logical_id(b - count, (int)gridDim.x - count), lds_f);
 }
 
+// Dynamic LDS of the fused launch: the Newton-Schulz block (X copy + A),
+// the staging of its gradient prologue and step epilogue (8 waves x [32][128]
+// fp32), and the read's tiles - whichever is largest.
 template <int COLS>
-static hipError_t run_ns_apply(int count, const NsGrad& g, float eps, const NsStep& st,
-                               const ApplyArgs& a, hipStream_t s) {
-  const size_t lns = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
-  const size_t lap = (size_t)ApplyLds<bf16, 128>::ELEMS * sizeof(bf16);
-  const size_t lds = lns > lap ? lns : lap;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ns_apply<COLS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+constexpr size_t ns_apply_lds() {
+  constexpr size_t lns = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
+  constexpr size_t lstep = (size_t)8 * 32 * 128 * sizeof(float);
+  constexpr size_t lap = (size_t)ApplyLds<bf16, 128>::ELEMS * sizeof(bf16);
+  constexpr size_t m = lns > lstep ? lns : lstep;
+  return m > lap ? m : lap;
+}
+static_assert(ns_apply_lds<512>() <= 160 * 1024 && ns_apply_lds<256>() <= 160 * 1024, "LDS");
+// the W2 step of the epilogue stages up to 128 rows of COLS fp32
+static_assert((size_t)64 * 512 * 4 <= ns_apply_lds<512>() && (size_t)128 * 256 * 4 <= ns_apply_lds<256>(),
+              "W2 staging");
+
+template <int COLS>
+static hipError_t run_ns_apply(int count, const NsGrad& g, float eps, int shift_from,
+                               const NsStep& st, const ApplyArgs& a, hipStream_t s) {
+  constexpr size_t lds = ns_apply_lds<COLS>();
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_ns_apply<COLS>), (int)lds);
+  if (e != hipSuccess) return e;
   const int64_t napply = a.n_tok > 0 ? (a.n_tok + 255) / 256 * a.bh : 0;
   hipLaunchKernelGGL((k_ns_apply<COLS>), dim3((unsigned)(count + napply)), dim3(512), lds, s, g,
-                     eps, count, st, a);
+                     eps, shift_from, count, st, a);
   return hipGetLastError();
 }
 
 template <int COLS>
-static hipError_t run_ns_r128(int count, NsIn g, float* u, float eps, hipStream_t s) {
+static hipError_t run_ns_r128(int count, NsIn g, float* u, float eps, int shift_from,
+                              hipStream_t s) {
   const size_t lds = (size_t)(128 * COLS + 128 * 128) * sizeof(bf16);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ns_r128<COLS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL((k_ns_r128<COLS>), dim3(count), dim3(512), lds, s, g, u, eps);
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_ns_r128<COLS>), (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_ns_r128<COLS>), dim3(count), dim3(512), lds, s, g, u, eps, shift_from);
   return hipGetLastError();
 }
 
 template <int ROWS, int COLS, int NW, bool XG>
-static hipError_t run_ns_fused(int count, NsIn g, float* u, float eps, hipStream_t s) {
+static hipError_t run_ns_fused(int count, NsIn g, float* u, float eps, int shift_from,
+                               hipStream_t s) {
   const size_t lds = (size_t)ns_lds_elems(ROWS, COLS) * sizeof(bf16);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ns_fused<ROWS, COLS, NW, XG>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL((k_ns_fused<ROWS, COLS, NW, XG>), dim3(count), dim3(NW * 64), lds, s, g, u, eps);
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_ns_fused<ROWS, COLS, NW, XG>),
+                                   (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_ns_fused<ROWS, COLS, NW, XG>), dim3(count), dim3(NW * 64), lds, s, g, u, eps,
+                     shift_from);
   return hipGetLastError();
 }
 
 // Returns hipErrorNotSupported when no fused variant covers the shape.
 hipError_t launch_ns_step_apply(int count, int rows, int cols, const NsGrad& g, float eps,
-                                const NsStep& st, const ApplyArgs& a, hipStream_t s) {
+                                int shift_from, const NsStep& st, const ApplyArgs& a,
+                                hipStream_t s) {
   if (rows != 128 || (a.n_tok > 0 && a.d != 128) || count != 3 * st.bh || g.bh != st.bh ||
       g.nsplit < 1)
     return hipErrorNotSupported;
-  if (cols == 512) return run_ns_apply<512>(count, g, eps, st, a, s);
-  if (cols == 256) return run_ns_apply<256>(count, g, eps, st, a, s);
+  if (cols == 512) return run_ns_apply<512>(count, g, eps, shift_from, st, a, s);
+  if (cols == 256) return run_ns_apply<256>(count, g, eps, shift_from, st, a, s);
   return hipErrorNotSupported;
 }
 
@@ -936,13 +1027,12 @@ hipError_t launch_copy16(void* dst, const void* src, int64_t bytes, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
-                           float eps, hipStream_t s) {
-  if (dtype != 1) return hipErrorNotSupported;
-  if (rows == 128 && cols == 512) return run_ns_r128<512>(count, g, u, eps, s);
-  if (rows == 128 && cols == 256) return run_ns_r128<256>(count, g, u, eps, s);
-  if (rows == 64 && cols == 256) return run_ns_fused<64, 256, 16, false>(count, g, u, eps, s);
-  if (rows == 64 && cols == 512) return run_ns_fused<64, 512, 16, true>(count, g, u, eps, s);
+hipError_t launch_ns_fused(int count, int rows, int cols, NsIn g, float* u, float eps,
+                           int shift_from, hipStream_t s) {
+  if (rows == 128 && cols == 512) return run_ns_r128<512>(count, g, u, eps, shift_from, s);
+  if (rows == 128 && cols == 256) return run_ns_r128<256>(count, g, u, eps, shift_from, s);
+  if (rows == 64 && cols == 256) return run_ns_fused<64, 256, 16, false>(count, g, u, eps, shift_from, s);
+  if (rows == 64 && cols == 512) return run_ns_fused<64, 512, 16, true>(count, g, u, eps, shift_from, s);
   return hipErrorNotSupported;
 }
 

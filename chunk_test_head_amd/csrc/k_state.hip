@@ -179,6 +179,7 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
       }
       ss[k] = w[k][0] * w[k][0] + w[k][1] * w[k][1] + w[k][2] * w[k][2] + w[k][3] * w[k][3];
       for (int o = 1; o < q4; o <<= 1) ss[k] += __shfl_xor(ss[k], o);
+      if (a.nonfinite != nullptr && c4 == 0 && !(ss[k] <= 3.402823466e38f)) atomicOr(a.nonfinite, 1);
     }
   }
   const bool write_w = U != nullptr || a.renorm;
@@ -229,6 +230,7 @@ __device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (a.nonfinite != nullptr && lane == 0 && !(ss <= 3.402823466e38f)) atomicOr(a.nonfinite, 1);
     float f = 1.f;
     if (a.renorm) f = a.n2[(int64_t)head * d + i0 + row] / (sqrtf(ss) + a.eps);
     if (a.init && lane == 0) a.n2[(int64_t)head * d + i0 + row] = sqrtf(ss);  // sequence-start norm
@@ -282,13 +284,9 @@ static hipError_t run_step(const StepArgs& a, hipStream_t s) {
   const size_t l13 = (size_t)32 * (a.d + 1) * sizeof(float);
   const size_t l2 = (size_t)8 * a.dh * sizeof(T);
   const size_t lds = l13 > l2 ? l13 : l2;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step<T, KMAX>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * 4096 * sizeof(T)));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_step<T, KMAX>),
+                                   (int)(8 * 4096 * sizeof(T)));
+  if (e != hipSuccess) return e;
   const int n13 = a.bh * 2 * (a.dh / 32), n2 = a.bh * (a.d / 8);
   hipLaunchKernelGGL((k_step<T, KMAX>), dim3((unsigned)(n13 + n2)), dim3(256), lds, s, a, n13);
   return hipGetLastError();

@@ -1,19 +1,34 @@
 // C ABI of the LaCT fast-weight layer: host-side validation, workspace
 // layout and the chunk sequence driver.  Every entry point checks all of its
-// arguments before it enqueues anything, allocates nothing and never
-// synchronises.
+// arguments before it enqueues anything and allocates no device memory; only
+// lact_check_finite and lact_prof_end wait for the device.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "../../include/lact.h"
 #include "lact_internal.hpp"
-#include <utility>
 
 namespace lact {
+
+hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev}) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
 
 static thread_local int g_last_hip_error = 0;
 
@@ -102,7 +117,9 @@ static lact_status check_act(const lact_shape* sh, const void* p, lact_layout l,
 static lact_status check_opts(const lact_update_opts* o) {
   if (o == nullptr) return LACT_ERR_INVALID_ARG;
   if (!(o->renorm_eps >= 0.f) || !(o->ns_eps >= 0.f)) return LACT_ERR_INVALID_ARG;
-  if (o->ns_fp32 != 0 && o->ns_fp32 != 1) return LACT_ERR_INVALID_ARG;
+  if (o->ns_prec != LACT_NS_BF16_SHIFTED && o->ns_prec != LACT_NS_BF16 && o->ns_prec != LACT_NS_F32)
+    return LACT_ERR_INVALID_ARG;
+  if (o->nonfinite != nullptr && ((uintptr_t)o->nonfinite & 3u) != 0) return LACT_ERR_ALIGNMENT;
   return LACT_OK;
 }
 
@@ -162,6 +179,7 @@ struct Workspace {
   float* xh;
   float* amat;    // [3 bh][d][d]
   float* bmat;
+  float* ssp;     // Newton-Schulz tile sums of squares, 2 x [3 bh][tiles]
   void* shadow2;  // second operand copy of the weights (ns_step_fused shapes)
   int64_t bytes;
 };
@@ -169,9 +187,18 @@ struct Workspace {
 // Shapes whose Newton-Schulz workgroups also take the weight step (and can
 // share their launch with a read, which then needs a second shadow).
 static bool ns_step_fused(const lact_shape* sh, const lact_update_opts* op) {
-  return op != nullptr && op->use_muon && !op->ns_fp32 && sh->dtype == LACT_BF16 && sh->d == 128 &&
-         (sh->dh == 256 || sh->dh == 512);
+  return op != nullptr && op->use_muon && op->ns_prec != LACT_NS_F32 && sh->dtype == LACT_BF16 &&
+         sh->d == 128 && (sh->dh == 256 || sh->dh == 512);
 }
+
+// Precision of a write's Newton-Schulz products: fp32 shapes always use fp32
+// operands.
+static int ns_prec_of(const lact_shape* sh, const lact_update_opts* op) {
+  return sh->dtype == LACT_F32 ? (int)LACT_NS_F32 : op->ns_prec;
+}
+
+// First shifted step (lact_ns_prec): the last three of the five.
+static int ns_shift_from(int prec) { return prec == LACT_NS_BF16_SHIFTED ? 2 : 5; }
 
 static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* base,
                            bool shadow2 = false) {
@@ -195,8 +222,9 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
     w.xh = take((int64_t)3 * sh->bh * msz);
     w.amat = take((int64_t)3 * sh->bh * sh->d * sh->d);
     w.bmat = take((int64_t)3 * sh->bh * sh->d * sh->d);
+    w.ssp = take((int64_t)2 * 3 * sh->bh * (sh->d / 64) * (sh->dh / 64));
   } else {
-    w.xa = w.xb = w.xh = w.amat = w.bmat = nullptr;
+    w.xa = w.xb = w.xh = w.amat = w.bmat = w.ssp = nullptr;
   }
   w.bytes = off;
   return w;
@@ -208,27 +236,33 @@ static const float kNS[5][3] = {
     {2.8769f, -3.1427f, 1.2046f}, {2.8366f, -3.0525f, 1.2012f}};
 
 // Newton-Schulz workspace: X fp32 twice, the bf16 copies of X (two, in one
-// fp32-sized region), A / B bf16 (one region) and A fp32.
+// fp32-sized region), A / B bf16 (one region), A fp32, and the tile sums of
+// squares of X (the shifted steps' mu).
 static int64_t ns_ws_bytes(int count, int rows, int cols) {
   const int64_t m = (int64_t)rows * cols;
-  return 3 * align256((int64_t)count * m * 4) + 2 * align256((int64_t)count * rows * rows * 4);
+  const int64_t tiles = (int64_t)(rows / 64) * (cols / 64);
+  return 3 * align256((int64_t)count * m * 4) + 2 * align256((int64_t)count * rows * rows * 4) +
+         align256(2 * (int64_t)count * tiles * 4);
 }
 
-static hipError_t run_ns(int dtype, int count, int rows, int cols, NsIn g, float* u,
+static hipError_t run_ns(int prec, int count, int rows, int cols, NsIn g, float* u,
                          float eps, float* xa, float* xb, float* xh, float* am, float* bm,
-                         hipStream_t s) {
+                         float* ssp, hipStream_t s) {
   const int64_t m = (int64_t)rows * cols;
-  hipError_t e = launch_ns_fused(dtype, count, rows, cols, g, u, eps, s);
+  const int shift_from = ns_shift_from(prec);
+  hipError_t e = hipErrorNotSupported;
+  if (prec != LACT_NS_F32) e = launch_ns_fused(count, rows, cols, g, u, eps, shift_from, s);
   if (e != hipErrorNotSupported) return e;
-  if (dtype == LACT_BF16) {
+  if (prec != LACT_NS_F32) {
     // X fp32 in xa / xb, its bf16 copy in the two halves of xh; A fp32 in bm,
-    // A and B bf16 in am
+    // A and B bf16 in am; ssp: the tile sums of squares of X_k in half k % 2
     typedef __bf16 bf16;
     bf16* xh0 = reinterpret_cast<bf16*>(xh);
     bf16* xh1 = xh0 + (int64_t)count * m;
     bf16* ah = reinterpret_cast<bf16*>(am);
     bf16* bh = ah + (int64_t)count * rows * rows;
     const int64_t rr = (int64_t)rows * rows;
+    const int tiles = (rows / 64) * (cols / 64);
     if ((e = launch_nsn(g, bm, xa, xh0, count, m, eps, s)) != hipSuccess) return e;
     float* x = xa;
     float* y = xb;
@@ -236,16 +270,26 @@ static hipError_t run_ns(int dtype, int count, int rows, int cols, NsIn g, float
     bf16* yc = xh1;
     for (int it = 0; it < 5; ++it) {
       const float ca = kNS[it][0], cb = kNS[it][1], cc = kNS[it][2];
+      // shifted step (mu = ||X||_F^2 / rows = trace(A) / rows from the tile
+      // sums the previous step left): A_s = A - mu I, B_s = c A_s A_s +
+      // (b + 2 c mu) A_s = B - (b mu + c mu^2) I, X' = B_s X + (a + b mu +
+      // c mu^2) X - the same step in exact arithmetic
+      const bool shf = it >= shift_from;
+      const float* mp = shf ? ssp + (int64_t)(it & 1) * count * tiles : nullptr;
       // A = X X^T (fp32 for the b A term, bf16 operand)
-      NsGemmArgs ga{xc, m, cols, xc, m, cols, nullptr, 0, bm, ah, rr, rows, rows, cols, 1.f, 0.f};
+      NsGemmArgs ga{xc, m, cols, xc, m, cols, nullptr, 0, bm, ah, rr, rows, rows, cols, 1.f, 0.f,
+                    mp, tiles, (float)rows, 0.f, 0.f, -1.f, nullptr};
       if ((e = launch_nsgemm(false, ga, count, s)) != hipSuccess) return e;
       // B = c A A + b A (A symmetric: its rows are the B operand)
-      NsGemmArgs gb{ah, rr, rows, ah, rr, rows, bm, rr, nullptr, bh, rr, rows, rows, rows, cc, cb};
+      NsGemmArgs gb{ah, rr, rows, ah, rr, rows, bm, rr, nullptr, bh, rr, rows, rows, rows, cc, cb,
+                    mp, tiles, (float)rows, 2.f * cc, 0.f, 0.f, nullptr};
       if ((e = launch_nsgemm(false, gb, count, s)) != hipSuccess) return e;
-      // X' = B X + a X
+      // X' = B X + a X (and its tile sums of squares for a shifted next step)
       const bool last = it == 4;
       NsGemmArgs gx{bh, rr, rows, xc, m, cols, x, m, last ? u : y, last ? nullptr : yc, m,
-                    rows, cols, rows, 1.f, ca};
+                    rows, cols, rows, 1.f, ca, mp, tiles, (float)rows, cb, cc, 0.f,
+                    (!last && it + 1 >= shift_from) ? ssp + (int64_t)((it + 1) & 1) * count * tiles
+                                                    : nullptr};
       if ((e = launch_nsgemm(true, gx, count, s)) != hipSuccess) return e;
       std::swap(x, y);
       std::swap(xc, yc);
@@ -261,15 +305,15 @@ static hipError_t run_ns(int dtype, int count, int rows, int cols, NsIn g, float
     const float ca = kNS[it][0], cb = kNS[it][1], cc = kNS[it][2];
     // A = X X^T
     GemmArgs ga{x, m, x, m, 0, nullptr, 0, am, (int64_t)rows * rows, rows, rows, cols, count, 1.f, 0.f};
-    if ((e = launch_gemm(dtype, ga, s)) != hipSuccess) return e;
+    if ((e = launch_gemm(LACT_F32, ga, s)) != hipSuccess) return e;
     // B = c A A + b A
     GemmArgs gb{am, (int64_t)rows * rows, am, (int64_t)rows * rows, 1, am, (int64_t)rows * rows,
                 bm, (int64_t)rows * rows, rows, rows, rows, count, cc, cb};
-    if ((e = launch_gemm(dtype, gb, s)) != hipSuccess) return e;
+    if ((e = launch_gemm(LACT_F32, gb, s)) != hipSuccess) return e;
     // X' = B X + a X
     float* out = (it == 4) ? u : y;
     GemmArgs gx{bm, (int64_t)rows * rows, x, m, 1, x, m, out, m, rows, cols, rows, count, 1.f, ca};
-    if ((e = launch_gemm(dtype, gx, s)) != hipSuccess) return e;
+    if ((e = launch_gemm(LACT_F32, gx, s)) != hipSuccess) return e;
     float* t = x;
     x = y;
     y = t;
@@ -353,7 +397,7 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
 
 static lact_status do_step(const lact_shape* sh, const lact_state* st, const float* u1,
                            const float* u3, const float* u2, int renorm, float eps,
-                           void* shadow_out, hipStream_t s) {
+                           int* nonfinite, void* shadow_out, hipStream_t s) {
   StepArgs a;
   memset(&a, 0, sizeof(a));
   a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
@@ -362,6 +406,7 @@ static lact_status do_step(const lact_shape* sh, const lact_state* st, const flo
   a.sh = make_shadow(shadow_out, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
   a.renorm = renorm; a.eps = eps;
+  a.nonfinite = nonfinite;
   hipError_t e;
   {
     ProfScope p(LACT_PROF_STEP, s);
@@ -420,18 +465,20 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
       }
       const NsStep ns{st->w1, st->w3, st->w2, st->n1, st->n3, st->n2,
                       make_shadow(shadow_out, sh->d, sh->dh), sh->bh, op->renorm ? 1 : 0,
-                      op->renorm_eps};
+                      op->renorm_eps, op->nonfinite};
       const NsGrad gr{w.partial, nsplit, sh->bh,
                       {mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr}};
-      e = launch_ns_step_apply(3 * sh->bh, sh->d, sh->dh, gr, op->ns_eps, ns, aa, s);
+      e = launch_ns_step_apply(3 * sh->bh, sh->d, sh->dh, gr, op->ns_eps,
+                               ns_shift_from(ns_prec_of(sh, op)), ns, aa, s);
       return e == hipSuccess ? LACT_OK : hip_fail(e);
     }
-    e = run_ns(op->ns_fp32 ? LACT_F32 : sh->dtype, 3 * sh->bh, sh->d, sh->dh, in, w.g,
-               op->ns_eps, w.xa, w.xb, w.xh, w.amat, w.bmat, s);
+    e = run_ns(ns_prec_of(sh, op), 3 * sh->bh, sh->d, sh->dh, in, w.g, op->ns_eps, w.xa, w.xb,
+               w.xh, w.amat, w.bmat, w.ssp, s);
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
   }
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, shadow_out, s);
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, op->nonfinite, shadow_out,
+                 s);
 }
 
 static lact_status check_update_args(const lact_shape* sh, const lact_state* st, const void* k,
@@ -540,11 +587,12 @@ lact_status lact_gradient(const lact_shape* sh, const lact_state* st, const void
                  nullptr, nullptr, nullptr, (hipStream_t)stream);
 }
 
-lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_t dtype,
+lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_t prec,
                                const float* g, float* u, float eps, void* ws, size_t ws_bytes,
                                void* stream) {
   if (count < 1 || rows < 1 || cols < 1 || g == nullptr || u == nullptr) return LACT_ERR_INVALID_ARG;
-  if (dtype != LACT_F32 && dtype != LACT_BF16) return LACT_ERR_INVALID_ARG;
+  if (prec != LACT_NS_BF16_SHIFTED && prec != LACT_NS_BF16 && prec != LACT_NS_F32)
+    return LACT_ERR_INVALID_ARG;
   if (!(eps >= 0.f)) return LACT_ERR_INVALID_ARG;
   if (rows % 64 != 0 || cols % 64 != 0 || rows > cols) return LACT_ERR_UNSUPPORTED;
   if (!aligned16(g) || !aligned16(u)) return LACT_ERR_ALIGNMENT;
@@ -558,8 +606,10 @@ lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols, int32_
   float* xh = reinterpret_cast<float*>(b + 2 * xm);
   float* a_ = reinterpret_cast<float*>(b + 3 * xm);
   float* b_ = reinterpret_cast<float*>(b + 3 * xm + am);
+  float* ssp = reinterpret_cast<float*>(b + 3 * xm + 2 * am);
   const NsIn in{{g, g, g}, count};
-  hipError_t e = run_ns(dtype, count, rows, cols, in, u, eps, xa, xb, xh, a_, b_, (hipStream_t)stream);
+  hipError_t e = run_ns(prec, count, rows, cols, in, u, eps, xa, xb, xh, a_, b_, ssp,
+                        (hipStream_t)stream);
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
@@ -576,7 +626,7 @@ lact_status lact_step_renorm(const lact_shape* sh, const lact_state* st, const f
   }
   if (ws == nullptr || ws_bytes < lact_workspace_bytes(sh, 0, op)) return LACT_ERR_WORKSPACE;
   if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, st->shadow,
+  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, op->nonfinite, st->shadow,
                  (hipStream_t)stream);
 }
 
@@ -756,10 +806,22 @@ const char* lact_status_string(lact_status st) {
     case LACT_ERR_ALIGNMENT: return "pointer or stride not 16-byte aligned";
     case LACT_ERR_WORKSPACE: return "workspace missing or too small";
     case LACT_ERR_HIP: return "HIP error";
+    case LACT_ERR_NONFINITE: return "a write produced non-finite weights";
   }
   return "unknown status";
 }
 
 int lact_last_hip_error(void) { return g_last_hip_error; }
+
+lact_status lact_check_finite(const int32_t* flag, void* stream) {
+  if (flag == nullptr) return LACT_ERR_INVALID_ARG;
+  if (((uintptr_t)flag & 3u) != 0) return LACT_ERR_ALIGNMENT;
+  int32_t h = 0;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  return h != 0 ? LACT_ERR_NONFINITE : LACT_OK;
+}
 
 }  // extern "C"

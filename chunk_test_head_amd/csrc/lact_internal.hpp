@@ -72,6 +72,14 @@ struct NsGemmArgs {
   float* C; __bf16* Ch; int64_t c_bs;
   int M, N, K;
   float alpha, beta;
+  // Shifted Newton-Schulz steps: mu = (sum of mu_part[batch][0 .. mu_np)) /
+  // mu_div (0 when mu_part is NULL); the D coefficient is then beta +
+  // beta_mu mu + beta_mu2 mu^2 and diag_mu mu is added to the diagonal.
+  const float* mu_part; int mu_np; float mu_div;
+  float beta_mu, beta_mu2, diag_mu;
+  // NULL, or [batch][tiles]: sum of squares of each 64 x 64 tile of the fp32
+  // result, in tile order (the next step's mu)
+  float* ss_part;
 };
 
 // Input matrices of a Newton-Schulz batch: matrix m is p[m / per] +
@@ -102,15 +110,23 @@ struct StepArgs {
   // written to n1, n3, n2 and the momentum buffers (non-NULL ones) zeroed
   int init;
   float* mz1; float* mz3; float* mz2;
+  int* nonfinite;  // NULL, or set to 1 when a row's sum of squares is not finite
 };
+
+// Raises a kernel's dynamic LDS limit to `bytes`, once per (kernel, device);
+// safe to call from several threads.
+hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
 hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
 int grad_hidden_per_block(int dtype, int d);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ns_fused(int dtype, int count, int rows, int cols, NsIn g, float* u,
-                           float eps, hipStream_t s);
+// Newton-Schulz in one workgroup per matrix (bf16 operands; steps from
+// shift_from on are shifted, see k_ns.hip); hipErrorNotSupported for shapes
+// without such a kernel.
+hipError_t launch_ns_fused(int count, int rows, int cols, NsIn g, float* u, float eps,
+                           int shift_from, hipStream_t s);
 // Weight step done by the Newton-Schulz workgroups themselves: matrix
 // m = mat * bh + head (mat 0: W1, 1: W3, 2: W2) adds its result U (wide
 // orientation) to W, rescales the rows (renorm) and writes the operand copies
@@ -122,6 +138,7 @@ struct NsStep {
   int bh;
   int renorm;
   float eps;
+  int* nonfinite;  // NULL, or set to 1 when a row's sum of squares is not finite
 };
 // Input of a Newton-Schulz launch that also finishes the gradient: matrix
 // m = mat * bh + head starts from G = the sum over splits s (in split order)
@@ -136,7 +153,8 @@ struct NsGrad {
 // columns), with the tiles of a d = 128 bf16 read (a.n_tok > 0) in the same
 // launch; hipErrorNotSupported for other shapes.
 hipError_t launch_ns_step_apply(int count, int rows, int cols, const NsGrad& gr, float eps,
-                                const NsStep& st, const ApplyArgs& a, hipStream_t s);
+                                int shift_from, const NsStep& st, const ApplyArgs& a,
+                                hipStream_t s);
 // Device copy of `bytes` (a multiple of 16, 16-byte aligned pointers).
 hipError_t launch_copy16(void* dst, const void* src, int64_t bytes, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);

@@ -10,13 +10,19 @@
  *
  * Conventions shared by every call:
  *  - All pointers are DEVICE pointers unless stated otherwise.  The caller
- *    owns every buffer; the library allocates nothing and keeps no state
- *    between calls.
+ *    owns every buffer; the library allocates no device memory and keeps no
+ *    device state between calls.  Its only process-wide host state is the
+ *    kernel-timing window (lact_prof_begin / lact_prof_end) and a record of
+ *    which kernels have had their LDS limit raised on which device.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream) and never synchronises.  Argument checks run on the host before
- *    anything is enqueued: on any error nothing is enqueued and the state is
- *    untouched.  A HIP launch error returns LACT_ERR_HIP and
- *    lact_last_hip_error() gives the hipError_t.
+ *    stream) and never synchronises, except lact_check_finite and
+ *    lact_prof_end, which exist to wait.  Argument checks run on the host
+ *    before anything is enqueued: on an argument error nothing is enqueued
+ *    and the state is untouched.
+ *  - A HIP launch error returns LACT_ERR_HIP and lact_last_hip_error() gives
+ *    the hipError_t.  A call that enqueues several kernels (a write, a chunk
+ *    step, a sequence) may fail after some of them were enqueued: the state
+ *    is then partly updated and must be re-initialised.
  *  - Activations (q, k, v, o) are element arrays with the head dim contiguous;
  *    token t of head b starts at element  b * stride_bh + t * stride_tok.
  *    Both [BH, T, d] and [B, T, H, d] layouts are expressible.  Their element
@@ -46,7 +52,9 @@ typedef enum {
   LACT_ERR_UNSUPPORTED = 2,  /* shape outside the supported set            */
   LACT_ERR_ALIGNMENT = 3,    /* pointer or stride not 16-byte aligned      */
   LACT_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required    */
-  LACT_ERR_HIP = 5           /* a HIP call failed (see lact_last_hip_error) */
+  LACT_ERR_HIP = 5,          /* a HIP call failed (see lact_last_hip_error) */
+  LACT_ERR_NONFINITE = 6     /* lact_check_finite: a write produced a
+                                weight row that is NaN or infinite          */
 } lact_status;
 
 typedef enum { LACT_F32 = 0, LACT_BF16 = 1 } lact_dtype;
@@ -85,15 +93,33 @@ typedef struct {
   int64_t stride_tok;  /* elements between consecutive tokens    */
 } lact_layout;
 
+/* Precision of the Newton-Schulz products for bf16 shapes (fp32 shapes
+ * always use fp32 operands).  In every mode the iterate X stays fp32
+ * between the five steps and every product accumulates in fp32.
+ *  LACT_NS_BF16_SHIFTED (default): bf16 operands; the last three steps,
+ *    where A = X X^T is near the identity, store A - I and form
+ *    B - (b + c) I from it, and take X <- (a + b + c) X + (B - (b + c) I) X.
+ *    The same polynomial in exact arithmetic; the identity parts stay in
+ *    fp32, so the rounded operands are small and the step is about as
+ *    accurate as fp32 operands at the cost of bf16 ones.
+ *  LACT_NS_BF16: bf16 operands in every step, as the rebuttal page's
+ *    zeropower_via_newtonschulz5 (which casts the iterate to bf16).
+ *  LACT_NS_F32: fp32 operands (fp32 MFMA; slow, for reference runs).     */
+typedef enum { LACT_NS_BF16_SHIFTED = 0, LACT_NS_BF16 = 1, LACT_NS_F32 = 2 } lact_ns_prec;
+
 typedef struct {
   int32_t use_muon;      /* orthogonalise the step with Newton-Schulz-5      */
   int32_t use_momentum;  /* G <- G + beta M, M <- G (beta = mean coefficient) */
   int32_t renorm;        /* rescale rows to their sequence-start norms       */
   float renorm_eps;      /* added to the row norm (page: 1e-5)               */
   float ns_eps;          /* added to the Frobenius norm (page: 1e-7)         */
-  int32_t ns_fp32;       /* 0: Newton-Schulz products on bf16 operands, as
-                            the page (X stays fp32 between steps);
-                            1: fp32 operands (slower, for precision)         */
+  int32_t ns_prec;       /* lact_ns_prec                                     */
+  int32_t* nonfinite;    /* NULL, or a device int32 that the caller zeroes:
+                            every write then ORs 1 into it when a row of the
+                            new weights has a sum of squares that is not a
+                            finite fp32 number (NaN or Inf anywhere in the
+                            row).  Nothing waits for it; read it with
+                            lact_check_finite or a copy of your own.       */
 } lact_update_opts;
 
 /* Bytes of lact_state.shadow for this shape. */
@@ -131,15 +157,15 @@ lact_status lact_gradient(const lact_shape* shape, const lact_state* state,
                           float* g1, float* g3, float* g2,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Newton-Schulz-5 on `count` matrices [rows, cols] (rows <= cols), fp32 in,
- * fp32 out (in == out allowed): X = G / (||G||_F + eps), then five quintic
- * steps A = X X^T, B = b A + c A A, X = a X + B X with the page's
- * coefficients.  MFMA operands are rounded to `dtype` (bf16, as the page
- * does; or fp32).  (Rebuttal page, zeropower_via_newtonschulz5; summary page
- * section 3.2, Eq. 9-10.)  Workspace: lact_ns_workspace_bytes(). */
+/* Newton-Schulz-5 on `count` matrices [rows, cols] (rows <= cols, both
+ * multiples of 64), fp32 in, fp32 out (in == out allowed): X = G /
+ * (||G||_F + eps), then five quintic steps A = X X^T, B = b A + c A A,
+ * X = a X + B X with the page's coefficients.  `prec` is a lact_ns_prec.
+ * (Rebuttal page, zeropower_via_newtonschulz5; summary page section 3.2,
+ * Eq. 9-10.)  Workspace: lact_ns_workspace_bytes(). */
 size_t lact_ns_workspace_bytes(int32_t count, int32_t rows, int32_t cols);
 lact_status lact_newton_schulz(int32_t count, int32_t rows, int32_t cols,
-                               int32_t dtype, const float* g, float* u, float eps,
+                               int32_t prec, const float* g, float* u, float eps,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -153,9 +179,13 @@ lact_status lact_step_renorm(const lact_shape* shape, const lact_state* state,
                              const lact_update_opts* opts,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* One write on n_tok tokens: gradient -> momentum (beta = mean of mom over
- * the n_tok tokens; mom may be NULL when momentum is off) -> Newton-Schulz
- * -> step + renorm.  State updated in place.  n_tok = 0 writes nothing. */
+/* One write on n_tok tokens, as the body of the chunk loop of the rebuttal
+ * page's block_causal_lact_swiglu after its read: chunk gradient ->
+ * momentum (beta = mean of mom over the n_tok tokens; mom may be NULL when
+ * momentum is off; the buffer keeps the pre-Newton-Schulz sum) ->
+ * Newton-Schulz -> W <- W + step -> row renorm to the sequence-start norms
+ * (summary page section 3.2, Eq. 4-5, 8-10).  State updated in place.
+ * n_tok = 0 writes nothing. */
 lact_status lact_update(const lact_shape* shape, const lact_state* state,
                         const void* k, lact_layout k_layout,
                         const void* v, lact_layout v_layout,
@@ -164,7 +194,11 @@ lact_status lact_update(const lact_shape* shape, const lact_state* state,
                         const lact_update_opts* opts,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* One causal chunk: read q with W_c into o, then write (k, v) -> W_{c+1}. */
+/* One causal chunk, one iteration of the chunk loop of the rebuttal page's
+ * block_causal_lact_swiglu (apply then update, summary page section 3.1 /
+ * Fig. 3): read q with W_c into o, then write (k, v) -> W_{c+1} as
+ * lact_update.  The read may run inside the write's Newton-Schulz launch
+ * (it only needs W_c). */
 lact_status lact_chunk_step(const lact_shape* shape, const lact_state* state,
                             const void* q, lact_layout q_layout,
                             const void* k, lact_layout k_layout,
@@ -176,7 +210,11 @@ lact_status lact_chunk_step(const lact_shape* shape, const lact_state* state,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Whole sequence of T tokens in chunks of `chunk` (the last may be short),
- * starting at token 0 of every array:
+ * starting at token 0 of every array: the update/apply orderings of the
+ * summary page (section 3.1, Fig. 3) as the rebuttal page's two functions
+ * run them (block_causal_lact_swiglu: chunks starting before T - chunk are
+ * read then written, the rest read only; bidirectional_lact_swiglu: one
+ * write, then the read):
  *  - APPLY_THEN_UPDATE: each chunk is read with the current weights and then
  *    written; the chunk that ends at T is read only unless update_last.
  *  - UPDATE_THEN_APPLY: each chunk is written, then read.
@@ -210,6 +248,11 @@ enum { LACT_PROF_APPLY = 1, LACT_PROF_GRAD = 2, LACT_PROF_REDUCE = 3, LACT_PROF_
        LACT_PROF_STEP = 5 };
 lact_status lact_prof_begin(int32_t kind, int32_t max_launches);
 lact_status lact_prof_end(int32_t* launches, float* total_ms, float* min_ms, float* max_ms);
+
+/* Waits for `stream`, then returns LACT_ERR_NONFINITE if the device int32
+ * `flag` (lact_update_opts.nonfinite) is non-zero, else LACT_OK.  The flag
+ * is left as it is. */
+lact_status lact_check_finite(const int32_t* flag, void* stream);
 
 const char* lact_status_string(lact_status status);
 

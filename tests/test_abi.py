@@ -22,8 +22,26 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.lact_status_string(s)
+    assert lib.lact_status_string(6) != lib.lact_status_string(99)
+
+
+def test_opts_and_finite_checks(lib):
+    """Bad Newton-Schulz precision and a misaligned non-finite flag are
+    rejected before anything is enqueued; lact_check_finite rejects a NULL or
+    misaligned flag without touching the device."""
+    sh = _shape()
+    st = L.State(*([256] * 10))
+    lay = L.Layout(512 * 128, 128)
+    for prec, flag, code in ((3, None, 1), (-1, None, 1), (L.NS_F32, 1026, 3)):
+        o = L.opts(use_muon=True, ns_prec=prec, nonfinite=flag)
+        need = 1 << 30
+        assert lib.lact_update(ctypes.byref(sh), ctypes.byref(st), 256, lay, 512, lay, 1024, 1024, 1024,
+                               None, 100, 100, ctypes.byref(o), 4096, need, None) == code
+    assert lib.lact_check_finite(None, None) == 1
+    assert lib.lact_check_finite(1026, None) == 3
+    assert lib.lact_newton_schulz(1, 128, 512, 7, 256, 256, 1e-7, 256, 1 << 30, None) == 1
 
 
 def _shape(bh=2, d=128, dh=512, dtype=L.BF16):
@@ -60,9 +78,15 @@ def test_null_and_alignment(lib):
     assert lib.lact_apply(ctypes.byref(sh), ctypes.byref(bad), 256, lay, 512, lay, 10, None) == 1
     # misaligned activation
     assert lib.lact_apply(ctypes.byref(sh), ctypes.byref(st), 258, lay, 512, lay, 10, None) == 3
-    # misaligned token stride (127 bf16 = 254 bytes)
+    # token stride shorter than a token
     assert lib.lact_apply(ctypes.byref(sh), ctypes.byref(st), 256, L.Layout(512 * 128, 127), 512,
                           lay, 10, None) == 1
+    # token stride long enough but not a multiple of 16 bytes (132 bf16 = 264 bytes)
+    assert lib.lact_apply(ctypes.byref(sh), ctypes.byref(st), 256, L.Layout(512 * 132, 132), 512,
+                          lay, 10, None) == 3
+    # head stride not a multiple of 16 bytes
+    assert lib.lact_apply(ctypes.byref(sh), ctypes.byref(st), 256, L.Layout(512 * 128 + 4, 128), 512,
+                          lay, 10, None) == 3
     # o aliasing q
     assert lib.lact_apply(ctypes.byref(sh), ctypes.byref(st), 256, lay, 256, lay, 10, None) == 1
     # negative token count
