@@ -4,9 +4,12 @@
 One step = one whole sequence of the workload through lact_sequence (every
 chunk read, every chunk but the last written with momentum, Muon, step and
 row renorm), starting from the initial fast weights, inputs already resident
-in HBM.  Prints one JSON line.
+in HBM.  The headline workload is the largest one that fits one GPU
+(long-context: 1,048,576 tokens, 4 heads, d 256, dh 1024); the other bf16
+workloads are timed the same way and reported beside it.  Prints one JSON
+line.
 
-  python bench.py [--steps K] [--warmup W] [--workload lm-causal] [--gpus 1]
+  python bench.py [--steps K] [--warmup W] [--workload long-context] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -28,10 +31,14 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="lm-causal")
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="long-context")
+    p.add_argument("--ns-prec", default="bf16-shifted", choices=["bf16-shifted", "bf16", "f32"],
+                   help="Newton-Schulz operand precision")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=32, help="heads of the oracle sample (10-30 s of host work)")
+    p.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="host time budget of the oracle sample (about 10-30 s)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES (counter calibration)")
     return p.parse_args()
@@ -50,7 +57,7 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def measured_traffic(kernel_src, workload):
+def measured_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed counter
     profile (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when the
     profile is for another workload or the kernel source changed since."""
@@ -67,50 +74,83 @@ def measured_traffic(kernel_src, workload):
         return None
 
 
-def cpu_baseline(w, W, inp, heads):
-    """The float64 oracle as it stands, on the host cores, on `heads` of the
-    workload's heads over the whole sequence; scaled to all heads."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, W, inp, budget_s):
+    """The float64 oracle as it stands, on the host cores: head 0 of the
+    workload, chunk by chunk from the start of the sequence (the oracle's
+    own state carried from chunk to chunk), until about `budget_s` seconds of
+    host time are spent; scaled to the whole workload by the number of
+    (head, chunk) steps."""
     import threadpoolctl
     from oracle import lact_oracle as O
-    heads = min(heads, w.bh)
+    from chunk_test_head_amd import workloads as WL
+    bounds = w.chunk_bounds()
+    b = 0
+    st = O.HeadState(W[0][b], W[1][b], W[2][b])
+    e = inp["eta"][b]
+    m = None if inp["mom"] is None else inp["mom"][b]
     t0 = time.perf_counter()
-    for b in range(heads):
-        e = inp["eta"][b]
-        m = None if inp["mom"] is None else inp["mom"][b]
-        O.sequence(W[0][b], W[1][b], W[2][b], inp["q"][b], inp["k"][b], inp["v"][b], e, e, e, w.chunk,
-                   mom=m, order=w.order, subset=w.subset, update_last=w.update_last,
-                   use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+    done = 0
+    for ci, (s0, e0) in enumerate(bounds):
+        kw = dict(mom=None if m is None else m[s0:e0], order=w.order, subset=w.subset,
+                  update_last=w.update_last or ci < len(bounds) - 1, use_muon=w.use_muon,
+                  use_momentum=w.use_momentum, renorm=w.renorm, state=st)
+        _, st = O.sequence(W[0][b], W[1][b], W[2][b], WL.token_values(inp, "q", b, s0, e0),
+                           WL.token_values(inp, "k", b, s0, e0), WL.token_values(inp, "v", b, s0, e0),
+                           e[s0:e0], e[s0:e0], e[s0:e0], w.chunk, **kw)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
     dt = time.perf_counter() - t0
-    full = dt * w.bh / heads
+    full = dt * w.bh * len(bounds) / done
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     return {
         "value": w.batch * w.T / full,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{heads} of {w.bh} (batch, head) states over the whole {w.T}-token sequence, "
-                  f"{dt:.1f} s, scaled by {w.bh}/{heads}; numpy float64, BLAS threads={threads}",
+        "sample": f"head 0 of {w.bh}, the first {done} of {len(bounds)} chunks of the {w.T}-token "
+                  f"sequence, {dt:.1f} s, scaled by {w.bh} x {len(bounds)} / {done} (head, chunk) steps; "
+                  f"numpy float64 with {threads} BLAS threads on a host with {os.cpu_count()} logical "
+                  f"CPUs ({cpu_model()})",
+        "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        sys.exit(2)
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
+# The pages' own throughput figures for this layer, with their hardware
+# (context only: another machine, whole-layer or whole-model numbers).
+PAGE_CONTEXT = {
+    "ttt_layer_flops_utilization": "about 70% of peak on an NVIDIA A100 with large chunks in plain "
+                                   "PyTorch (summary page, section 1, Fig. 1a)",
+    "lm_training_tokens_per_s": "4.3K and 5.0K tokens/s for the Muon LM variant and its comparison model, "
+                                "A100-40GB training runs (summary page, section 5.2, Table 3)",
+}
+
+
+def time_workload(w, steps, warmup, ns_prec, profile, values=False):
+    """Times `steps` whole sequences of workload w (after `warmup`); with
+    profile, also the mean launch time of the gradient kernel over the writes
+    of the first timed sequence.  Returns a dict (and the inputs)."""
     import numpy as np
     import torch
 
     from chunk_test_head_amd import _lib as L
     from chunk_test_head_amd import workloads as WL
 
-    w = WL.get(args.workload)
     dev = torch.device("cuda:0")
     W = WL.weights(w)
-    inp = WL.tokens(w, threads=16)
+    inp = WL.tokens(w, threads=16, values=values or w.dtype != "bf16")
     bf = w.dtype == "bf16"
 
     def up(name):
@@ -125,7 +165,7 @@ def main():
     shape = L.Shape(w.bh, w.d, w.dh, L.BF16 if bf else L.F32)
     W0 = [torch.from_numpy(x).to(dev) for x in W]
     fw = L.FastWeights(shape, *W0, momentum=w.use_momentum)
-    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm, ns_prec=ns_prec)
     writes = w.writes()
     max_upd = max((z - a for _, a, z in writes), default=0)
     ws = torch.empty(L.workspace_bytes(shape, max_upd, o), dtype=torch.uint8, device=dev)
@@ -140,43 +180,72 @@ def main():
         L.lact_sequence(shape, fw, q, k, v, out, eta, eta, eta, mom, w.T, w.chunk, w.order, w.subset,
                         int(w.update_last), o, ws, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region; the dominant kernel (k_grad) is bracketed by HIP events on
-    # the same stream to give its average launch duration.  Only the launches
-    # of the first timed step are bracketed: each event record costs a few us
-    # of queue bubble, which would otherwise be charged to every step.
+    # timed region; the dominant kernel (the gradient launch) is bracketed by
+    # HIP events on the same stream to give its average launch duration.
+    # Only the launches of the first timed step are bracketed: each event
+    # record costs a few us of queue bubble, which would otherwise be charged
+    # to every step.
     n_grad = len(writes)
-    L.lact_prof_begin(L.PROF_GRAD, max(1, n_grad))
+    if profile:
+        L.lact_prof_begin(L.PROF_GRAD, max(1, n_grad))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launches, grad_ms, grad_min, grad_max = L.lact_prof_end()
     gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-
-    tokens = w.batch * w.T
+    ms_per_step = max(gpu_ms, wall * 1e3) / steps
     flops = WL.algorithmic_flops(w)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS if bf else F32_PEAK_TFLOPS
+    res = {"ms_per_step": ms_per_step, "tokens_per_s": w.batch * w.T / (ms_per_step * 1e-3),
+           "tflops_algorithmic": tflops, "pct_of_peak": 100.0 * tflops / peak,
+           "tflops_page_convention": WL.page_convention_flops(w) / (ms_per_step * 1e-3) / 1e12,
+           "peak": peak, "max_upd": max_upd}
+    if profile:
+        launches, grad_ms, grad_min, grad_max = L.lact_prof_end()
+        res.update(launches=launches, grad_ms=grad_ms, grad_min=grad_min, grad_max=grad_max)
+    del fw, q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res, W, inp
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only (one process, one device); "
+                                   "--gpus must be 1"}))
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    from chunk_test_head_amd import _lib as L
+    from chunk_test_head_amd import workloads as WL
+
+    prec = {"bf16-shifted": L.NS_BF16_SHIFTED, "bf16": L.NS_BF16, "f32": L.NS_F32}[args.ns_prec]
+    w = WL.get(args.workload)
+    bf = w.dtype == "bf16"
+    r, W, inp = time_workload(w, args.steps, args.warmup, prec, profile=True)
+    ms_per_step = r["ms_per_step"]
+    peak = r["peak"]
 
     # roofline of the dominant kernel: 12 d dh flops per written token
     # (forward on keys 6 d dh + gradient contractions 6 d dh), bh heads
-    n_written = max_upd
-    grad_flops = 12.0 * w.d * w.dh * n_written * w.bh
-    grad_avg_ms = grad_ms / max(1, launches)
+    grad_flops = 12.0 * w.d * w.dh * r["max_upd"] * w.bh
+    launches = r["launches"]
+    grad_avg_ms = r["grad_ms"] / max(1, launches)
     achieved = grad_flops / (grad_avg_ms * 1e-3) / 1e12
     line = {
         "metric": "fast-weight chunk-step tokens/s (LaCT SwiGLU layer, whole sequence)",
-        "value": tokens / (ms_per_step * 1e-3),
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -190,19 +259,32 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "d": w.d, "dh": w.dh,
                    "T": w.T, "chunk": w.chunk, "muon": w.use_muon,
                    "momentum": w.momentum if w.use_momentum else None, "renorm": w.renorm,
-                   "subset": list(w.subset) if w.subset else None},
-        "tflops_algorithmic": tflops,
-        "pct_of_peak": 100.0 * tflops / peak,
-        "tflops_page_convention": WL.page_convention_flops(w) / (ms_per_step * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "k_grad", "achieved": achieved, "peak": peak,
+                   "subset": list(w.subset) if w.subset else None,
+                   "ns_prec": args.ns_prec if w.use_muon else None},
+        "tflops_algorithmic": r["tflops_algorithmic"],
+        "pct_of_peak": r["pct_of_peak"],
+        "tflops_page_convention": r["tflops_page_convention"],
+        "roofline": {"bound": "mfma",
+                     "kernel": "k_grad" if not bf else ("k_grad_solo" if w.d == 256 else "k_grad_bf16"),
+                     "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic("k_mlp.hip", w.name),
-                     "launch_ms_avg": grad_avg_ms, "launch_ms_min": grad_min,
-                     "launch_ms_max": grad_max, "launches": launches,
+                     "traffic": measured_traffic(w.name),
+                     "launch_ms_avg": grad_avg_ms, "launch_ms_min": r["grad_min"],
+                     "launch_ms_max": r["grad_max"], "launches": launches,
                      "flops_per_launch": grad_flops},
+        "page_context": PAGE_CONTEXT,
     }
+    if not args.no_others:
+        others = {}
+        for name in ("lm-causal", "nvs-bidirectional", "ar-video", "long-context"):
+            if name == w.name:
+                continue
+            ro, _, _ = time_workload(WL.get(name), args.steps, args.warmup, prec, profile=False)
+            others[name] = {k: ro[k] for k in ("tokens_per_s", "ms_per_step", "tflops_algorithmic",
+                                               "pct_of_peak", "tflops_page_convention")}
+        line["other_workloads"] = others
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, W, inp, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(w, W, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
