@@ -200,8 +200,11 @@ static int ns_prec_of(const lact_shape* sh, const lact_update_opts* op) {
 // First shifted step (lact_ns_prec): the last three of the five.
 static int ns_shift_from(int prec) { return prec == LACT_NS_BF16_SHIFTED ? 2 : 5; }
 
+// fused: the shape's Newton-Schulz workgroups sum the split partials and take
+// the step themselves (ns_step_fused), so the write needs the second operand
+// copy but neither the reduced gradient nor the batched Newton-Schulz buffers.
 static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* base,
-                           bool shadow2 = false) {
+                           bool fused = false) {
   Workspace w;
   const int64_t msz = (int64_t)sh->d * sh->dh;
   int64_t off = 0;
@@ -212,11 +215,11 @@ static Workspace layout_ws(const lact_shape* sh, int nsplit, bool muon, char* ba
   };
   // first, so that its place does not depend on the split count: operand
   // copies, 4 d dh bf16 per head
-  w.shadow2 = shadow2 ? take((int64_t)sh->bh * 2 * msz) : nullptr;
+  w.shadow2 = fused ? take((int64_t)sh->bh * 2 * msz) : nullptr;
   w.partial = take((int64_t)nsplit * sh->bh * 3 * msz);
   w.beta = take(sh->bh);
-  w.g = take((int64_t)3 * sh->bh * msz);
-  if (muon) {
+  w.g = fused ? nullptr : take((int64_t)3 * sh->bh * msz);
+  if (muon && !fused) {
     w.xa = take((int64_t)3 * sh->bh * msz);
     w.xb = take((int64_t)3 * sh->bh * msz);
     w.xh = take((int64_t)3 * sh->bh * msz);
@@ -436,9 +439,11 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   Workspace w = layout_ws(sh, nsplit, op->use_muon != 0, reinterpret_cast<char*>(ws), nsstep);
   const int64_t msz = (int64_t)sh->d * sh->dh;
   const int64_t mall = (int64_t)sh->bh * msz;
+  // the reduced gradient (not laid out when the Newton-Schulz workgroups sum
+  // the partials themselves)
   float* g1 = w.g;
-  float* g3 = w.g + mall;
-  float* g2 = w.g + 2 * mall;
+  float* g3 = w.g ? w.g + mall : nullptr;
+  float* g2 = w.g ? w.g + 2 * mall : nullptr;
   // with momentum the reduced gradient lives in M only (M <- G + beta M)
   const bool mo = op->use_momentum != 0;
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
