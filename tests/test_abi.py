@@ -55,8 +55,16 @@ def test_shadow_and_workspace_sizes(lib):
     a = L.workspace_bytes(sh, 2048, o)
     b = L.workspace_bytes(sh, 4096, o)
     assert 0 < a <= b
-    assert L.workspace_bytes(sh, 2048, L.opts()) < a  # no Muon buffers
     assert L.shadow_bytes(_shape(d=96)) == 0
+    # d = 256: Newton-Schulz runs as batched GEMMs with buffers of their own
+    big = _shape(bh=4, d=256, dh=1024)
+    assert L.workspace_bytes(big, 16384, L.opts()) < L.workspace_bytes(big, 16384, L.opts(use_muon=True))
+    # d = 128, dh = 512 with Muon: the Newton-Schulz workgroups sum the split
+    # partials and step, so the write needs the partials, the per-head beta
+    # and the second operand copy (2 d dh per head, 4 bytes) and nothing else
+    plain = L.workspace_bytes(sh, 2048, L.opts())
+    fused = L.workspace_bytes(sh, 2048, o)
+    assert fused - plain == 2 * 2 * 128 * 512 * 4 - 2 * 3 * 128 * 512 * 4
 
 
 @pytest.mark.parametrize("d,dh,dtype,code", [
