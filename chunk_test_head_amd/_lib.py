@@ -82,6 +82,8 @@ def load():
         "lact_chunk_step": (I32, [pS, pSt, P, L, P, L, P, L, P, L, P, P, P, P, I64, I64, pO, P, SZ, P]),
         "lact_sequence": (I32, [pS, pSt, P, L, P, L, P, L, P, L, P, P, P, P, I64, I64, I64, I32,
                                 I64, I64, I32, pO, P, SZ, P]),
+        "lact_sequence_noalloc": (I32, [pS, pSt, P, L, P, L, P, L, P, L, P, P, P, P, I64, I64, I64, I32,
+                                        I64, I64, I32, pO, P]),
         "lact_prof_begin": (I32, [I32, I32]),
         "lact_prof_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(F), ctypes.POINTER(F),
                                 ctypes.POINTER(F)]),
@@ -261,3 +263,18 @@ def lact_sequence(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, T, chunk, orde
                                 eta1.stride(0), int(T), int(chunk), int(order), int(sub_off), int(sub_len),
                                 int(update_last), ctypes.byref(o), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "lact_sequence")
+
+
+NOALLOC_SCRATCH_BYTES = 160 * 1024 * 1024
+
+
+def lact_sequence_noalloc(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, T, chunk, order, subset, update_last,
+                          o, stream=None, layouts=None):
+    """lact_sequence with the library's own scratch instead of a workspace."""
+    sub_off, sub_len = (0, -1) if subset is None else subset
+    ql, kl, vl, ol = layouts or (layout_of(q), layout_of(k), layout_of(v), layout_of(out))
+    _check(load().lact_sequence_noalloc(ctypes.byref(shape), fw.ref(), _ptr(q), ql, _ptr(k), kl, _ptr(v), vl,
+                                        _ptr(out), ol, _ptr(eta1), _ptr(eta3), _ptr(eta2), _ptr(mom),
+                                        eta1.stride(0), int(T), int(chunk), int(order), int(sub_off),
+                                        int(sub_len), int(update_last), ctypes.byref(o), _stream(stream)),
+           "lact_sequence_noalloc")

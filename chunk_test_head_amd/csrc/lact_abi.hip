@@ -672,13 +672,22 @@ lact_status lact_chunk_step(const lact_shape* sh, const lact_state* st, const vo
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
-lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void* q,
-                          lact_layout ql, const void* k, lact_layout kl, const void* v,
-                          lact_layout vl, void* o, lact_layout ol, const float* e1,
-                          const float* e3, const float* e2, const float* mom, int64_t esbh,
-                          int64_t T, int64_t chunk, int32_t order, int64_t sub_off,
-                          int64_t sub_len, int32_t update_last, const lact_update_opts* op,
-                          void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace lact {
+
+#define LACT_SEQ_PARAMS                                                                       \
+  const lact_shape *sh, const lact_state *st, const void *q, lact_layout ql, const void *k, \
+      lact_layout kl, const void *v, lact_layout vl, void *o, lact_layout ol, const float *e1, \
+      const float *e3, const float *e2, const float *mom, int64_t esbh, int64_t T,             \
+      int64_t chunk, int32_t order, int64_t sub_off, int64_t sub_len, int32_t update_last,     \
+      const lact_update_opts *op
+#define LACT_SEQ_ARGS                                                                          \
+  sh, st, q, ql, k, kl, v, vl, o, ol, e1, e3, e2, mom, esbh, T, chunk, order, sub_off, sub_len, \
+      update_last, op
+
+// Every argument check of lact_sequence (ws, ws_bytes: the workspace offered).
+static lact_status check_sequence(LACT_SEQ_PARAMS, const void* ws, size_t ws_bytes) {
   if (T < 0 || chunk < 1) return LACT_ERR_INVALID_ARG;
   if (order != LACT_APPLY_THEN_UPDATE && order != LACT_UPDATE_THEN_APPLY) return LACT_ERR_INVALID_ARG;
   if (sub_len >= 0 && (sub_off < 0 || sub_off >= chunk)) return LACT_ERR_INVALID_ARG;
@@ -696,7 +705,12 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
   if (T > 0 && q == o) return LACT_ERR_INVALID_ARG;
   if (T > 0 && (e1 == nullptr || e3 == nullptr || e2 == nullptr)) return LACT_ERR_INVALID_ARG;
   if (op->use_momentum && T > 0 && mom == nullptr) return LACT_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
+  return LACT_OK;
+}
+
+// The sequence driver proper (arguments already checked).
+static lact_status run_sequence(LACT_SEQ_PARAMS, void* ws, hipStream_t s) {
+  lact_status r = LACT_OK;
   const int es = elem_size(sh->dtype);
   auto at = [&](const void* base, lact_layout l, int64_t t) {
     return reinterpret_cast<const char*>(base) + t * l.stride_tok * es;
@@ -753,6 +767,52 @@ lact_status lact_sequence(const lact_shape* sh, const lact_state* st, const void
     if (e != hipSuccess) return hip_fail(e);
   }
   return LACT_OK;
+}
+
+// Scratch of lact_sequence_noalloc: one array per device the library runs
+// on, held until the process ends.  Host code never uses the array's name
+// as an address: each device's address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[LACT_NOALLOC_SCRATCH_BYTES];
+
+static lact_status scratch_on_current_device(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return LACT_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (p == nullptr) return LACT_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return LACT_OK;
+}
+
+}  // namespace lact
+
+extern "C" {
+
+lact_status lact_sequence(LACT_SEQ_PARAMS, void* ws, size_t ws_bytes, void* stream) {
+  const lact_status r = check_sequence(LACT_SEQ_ARGS, ws, ws_bytes);
+  if (r != LACT_OK) return r;
+  return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream);
+}
+
+lact_status lact_sequence_noalloc(LACT_SEQ_PARAMS, void* stream) {
+  // checked against the scratch's size (the address only has to pass the
+  // null and alignment checks here; the real one is looked up below)
+  static const unsigned char* const kAnyAligned = reinterpret_cast<const unsigned char*>(256);
+  lact_status r = check_sequence(LACT_SEQ_ARGS, kAnyAligned, (size_t)LACT_NOALLOC_SCRATCH_BYTES);
+  if (r != LACT_OK) return r;
+  void* ws = nullptr;
+  if ((r = scratch_on_current_device(&ws)) != LACT_OK) return r;
+  return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream);
 }
 
 lact_status lact_prof_begin(int32_t kind, int32_t max_launches) {

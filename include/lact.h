@@ -235,6 +235,30 @@ lact_status lact_sequence(const lact_shape* shape, const lact_state* state,
                           int32_t update_last, const lact_update_opts* opts,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* lact_sequence for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, which is instead a device array
+ * of LACT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on, from the first call on that GPU until the process ends.  The call
+ * allocates nothing.  A sequence whose writes need more workspace than that
+ * (lact_workspace_bytes) returns LACT_ERR_WORKSPACE.  Every call on one GPU
+ * shares the array: calls that may overlap on one GPU (different streams or
+ * threads without ordering between them) race and must not be made; calls
+ * on one stream are ordered and safe.  The array keeps the last call's
+ * contents; nothing in it needs to start at zero. */
+#define LACT_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+lact_status lact_sequence_noalloc(const lact_shape* shape, const lact_state* state,
+                                  const void* q, lact_layout q_layout,
+                                  const void* k, lact_layout k_layout,
+                                  const void* v, lact_layout v_layout,
+                                  void* o, lact_layout o_layout,
+                                  const float* eta1, const float* eta3, const float* eta2,
+                                  const float* mom, int64_t eta_stride_bh,
+                                  int64_t T, int64_t chunk, int32_t order,
+                                  int64_t subset_offset, int64_t subset_len,
+                                  int32_t update_last, const lact_update_opts* opts,
+                                  void* stream);
+
 /* Kernel timing for benchmarks.  lact_prof_begin(kind, max_launches)
  * creates 2 * max_launches HIP events; until lact_prof_end, every launch of
  * the kernel `kind` made by the calls above is bracketed by events recorded

@@ -141,3 +141,22 @@ def test_newton_schulz_checks(lib):
     assert lib.lact_newton_schulz(1, 100, 128, L.BF16, 256, 256, 1e-7, 256, 1 << 30, None) == 2
     need = L.ns_workspace_bytes(1, 128, 512)
     assert lib.lact_newton_schulz(1, 128, 512, L.BF16, 256, 256, 1e-7, 256, need - 1, None) == 4
+
+
+def test_sequence_noalloc_checks(lib):
+    """The entry point without a workspace checks its arguments like
+    lact_sequence, and a sequence whose writes need more workspace than the
+    library's scratch returns LACT_ERR_WORKSPACE, before any device call."""
+    lay = L.Layout(512 * 128, 128)
+    st = L.State(*([256] * 10))
+    o = L.opts(use_muon=True, use_momentum=True)
+    def call(sh, T, chunk, order=0):
+        return lib.lact_sequence_noalloc(ctypes.byref(sh), ctypes.byref(st), 256, lay, 256, lay, 256, lay, 512, lay,
+                                         1024, 1024, 1024, 1024, 100, T, chunk, order, 0, -1, 0, ctypes.byref(o),
+                                         None)
+    assert call(_shape(bh=4), 100, 0) == 1                  # chunk < 1
+    assert call(_shape(bh=4), 100, 64, order=9) == 1        # bad order
+    big = _shape(bh=256)                                    # lm-causal shape with 256 heads
+    assert L.workspace_bytes(big, 2048, o) > L.NOALLOC_SCRATCH_BYTES
+    assert call(big, 4096, 2048) == 4
+    assert L.workspace_bytes(_shape(bh=32), 2048, o) <= L.NOALLOC_SCRATCH_BYTES
