@@ -218,6 +218,85 @@ def time_workload(w, steps, warmup, ns_prec, profile, values=False):
     return res, W, inp
 
 
+def time_decode(w, calls=200, warmup=20):
+    """Streaming decode of workload w's shape: one new token per head per
+    step through lact_decode_apply (weight-streaming read), timed over
+    `calls` steps; the write that follows every `chunk` tokens is timed too
+    (lact_update on one chunk), and the amortised per-token cost reported."""
+    import numpy as np
+    import torch
+
+    from chunk_test_head_amd import _lib as L
+    from chunk_test_head_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    W = WL.weights(w)
+    shape = L.Shape(w.bh, w.d, w.dh, L.BF16)
+    fw = L.FastWeights(shape, *(torch.from_numpy(x).to(dev) for x in W), momentum=w.use_momentum)
+    L.lact_init_state(shape, fw)
+    g = torch.Generator(device="cpu").manual_seed(w.index)
+    q = torch.randn(w.bh, calls, w.d, generator=g).to(dev, torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.zeros(L.decode_workspace_bytes(shape, 1), dtype=torch.uint8, device=dev)
+    lay = L.layout_of(q)
+    stream = torch.cuda.current_stream()
+    for t in range(warmup):
+        L.lact_decode_apply(shape, fw, q[:, t:t + 1], out[:, t:t + 1], ws, n_tok=1, q_layout=lay,
+                            o_layout=lay, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(calls):
+        L.lact_decode_apply(shape, fw, q[:, t:t + 1], out[:, t:t + 1], ws, n_tok=1, q_layout=lay,
+                            o_layout=lay, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    # the same steps captured once into a HIP graph and replayed (a serving
+    # loop would replay a captured step: launches then cost less)
+    gs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            for t in range(calls):
+                L.lact_decode_apply(shape, fw, q[:, t:t + 1], out[:, t:t + 1], ws, n_tok=1, q_layout=lay,
+                                    o_layout=lay, stream=gs)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / (3 * calls)
+    # the write of one full chunk
+    C = w.chunk
+    k = torch.randn(w.bh, C, w.d, generator=g).to(dev, torch.bfloat16)
+    v = torch.randn(w.bh, C, w.d, generator=g).to(dev, torch.bfloat16)
+    eta = torch.full((w.bh, C), 0.01, device=dev)
+    mom = torch.full((w.bh, C), w.momentum, device=dev) if w.use_momentum else None
+    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+    wsu = torch.empty(L.workspace_bytes(shape, C, o), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        L.lact_update(shape, fw, k, v, eta, eta, eta, mom, o, wsu, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        L.lact_update(shape, fw, k, v, eta, eta, eta, mom, o, wsu, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    write_us = e0.elapsed_time(e1) * 1e3 / 5
+    wbytes = 3.0 * w.d * w.dh * 2 * w.bh
+    return {"heads": w.bh, "d": w.d, "dh": w.dh, "weight_bytes_per_step": wbytes,
+            "us_per_token_step": us, "tokens_per_s": w.batch / (us * 1e-6),
+            "weight_gbs": wbytes / (us * 1e-6) / 1e9, "pct_of_hbm": 100.0 * wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "graph_us_per_token_step": us_graph, "graph_tokens_per_s": w.batch / (us_graph * 1e-6),
+            "graph_weight_gbs": wbytes / (us_graph * 1e-6) / 1e9,
+            "write_us_per_chunk": write_us, "chunk": C,
+            "amortised_us_per_token_step": us + write_us / C}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +362,7 @@ def main():
             others[name] = {k: ro[k] for k in ("tokens_per_s", "ms_per_step", "tflops_algorithmic",
                                                "pct_of_peak", "tflops_page_convention")}
         line["other_workloads"] = others
+        line["streaming_decode"] = {name: time_decode(WL.get(name)) for name in ("lm-causal", "long-context")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, W, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -84,6 +84,8 @@ def load():
                                 I64, I64, I32, pO, P, SZ, P]),
         "lact_sequence_noalloc": (I32, [pS, pSt, P, L, P, L, P, L, P, L, P, P, P, P, I64, I64, I64, I32,
                                         I64, I64, I32, pO, P]),
+        "lact_decode_workspace_bytes": (SZ, [pS, I64]),
+        "lact_decode_apply": (I32, [pS, pSt, P, L, P, L, I64, P, SZ, P]),
         "lact_prof_begin": (I32, [I32, I32]),
         "lact_prof_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(F), ctypes.POINTER(F),
                                 ctypes.POINTER(F)]),
@@ -206,6 +208,20 @@ def lact_apply(shape, fw, q, o, n_tok=None, stream=None, q_layout=None, o_layout
     n = q.shape[1] if n_tok is None else n_tok
     _check(load().lact_apply(ctypes.byref(shape), fw.ref(), _ptr(q), q_layout or layout_of(q), _ptr(o),
                              o_layout or layout_of(o), int(n), _stream(stream)), "lact_apply")
+
+
+DECODE_MAX_TOKENS = 8
+
+
+def decode_workspace_bytes(shape, n_tok):
+    return load().lact_decode_workspace_bytes(ctypes.byref(shape), int(n_tok))
+
+
+def lact_decode_apply(shape, fw, q, o, ws, n_tok=None, stream=None, q_layout=None, o_layout=None):
+    n = q.shape[1] if n_tok is None else n_tok
+    _check(load().lact_decode_apply(ctypes.byref(shape), fw.ref(), _ptr(q), q_layout or layout_of(q), _ptr(o),
+                                    o_layout or layout_of(o), int(n), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)), "lact_decode_apply")
 
 
 def lact_gradient(shape, fw, k, v, eta1, eta3, eta2, g1, g3, g2, ws, n_tok=None, stream=None,

@@ -572,6 +572,36 @@ lact_status lact_apply(const lact_shape* sh, const lact_state* st, const void* q
   return do_apply(sh, st, q, ql, o, ol, n_tok, (hipStream_t)stream);
 }
 
+size_t lact_decode_workspace_bytes(const lact_shape* sh, int64_t n_tok) {
+  if (check_shape(sh) != LACT_OK || n_tok < 1 || n_tok > LACT_DECODE_MAX_TOKENS) return 0;
+  const int nb = decode_blocks(sh->dtype, sh->bh, sh->d, sh->dh);
+  return (size_t)align256((int64_t)sh->bh * nb * n_tok * sh->d * 4);
+}
+
+lact_status lact_decode_apply(const lact_shape* sh, const lact_state* st, const void* q,
+                              lact_layout ql, void* o, lact_layout ol, int64_t n_tok, void* ws,
+                              size_t ws_bytes, void* stream) {
+  lact_status r;
+  if ((r = check_shape(sh)) != LACT_OK) return r;
+  if ((r = check_state(sh, st, false)) != LACT_OK) return r;
+  if (n_tok < 0 || n_tok > LACT_DECODE_MAX_TOKENS) return LACT_ERR_INVALID_ARG;
+  if ((r = check_act(sh, q, ql, n_tok)) != LACT_OK) return r;
+  if ((r = check_act(sh, o, ol, n_tok)) != LACT_OK) return r;
+  if (n_tok == 0) return LACT_OK;
+  if (q == o) return LACT_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < lact_decode_workspace_bytes(sh, n_tok)) return LACT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
+  DecodeArgs a;
+  a.q = q; a.q_sbh = ql.stride_bh; a.q_st = ql.stride_tok;
+  a.o = o; a.o_sbh = ol.stride_bh; a.o_st = ol.stride_tok;
+  a.sh = make_shadow(st->shadow, sh->d, sh->dh);
+  a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh; a.n = (int)n_tok;
+  a.nblk = decode_blocks(sh->dtype, sh->bh, sh->d, sh->dh);
+  a.part = reinterpret_cast<float*>(ws);
+  const hipError_t e = launch_decode(sh->dtype, a, (hipStream_t)stream);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
 lact_status lact_gradient(const lact_shape* sh, const lact_state* st, const void* k,
                           lact_layout kl, const void* v, lact_layout vl, const float* e1,
                           const float* e3, const float* e2, int64_t esbh, int64_t n_tok,

@@ -23,6 +23,17 @@ struct ApplyArgs {
   int64_t n_tok;
 };
 
+// Read of 1..8 tokens per head (k_decode.hip): q, o as for ApplyArgs; part:
+// [bh][nblk][n][d] fp32 partial outputs of the hidden blocks.
+struct DecodeArgs {
+  const void* q; int64_t q_sbh, q_st;
+  void* o; int64_t o_sbh, o_st;
+  Shadow sh;
+  int bh, d, dh, n;
+  int nblk;
+  float* part;
+};
+
 struct GradArgs {
   const void* k; int64_t k_sbh, k_st;
   const void* v; int64_t v_sbh, v_st;
@@ -119,6 +130,8 @@ hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
 hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
+int decode_blocks(int dtype, int bh, int d, int dh);
+hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
 int grad_hidden_per_block(int dtype, int d);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);

@@ -144,6 +144,23 @@ lact_status lact_apply(const lact_shape* shape, const lact_state* state,
                        void* o, lact_layout o_layout,
                        int64_t n_tok, void* stream);
 
+/* Streaming decode read: the read of lact_apply for 1 <= n_tok <=
+ * LACT_DECODE_MAX_TOKENS tokens per head (e.g. the newest token of each of
+ * bh streams), as a weight-streaming matrix-vector kernel: each hidden unit's
+ * rows of the operand copies are read once for all n_tok tokens, so the
+ * call is bound by reading 3 d dh operand values per head (plus a second,
+ * small launch that adds the hidden blocks' partial outputs).  A stream
+ * reads every token this way and writes (lact_update) only when a chunk of
+ * keys and values has filled (uTTT page section 2; rebuttal page, the causal
+ * function's chunk loop).  Fp32 sums in a fixed order; o in shape.dtype.
+ * n_tok = 0 does nothing.  Workspace: lact_decode_workspace_bytes(). */
+#define LACT_DECODE_MAX_TOKENS 8
+size_t lact_decode_workspace_bytes(const lact_shape* shape, int64_t n_tok);
+lact_status lact_decode_apply(const lact_shape* shape, const lact_state* state,
+                              const void* q, lact_layout q_layout,
+                              void* o, lact_layout o_layout, int64_t n_tok,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunk gradient (descent direction) of L_j = -sum_t eta_j,t <f_W(k_t), v_t>
  * over n_tok tokens, written in the wide orientation, fp32:
  *   g1 <- G1^T, g3 <- G3^T, g2 <- G2, each [bh, d, dh].

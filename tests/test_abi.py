@@ -160,3 +160,20 @@ def test_sequence_noalloc_checks(lib):
     assert L.workspace_bytes(big, 2048, o) > L.NOALLOC_SCRATCH_BYTES
     assert call(big, 4096, 2048) == 4
     assert L.workspace_bytes(_shape(bh=32), 2048, o) <= L.NOALLOC_SCRATCH_BYTES
+
+
+def test_decode_checks(lib):
+    """Decode reads: more than LACT_DECODE_MAX_TOKENS tokens, a missing or
+    short workspace and o aliasing q are rejected before any device call."""
+    sh = _shape(bh=4)
+    st = L.State(*([256] * 10))
+    lay = L.Layout(512 * 128, 128)
+    need = L.decode_workspace_bytes(sh, 1)
+    assert need > 0 and L.decode_workspace_bytes(sh, 9) == 0 and L.decode_workspace_bytes(sh, 0) == 0
+    call = lambda n, ws, wsb, o=512: lib.lact_decode_apply(ctypes.byref(sh), ctypes.byref(st), 256, lay, o, lay,
+                                                           n, ws, wsb, None)
+    assert call(9, 4096, 1 << 20) == 1
+    assert call(1, 4096, need - 1) == 4
+    assert call(1, None, need) == 4
+    assert call(1, 4096, need, o=256) == 1
+    assert call(0, None, 0) == 0          # nothing to read: nothing enqueued
