@@ -42,7 +42,7 @@ class UpdateOpts(ctypes.Structure):
     _fields_ = [("use_muon", ctypes.c_int32), ("use_momentum", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("renorm_eps", ctypes.c_float),
                 ("ns_eps", ctypes.c_float), ("ns_prec", ctypes.c_int32),
-                ("nonfinite", ctypes.c_void_p)]
+                ("nonfinite", ctypes.c_void_p), ("eta_per_channel", ctypes.c_int32)]
 
 
 class LactError(RuntimeError):
@@ -131,16 +131,23 @@ def _check(st, where):
         raise LactError(st, where)
 
 
+def _eta_stride(eta):
+    """eta_stride_bh of a [bh, T] (per token) or [bh, T, channels] (per
+    channel) learning-rate tensor: tokens between heads."""
+    return eta.stride(0) // eta.shape[2] if eta.dim() == 3 else eta.stride(0)
+
+
 def layout_of(t):
     """Layout of a [bh, T, d] (or [bh, T, d]-strided) tensor."""
     return Layout(t.stride(0), t.stride(1))
 
 
 def opts(use_muon=False, use_momentum=False, renorm=True, renorm_eps=1e-5, ns_eps=1e-7,
-         ns_prec=NS_BF16_SHIFTED, nonfinite=None):
-    """lact_update_opts; nonfinite: a device int32 tensor (or None)."""
+         ns_prec=NS_BF16_SHIFTED, nonfinite=None, eta_per_channel=False):
+    """lact_update_opts; nonfinite: a device int32 tensor (or None); renorm:
+    False / True / 2 (master state with a rescaled operand copy)."""
     return UpdateOpts(int(use_muon), int(use_momentum), int(renorm), renorm_eps, ns_eps, int(ns_prec),
-                      _ptr(nonfinite))
+                      _ptr(nonfinite), int(eta_per_channel))
 
 
 def shadow_bytes(shape):
@@ -229,7 +236,7 @@ def lact_gradient(shape, fw, k, v, eta1, eta3, eta2, g1, g3, g2, ws, n_tok=None,
     n = k.shape[1] if n_tok is None else n_tok
     _check(load().lact_gradient(ctypes.byref(shape), fw.ref(), _ptr(k), k_layout or layout_of(k), _ptr(v),
                                 v_layout or layout_of(v), _ptr(eta1), _ptr(eta3), _ptr(eta2),
-                                eta1.stride(0), int(n), _ptr(g1), _ptr(g3), _ptr(g2), _ptr(ws),
+                                _eta_stride(eta1), int(n), _ptr(g1), _ptr(g3), _ptr(g2), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)), "lact_gradient")
 
 
@@ -258,7 +265,7 @@ def lact_update(shape, fw, k, v, eta1, eta3, eta2, mom, o, ws, n_tok=None, strea
     n = k.shape[1] if n_tok is None else n_tok
     _check(load().lact_update(ctypes.byref(shape), fw.ref(), _ptr(k), k_layout or layout_of(k), _ptr(v),
                               v_layout or layout_of(v), _ptr(eta1), _ptr(eta3), _ptr(eta2), _ptr(mom),
-                              eta1.stride(0), int(n), ctypes.byref(o), _ptr(ws),
+                              _eta_stride(eta1), int(n), ctypes.byref(o), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "lact_update")
 
 
@@ -266,7 +273,7 @@ def lact_chunk_step(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, o, ws, n_tok
     n = q.shape[1] if n_tok is None else n_tok
     _check(load().lact_chunk_step(ctypes.byref(shape), fw.ref(), _ptr(q), layout_of(q), _ptr(k), layout_of(k),
                                   _ptr(v), layout_of(v), _ptr(out), layout_of(out), _ptr(eta1), _ptr(eta3),
-                                  _ptr(eta2), _ptr(mom), eta1.stride(0), int(n), ctypes.byref(o), _ptr(ws),
+                                  _ptr(eta2), _ptr(mom), _eta_stride(eta1), int(n), ctypes.byref(o), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)), "lact_chunk_step")
 
 
@@ -276,7 +283,7 @@ def lact_sequence(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, T, chunk, orde
     ql, kl, vl, ol = layouts or (layout_of(q), layout_of(k), layout_of(v), layout_of(out))
     _check(load().lact_sequence(ctypes.byref(shape), fw.ref(), _ptr(q), ql, _ptr(k), kl, _ptr(v), vl,
                                 _ptr(out), ol, _ptr(eta1), _ptr(eta3), _ptr(eta2), _ptr(mom),
-                                eta1.stride(0), int(T), int(chunk), int(order), int(sub_off), int(sub_len),
+                                _eta_stride(eta1), int(T), int(chunk), int(order), int(sub_off), int(sub_len),
                                 int(update_last), ctypes.byref(o), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "lact_sequence")
 
@@ -291,6 +298,6 @@ def lact_sequence_noalloc(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, T, chu
     ql, kl, vl, ol = layouts or (layout_of(q), layout_of(k), layout_of(v), layout_of(out))
     _check(load().lact_sequence_noalloc(ctypes.byref(shape), fw.ref(), _ptr(q), ql, _ptr(k), kl, _ptr(v), vl,
                                         _ptr(out), ol, _ptr(eta1), _ptr(eta3), _ptr(eta2), _ptr(mom),
-                                        eta1.stride(0), int(T), int(chunk), int(order), int(sub_off),
+                                        _eta_stride(eta1), int(T), int(chunk), int(order), int(sub_off),
                                         int(sub_len), int(update_last), ctypes.byref(o), _stream(stream)),
            "lact_sequence_noalloc")

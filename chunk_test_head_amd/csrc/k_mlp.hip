@@ -40,7 +40,12 @@ void k_apply_solo(ApplyArgs a) {
 // the gradient contractions, K = tokens).  The forward results (tokens x
 // hidden, in MFMA accumulators) go through the SwiGLU backward and the eta
 // scaling in registers and feed the gradient contractions directly.
-template <class T, int D, int JW, int WAVES>
+// PERCH: per-channel learning rates (eta1, eta3 [bh][*][D] scale k channel
+// by channel, eta2 [bh][*][dh] the hidden activations): the gradient
+// contractions of G1 and G3 then read (eta1 k)^T and (eta3 k)^T tiles staged
+// beside k^T, and each token's eta2 values for the workgroup's hidden units
+// are staged in LDS.
+template <class T, int D, int JW, int WAVES, bool PERCH = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
   constexpr int NTH = WAVES * 64;
   constexpr int NT = 32;                 // tokens per tile (one K slab)
@@ -58,6 +63,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
   __shared__ __attribute__((aligned(16))) T sKt[D * PT];
   __shared__ __attribute__((aligned(16))) T sVt[D * PT];
   __shared__ float sEta[3][NT];
+  constexpr int WB = WAVES * JW;         // hidden units per workgroup
+  __shared__ __attribute__((aligned(16))) T sK1t[PERCH ? D * PT : 1];
+  __shared__ __attribute__((aligned(16))) T sK3t[PERCH ? D * PT : 1];
+  __shared__ float sE2[PERCH ? NT * WB : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -77,9 +86,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
 
   const T* kp = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.k_sbh;
   const T* vp = reinterpret_cast<const T*>(a.v) + (int64_t)head * a.v_sbh;
-  const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh;
-  const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh;
-  const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh;
+  // per token (or, PERCH, per token and channel: eta_sbh counts tokens)
+  const float* e1 = a.eta1 + (int64_t)head * a.eta_sbh * (PERCH ? D : 1);
+  const float* e3 = a.eta3 + (int64_t)head * a.eta_sbh * (PERCH ? D : 1);
+  const float* e2 = a.eta2 + (int64_t)head * a.eta_sbh * (PERCH ? a.dh : 1);
   const T* sb = reinterpret_cast<const T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
   const T* w1 = sb + a.sh.off_w1;
   const T* w3 = sb + a.sh.off_w3;
@@ -127,8 +137,25 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
         sKt[(col + e) * PT + r] = ke[e];
         sVt[(col + e) * PT + r] = ve[e];
       }
+      if constexpr (PERCH) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float x1 = t < s1 ? e1[t * D + col + e] : 0.f;
+          const float x3 = t < s1 ? e3[t * D + col + e] : 0.f;
+          sK1t[(col + e) * PT + r] = to_t<T>(x1 * to_f(ke[e]));
+          sK3t[(col + e) * PT + r] = to_t<T>(x3 * to_f(ke[e]));
+        }
+      }
     }
-    if (tid < NT) {
+    if constexpr (PERCH) {
+      for (int x = tid; x < NT * WB; x += NTH) {
+        const int r = x / WB, jj = x % WB;
+        const int64_t t = t0 + r;
+        const int j = hb * WB + jj;
+        sE2[x] = (t < s1 && j < a.dh) ? e2[t * a.dh + j] : 0.f;
+      }
+    }
+    if (!PERCH && tid < NT) {
       const int64_t t = t0 + tid;
       const bool in = t < s1;
       sEta[0][tid] = in ? e1[t] : 0.f;
@@ -174,9 +201,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
           const float sg = sigmoidf_(p);
           const float sl = p * sg;
           const float dsl = sg * (1.f + p * (1.f - sg));
-          fh[jt][4 * tt + i] = to_t<T>(sEta[2][r] * sl * u);
-          fu[jt][4 * tt + i] = to_t<T>(sEta[1][r] * e * sl);
-          fg[jt][4 * tt + i] = to_t<T>(sEta[0][r] * e * u * dsl);
+          if constexpr (PERCH) {
+            fh[jt][4 * tt + i] = to_t<T>(sE2[r * WB + wave * JW + 16 * jt + c] * sl * u);
+            fu[jt][4 * tt + i] = to_t<T>(e * sl);
+            fg[jt][4 * tt + i] = to_t<T>(e * u * dsl);
+          } else {
+            fh[jt][4 * tt + i] = to_t<T>(sEta[2][r] * sl * u);
+            fu[jt][4 * tt + i] = to_t<T>(sEta[1][r] * e * sl);
+            fg[jt][4 * tt + i] = to_t<T>(sEta[0][r] * e * u * dsl);
+          }
         }
 
     // ---- gradient contractions over the tile's tokens ----
@@ -184,13 +217,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
     for (int it = 0; it < IT; ++it) {
       const T* kr = sKt + (16 * it + c) * PT;
       const T* vr = sVt + (16 * it + c) * PT;
-      const frag_t<T> akt = ld4x2(kr + 4 * g, kr + 16 + 4 * g);
       const frag_t<T> avt = ld4x2(vr + 4 * g, vr + 16 + 4 * g);
+      if constexpr (PERCH) {
+        const T* k1 = sK1t + (16 * it + c) * PT;
+        const T* k3 = sK3t + (16 * it + c) * PT;
+        const frag_t<T> ak1 = ld4x2(k1 + 4 * g, k1 + 16 + 4 * g);
+        const frag_t<T> ak3 = ld4x2(k3 + 4 * g, k3 + 16 + 4 * g);
 #pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        mma(G1[it][jt], akt, fg[jt]);
-        mma(G3[it][jt], akt, fu[jt]);
-        mma(G2[it][jt], avt, fh[jt]);
+        for (int jt = 0; jt < JT; ++jt) {
+          mma(G1[it][jt], ak1, fg[jt]);
+          mma(G3[it][jt], ak3, fu[jt]);
+          mma(G2[it][jt], avt, fh[jt]);
+        }
+      } else {
+        const frag_t<T> akt = ld4x2(kr + 4 * g, kr + 16 + 4 * g);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          mma(G1[it][jt], akt, fg[jt]);
+          mma(G3[it][jt], akt, fu[jt]);
+          mma(G2[it][jt], avt, fh[jt]);
+        }
       }
     }
     }  // active
@@ -784,9 +830,9 @@ hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-int grad_hidden_per_block(int dtype, int d) {
-  if (dtype == 1) return d == 256 ? 4 * 16 : 128;   // k_grad_bf16: WAVES x 16 x HT (d = 64, 128: 8 x 16)
-  return 4 * (d == 64 ? 32 : 16);
+int grad_hidden_per_block(int dtype, int d, bool generic) {
+  if (dtype == 1 && !generic) return d == 256 ? 4 * 16 : 128;   // k_grad_bf16: WAVES x 16 x HT (d = 64, 128: 8 x 16)
+  return 4 * (d == 64 ? 32 : 16);                               // k_grad: WAVES x JW
 }
 
 template <int D, int WAVES, int HT>
@@ -806,18 +852,34 @@ static hipError_t run_grad_solo(const GradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class T, int D, int JW, int WAVES>
+template <class T, int D, int JW, int WAVES, bool PERCH = false>
 static hipError_t run_grad(const GradArgs& a, hipStream_t s) {
   const int hblocks = (a.dh + WAVES * JW - 1) / (WAVES * JW);
   const int64_t blocks = (int64_t)hblocks * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_grad<T, D, JW, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_grad<T, D, JW, WAVES, PERCH>), dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s) {
   // folding the old momentum in is a k_grad_bf16 feature
-  if (a.mo1 != nullptr && !(dtype == 1 && a.d <= 128 && a.mom != nullptr)) return hipErrorInvalidValue;
+  if (a.mo1 != nullptr && !(dtype == 1 && a.d <= 128 && a.mom != nullptr && !a.eta_per_channel))
+    return hipErrorInvalidValue;
+  if (a.eta_per_channel) {
+    // per-channel learning rates: the generic kernel, d <= 128
+    if (dtype == 1) {
+      switch (a.d) {
+        case 64: return run_grad<bf16, 64, 32, 4, true>(a, s);
+        case 128: return run_grad<bf16, 128, 16, 4, true>(a, s);
+      }
+    } else {
+      switch (a.d) {
+        case 64: return run_grad<float, 64, 32, 4, true>(a, s);
+        case 128: return run_grad<float, 128, 16, 4, true>(a, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (dtype == 1) {
     switch (a.d) {
       case 64: return run_grad_bf16<64, 8, 1>(a, s);

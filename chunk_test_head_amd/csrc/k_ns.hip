@@ -784,7 +784,8 @@ __device__ __forceinline__ void ns_load_grad(f32x4 (&yv)[NMT][NRT], int m, const
 // The result X5 = P Y (this wave's columns col0 .. col0 + COLS / 8 of the
 // 128 x COLS wide matrix, accumulator layout) is added to the fp32 weights,
 // each row rescaled to n0 / (||row|| + eps) (renorm; else left as is), and
-// the weights and their bf16 operand copies written.  Part of X5 at a time is
+// the weights and their bf16 operand copies written (master variant: the
+// weights keep the unscaled sum, the copies the rescaled rows).  Part of X5 at a time is
 // staged in LDS (fp32) and each W row goes to 8 consecutive lanes (128-byte
 // segments, 16 float4 per lane), so a row norm is three shuffles.  W loads
 // are issued after the staging stores, when those registers of X5 are free.
@@ -860,7 +861,7 @@ __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], fl
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const f32x4 y = x[v][kk] * f;
-          *reinterpret_cast<f32x4*>(W + row + 4 * (lk + 8 * kk)) = y;
+          *reinterpret_cast<f32x4*>(W + row + 4 * (lk + 8 * kk)) = st.renorm == 2 ? x[v][kk] : y;
           st4(S + row + 4 * (lk + 8 * kk), y[0], y[1], y[2], y[3]);
         }
       }
@@ -917,7 +918,7 @@ __device__ __forceinline__ void ns_step_epilogue(const f32x4 (&yv)[NMT][NRT], fl
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const f32x4 y = x[v][kk] * f;
-          *reinterpret_cast<f32x4*>(W + row + 4 * (lk + 8 * kk)) = y;
+          *reinterpret_cast<f32x4*>(W + row + 4 * (lk + 8 * kk)) = st.renorm == 2 ? x[v][kk] : y;
           st4(S + row + 4 * (lk + 8 * kk), y[0], y[1], y[2], y[3]);
           *reinterpret_cast<f32x4*>(stg + off(r, 4 * (lk + 8 * kk))) = y;  // own slot
         }

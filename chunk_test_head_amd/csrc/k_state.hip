@@ -6,7 +6,9 @@
 //   G <- G + beta M,  M <- G   (before Muon).
 // Step + renorm (same page, end of the chunk loop; summary page section 3.2
 // Eq. 8):  W <- W + U,  row <- row / (||row|| + eps) * n0[row], with n0 the
-// row norms at sequence start.
+// row norms at sequence start.  Master variant (uTTT page section C.1,
+// renorm = 2): the fp32 state keeps W + U unscaled and only the operand
+// copies, which reads and gradients use, hold the rescaled rows.
 #include "lact_internal.hpp"
 #include "mfma.hpp"
 
@@ -193,7 +195,7 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
       const float f = a.renorm ? N0[r] / (sqrtf(ss[k]) + a.eps) : 1.f;
       if (a.init && c4 == 0) N0[r] = sqrtf(ss[k]);  // sequence-start norm
       const f32x4 v = w[k] * f;
-      if (write_w) *reinterpret_cast<f32x4*>(W + (int64_t)r * d + c4) = v;
+      if (write_w) *reinterpret_cast<f32x4*>(W + (int64_t)r * d + c4) = a.renorm == 2 ? w[k] : v;
       st4(S + (int64_t)r * d + c4, v[0], v[1], v[2], v[3]);
     }
   }
@@ -240,7 +242,7 @@ __device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
       const int col = 4 * lane + 256 * k;
       if (k < nk || (k == nk && 4 * lane < rem)) {
         const f32x4 v = w[k] * f;
-        if (write_w) *reinterpret_cast<f32x4*>(W + col) = v;
+        if (write_w) *reinterpret_cast<f32x4*>(W + col) = a.renorm == 2 ? w[k] : v;
         st4(S + col, v[0], v[1], v[2], v[3]);
         st4(tl + row * dh + col, v[0], v[1], v[2], v[3]);
       }

@@ -117,9 +117,11 @@ static lact_status check_act(const lact_shape* sh, const void* p, lact_layout l,
 static lact_status check_opts(const lact_update_opts* o) {
   if (o == nullptr) return LACT_ERR_INVALID_ARG;
   if (!(o->renorm_eps >= 0.f) || !(o->ns_eps >= 0.f)) return LACT_ERR_INVALID_ARG;
+  if (o->renorm < 0 || o->renorm > 2) return LACT_ERR_INVALID_ARG;
   if (o->ns_prec != LACT_NS_BF16_SHIFTED && o->ns_prec != LACT_NS_BF16 && o->ns_prec != LACT_NS_F32)
     return LACT_ERR_INVALID_ARG;
   if (o->nonfinite != nullptr && ((uintptr_t)o->nonfinite & 3u) != 0) return LACT_ERR_ALIGNMENT;
+  if (o->eta_per_channel != 0 && o->eta_per_channel != 1) return LACT_ERR_INVALID_ARG;
   return LACT_OK;
 }
 
@@ -135,7 +137,7 @@ static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // t_partial = 2 x 3 d dh bh x 4 bytes at ~5 TB/s, over at most two rounds
 // (so the workspace bound below holds for every token count).
 static int nsplit_bound(const lact_shape* sh, int64_t n_tok) {
-  const int hpb = grad_hidden_per_block(sh->dtype, sh->d);
+  const int hpb = grad_hidden_per_block(sh->dtype, sh->d, false);
   const int64_t base = (int64_t)sh->bh * ((sh->dh + hpb - 1) / hpb);
   int64_t ns = (512 + base - 1) / base;
   const int64_t tiles = (n_tok + 31) / 32;
@@ -144,11 +146,13 @@ static int nsplit_bound(const lact_shape* sh, int64_t n_tok) {
   return ns < 1 ? 1 : (int)ns;
 }
 
-static int choose_nsplit(const lact_shape* sh, int64_t n_tok) {
-  const int hpb = grad_hidden_per_block(sh->dtype, sh->d);
+// generic: the gradient runs on the generic kernel (fp32 shapes, per-channel
+// learning rates).
+static int choose_nsplit(const lact_shape* sh, int64_t n_tok, bool generic) {
+  const int hpb = grad_hidden_per_block(sh->dtype, sh->d, generic);
   const int64_t base = (int64_t)sh->bh * ((sh->dh + hpb - 1) / hpb);
-  if (sh->dtype != LACT_BF16) {
-    // fp32: several workgroups per CU; at least 256 tokens per split
+  if (generic) {
+    // several workgroups per CU; at least 256 tokens per split
     int64_t ns = (256 + base - 1) / base;
     const int64_t cap = (n_tok + 255) / 256;
     if (ns > cap) ns = cap;
@@ -188,7 +192,12 @@ struct Workspace {
 // share their launch with a read, which then needs a second shadow).
 static bool ns_step_fused(const lact_shape* sh, const lact_update_opts* op) {
   return op != nullptr && op->use_muon && op->ns_prec != LACT_NS_F32 && sh->dtype == LACT_BF16 &&
-         sh->d == 128 && (sh->dh == 256 || sh->dh == 512);
+         !op->eta_per_channel && sh->d == 128 && (sh->dh == 256 || sh->dh == 512);
+}
+
+// The write's gradient runs on the generic kernel.
+static bool generic_grad(const lact_shape* sh, const lact_update_opts* op) {
+  return sh->dtype != LACT_BF16 || (op != nullptr && op->eta_per_channel);
 }
 
 // Precision of a write's Newton-Schulz products: fp32 shapes always use fp32
@@ -365,11 +374,12 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
                            const float* e3, const float* e2, int64_t esbh, int64_t n_tok,
                            const Workspace& w, int nsplit, float* o1, float* o3, float* o2,
                            float* m1, float* m3, float* m2, const float* mom, hipStream_t s,
-                           bool reduce = true) {
+                           bool reduce = true, int eta_per_channel = 0) {
   GradArgs a;
   a.k = k; a.k_sbh = kl.stride_bh; a.k_st = kl.stride_tok;
   a.v = v; a.v_sbh = vl.stride_bh; a.v_st = vl.stride_tok;
   a.eta1 = e1; a.eta3 = e3; a.eta2 = e2; a.eta_sbh = esbh;
+  a.eta_per_channel = eta_per_channel;
   a.sh = make_shadow(st->shadow, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh; a.n_tok = n_tok;
   a.nsplit = nsplit;
@@ -435,7 +445,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
     lact_status r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, s);
     if (r != LACT_OK) return r;
   }
-  const int nsplit = choose_nsplit(sh, n_tok);
+  const int nsplit = choose_nsplit(sh, n_tok, generic_grad(sh, op));
   Workspace w = layout_ws(sh, nsplit, op->use_muon != 0, reinterpret_cast<char*>(ws), nsstep);
   const int64_t msz = (int64_t)sh->d * sh->dh;
   const int64_t mall = (int64_t)sh->bh * msz;
@@ -449,7 +459,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
                           mo ? nullptr : g1, mo ? nullptr : g3, mo ? nullptr : g2,
                           mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr,
-                          mo ? mom : nullptr, s, !nsstep);
+                          mo ? mom : nullptr, s, !nsstep, op->eta_per_channel);
   if (r != LACT_OK) return r;
   const float* u1 = mo ? st->m1 : g1;
   const float* u3 = mo ? st->m3 : g3;
@@ -469,7 +479,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
         aa.n_tok = 0;
       }
       const NsStep ns{st->w1, st->w3, st->w2, st->n1, st->n3, st->n2,
-                      make_shadow(shadow_out, sh->d, sh->dh), sh->bh, op->renorm ? 1 : 0,
+                      make_shadow(shadow_out, sh->d, sh->dh), sh->bh, op->renorm,
                       op->renorm_eps, op->nonfinite};
       const NsGrad gr{w.partial, nsplit, sh->bh,
                       {mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr}};
@@ -482,7 +492,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
   }
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, op->nonfinite, shadow_out,
+  return do_step(sh, st, u1, u3, u2, op->renorm, op->renorm_eps, op->nonfinite, shadow_out,
                  s);
 }
 
@@ -495,6 +505,7 @@ static lact_status check_update_args(const lact_shape* sh, const lact_state* st,
   lact_status r;
   if ((r = check_shape(sh)) != LACT_OK) return r;
   if ((r = check_opts(op)) != LACT_OK) return r;
+  if (op->eta_per_channel && sh->d > 128) return LACT_ERR_UNSUPPORTED;
   if ((r = check_state(sh, st, op->use_momentum != 0)) != LACT_OK) return r;
   if (n_tok < 0) return LACT_ERR_INVALID_ARG;
   if ((r = check_act(sh, k, kl, n_tok)) != LACT_OK) return r;
@@ -529,8 +540,8 @@ size_t lact_workspace_bytes(const lact_shape* sh, int64_t max_update_tokens,
                             const lact_update_opts* opts) {
   if (check_shape(sh) != LACT_OK || max_update_tokens < 0) return 0;
   const bool muon = opts != nullptr && opts->use_muon != 0;
-  const int ns = sh->dtype == LACT_BF16 ? nsplit_bound(sh, max_update_tokens)
-                                         : choose_nsplit(sh, max_update_tokens);
+  const int ns = generic_grad(sh, opts) ? choose_nsplit(sh, max_update_tokens, true)
+                                        : nsplit_bound(sh, max_update_tokens);
   return (size_t)layout_ws(sh, ns, muon, nullptr, ns_step_fused(sh, opts)).bytes;
 }
 
@@ -616,7 +627,7 @@ lact_status lact_gradient(const lact_shape* sh, const lact_state* st, const void
     if (gp == nullptr) return LACT_ERR_INVALID_ARG;
     if (!aligned16(gp)) return LACT_ERR_ALIGNMENT;
   }
-  const int nsplit = choose_nsplit(sh, n_tok);
+  const int nsplit = choose_nsplit(sh, n_tok, generic_grad(sh, &op));
   Workspace w = layout_ws(sh, nsplit, false, reinterpret_cast<char*>(ws));
   return do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit, g1, g3, g2, nullptr,
                  nullptr, nullptr, nullptr, (hipStream_t)stream);
@@ -661,7 +672,7 @@ lact_status lact_step_renorm(const lact_shape* sh, const lact_state* st, const f
   }
   if (ws == nullptr || ws_bytes < lact_workspace_bytes(sh, 0, op)) return LACT_ERR_WORKSPACE;
   if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
-  return do_step(sh, st, u1, u3, u2, op->renorm ? 1 : 0, op->renorm_eps, op->nonfinite, st->shadow,
+  return do_step(sh, st, u1, u3, u2, op->renorm, op->renorm_eps, op->nonfinite, st->shadow,
                  (hipStream_t)stream);
 }
 
@@ -755,7 +766,9 @@ static lact_status run_sequence(LACT_SEQ_PARAMS, void* ws, hipStream_t s) {
   auto write = [&](const void* kp, const void* vp, int64_t a0, int64_t n, const ApplyJob* job) {
     void* out = cs.shadow;
     if (alt != nullptr && job != nullptr && job->n_tok > 0) out = cs.shadow == st->shadow ? alt : st->shadow;
-    const lact_status rr = do_update(sh, &cs, kp, kl, vp, vl, e1 + a0, e3 + a0, e2 + a0,
+    // learning rates: one per token, or (per channel) d or dh per token
+    const int64_t c13 = op->eta_per_channel ? sh->d : 1, c2 = op->eta_per_channel ? sh->dh : 1;
+    const lact_status rr = do_update(sh, &cs, kp, kl, vp, vl, e1 + a0 * c13, e3 + a0 * c13, e2 + a0 * c2,
                                      mom ? mom + a0 : nullptr, esbh, n, op, ws, s, job, out);
     if (rr == LACT_OK) cs.shadow = out;
     return rr;

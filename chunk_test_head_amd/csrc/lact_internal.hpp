@@ -38,6 +38,9 @@ struct GradArgs {
   const void* k; int64_t k_sbh, k_st;
   const void* v; int64_t v_sbh, v_st;
   const float* eta1; const float* eta3; const float* eta2; int64_t eta_sbh;
+  // 0: one learning rate per token; 1: per channel (eta1, eta3 [bh][*][d],
+  // eta2 [bh][*][dh]; eta_sbh counts tokens)
+  int eta_per_channel;
   Shadow sh;
   int bh, d, dh;
   int64_t n_tok;
@@ -115,7 +118,8 @@ struct StepArgs {
   float* n1; float* n3; float* n2;                    // renorm targets
   Shadow sh;
   int bh, d, dh;
-  int renorm;  // 0: factor 1 (copies only), 1: n0 / (||row|| + eps)
+  int renorm;  // 0: factor 1 (copies only), 1: n0 / (||row|| + eps), 2: the
+               // rescaled rows go to the copies only, W keeps W + U
   float eps;
   // sequence start (init = 1, with renorm = 0 and no U): the row norms are
   // written to n1, n3, n2 and the momentum buffers (non-NULL ones) zeroed
@@ -132,7 +136,9 @@ hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
 int decode_blocks(int dtype, int bh, int d, int dh);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
-int grad_hidden_per_block(int dtype, int d);
+// Hidden units per workgroup of the gradient launch (generic: the kernel
+// that fp32 shapes and per-channel learning rates use).
+int grad_hidden_per_block(int dtype, int d, bool generic);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
 // Newton-Schulz in one workgroup per matrix (bf16 operands; steps from
@@ -149,7 +155,7 @@ struct NsStep {
   const float* n1; const float* n3; const float* n2;
   Shadow sh;
   int bh;
-  int renorm;
+  int renorm;      // as StepArgs::renorm
   float eps;
   int* nonfinite;  // NULL, or set to 1 when a row's sum of squares is not finite
 };

@@ -110,7 +110,12 @@ typedef enum { LACT_NS_BF16_SHIFTED = 0, LACT_NS_BF16 = 1, LACT_NS_F32 = 2 } lac
 typedef struct {
   int32_t use_muon;      /* orthogonalise the step with Newton-Schulz-5      */
   int32_t use_momentum;  /* G <- G + beta M, M <- G (beta = mean coefficient) */
-  int32_t renorm;        /* rescale rows to their sequence-start norms       */
+  int32_t renorm;        /* 0: no renorm; 1: every row of W + U rescaled to
+                            its sequence-start norm (the rebuttal page's
+                            loop); 2: master variant (uTTT page section
+                            C.1): w* accumulate W + U unscaled and only the
+                            operand copies, which every read and gradient
+                            uses, hold the rescaled rows                  */
   float renorm_eps;      /* added to the row norm (page: 1e-5)               */
   float ns_eps;          /* added to the Frobenius norm (page: 1e-7)         */
   int32_t ns_prec;       /* lact_ns_prec                                     */
@@ -120,6 +125,14 @@ typedef struct {
                             finite fp32 number (NaN or Inf anywhere in the
                             row).  Nothing waits for it; read it with
                             lact_check_finite or a copy of your own.       */
+  int32_t eta_per_channel; /* 0: eta1, eta3, eta2 hold one rate per token;
+                            1: per channel (the rebuttal page's learning-rate
+                            tensors of shape [b, l, d]): eta1, eta3 are
+                            [bh, *, d] and scale k channel by channel, eta2
+                            is [bh, *, dh] and scales the hidden units;
+                            eta_stride_bh still counts tokens.  Shapes with
+                            d <= 128 (else LACT_ERR_UNSUPPORTED); the
+                            gradient then runs on the generic kernel.      */
 } lact_update_opts;
 
 /* Bytes of lact_state.shadow for this shape. */

@@ -35,6 +35,10 @@ Everything is the plain definition, in float64, one (batch, head) at a time:
 * step + L2 row renorm: W <- W + G, then each row rescaled to its norm at
   sequence start, with eps 1e-5 added to the current norm (rebuttal page,
   end of the chunk loop; summary page section 3.2 Eq. 8).
+* variant "master" (uTTT page section C.1): the steps accumulate into a
+  master state S <- S + G that is never rescaled, and the weights that reads
+  and gradients use are a fast copy, S with every row rescaled to its
+  sequence-start norm after each write (W0 itself before the first write).
 * orderings (summary page section 3.1 / Fig. 3; rebuttal page, the two
   functions and the answer on the video experiment).
 
@@ -126,9 +130,21 @@ def chunk_gradient(W1, W3, W2, K, V, eta1, eta3, eta2):
       G2  = sum_t eta2_t v_t (silu(g_t) * u_t)^T          [d, dh]
       G3  = sum_t eta3_t (e_t * silu(g_t)) k_t^T          [dh, d]
       G1  = sum_t eta1_t (e_t * u_t * silu'(g_t)) k_t^T   [dh, d]
+
+    Per-channel variant (rebuttal page: the learning-rate tensors of the
+    block-causal function are [b, l, d] or [b, l, 1]): eta1, eta3 of shape
+    [n, d] scale k_t channel by channel (G1 = sum_t (e u silu') (eta1_t * k_t)^T,
+    likewise G3) and eta2 of shape [n, dh] scales the hidden activations
+    (G2 = sum_t v_t (eta2_t * h_t)^T), which is where the page multiplies
+    them in; with one value per token the two forms coincide.
     """
     W1, W3, W2, K, V = _f64(W1), _f64(W3), _f64(W2), _f64(K), _f64(V)
-    eta1, eta3, eta2 = _f64(eta1).reshape(-1), _f64(eta3).reshape(-1), _f64(eta2).reshape(-1)
+
+    def per(eta):
+        eta = _f64(eta)
+        return eta if eta.ndim == 2 else eta.reshape(-1)[:, None]
+
+    eta1, eta3, eta2 = per(eta1), per(eta3), per(eta2)
     g = K @ W1.T                      # [n, dh]
     u = K @ W3.T                      # [n, dh]
     e = V @ W2                        # [n, dh]  rows are (W2^T v_t)^T
@@ -136,9 +152,9 @@ def chunk_gradient(W1, W3, W2, K, V, eta1, eta3, eta2):
     h = s * u
     d_up = e * s
     d_gate = e * u * silu_grad(g)
-    G2 = V.T @ (h * eta2[:, None])            # [d, dh]
-    G3 = (d_up * eta3[:, None]).T @ K         # [dh, d]
-    G1 = (d_gate * eta1[:, None]).T @ K       # [dh, d]
+    G2 = V.T @ (h * eta2)             # [d, dh]
+    G3 = d_up.T @ (K * eta3)          # [dh, d]
+    G1 = d_gate.T @ (K * eta1)        # [dh, d]
     return G1, G3, G2
 
 
@@ -176,9 +192,21 @@ def step_renorm(W, U, n0, eps=RENORM_EPS):
 
 
 # ------------------------------------------------------- one head state ----
+RENORM_OFF, RENORM_ROWS, RENORM_MASTER = 0, 1, 2
+
+
+def renorm_mode(renorm):
+    """True / False / "master" (or the mode number) -> RENORM_* mode."""
+    if renorm == "master" or renorm == RENORM_MASTER:
+        return RENORM_MASTER
+    return RENORM_ROWS if renorm else RENORM_OFF
+
+
 class HeadState:
-    """Fast-weight state of one (batch, head): W, the sequence-start row
-    norms, and the momentum buffers (zero at sequence start)."""
+    """Fast-weight state of one (batch, head): W (the weights reads and
+    gradients use), the sequence-start row norms, the momentum buffers (zero
+    at sequence start) and, once a "master" write has happened, the master
+    state S1, S3, S2 (None before)."""
 
     def __init__(self, W1, W3, W2):
         self.W1, self.W3, self.W2 = _f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()
@@ -186,11 +214,12 @@ class HeadState:
         self.M1 = np.zeros_like(self.W1)
         self.M3 = np.zeros_like(self.W3)
         self.M2 = np.zeros_like(self.W2)
+        self.S1 = self.S3 = self.S2 = None
 
     def copy(self):
         c = HeadState.__new__(HeadState)
         for k, v in self.__dict__.items():
-            c.__dict__[k] = v.copy()
+            c.__dict__[k] = None if v is None else v.copy()
         return c
 
 
@@ -213,7 +242,16 @@ def update(state, K, V, eta1, eta3, eta2, mom=None, use_muon=False,
     pre_ns = (G1.copy(), G3.copy(), G2.copy())
     if use_muon:
         G1, G3, G2 = newton_schulz5(G1), newton_schulz5(G3), newton_schulz5(G2)
-    if renorm:
+    mode = renorm_mode(renorm)
+    if mode == RENORM_MASTER:
+        if s.S1 is None:   # the master starts at the weights of the first write
+            s.S1, s.S3, s.S2 = s.W1.copy(), s.W3.copy(), s.W2.copy()
+        s.S1, s.S3, s.S2 = s.S1 + G1, s.S3 + G3, s.S2 + G2
+        zero = np.zeros_like
+        s.W1 = step_renorm(s.S1, zero(s.S1), s.n1)
+        s.W3 = step_renorm(s.S3, zero(s.S3), s.n3)
+        s.W2 = step_renorm(s.S2, zero(s.S2), s.n2)
+    elif mode == RENORM_ROWS:
         s.W1 = step_renorm(s.W1, G1, s.n1)
         s.W3 = step_renorm(s.W3, G3, s.n3)
         s.W2 = step_renorm(s.W2, G2, s.n2)

@@ -177,3 +177,15 @@ def test_decode_checks(lib):
     assert call(1, None, need) == 4
     assert call(1, 4096, need, o=256) == 1
     assert call(0, None, 0) == 0          # nothing to read: nothing enqueued
+
+
+def test_per_channel_eta_checks(lib):
+    """Per-channel learning rates are for d <= 128; other values of the flag
+    are invalid."""
+    lay = L.Layout(512 * 256, 256)
+    st = L.State(*([256] * 10))
+    for d, flag, code in ((256, 1, 2), (128, 2, 1)):
+        sh = L.Shape(2, d, 1024, L.BF16)
+        o = L.opts(eta_per_channel=flag)
+        assert lib.lact_update(ctypes.byref(sh), ctypes.byref(st), 256, lay, 512, lay, 1024, 1024, 1024, None,
+                               100, 100, ctypes.byref(o), 4096, 1 << 30, None) == code

@@ -418,3 +418,87 @@ def test_nonfinite_flag(device, wi, renorm):
     # other heads are independent: their weights stay finite
     if w.bh > 1:
         assert torch.isfinite(fw.w1[1:]).all() and torch.isfinite(fw.w2[1:]).all()
+
+
+@pytest.mark.parametrize("wi", [1, 2, 3, 4])
+def test_sequence_master_variant(device, wi):
+    """Master-state variant (renorm = 2; uTTT page section C.1): the fp32
+    state accumulates W + U unscaled and the operand copies that reads and
+    gradients use hold its rows rescaled to the sequence-start norms.  Whole
+    sequences against the oracle's "master" mode: outputs, and the master
+    state itself; the copies are the rescaled master rows."""
+    import dataclasses
+    import torch
+    T, C, sub = SEQ_CASES[wi]
+    w = small(wi, T, C, subset=sub)
+    W, inp = inputs(w)
+    q, k, v = (H.act_to_dev(w, inp, n, device) for n in ("q", "k", "v"))
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    mom = torch.from_numpy(inp["mom"]).to(device) if inp["mom"] is not None else None
+    out = H.out_buffer(w, w.T, device)
+    fw = H.make_state(w, W, device)
+    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=2)
+    max_upd = max(z - a for _, a, z in w.writes())
+    ws = torch.full(((L.workspace_bytes(fw.shape, max_upd, o) + 3) // 4,), float("nan"), device=device)
+    print(f"master variant wl={wi} T={w.T} C={w.chunk}", flush=True)
+    L.lact_sequence(fw.shape, fw, q, k, v, out, eta, eta, eta, mom, w.T, w.chunk, w.order, w.subset,
+                    int(w.update_last), o, ws)
+    torch.cuda.synchronize()
+    got = H.to64(out)
+    W1, W3, W2, *_ = H.state64(fw)
+    for b in range(w.bh):
+        m = None if inp["mom"] is None else inp["mom"][b]
+        e = inp["eta"][b]
+        ref, st = O.sequence(W[0][b], W[1][b], W[2][b], inp["q"][b], inp["k"][b], inp["v"][b], e, e, e,
+                             w.chunk, mom=m, order=w.order, subset=w.subset, update_last=w.update_last,
+                             use_muon=w.use_muon, use_momentum=w.use_momentum, renorm="master")
+        assert H.rel(got[b], ref) < 2e-2, (b, H.rel(got[b], ref))
+        assert H.rel(W1[b], st.S1) < 2e-2 and H.rel(W2[b], st.S2) < 2e-2
+        # the master is not rescaled: its rows drift from the sequence-start
+        # norms by far more than the renorm eps would (1e-5 relative)
+        assert np.max(np.abs(np.sqrt((W1[b] ** 2).sum(1)) / st.n1 - 1.0)) > 1e-3
+    m = w.d * w.dh
+    sh = fw.shadow.view(torch.bfloat16).view(w.bh, 4, m).float().cpu().numpy().astype(np.float64)
+    n1 = H.to64(fw.n1)
+    for b in range(w.bh):
+        want = W1[b] * (n1[b] / (np.sqrt((W1[b] ** 2).sum(1)) + 1e-5))[:, None]
+        assert H.rel(sh[b, 0].reshape(w.dh, w.d), want) < 1e-2
+
+
+@pytest.mark.parametrize("wi", [0, 1, 3])
+def test_sequence_per_channel_eta(device, wi):
+    """Per-channel learning rates (the rebuttal page's [b, l, d] learning-rate
+    tensors): eta1, eta3 [bh, T, d] scale k channel by channel, eta2
+    [bh, T, dh] the hidden units.  Whole sequences (Muon, momentum, subset
+    as the family has them) against the oracle with the same rates."""
+    import torch
+    T, C, sub = SEQ_CASES[wi]
+    w = small(wi, T, C, subset=sub)
+    if wi == 0:
+        w = WL.WORKLOADS[0].scaled(T=3 * 128 + 40, chunk=128)
+    W, inp = inputs(w)
+    rng = np.random.default_rng(40 + wi)
+    sp = lambda shape: (np.log1p(np.exp(rng.standard_normal(shape))) * 1e-2).astype(np.float32)
+    e1, e3, e2 = sp((w.bh, w.T, w.d)), sp((w.bh, w.T, w.d)), sp((w.bh, w.T, w.dh))
+    q, k, v = (H.act_to_dev(w, inp, n, device) for n in ("q", "k", "v"))
+    et = [torch.from_numpy(x).to(device) for x in (e1, e3, e2)]
+    mom = torch.from_numpy(inp["mom"]).to(device) if inp["mom"] is not None else None
+    out = H.out_buffer(w, w.T, device)
+    fw = H.make_state(w, W, device)
+    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm, eta_per_channel=True)
+    max_upd = max(z - a for _, a, z in w.writes())
+    ws = torch.full(((L.workspace_bytes(fw.shape, max_upd, o) + 3) // 4,), float("nan"), device=device)
+    print(f"per-channel eta wl={wi} T={w.T} C={w.chunk}", flush=True)
+    L.lact_sequence(fw.shape, fw, q, k, v, out, et[0], et[1], et[2], mom, w.T, w.chunk, w.order, w.subset,
+                    int(w.update_last), o, ws)
+    torch.cuda.synchronize()
+    got = H.to64(out)
+    W1, W3, W2, *_ = H.state64(fw)
+    for b in range(w.bh):
+        m = None if inp["mom"] is None else inp["mom"][b]
+        ref, st = O.sequence(W[0][b], W[1][b], W[2][b], inp["q"][b], inp["k"][b], inp["v"][b], e1[b], e3[b],
+                             e2[b], w.chunk, mom=m, order=w.order, subset=w.subset, update_last=w.update_last,
+                             use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+        assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
+        assert H.rel(W1[b], st.W1) < H.TOL[w.dtype] and H.rel(W2[b], st.W2) < H.TOL[w.dtype]
+    H.check_shadow(fw)

@@ -141,6 +141,45 @@ def test_gradient_eta_selects_matrix():
     assert np.abs(G1).max() == 0 and np.abs(G3).max() == 0 and np.abs(G2).max() > 0
 
 
+def test_gradient_per_channel_eta_brute_force():
+    """Per-channel learning rates: scalar loops of the definition
+    G1[j][i] = sum_t (e u silu')_tj eta1_ti k_ti (likewise G3 with e s) and
+    G2[i][j] = sum_t v_ti eta2_tj h_tj; and constant channels reduce to the
+    per-token form."""
+    rng = np.random.default_rng(21)
+    d, dh, n = 3, 5, 4
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    e1, e3 = np.abs(rng.standard_normal((n, d))), np.abs(rng.standard_normal((n, d)))
+    e2 = np.abs(rng.standard_normal((n, dh)))
+    G1, G3, G2 = O.chunk_gradient(W1, W3, W2, K, V, e1, e3, e2)
+    for j in range(dh):
+        for i in range(d):
+            a1 = a3 = 0.0
+            for t in range(n):
+                g = sum(W1[j][x] * K[t][x] for x in range(d))
+                u = sum(W3[j][x] * K[t][x] for x in range(d))
+                e = sum(W2[x][j] * V[t][x] for x in range(d))
+                sg = 1.0 / (1.0 + math.exp(-g))
+                a1 += e * u * sg * (1 + g * (1 - sg)) * e1[t][i] * K[t][i]
+                a3 += e * g * sg * e3[t][i] * K[t][i]
+            assert abs(G1[j][i] - a1) < 1e-13 and abs(G3[j][i] - a3) < 1e-13
+    for i in range(d):
+        for j in range(dh):
+            a2 = 0.0
+            for t in range(n):
+                g = sum(W1[j][x] * K[t][x] for x in range(d))
+                u = sum(W3[j][x] * K[t][x] for x in range(d))
+                a2 += V[t][i] * e2[t][j] * g / (1.0 + math.exp(-g)) * u
+            assert abs(G2[i][j] - a2) < 1e-13
+    c = np.abs(rng.standard_normal(n))
+    per_tok = O.chunk_gradient(W1, W3, W2, K, V, c, c, c)
+    per_ch = O.chunk_gradient(W1, W3, W2, K, V, np.repeat(c[:, None], d, 1), np.repeat(c[:, None], d, 1),
+                              np.repeat(c[:, None], dh, 1))
+    for a, b in zip(per_tok, per_ch):
+        assert np.max(np.abs(a - b)) < 1e-14
+
+
 # ----------------------------------------------------- Newton-Schulz ----
 def _golden_coeffs():
     rows = []
@@ -331,6 +370,35 @@ def test_renorm_targets_are_sequence_start_norms(muon):
                 prev = np.sqrt((W_prev * W_prev).sum(1))
                 assert np.min(np.abs(got - prev * nr / (nr + 1e-5)) / got) > 0.2
         st = new
+
+
+def test_master_state_variant():
+    """Variant with a master state (uTTT page section C.1): over two writes
+    the master is W0 + U1 + U2 (the Newton-Schulz steps, never rescaled),
+    the weights used afterwards are the master's rows rescaled to
+    n0 ||S|| / (||S|| + 1e-5), and the second write's gradient is taken at
+    that rescaled copy, not at the master."""
+    rng = np.random.default_rng(20)
+    d, dh, n = 5, 9, 13
+    W1, W3, W2 = _rand_state(rng, d, dh)
+    n0 = [np.sqrt((W * W).sum(1)) for W in (W1, W3, W2)]
+    st0 = O.HeadState(W1, W3, W2)
+    ks = [rng.standard_normal((n, d)) for _ in range(2)]
+    vs = [rng.standard_normal((n, d)) for _ in range(2)]
+    eta = np.full(n, 0.02)
+    st1, p1 = O.update(st0, ks[0], vs[0], eta, eta, eta, use_muon=True, renorm="master", return_parts=True)
+    st2, p2 = O.update(st1, ks[1], vs[1], eta, eta, eta, use_muon=True, renorm="master", return_parts=True)
+    for i, (W0, S, Wf) in enumerate(zip((W1, W3, W2), (st2.S1, st2.S3, st2.S2), (st2.W1, st2.W3, st2.W2))):
+        assert np.max(np.abs(S - (W0 + p1["step"][i] + p2["step"][i]))) < 1e-14
+        ns = np.sqrt((S * S).sum(1))
+        want = S * (n0[i] / (ns + 1e-5))[:, None]
+        assert np.max(np.abs(Wf - want)) < 1e-14
+    g2 = O.chunk_gradient(st1.W1, st1.W3, st1.W2, ks[1], vs[1], eta, eta, eta)
+    for a, b in zip(p2["raw"], g2):
+        assert np.max(np.abs(a - b)) < 1e-15 * max(1.0, np.max(np.abs(b)))
+    # it differs from rescaling in place (rows of W1 + U2 from the rescaled W1)
+    inplace = O.update(st1, ks[1], vs[1], eta, eta, eta, use_muon=True, renorm=True)
+    assert np.max(np.abs(inplace.W1 - st2.W1)) > 1e-3
 
 
 # ---------------------------------------------------------- orderings ----
