@@ -86,6 +86,11 @@ def load():
                                         I64, I64, I32, pO, P]),
         "lact_decode_workspace_bytes": (SZ, [pS, I64]),
         "lact_decode_apply": (I32, [pS, pSt, P, L, P, L, I64, P, SZ, P]),
+        "lact_linear_shadow_bytes": (SZ, [pS]),
+        "lact_linear_workspace_bytes": (SZ, [pS, pO]),
+        "lact_linear_init_state": (I32, [pS, P, P]),
+        "lact_linear_sequence": (I32, [pS, P, P, L, P, L, P, L, P, L, P, P, I64, I64, I64, I32, I64, I64, I32,
+                                       pO, P, SZ, P]),
         "lact_prof_begin": (I32, [I32, I32]),
         "lact_prof_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(F), ctypes.POINTER(F),
                                 ctypes.POINTER(F)]),
@@ -301,3 +306,44 @@ def lact_sequence_noalloc(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, T, chu
                                         _eta_stride(eta1), int(T), int(chunk), int(order), int(sub_off),
                                         int(sub_len), int(update_last), ctypes.byref(o), _stream(stream)),
            "lact_sequence_noalloc")
+
+
+# ---------------------------------------------------- linear variant ----
+class LinearState(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w", "n", "m", "shadow")]
+
+
+class LinearWeights:
+    """Device buffers of one lact_linear_state (w [bh, d, d] fp32)."""
+
+    def __init__(self, shape, w, momentum=True):
+        import torch
+        dev = w.device
+        self.shape = shape
+        self.w = w.detach().to(dev, torch.float32).contiguous().clone()
+        self.n = torch.empty(shape.bh, shape.d, device=dev)
+        self.m = torch.empty_like(self.w) if momentum else None
+        self.shadow = torch.empty(load().lact_linear_shadow_bytes(ctypes.byref(shape)), dtype=torch.uint8,
+                                  device=dev)
+        self.struct = LinearState(*(_ptr(x) for x in (self.w, self.n, self.m, self.shadow)))
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def linear_workspace_bytes(shape, o):
+    return load().lact_linear_workspace_bytes(ctypes.byref(shape), ctypes.byref(o))
+
+
+def lact_linear_init_state(shape, lw, stream=None):
+    _check(load().lact_linear_init_state(ctypes.byref(shape), lw.ref(), _stream(stream)), "lact_linear_init_state")
+
+
+def lact_linear_sequence(shape, lw, q, k, v, out, eta, mom, T, chunk, order, subset, update_last, o, ws,
+                         stream=None):
+    sub_off, sub_len = (0, -1) if subset is None else subset
+    _check(load().lact_linear_sequence(ctypes.byref(shape), lw.ref(), _ptr(q), layout_of(q), _ptr(k), layout_of(k),
+                                       _ptr(v), layout_of(v), _ptr(out), layout_of(out), _ptr(eta), _ptr(mom),
+                                       eta.stride(0), int(T), int(chunk), int(order), int(sub_off), int(sub_len),
+                                       int(update_last), ctypes.byref(o), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "lact_linear_sequence")

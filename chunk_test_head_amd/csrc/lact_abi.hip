@@ -858,6 +858,125 @@ lact_status lact_sequence_noalloc(LACT_SEQ_PARAMS, void* stream) {
   return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream);
 }
 
+// ------------------------------------------------- linear variant --
+size_t lact_linear_shadow_bytes(const lact_shape* sh) {
+  if (check_shape(sh) != LACT_OK || sh->dh != sh->d) return 0;
+  return (size_t)sh->bh * sh->d * sh->d * elem_size(sh->dtype);
+}
+
+size_t lact_linear_workspace_bytes(const lact_shape* sh, const lact_update_opts* opts) {
+  if (check_shape(sh) != LACT_OK || sh->dh != sh->d) return 0;
+  const int64_t g = align256((int64_t)sh->bh * sh->d * sh->d * 4);
+  const bool muon = opts != nullptr && opts->use_muon;
+  return (size_t)(g + (muon ? ns_ws_bytes(sh->bh, sh->d, sh->d) : 0));
+}
+
+static lact_status check_linear(const lact_shape* sh, const lact_linear_state* st, bool need_m) {
+  lact_status r;
+  if ((r = check_shape(sh)) != LACT_OK) return r;
+  if (sh->dh != sh->d) return LACT_ERR_UNSUPPORTED;
+  if (st == nullptr || st->w == nullptr || st->n == nullptr || st->shadow == nullptr) return LACT_ERR_INVALID_ARG;
+  if (!aligned16(st->w) || !aligned16(st->n) || !aligned16(st->shadow)) return LACT_ERR_ALIGNMENT;
+  if (need_m && st->m == nullptr) return LACT_ERR_INVALID_ARG;
+  if (st->m != nullptr && !aligned16(st->m)) return LACT_ERR_ALIGNMENT;
+  return LACT_OK;
+}
+
+static LinArgs lin_args(const lact_shape* sh, const lact_linear_state* st) {
+  LinArgs a;
+  memset(&a, 0, sizeof(a));
+  a.w = st->w; a.n = st->n; a.m = st->m; a.shadow = st->shadow;
+  a.bh = sh->bh; a.d = sh->d;
+  return a;
+}
+
+lact_status lact_linear_init_state(const lact_shape* sh, const lact_linear_state* st, void* stream) {
+  lact_status r;
+  if ((r = check_linear(sh, st, false)) != LACT_OK) return r;
+  const LinArgs a = lin_args(sh, st);
+  const hipError_t e = launch_linear(sh->dtype, 3, a, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+lact_status lact_linear_sequence(const lact_shape* sh, const lact_linear_state* st, const void* q,
+                                 lact_layout ql, const void* k, lact_layout kl, const void* v,
+                                 lact_layout vl, void* o, lact_layout ol, const float* eta,
+                                 const float* mom, int64_t esbh, int64_t T, int64_t chunk,
+                                 int32_t order, int64_t sub_off, int64_t sub_len, int32_t update_last,
+                                 const lact_update_opts* op, void* ws, size_t ws_bytes, void* stream) {
+  lact_status r;
+  if ((r = check_opts(op)) != LACT_OK) return r;
+  if (op->eta_per_channel) return LACT_ERR_UNSUPPORTED;
+  if ((r = check_linear(sh, st, op->use_momentum != 0)) != LACT_OK) return r;
+  if (T < 0 || chunk < 1 || esbh < 0) return LACT_ERR_INVALID_ARG;
+  if (order != LACT_APPLY_THEN_UPDATE && order != LACT_UPDATE_THEN_APPLY) return LACT_ERR_INVALID_ARG;
+  if (sub_len >= 0 && (sub_off < 0 || sub_off >= chunk)) return LACT_ERR_INVALID_ARG;
+  if ((r = check_act(sh, q, ql, T)) != LACT_OK) return r;
+  if ((r = check_act(sh, o, ol, T)) != LACT_OK) return r;
+  if ((r = check_act(sh, k, kl, T)) != LACT_OK) return r;
+  if ((r = check_act(sh, v, vl, T)) != LACT_OK) return r;
+  if (T > 0 && (q == o || eta == nullptr)) return LACT_ERR_INVALID_ARG;
+  if (op->use_momentum && T > 0 && mom == nullptr) return LACT_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < lact_linear_workspace_bytes(sh, op)) return LACT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  const int es = elem_size(sh->dtype);
+  LinArgs a = lin_args(sh, st);
+  a.renorm = op->renorm; a.eps = op->renorm_eps; a.nonfinite = op->nonfinite;
+  a.eta_sbh = esbh; a.mom_sbh = esbh;
+  if (!op->use_momentum) a.m = nullptr;
+  char* wsb = reinterpret_cast<char*>(ws);
+  a.g = reinterpret_cast<float*>(wsb);
+  const int64_t gsz = align256((int64_t)sh->bh * sh->d * sh->d * 4);
+  auto read = [&](int64_t s0, int64_t n) {
+    LinArgs x = a;
+    x.q = reinterpret_cast<const char*>(q) + s0 * ql.stride_tok * es; x.q_sbh = ql.stride_bh; x.q_st = ql.stride_tok;
+    x.o = reinterpret_cast<char*>(o) + s0 * ol.stride_tok * es; x.o_sbh = ol.stride_bh; x.o_st = ol.stride_tok;
+    x.n_tok = n;
+    const hipError_t e = launch_linear(sh->dtype, 0, x, nullptr, s);
+    return e == hipSuccess ? LACT_OK : hip_fail(e);
+  };
+  auto write = [&](int64_t a0, int64_t n) {
+    LinArgs x = a;
+    x.k = reinterpret_cast<const char*>(k) + a0 * kl.stride_tok * es; x.k_sbh = kl.stride_bh; x.k_st = kl.stride_tok;
+    x.v = reinterpret_cast<const char*>(v) + a0 * vl.stride_tok * es; x.v_sbh = vl.stride_bh; x.v_st = vl.stride_tok;
+    x.eta = eta + a0;
+    x.mom = mom != nullptr ? mom + a0 : nullptr;
+    x.n_tok = n;
+    hipError_t e = launch_linear(sh->dtype, 1, x, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (op->use_muon) {
+      const int prec = ns_prec_of(sh, op);
+      float* nb = reinterpret_cast<float*>(wsb + gsz);
+      const int64_t xm = align256((int64_t)sh->bh * sh->d * sh->d * 4);
+      const int64_t am = align256((int64_t)sh->bh * sh->d * sh->d * 4);
+      char* b = reinterpret_cast<char*>(nb);
+      const NsIn in{{a.g, a.g, a.g}, sh->bh};
+      e = run_ns(prec, sh->bh, sh->d, sh->d, in, a.g, op->ns_eps, reinterpret_cast<float*>(b),
+                 reinterpret_cast<float*>(b + xm), reinterpret_cast<float*>(b + 2 * xm),
+                 reinterpret_cast<float*>(b + 3 * xm), reinterpret_cast<float*>(b + 3 * xm + am),
+                 reinterpret_cast<float*>(b + 3 * xm + 2 * am), s);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    e = launch_linear(sh->dtype, 2, x, a.g, s);
+    return e == hipSuccess ? LACT_OK : hip_fail(e);
+  };
+  for (int64_t s0 = 0; s0 < T; s0 += chunk) {
+    const int64_t e0 = s0 + chunk < T ? s0 + chunk : T;
+    const bool last = e0 == T;
+    int64_t a0 = s0, a1 = e0;
+    if (sub_len >= 0) {
+      a0 = s0 + sub_off;
+      a1 = a0 + sub_len < e0 ? a0 + sub_len : e0;
+    }
+    const bool do_write = ((order == LACT_UPDATE_THEN_APPLY) || !last || update_last) && a1 > a0;
+    if (order == LACT_APPLY_THEN_UPDATE && (r = read(s0, e0 - s0)) != LACT_OK) return r;
+    if (do_write && (r = write(a0, a1 - a0)) != LACT_OK) return r;
+    if (order == LACT_UPDATE_THEN_APPLY && (r = read(s0, e0 - s0)) != LACT_OK) return r;
+  }
+  return LACT_OK;
+}
+
 lact_status lact_prof_begin(int32_t kind, int32_t max_launches) {
   if (kind < LACT_PROF_APPLY || kind > LACT_PROF_STEP || max_launches < 1) return LACT_ERR_INVALID_ARG;
   if (g_prof.kind != 0) return LACT_ERR_INVALID_ARG;

@@ -34,6 +34,24 @@ struct DecodeArgs {
   float* part;
 };
 
+// Linear fast-weight variant (k_linear.hip): one d x d matrix per head.
+struct LinArgs {
+  const void* q; int64_t q_sbh, q_st;
+  void* o; int64_t o_sbh, o_st;
+  const void* k; int64_t k_sbh, k_st;
+  const void* v; int64_t v_sbh, v_st;
+  const float* eta; int64_t eta_sbh;   // one rate per token
+  const float* mom; int64_t mom_sbh;   // momentum coefficients (with m)
+  float* w; float* n; float* m;        // [bh][d][d], [bh][d], [bh][d][d] or NULL
+  void* shadow;                        // [bh][d][d] operand copy
+  float* g;                            // [bh][d][d] gradient (+ momentum)
+  int bh, d;
+  int64_t n_tok;
+  int renorm; float eps;
+  int* nonfinite;
+};
+hipError_t launch_linear(int dtype, int what, const LinArgs& a, const float* U, hipStream_t s);
+
 struct GradArgs {
   const void* k; int64_t k_sbh, k_st;
   const void* v; int64_t v_sbh, v_st;

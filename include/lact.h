@@ -289,6 +289,38 @@ lact_status lact_sequence_noalloc(const lact_shape* shape, const lact_state* sta
                                   int32_t update_last, const lact_update_opts* opts,
                                   void* stream);
 
+/* Linear fast-weight variant (the rebuttal page's comparison of fast-weight
+ * networks, Fig. 8(a)): one d x d matrix per head, f_W(x) = W x.  A write's
+ * descent direction of -sum_t eta_t <W k_t, v_t> is G = sum_t eta_t v_t k_t^T
+ * (one rate per token); momentum, Newton-Schulz (opts->ns_prec, on the
+ * square matrix), the step and the renorm modes are those of lact_update.
+ * shape.dh must equal shape.d (d in {64, 128, 256}, bf16 or fp32).
+ *   w : [bh, d, d] fp32 (row-major)   n : [bh, d] sequence-start row norms
+ *   m : [bh, d, d] momentum (NULL without momentum)
+ *   shadow : lact_linear_shadow_bytes() operand copy.
+ * lact_linear_sequence has the arguments and orderings of lact_sequence with
+ * one learning-rate array; workspace: lact_linear_workspace_bytes(). */
+typedef struct {
+  float* w;
+  float* n;
+  float* m;
+  void* shadow;
+} lact_linear_state;
+size_t lact_linear_shadow_bytes(const lact_shape* shape);
+size_t lact_linear_workspace_bytes(const lact_shape* shape, const lact_update_opts* opts);
+lact_status lact_linear_init_state(const lact_shape* shape, const lact_linear_state* state,
+                                   void* stream);
+lact_status lact_linear_sequence(const lact_shape* shape, const lact_linear_state* state,
+                                 const void* q, lact_layout q_layout,
+                                 const void* k, lact_layout k_layout,
+                                 const void* v, lact_layout v_layout,
+                                 void* o, lact_layout o_layout,
+                                 const float* eta, const float* mom, int64_t eta_stride_bh,
+                                 int64_t T, int64_t chunk, int32_t order,
+                                 int64_t subset_offset, int64_t subset_len,
+                                 int32_t update_last, const lact_update_opts* opts,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernel timing for benchmarks.  lact_prof_begin(kind, max_launches)
  * creates 2 * max_launches HIP events; until lact_prof_end, every launch of
  * the kernel `kind` made by the calls above is bracketed by events recorded

@@ -318,3 +318,61 @@ def sequence(W1, W3, W2, Q, K, V, eta1, eta3, eta2, chunk, mom=None,
         return O, st, states
     return O, st
 
+
+
+# ------------------------------------------- linear fast-weight variant ----
+# The rebuttal page compares fast-weight networks (Fig. 8(a)); the simplest
+# is linear, f_W(x) = W x with one d x d matrix per head.  Its associative
+# loss L = -sum_t eta_t <W k_t, v_t> has the descent direction
+# G = sum_t eta_t v_t k_t^T, which does not depend on W; momentum, Muon, the
+# step and the row renorm are those of the SwiGLU layer.
+
+def linear_apply(W, X):
+    """Read of the linear variant: rows of X are tokens; returns W x_t."""
+    return _f64(X) @ _f64(W).T
+
+
+def linear_gradient(K, V, eta):
+    """G = sum_t eta_t v_t k_t^T  [d, d]."""
+    K, V = _f64(K), _f64(V)
+    return (V * _f64(eta).reshape(-1)[:, None]).T @ K
+
+
+def linear_sequence(W, Q, K, V, eta, chunk, mom=None, order=ORDER_APPLY_THEN_UPDATE,
+                    subset=None, update_last=False, use_muon=False, use_momentum=False,
+                    renorm=True):
+    """Whole sequence of the linear variant for one head, with the orderings
+    and renorm modes of ``sequence``.  Returns O [T, d] and the final
+    (W, M) - W being the master state in the "master" mode."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    W = _f64(W).copy()
+    n0 = row_norms(W)
+    M = np.zeros_like(W)
+    mode = renorm_mode(renorm)
+    S = W.copy()   # the master state of the "master" mode
+    T = Q.shape[0]
+    O = np.zeros((T, W.shape[0]))
+    bounds = chunk_bounds(T, chunk)
+    for ci, (s, e) in enumerate(bounds):
+        last = ci == len(bounds) - 1
+        a, b = (s, e) if subset is None else (s + subset[0], min(s + subset[0] + subset[1], e))
+        writes = (order == ORDER_UPDATE_THEN_APPLY or not last or update_last) and b > a
+        if order == ORDER_APPLY_THEN_UPDATE:
+            O[s:e] = linear_apply(W, Q[s:e])
+        if writes:
+            G = linear_gradient(K[a:b], V[a:b], _f64(eta)[a:b])
+            if use_momentum:
+                beta = float(np.mean(_f64(mom)[a:b]))
+                G, M = momentum_step(G, M, beta)
+            if use_muon:
+                G = newton_schulz5(G)
+            if mode == RENORM_MASTER:
+                S = S + G
+                W = step_renorm(S, np.zeros_like(S), n0)
+            elif mode == RENORM_ROWS:
+                W = step_renorm(W, G, n0)
+            else:
+                W = W + G
+        if order == ORDER_UPDATE_THEN_APPLY:
+            O[s:e] = linear_apply(W, Q[s:e])
+    return O, (S if mode == RENORM_MASTER else W, M)

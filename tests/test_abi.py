@@ -189,3 +189,19 @@ def test_per_channel_eta_checks(lib):
         o = L.opts(eta_per_channel=flag)
         assert lib.lact_update(ctypes.byref(sh), ctypes.byref(st), 256, lay, 512, lay, 1024, 1024, 1024, None,
                                100, 100, ctypes.byref(o), 4096, 1 << 30, None) == code
+
+
+def test_linear_variant_checks(lib):
+    """The linear variant has one d x d matrix: shape.dh must equal d; a
+    missing momentum buffer or a short workspace is rejected on the host."""
+    st = L.LinearState(256, 256, 0, 256)
+    assert lib.lact_linear_init_state(ctypes.byref(L.Shape(2, 128, 512, L.BF16)), ctypes.byref(st), None) == 2
+    sh = L.Shape(2, 128, 128, L.BF16)
+    assert L.linear_workspace_bytes(L.Shape(2, 128, 512, L.BF16), L.opts()) == 0
+    lay = L.Layout(512 * 128, 128)
+    def call(o, wsb):
+        return lib.lact_linear_sequence(ctypes.byref(sh), ctypes.byref(st), 256, lay, 512, lay, 768, lay, 1024, lay,
+                                        2048, 2048, 100, 100, 50, 0, 0, -1, 0, ctypes.byref(o), 4096, wsb, None)
+    assert call(L.opts(use_momentum=True), 1 << 30) == 1          # no momentum buffer
+    o = L.opts(use_muon=True)
+    assert call(o, L.linear_workspace_bytes(sh, o) - 1) == 4

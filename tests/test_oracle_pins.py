@@ -401,6 +401,38 @@ def test_master_state_variant():
     assert np.max(np.abs(inplace.W1 - st2.W1)) > 1e-3
 
 
+def test_linear_variant_gradient_and_sequence():
+    """Linear fast weight f_W(x) = W x: the gradient is -dL/dW of
+    L = -sum eta <W k, v> (central differences), and one write from W0
+    followed by a read is, written out by hand, the rows of W0 + NS(G)
+    rescaled to their initial norms, applied to the next chunk's queries."""
+    rng = np.random.default_rng(22)
+    d, n = 4, 6
+    W = rng.standard_normal((d, d)) * 0.5
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    eta = np.abs(rng.standard_normal(n))
+    G = O.linear_gradient(K, V, eta)
+    loss = lambda W_: -sum(eta[t] * float(np.dot(W_ @ K[t], V[t])) for t in range(n))
+    h = 1e-6
+    for i in range(d):
+        for j in range(d):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += h
+            Wm[i, j] -= h
+            assert abs(-(loss(Wp) - loss(Wm)) / (2 * h) - G[i, j]) < 1e-7
+    Q = rng.standard_normal((2 * n, d))
+    Kk = np.concatenate([K, rng.standard_normal((n, d))])
+    Vv = np.concatenate([V, rng.standard_normal((n, d))])
+    ee = np.concatenate([eta, eta])
+    out, (Wf, _) = O.linear_sequence(W, Q, Kk, Vv, ee, n, use_muon=True)
+    assert np.max(np.abs(out[:n] - Q[:n] @ W.T)) < 1e-14
+    R = W + _ns_matrix_iteration(G)
+    n0 = np.sqrt((W * W).sum(1))
+    W1 = R / (np.sqrt((R * R).sum(1)) + 1e-5)[:, None] * n0[:, None]
+    assert np.max(np.abs(out[n:] - Q[n:] @ W1.T)) < 1e-12
+    assert np.max(np.abs(Wf - W1)) < 1e-12   # the last chunk is not written
+
+
 # ---------------------------------------------------------- orderings ----
 def _seq_inputs(rng, T, d, dh):
     W = _rand_state(rng, d, dh)
