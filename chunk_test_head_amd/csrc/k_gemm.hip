@@ -115,9 +115,11 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s) {
 // transpose reads of the [k][n] tile.  The result tile goes through LDS so
 // that D, C and Ch move as whole 16-byte row pieces.  beta' and diag' take
 // the step's shift mu into account (NsGemmArgs), and the launch can leave the
-// sum of squares of every result tile for the next step's mu.  The small slabs keep
-// the LDS at 40 KiB, four workgroups per CU: the loop is bound by the
-// latency of each slab's loads, so more workgroups in flight is what counts.
+// sum of squares of every result tile for the next step's mu.  The loop is
+// bound by the latency of the slabs' loads (a slab is only 8 MFMAs per
+// wave), so four slabs are in flight in registers ahead of the LDS stores,
+// and the epilogue's D tile is loaded before the loop; the small slabs keep
+// the LDS at 40 KiB.
 namespace {
 constexpr int NSG_T = 64, NSG_K = 64;
 constexpr int NSG_PA = NSG_K + 16;                    // [m][k] / [n][k] tiles
@@ -127,6 +129,7 @@ constexpr int NSG_RA = NSG_K / 8;                     // vectors per [m][k] row
 constexpr int NSG_SA = NSG_T * NSG_PA;                // elements per A stage
 constexpr int NSG_SB = NSG_T * NSG_PA > NSG_K * NSG_PB ? NSG_T * NSG_PA : NSG_K * NSG_PB;
 constexpr int NSG_PC = NSG_T + 4;                     // fp32 result tile pitch
+constexpr int NSG_PD = 4;                             // K slabs in flight
 }
 
 template <bool BKN>
@@ -137,75 +140,107 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
   const int c = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int tn = a.N / NSG_T;
-  const int m0 = (blockIdx.x / tn) * NSG_T, n0 = (blockIdx.x % tn) * NSG_T;
-  const int64_t bidx = blockIdx.y;
+  // one launch-wide id per (matrix, tile), dealt so that the tiles of a
+  // matrix run on one or two XCDs and share their L2's copy of the operands
+  const int ntile = (a.M / NSG_T) * tn;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tile = lid % ntile;
+  const int m0 = (tile / tn) * NSG_T, n0 = (tile % tn) * NSG_T;
+  const int64_t bidx = lid / ntile;
   const bf16* A = a.A + bidx * a.a_bs;
   const bf16* B = a.B + bidx * a.b_bs;
 
   // staging: 16-byte vectors vi = tid + 256 x; A: row vi / 16, chunk vi % 16
-  // ([m][k]); B: [n][k] likewise, or ([k][n]) row vi / 8, chunk vi % 8
-  bf16x8 ra[NSG_VA], rb[NSG_VA];
-  // (K is a multiple of 64)
-#define LACT_NSG_GLOAD(K0)                                                                   \
+  // ([m][k]); B: [n][k] likewise, or ([k][n]) row vi / 8, chunk vi % 8.
+  // NSG_PD slabs are in flight in registers (the loop is bound by load
+  // latency, not by the few MFMAs per slab): slab j sits in slot j % NSG_PD
+  // until it is stored to LDS buffer j % 2, and its slot is then refilled
+  // with slab j + NSG_PD.
+  constexpr int PD = NSG_PD;
+  bf16x8 ra[PD][NSG_VA], rb[PD][NSG_VA];
+  const int nslab = a.K / NSG_K;  // (K is a multiple of 64)
+#define LACT_NSG_GLOAD(P, K0)                                                                \
   {                                                                                          \
     _Pragma("unroll") for (int x = 0; x < NSG_VA; ++x) {                                     \
       const int vi = tid + 256 * x;                                                          \
       const int ka = (K0) + 8 * (vi % NSG_RA), kb = BKN ? (K0) + (vi >> 3) : ka;             \
-      ra[x] = ld8(A + (int64_t)(m0 + vi / NSG_RA) * a.lda + ka);                              \
-      rb[x] = BKN ? ld8(B + (int64_t)kb * a.ldb + n0 + 8 * (vi & 7))                           \
-                  : ld8(B + (int64_t)(n0 + vi / NSG_RA) * a.ldb + kb);                         \
+      ra[P][x] = ld8(A + (int64_t)(m0 + vi / NSG_RA) * a.lda + ka);                           \
+      rb[P][x] = BKN ? ld8(B + (int64_t)kb * a.ldb + n0 + 8 * (vi & 7))                        \
+                     : ld8(B + (int64_t)(n0 + vi / NSG_RA) * a.ldb + kb);                      \
     }                                                                                        \
   }
-#define LACT_NSG_LSTORE(BUF)                                                                 \
+#define LACT_NSG_LSTORE(P, BUF)                                                              \
   {                                                                                          \
     bf16* sa_ = lds_g + (BUF) * NSG_SA;                                                      \
     bf16* sb_ = lds_g + 2 * NSG_SA + (BUF) * NSG_SB;                                         \
     _Pragma("unroll") for (int x = 0; x < NSG_VA; ++x) {                                     \
       const int vi = tid + 256 * x;                                                          \
-      *reinterpret_cast<bf16x8*>(sa_ + (vi / NSG_RA) * NSG_PA + 8 * (vi % NSG_RA)) = ra[x]; \
-      if (BKN) *reinterpret_cast<bf16x8*>(sb_ + (vi >> 3) * NSG_PB + 8 * (vi & 7)) = rb[x]; \
-      else *reinterpret_cast<bf16x8*>(sb_ + (vi / NSG_RA) * NSG_PA + 8 * (vi % NSG_RA)) = rb[x]; \
+      *reinterpret_cast<bf16x8*>(sa_ + (vi / NSG_RA) * NSG_PA + 8 * (vi % NSG_RA)) = ra[P][x]; \
+      if (BKN) *reinterpret_cast<bf16x8*>(sb_ + (vi >> 3) * NSG_PB + 8 * (vi & 7)) = rb[P][x]; \
+      else *reinterpret_cast<bf16x8*>(sb_ + (vi / NSG_RA) * NSG_PA + 8 * (vi % NSG_RA)) = rb[P][x]; \
     }                                                                                        \
+  }
+  // the epilogue's own loads go out first: the D tile and the shift's partials
+  const float* D = a.D ? a.D + bidx * a.d_bs : nullptr;
+  f32x4 dv[4];
+  if (D) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
+      dv[x] = *reinterpret_cast<const f32x4*>(D + (int64_t)(m0 + r) * a.N + n0 + c4);
+    }
+  }
+  float mu_t = 0.f;
+  if (a.mu_part != nullptr) {
+    const float* mp = a.mu_part + bidx * a.mu_np;
+    for (int q = lane; q < a.mu_np; q += 64) mu_t += mp[q];
   }
   f32x4 acc[2][2];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  LACT_NSG_GLOAD(0);
-  LACT_NSG_LSTORE(0);
-  __syncthreads();
-  for (int k0 = 0; k0 < a.K; k0 += NSG_K) {
-    const int buf = (k0 / NSG_K) & 1;
-    const bool more = k0 + NSG_K < a.K;
-    if (more) LACT_NSG_GLOAD(k0 + NSG_K);
-    const bf16* sa = lds_g + buf * NSG_SA;
-    const bf16* sb = lds_g + 2 * NSG_SA + buf * NSG_SB;
 #pragma unroll
-    for (int s = 0; s < NSG_K / 32; ++s) {
-      bf16x8 fa[2], fb[2];
+  for (int p = 0; p < PD; ++p)
+    if (p < nslab) LACT_NSG_GLOAD(p, p * NSG_K);
+  for (int j0 = 0; j0 < nslab; j0 += PD) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) fa[x] = ld8(sa + (32 * wm + 16 * x + c) * NSG_PA + 32 * s + 8 * g);
+    for (int p = 0; p < PD; ++p) {
+      const int j = j0 + p;
+      if (j < nslab) {
+        // one barrier per slab: every thread is past its reads of buffer
+        // p % 2 from slab j - 2 (done before its store of slab j - 1)
+        LACT_NSG_LSTORE(p, p & 1);
+        __syncthreads();
+        if (j + PD < nslab) LACT_NSG_GLOAD(p, (j + PD) * NSG_K);
+        const bf16* sa = lds_g + (p & 1) * NSG_SA;
+        const bf16* sb = lds_g + 2 * NSG_SA + (p & 1) * NSG_SB;
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        if constexpr (BKN) {
-          const bf16* p = sb + (32 * s + 8 * g + (c >> 2)) * NSG_PB + 32 * wn + 16 * y + 4 * (c & 3);
-          fb[y] = cat8(ld_tr4(p), ld_tr4(p + 4 * NSG_PB));
-        } else {
-          fb[y] = ld8(sb + (32 * wn + 16 * y + c) * NSG_PA + 32 * s + 8 * g);
+        for (int s = 0; s < NSG_K / 32; ++s) {
+          bf16x8 fa[2], fb[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) fa[x] = ld8(sa + (32 * wm + 16 * x + c) * NSG_PA + 32 * s + 8 * g);
+#pragma unroll
+          for (int y = 0; y < 2; ++y) {
+            if constexpr (BKN) {
+              const bf16* q = sb + (32 * s + 8 * g + (c >> 2)) * NSG_PB + 32 * wn + 16 * y + 4 * (c & 3);
+              fb[y] = cat8(ld_tr4(q), ld_tr4(q + 4 * NSG_PB));
+            } else {
+              fb[y] = ld8(sb + (32 * wn + 16 * y + c) * NSG_PA + 32 * s + 8 * g);
+            }
+          }
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) mma(acc[x][y], fa[x], fb[y]);
         }
       }
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) mma(acc[x][y], fa[x], fb[y]);
     }
-    if (more) LACT_NSG_LSTORE(buf ^ 1);
-    __syncthreads();
   }
 #undef LACT_NSG_GLOAD
 #undef LACT_NSG_LSTORE
-  // result tile through LDS (every read of the operand tiles is done)
+  __syncthreads();  // every read of the operand tiles is done
+  // result tile through LDS
   float* sc = reinterpret_cast<float*>(lds_g);
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -215,19 +250,15 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
       for (int i = 0; i < 4; ++i)
         sc[(32 * wm + 16 * x + 4 * g + i) * NSG_PC + 32 * wn + 16 * y + c] = acc[x][y][i];
   __syncthreads();
-  const float* D = a.D ? a.D + bidx * a.d_bs : nullptr;
   float* C = a.C ? a.C + bidx * a.c_bs : nullptr;
   bf16* Ch = a.Ch ? a.Ch + bidx * a.c_bs : nullptr;
   // shift of this step (the same mu in every workgroup of the matrix: the
   // partial sums are added in a fixed order)
   float mu = 0.f;
   if (a.mu_part != nullptr) {
-    const float* mp = a.mu_part + bidx * a.mu_np;
-    float t = 0.f;
-    for (int q = lane; q < a.mu_np; q += 64) t += mp[q];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-    mu = t / a.mu_div;
+    for (int o = 32; o > 0; o >>= 1) mu_t += __shfl_xor(mu_t, o);
+    mu = mu_t / a.mu_div;
   }
   const float be = a.beta + (a.beta_mu + a.beta_mu2 * mu) * mu;
   const float dg = a.diag_mu * mu;
@@ -237,7 +268,7 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
     const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
     const int64_t o = (int64_t)(m0 + r) * a.N + n0 + c4;
     f32x4 v = *reinterpret_cast<const f32x4*>(sc + r * NSG_PC + c4) * a.alpha;
-    if (D) v += *reinterpret_cast<const f32x4*>(D + o) * be;
+    if (D) v += dv[x] * be;
     if (dg != 0.f) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] += (m0 + r == n0 + c4 + j) ? dg : 0.f;
@@ -253,12 +284,12 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
     if (lane == 0) sc[wave] = ss;
     __syncthreads();
     if (tid == 0)
-      a.ss_part[bidx * gridDim.x + blockIdx.x] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+      a.ss_part[bidx * ntile + tile] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
   }
 }
 
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s) {
-  const dim3 grid((unsigned)((a.M / NSG_T) * (a.N / NSG_T)), (unsigned)batch);
+  const dim3 grid((unsigned)((a.M / NSG_T) * (a.N / NSG_T) * batch));
   if (b_kn)
     hipLaunchKernelGGL(k_nsgemm<true>, grid, dim3(256), 0, s, a);
   else
