@@ -544,8 +544,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
 // pipeline over 32-token tiles, three stage buffers, one barrier per tile:
 // iteration n runs the forward contractions of tile n + 1 with the SwiGLU
 // backward of tile n spread between them, then the gradient contractions
-// of tile n with the staging stores of tile n + 2 between them; fragment
-// reads two steps ahead of their MFMAs, the order held by scheduling fences.
+// of tile n with the staging stores of tile n + 2 between its last steps
+// (as late as possible: the tile's loads, issued at the top of the
+// iteration, then have both regions to arrive); fragment reads two steps
+// ahead of their MFMAs, the order held by scheduling fences.
 template <int D, int HW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_grad_solo(GradArgs a) {
@@ -559,7 +561,7 @@ void k_grad_solo(GradArgs a) {
   constexpr int NST = 2 * KS;          // forward steps (K slab, token half)
   constexpr int EPS_ = 8 * HW / NST;   // backward elements per forward step
   constexpr int EVERY = NST / (8 * HW) > 0 ? NST / (8 * HW) : 1;  // steps per element
-  static_assert(NV % NTH == 0 && VPT <= IT - 4, "tile split");
+  static_assert(NV % NTH == 0 && VPT <= IT, "tile split");
   static_assert(EPS_ * NST == 8 * HW || EVERY * 8 * HW == NST, "backward spread");
   __shared__ __attribute__((aligned(16))) bf16 sKV[NBUF][2 * TILE];
   __shared__ float sEta[NBUF][3][NT];
@@ -756,8 +758,8 @@ void k_grad_solo(GradArgs a) {
           mma(G3[h][it], tk_[it % 3], fu[h]);
           mma(G2[h][it], tv_[it % 3], fh[h]);
         }
-        if (it >= 4 && it < 4 + VPT) {
-          const int x = it - 4, vi = tid + x * NTH;
+        if (it >= IT - VPT) {
+          const int x = it - (IT - VPT), vi = tid + x * NTH;
           const int o = tpad<D>(vi / (D / 8), (vi % (D / 8)) * 8);
           *reinterpret_cast<uint4*>(sK_ + o) = rk[x];
           *reinterpret_cast<uint4*>(sK_ + TILE + o) = rv[x];
