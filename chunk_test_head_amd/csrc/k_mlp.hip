@@ -23,11 +23,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_apply(ApplyArgs a) {
   apply_block<T, D, NTW, WAVES>(a, xcd_logical_id(blockIdx.x, gridDim.x), lds);
 }
 
+// One 128-token tile per workgroup; or, launched with fewer workgroups than
+// tiles (to leave compute units to Newton-Schulz on another stream), XCD x
+// works through the tiles [x N / 8, (x + 1) N / 8) with its own
+// workgroups, so that a head's weights stay in one L2.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_apply_solo(ApplyArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 lds[ApplySoloLds<D>::ELEMS];
-  apply_solo_block<D>(a, xcd_logical_id(blockIdx.x, gridDim.x), lds);
+  const int total = (int)((a.n_tok + 127) / 128) * a.bh;
+  const int nwg = (int)gridDim.x;
+  if (nwg >= total) {
+    apply_solo_block<D>(a, xcd_logical_id(blockIdx.x, nwg), lds);
+  } else if (nwg < 8) {
+    for (int t = blockIdx.x; t < total; t += nwg) apply_solo_block<D>(a, t, lds);
+  } else {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int nw = (nwg - xcd + 7) >> 3;  // workgroups on this XCD
+    const int t0 = (int)((int64_t)total * xcd / 8), t1 = (int)((int64_t)total * (xcd + 1) / 8);
+    for (int t = t0 + slot; t < t1; t += nw) apply_solo_block<D>(a, t, lds);
+  }
 }
 
 // ------------------------------------------------------------- gradient --
@@ -614,16 +629,34 @@ void k_grad_solo(GradArgs a) {
   const int er = tid % NT;
   uint4 rk[VPT], rv[VPT];
   float re = 0.f;
+  // A whole tile inside the split (every tile but a split's last): vector
+  // x of a thread is row tid / (D / 8) + x RX, piece tid % (D / 8), loaded
+  // from a uniform row base plus the thread's 32-bit byte offset (no
+  // per-lane 64-bit address arithmetic, no bounds checks).  A split's last
+  // tile checks every row and reads rows past the end as zeros.
+  constexpr int RX = NTH / (D / 8);
+  static_assert(NTH % (D / 8) == 0, "rows per vector step");
+  const uint32_t kob = (uint32_t)((tid / (D / 8)) * a.k_st + (tid % (D / 8)) * 8) * 2u;
+  const uint32_t vob = (uint32_t)((tid / (D / 8)) * a.v_st + (tid % (D / 8)) * 8) * 2u;
 #define LACT_GS_GLOAD(T0)                                                           \
   {                                                                                 \
-    _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
-      const int vi = tid + x * NTH;                                                 \
-      const int64_t t = (T0) + vi / (D / 8);                                        \
-      rk[x] = uint4{0u, 0u, 0u, 0u};                                                \
-      rv[x] = uint4{0u, 0u, 0u, 0u};                                                \
-      if (t < s1) {                                                                 \
-        rk[x] = *reinterpret_cast<const uint4*>(kp + t * a.k_st + (vi % (D / 8)) * 8); \
-        rv[x] = *reinterpret_cast<const uint4*>(vp + t * a.v_st + (vi % (D / 8)) * 8); \
+    if ((T0) + NT <= s1) {                                                          \
+      _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
+        const char* kb_ = reinterpret_cast<const char*>(kp + ((T0) + x * RX) * a.k_st); \
+        const char* vb_ = reinterpret_cast<const char*>(vp + ((T0) + x * RX) * a.v_st); \
+        rk[x] = *reinterpret_cast<const uint4*>(kb_ + kob);                         \
+        rv[x] = *reinterpret_cast<const uint4*>(vb_ + vob);                         \
+      }                                                                             \
+    } else {                                                                        \
+      _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
+        const int vi = tid + x * NTH;                                               \
+        const int64_t t = (T0) + vi / (D / 8);                                      \
+        rk[x] = uint4{0u, 0u, 0u, 0u};                                              \
+        rv[x] = uint4{0u, 0u, 0u, 0u};                                              \
+        if (t < s1) {                                                               \
+          rk[x] = *reinterpret_cast<const uint4*>(kp + t * a.k_st + (vi % (D / 8)) * 8); \
+          rv[x] = *reinterpret_cast<const uint4*>(vp + t * a.v_st + (vi % (D / 8)) * 8); \
+        }                                                                           \
       }                                                                             \
     }                                                                               \
     if (tid < 3 * NT) re = ((T0) + er < s1) ? ep[(T0) + er] : 0.f;                  \
@@ -800,9 +833,10 @@ void k_grad_solo(GradArgs a) {
 }
 
 // --------------------------------------------------------------- launch --
-static hipError_t run_apply_solo(const ApplyArgs& a, hipStream_t s) {
-  const int64_t blocks = (a.n_tok + 127) / 128 * a.bh;
+static hipError_t run_apply_solo(const ApplyArgs& a, hipStream_t s, int max_blocks) {
+  int64_t blocks = (a.n_tok + 127) / 128 * a.bh;
   if (blocks <= 0) return hipSuccess;
+  if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
   hipLaunchKernelGGL((k_apply_solo<256>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -816,12 +850,12 @@ static hipError_t run_apply(const ApplyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s) {
+hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s, int max_blocks) {
   if (dtype == 1) {
     switch (a.d) {
       case 64: return run_apply<bf16, 64, 64, 4>(a, s);
       case 128: return run_apply<bf16, 128, 32, 8>(a, s);
-      case 256: return run_apply_solo(a, s);
+      case 256: return run_apply_solo(a, s, max_blocks);
     }
   } else {
     switch (a.d) {

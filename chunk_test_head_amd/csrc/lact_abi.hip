@@ -358,15 +358,68 @@ static ApplyArgs apply_args(const lact_shape* sh, const lact_state* st, const vo
 
 static lact_status do_apply(const lact_shape* sh, const lact_state* st, const void* q,
                             lact_layout ql, void* o, lact_layout ol, int64_t n_tok,
-                            hipStream_t s) {
+                            hipStream_t s, int max_blocks = 0) {
   if (n_tok == 0) return LACT_OK;
   const ApplyArgs a = apply_args(sh, st, q, ql, o, ol, n_tok);
   hipError_t e;
   {
     ProfScope p(LACT_PROF_APPLY, s);
-    e = launch_apply(sh->dtype, a, s);
+    e = launch_apply(sh->dtype, a, s, max_blocks);
   }
   return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
+// ------------------------------------------- the read on a second stream --
+// With d = 256 and Muon, a write's Newton-Schulz is 17 small launches that
+// leave most compute units idle, while the read of the chunk (which needs
+// only the weights this write replaces) is a long MFMA launch.  The read
+// then runs on a library-owned stream: forked from the caller's stream
+// after the gradient launch, on three quarters of the compute units (its
+// workgroups loop over the tiles, so the rest stay free for Newton-Schulz),
+// and joined back before the step.  One stream and two events per device,
+// created on first use (never while the caller's stream is being captured:
+// the write then stays on one stream) and kept until the process ends.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int read_blocks = 0;
+  // held from the fork's record to the join's wait: the events are shared
+  // by every caller on the device, and a wait must see its own record
+  mutable std::mutex mu;
+};
+
+static const SideStream* side_stream(hipStream_t caller) {
+  static std::mutex mu;
+  static SideStream sides[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  SideStream& sd = sides[dev];
+  if (sd.s != nullptr) return &sd;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    return nullptr;
+  hipStream_t st = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    if (f != nullptr) hipEventDestroy(f);
+    hipStreamDestroy(st);
+    return nullptr;
+  }
+  sd.fork = f;
+  sd.join = j;
+  sd.read_blocks = cus * 3 / 4;
+  sd.s = st;
+  return &sd;
+}
+
+// The shapes whose writes fork their read (the large-matrix Newton-Schulz).
+static bool forks_read(const lact_shape* sh, const lact_update_opts* op) {
+  return sh->dtype == LACT_BF16 && sh->d == 256 && op->use_muon != 0;
 }
 
 static lact_status do_grad(const lact_shape* sh, const lact_state* st, const void* k,
@@ -437,11 +490,13 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                              const float* e3, const float* e2, const float* mom, int64_t esbh,
                              int64_t n_tok, const lact_update_opts* op, void* ws,
                              hipStream_t s, const ApplyJob* job = nullptr,
-                             void* shadow_out = nullptr) {
+                             void* shadow_out = nullptr, const SideStream* side = nullptr) {
   if (shadow_out == nullptr) shadow_out = st->shadow;
   const bool nsstep = ns_step_fused(sh, op);
   const bool fuse = nsstep && job != nullptr && job->n_tok > 0 && shadow_out != st->shadow;
-  if (job != nullptr && !fuse) {
+  const bool fork = side != nullptr && job != nullptr && job->n_tok > 0 && !fuse && !nsstep &&
+                    forks_read(sh, op);
+  if (job != nullptr && !fuse && !fork) {
     lact_status r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, s);
     if (r != LACT_OK) return r;
   }
@@ -464,6 +519,18 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   const float* u1 = mo ? st->m1 : g1;
   const float* u3 = mo ? st->m3 : g3;
   const float* u2 = mo ? st->m2 : g2;
+  std::unique_lock<std::mutex> side_lock;
+  if (fork) {
+    // the read leaves on the second stream once the gradient launch (the
+    // last user of this write's inputs before the step) is enqueued
+    side_lock = std::unique_lock<std::mutex>(side->mu);
+    hipError_t e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return hip_fail(e);
+    r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, side->s, side->read_blocks);
+    if (r != LACT_OK) return r;
+    if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return hip_fail(e);
+  }
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
     const NsIn in{{u1, u3, u2}, sh->bh};
@@ -491,6 +558,11 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                w.xh, w.amat, w.bmat, w.ssp, s);
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
+  }
+  if (fork) {
+    // the step rewrites the operand copies the read uses: join first
+    const hipError_t e = hipStreamWaitEvent(s, side->join, 0);
+    if (e != hipSuccess) return hip_fail(e);
   }
   return do_step(sh, st, u1, u3, u2, op->renorm, op->renorm_eps, op->nonfinite, shadow_out,
                  s);
@@ -707,7 +779,8 @@ lact_status lact_chunk_step(const lact_shape* sh, const lact_state* st, const vo
   // with the read in the Newton-Schulz launch, the new operand copies go to
   // the workspace shadow and are copied back
   void* alt = second_shadow(sh, op, ws);
-  r = do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s, &job, alt);
+  const SideStream* side = forks_read(sh, op) ? side_stream(s) : nullptr;
+  r = do_update(sh, st, k, kl, v, vl, e1, e3, e2, mom, esbh, n_tok, op, ws, s, &job, alt, side);
   if (r != LACT_OK || alt == nullptr) return r;
   const hipError_t e = launch_copy16(st->shadow, alt, (int64_t)lact_shadow_bytes(sh), s);
   return e == hipSuccess ? LACT_OK : hip_fail(e);
@@ -749,9 +822,11 @@ static lact_status check_sequence(LACT_SEQ_PARAMS, const void* ws, size_t ws_byt
   return LACT_OK;
 }
 
-// The sequence driver proper (arguments already checked).
-static lact_status run_sequence(LACT_SEQ_PARAMS, void* ws, hipStream_t s) {
+// The sequence driver proper (arguments already checked).  allow_side: the
+// read of a d = 256 Muon write may run on the library's second stream.
+static lact_status run_sequence(LACT_SEQ_PARAMS, void* ws, hipStream_t s, bool allow_side) {
   lact_status r = LACT_OK;
+  const SideStream* side = allow_side && forks_read(sh, op) ? side_stream(s) : nullptr;
   const int es = elem_size(sh->dtype);
   auto at = [&](const void* base, lact_layout l, int64_t t) {
     return reinterpret_cast<const char*>(base) + t * l.stride_tok * es;
@@ -769,7 +844,7 @@ static lact_status run_sequence(LACT_SEQ_PARAMS, void* ws, hipStream_t s) {
     // learning rates: one per token, or (per channel) d or dh per token
     const int64_t c13 = op->eta_per_channel ? sh->d : 1, c2 = op->eta_per_channel ? sh->dh : 1;
     const lact_status rr = do_update(sh, &cs, kp, kl, vp, vl, e1 + a0 * c13, e3 + a0 * c13, e2 + a0 * c2,
-                                     mom ? mom + a0 : nullptr, esbh, n, op, ws, s, job, out);
+                                     mom ? mom + a0 : nullptr, esbh, n, op, ws, s, job, out, side);
     if (rr == LACT_OK) cs.shadow = out;
     return rr;
   };
@@ -844,7 +919,7 @@ extern "C" {
 lact_status lact_sequence(LACT_SEQ_PARAMS, void* ws, size_t ws_bytes, void* stream) {
   const lact_status r = check_sequence(LACT_SEQ_ARGS, ws, ws_bytes);
   if (r != LACT_OK) return r;
-  return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream);
+  return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream, true);
 }
 
 lact_status lact_sequence_noalloc(LACT_SEQ_PARAMS, void* stream) {
@@ -855,7 +930,9 @@ lact_status lact_sequence_noalloc(LACT_SEQ_PARAMS, void* stream) {
   if (r != LACT_OK) return r;
   void* ws = nullptr;
   if ((r = scratch_on_current_device(&ws)) != LACT_OK) return r;
-  return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream);
+  // one stream only: the second stream and its events are created on first
+  // use, which this entry point's callers may not allow
+  return run_sequence(LACT_SEQ_ARGS, ws, (hipStream_t)stream, false);
 }
 
 // ------------------------------------------------- linear variant --

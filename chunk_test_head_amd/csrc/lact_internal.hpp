@@ -150,7 +150,9 @@ struct StepArgs {
 // safe to call from several threads.
 hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
-hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s);
+// max_blocks > 0: at most that many workgroups (d = 256 only; the tiles are
+// then dealt to them by XCD), else one per tile.
+hipError_t launch_apply(int dtype, const ApplyArgs& a, hipStream_t s, int max_blocks = 0);
 hipError_t launch_grad(int dtype, const GradArgs& a, hipStream_t s);
 int decode_blocks(int dtype, int bh, int d, int dh);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);

@@ -11,9 +11,18 @@
  * Conventions shared by every call:
  *  - All pointers are DEVICE pointers unless stated otherwise.  The caller
  *    owns every buffer; the library allocates no device memory and keeps no
- *    device state between calls.  Its only process-wide host state is the
- *    kernel-timing window (lact_prof_begin / lact_prof_end) and a record of
- *    which kernels have had their LDS limit raised on which device.
+ *    device state between calls.  Its process-wide state is the
+ *    kernel-timing window (lact_prof_begin / lact_prof_end), a record of
+ *    which kernels have had their LDS limit raised on which device, and
+ *    (lact_sequence and lact_chunk_step with d = 256 and Muon) one HIP
+ *    stream and two events per device, created on first use and kept until
+ *    the process ends: the read of a chunk runs there beside the write's
+ *    Newton-Schulz, forked from and joined back into `stream` within the
+ *    call, so the call stays ordered on `stream` as one unit (and can be
+ *    captured into a graph; a first call made under capture uses `stream`
+ *    alone).  That stream is shared by every caller on a device, so reads
+ *    of calls made on different streams may wait for one another; results
+ *    do not depend on it.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronises, except lact_check_finite and
  *    lact_prof_end, which exist to wait.  Argument checks run on the host
@@ -270,7 +279,7 @@ lact_status lact_sequence(const lact_shape* shape, const lact_state* state,
  * the same arguments without the workspace, which is instead a device array
  * of LACT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
  * on, from the first call on that GPU until the process ends.  The call
- * allocates nothing.  A sequence whose writes need more workspace than that
+ * allocates nothing and runs every kernel on `stream`.  A sequence whose writes need more workspace than that
  * (lact_workspace_bytes) returns LACT_ERR_WORKSPACE.  Every call on one GPU
  * shares the array: calls that may overlap on one GPU (different streams or
  * threads without ordering between them) race and must not be made; calls

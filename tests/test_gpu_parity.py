@@ -502,3 +502,36 @@ def test_sequence_per_channel_eta(device, wi):
         assert H.rel(got[b], ref) < H.TOL[w.dtype], (b, H.rel(got[b], ref))
         assert H.rel(W1[b], st.W1) < H.TOL[w.dtype] and H.rel(W2[b], st.W2) < H.TOL[w.dtype]
     H.check_shadow(fw)
+
+
+def test_sequence_forked_read_is_bitwise_the_plain_read(device):
+    """d = 256 with Muon: lact_sequence runs each chunk's read on the
+    library's second stream beside the write's Newton-Schulz, with fewer
+    workgroups than 128-token tiles (each loops over several).  Chunks of
+    16384 tokens on two heads (256 tiles) take that path; the outputs and
+    the final state must equal, bit for bit, the same sequence composed of
+    lact_apply (one workgroup per tile, caller's stream) and lact_update."""
+    import torch
+    C = 16384
+    w = WL.WORKLOADS[4].scaled(heads=2, batch=1, T=2 * C + 300, chunk=C)
+    W, inp = inputs(w)
+    q, k, v = (H.act_to_dev(w, inp, n, device) for n in ("q", "k", "v"))
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    mom = torch.from_numpy(inp["mom"]).to(device)
+    o = H.opts_of(w)
+    print(f"forked read T={w.T} chunk={C} bh={w.bh}", flush=True)
+    out_seq, fw_seq = H.run_sequence(w, inp, W, device)
+    fw = H.make_state(w, W, device)
+    out = H.out_buffer(w, w.T, device)
+    ws = H.workspace(w, C, device)
+    lay = L.layout_of(q)
+    for s0, e0 in w.chunk_bounds():
+        L.lact_apply(fw.shape, fw, q[:, s0:e0], out[:, s0:e0], q_layout=lay, o_layout=L.layout_of(out))
+        if e0 < w.T:
+            L.lact_update(fw.shape, fw, k[:, s0:e0], v[:, s0:e0], eta[:, s0:e0], eta[:, s0:e0], eta[:, s0:e0],
+                          mom[:, s0:e0], o, ws, k_layout=lay, v_layout=lay)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.to64(out), out_seq)
+    for name in ("w1", "w3", "w2", "m1", "m3", "m2", "shadow"):
+        a, b = getattr(fw, name), getattr(fw_seq, name)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
