@@ -369,16 +369,18 @@ static lact_status do_apply(const lact_shape* sh, const lact_state* st, const vo
   return e == hipSuccess ? LACT_OK : hip_fail(e);
 }
 
+
 // ------------------------------------------- the read on a second stream --
 // With d = 256 and Muon, a write's Newton-Schulz is 17 small launches that
 // leave most compute units idle, while the read of the chunk (which needs
 // only the weights this write replaces) is a long MFMA launch.  The read
 // then runs on a library-owned stream: forked from the caller's stream
-// after the gradient launch, on three quarters of the compute units (its
-// workgroups loop over the tiles, so the rest stay free for Newton-Schulz),
-// and joined back before the step.  One stream and two events per device,
-// created on first use (never while the caller's stream is being captured:
-// the write then stays on one stream) and kept until the process ends.
+// after the gradient launch (before the split sum), on three quarters of
+// the compute units (its workgroups loop over the tiles, so the rest stay
+// free for Newton-Schulz), and joined back before the step.  One stream and
+// two events per device, created on first use (never while the caller's
+// stream is being captured: the write then stays on one stream) and kept
+// until the process ends.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -404,8 +406,9 @@ static const SideStream* side_stream(hipStream_t caller) {
   hipStream_t st = nullptr;
   hipEvent_t f = nullptr, j = nullptr;
   if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+  // (same-device ordering only: no system-scope fence)
+  const unsigned fl = hipEventDisableTiming | hipEventDisableSystemFence;
+  if (hipEventCreateWithFlags(&f, fl) != hipSuccess || hipEventCreateWithFlags(&j, fl) != hipSuccess) {
     if (f != nullptr) hipEventDestroy(f);
     hipStreamDestroy(st);
     return nullptr;
@@ -422,12 +425,27 @@ static bool forks_read(const lact_shape* sh, const lact_update_opts* op) {
   return sh->dtype == LACT_BF16 && sh->d == 256 && op->use_muon != 0;
 }
 
+// The read of `job` on the second stream, after everything enqueued on s so
+// far; the caller holds side->mu until it has made s wait for side->join.
+static lact_status fork_read(const SideStream* side, const lact_shape* sh, const lact_state* st,
+                             const ApplyJob* job, hipStream_t s) {
+  hipError_t e = hipEventRecord(side->fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+  if (e != hipSuccess) return hip_fail(e);
+  const lact_status r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, side->s,
+                                 side->read_blocks);
+  if (r != LACT_OK) return r;
+  e = hipEventRecord(side->join, side->s);
+  return e == hipSuccess ? LACT_OK : hip_fail(e);
+}
+
 static lact_status do_grad(const lact_shape* sh, const lact_state* st, const void* k,
                            lact_layout kl, const void* v, lact_layout vl, const float* e1,
                            const float* e3, const float* e2, int64_t esbh, int64_t n_tok,
                            const Workspace& w, int nsplit, float* o1, float* o3, float* o2,
                            float* m1, float* m3, float* m2, const float* mom, hipStream_t s,
-                           bool reduce = true, int eta_per_channel = 0) {
+                           bool reduce = true, int eta_per_channel = 0,
+                           const SideStream* side = nullptr, const ApplyJob* job = nullptr) {
   GradArgs a;
   a.k = k; a.k_sbh = kl.stride_bh; a.k_st = kl.stride_tok;
   a.v = v; a.v_sbh = vl.stride_bh; a.v_st = vl.stride_tok;
@@ -452,6 +470,12 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
     e = launch_grad(sh->dtype, a, s);
   }
   if (e != hipSuccess) return hip_fail(e);
+  if (side != nullptr) {
+    // the gradient launch is the last one on s that the read must follow
+    // (it uses the weights the write replaces), so the read leaves here
+    const lact_status rr = fork_read(side, sh, st, job, s);
+    if (rr != LACT_OK) return rr;
+  }
   if (!reduce) return LACT_OK;  // the consumer sums the partials itself
   ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
   {
@@ -511,26 +535,19 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   float* g2 = w.g ? w.g + 2 * mall : nullptr;
   // with momentum the reduced gradient lives in M only (M <- G + beta M)
   const bool mo = op->use_momentum != 0;
+  // with a forked read, side->mu is held from the fork to the join's wait:
+  // the events are shared by every caller on the device
+  std::unique_lock<std::mutex> side_lock;
+  if (fork) side_lock = std::unique_lock<std::mutex>(side->mu);
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
                           mo ? nullptr : g1, mo ? nullptr : g3, mo ? nullptr : g2,
                           mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr,
-                          mo ? mom : nullptr, s, !nsstep, op->eta_per_channel);
+                          mo ? mom : nullptr, s, !nsstep, op->eta_per_channel,
+                          fork ? side : nullptr, fork ? job : nullptr);
   if (r != LACT_OK) return r;
   const float* u1 = mo ? st->m1 : g1;
   const float* u3 = mo ? st->m3 : g3;
   const float* u2 = mo ? st->m2 : g2;
-  std::unique_lock<std::mutex> side_lock;
-  if (fork) {
-    // the read leaves on the second stream once the gradient launch (the
-    // last user of this write's inputs before the step) is enqueued
-    side_lock = std::unique_lock<std::mutex>(side->mu);
-    hipError_t e = hipEventRecord(side->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-    if (e != hipSuccess) return hip_fail(e);
-    r = do_apply(sh, st, job->q, job->ql, job->o, job->ol, job->n_tok, side->s, side->read_blocks);
-    if (r != LACT_OK) return r;
-    if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return hip_fail(e);
-  }
   if (op->use_muon) {
     ProfScope p(LACT_PROF_NS, s);
     const NsIn in{{u1, u3, u2}, sh->bh};
