@@ -91,6 +91,9 @@ def load():
         "lact_linear_init_state": (I32, [pS, P, P]),
         "lact_linear_sequence": (I32, [pS, P, P, L, P, L, P, L, P, L, P, P, I64, I64, I64, I32, I64, I64, I32,
                                        pO, P, SZ, P]),
+        "lact_backward_workspace_bytes": (SZ, [pS, I64, I64, pO]),
+        "lact_sequence_backward": (I32, [pS, P, P, P, P, L, P, L, P, L, P, P, P, P, P, I64, I64, I64, I32, I64,
+                                         I64, I32, pO, ctypes.POINTER(Grads), P, SZ, P]),
         "lact_prof_begin": (I32, [I32, I32]),
         "lact_prof_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(F), ctypes.POINTER(F),
                                 ctypes.POINTER(F)]),
@@ -306,6 +309,30 @@ def lact_sequence_noalloc(shape, fw, q, k, v, out, eta1, eta3, eta2, mom, T, chu
                                         _eta_stride(eta1), int(T), int(chunk), int(order), int(sub_off),
                                         int(sub_len), int(update_last), ctypes.byref(o), _stream(stream)),
            "lact_sequence_noalloc")
+
+
+# ------------------------------------------------ outer-loop backward ----
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dq", "dk", "dv", "deta1", "deta3", "deta2", "dmom", "dw1", "dw3",
+                                                 "dw2")]
+
+
+def backward_workspace_bytes(shape, T, chunk, o):
+    return load().lact_backward_workspace_bytes(ctypes.byref(shape), int(T), int(chunk), ctypes.byref(o))
+
+
+def lact_sequence_backward(shape, w1, w3, w2, q, k, v, dout, eta1, eta3, eta2, mom, T, chunk, order, subset,
+                           update_last, o, grads, ws, stream=None, layouts=None):
+    """grads: dict with fp32 tensors dq, dk, dv ([bh, T, d]), deta1, deta3,
+    deta2, dmom ([bh, T], dmom None without momentum), dw1, dw3, dw2."""
+    sub_off, sub_len = (0, -1) if subset is None else subset
+    ql, kl, vl = layouts or (layout_of(q), layout_of(k), layout_of(v))
+    g = Grads(*(_ptr(grads.get(n)) for n, _ in Grads._fields_))
+    _check(load().lact_sequence_backward(ctypes.byref(shape), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(q), ql, _ptr(k),
+                                         kl, _ptr(v), vl, _ptr(dout), _ptr(eta1), _ptr(eta3), _ptr(eta2), _ptr(mom),
+                                         _eta_stride(eta1), int(T), int(chunk), int(order), int(sub_off),
+                                         int(sub_len), int(update_last), ctypes.byref(o), ctypes.byref(g), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)), "lact_sequence_backward")
 
 
 # ---------------------------------------------------- linear variant ----

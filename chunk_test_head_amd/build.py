@@ -11,7 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "liblact.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["lact_abi.hip", "k_mlp.hip", "k_state.hip", "k_gemm.hip", "k_ns.hip", "k_decode.hip", "k_linear.hip"]
+SOURCES = ["lact_abi.hip", "k_mlp.hip", "k_state.hip", "k_gemm.hip", "k_ns.hip", "k_decode.hip", "k_linear.hip",
+           "k_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,513 @@
+// Kernels of the outer-loop backward: the vector-Jacobian product of a whole
+// sequence of the fast-weight layer with respect to q, k, v, the learning
+// rates, the momentum coefficients and the initial weights (the layer is
+// trained through its writes; uTTT page section 2).  The chain rule is taken
+// step by step through the forward of the LaCT rebuttal page's chunk loop:
+// read (apply step), chunk gradient (its derivative needs silu''), momentum,
+// Newton-Schulz (the five quintic steps as matrix products; summary page
+// section 3.2, Eq. 9-10), step and row renorm (Eq. 8).
+//
+// Everything here is fp32 (the backward recomputes the forward in fp32 and
+// differentiates that):
+//   * k_bgemm: batched C = alpha op(A) op(B) + beta D with arbitrary strides
+//     (transposes are strides), bounds-checked 64 x 64 tiles, K in slabs of
+//     32 staged through LDS, v_mfma_f32_16x16x4f32;
+//   * elementwise passes over [bh][n][dh] activations (SwiGLU and its first
+//     and second derivatives), row reductions for the learning-rate
+//     gradients, row passes for the step + renorm and its VJP, per-matrix
+//     reductions (Frobenius norms, momentum dots) in a fixed order.
+#include "lact_internal.hpp"
+#include "mfma.hpp"
+
+namespace lact {
+
+// ------------------------------------------------------------- GEMM ----
+__device__ __forceinline__ float ldx(const void* p, int64_t i, int bf) {
+  return bf ? (float)reinterpret_cast<const bf16*>(p)[i] : reinterpret_cast<const float*>(p)[i];
+}
+
+__global__ __launch_bounds__(256) void k_bgemm(BGemm g) {
+  constexpr int T = 64, KS = 32, P = T + 4;
+  __shared__ float sA[KS][P];  // [k][m]
+  __shared__ float sB[KS][P];  // [k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tn = (g.N + T - 1) / T;
+  const int m0 = (blockIdx.x / tn) * T, n0 = (blockIdx.x % tn) * T;
+  const int64_t b = blockIdx.y;
+  const char* A = reinterpret_cast<const char*>(g.A) + b * g.a_bs * (g.a_bf16 ? 2 : 4);
+  const char* B = reinterpret_cast<const char*>(g.B) + b * g.b_bs * (g.b_bf16 ? 2 : 4);
+  const bool a_kfast = g.a_sk == 1, b_nfast = g.b_sn == 1;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < g.K; k0 += KS) {
+    // A tile 64 x 32 and B tile 32 x 64, zero outside the matrices; the
+    // thread-to-element map follows the unit stride (coalesced loads)
+#pragma unroll
+    for (int i = 0; i < T * KS / 256; ++i) {
+      const int e = tid + 256 * i;
+      const int m = a_kfast ? e / KS : e % T, k = a_kfast ? e % KS : e / T;
+      float x = 0.f;
+      if (m0 + m < g.M && k0 + k < g.K) x = ldx(A, (int64_t)(m0 + m) * g.a_sm + (int64_t)(k0 + k) * g.a_sk, g.a_bf16);
+      sA[k][m] = x;
+      const int n = b_nfast ? e % T : e / KS, kb = b_nfast ? e / T : e % KS;
+      float y = 0.f;
+      if (n0 + n < g.N && k0 + kb < g.K) y = ldx(B, (int64_t)(k0 + kb) * g.b_sk + (int64_t)(n0 + n) * g.b_sn, g.b_bf16);
+      sB[kb][n] = y;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS / 4; ++s) {
+      float fa[2], fb[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) fa[x] = sA[4 * s + q][32 * wm + 16 * x + c];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) fb[y] = sB[4 * s + q][32 * wn + 16 * y + c];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  const float* D = g.D ? g.D + b * g.d_bs : nullptr;
+  float* C = g.C + b * g.c_bs;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 32 * wm + 16 * x + 4 * q + i, n = n0 + 32 * wn + 16 * y + c;
+        if (m < g.M && n < g.N) {
+          float v = g.alpha * acc[x][y][i];
+          if (D) v += g.beta * D[(int64_t)m * g.d_sm + n];
+          C[(int64_t)m * g.c_sm + n] = v;
+        }
+      }
+}
+
+hipError_t launch_bgemm(const BGemm& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(((g.M + 63) / 64) * ((g.N + 63) / 64)), (unsigned)g.batch);
+  hipLaunchKernelGGL(k_bgemm, grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- elementwise ----
+__device__ __forceinline__ float sig(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Read: from g = x W1^T, u = x W3^T, dh = dO W2 (each [n][dh] per head):
+//   h = silu(g) u,  du = dh silu(g),  dg = dh u silu'(g)   (in place: g <- dg,
+//   u <- du, dh <- h).
+__global__ void k_bw_read(float* g, float* u, float* dh, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float x = g[i], uu = u[i], d = dh[i];
+  const float s = sig(x), sl = x * s, s1 = s * (1.f + x * (1.f - s));
+  g[i] = d * uu * s1;
+  u[i] = d * sl;
+  dh[i] = sl * uu;
+}
+
+// Chunk gradient, forward: from g = k W1^T, u = k W3^T, e = v W2 and the
+// per-token rates, the factors of the three token contractions:
+// o1 = eta1 e u silu'(g), o3 = eta3 e silu(g), o2 = eta2 silu(g) u  (rows t
+// of head b use eta[b * esbh + t0 + t]).
+__global__ void k_bw_grad_fwd(const float* g, const float* u, const float* e, float* o1, float* o3,
+                              float* o2, const float* e1, const float* e3, const float* e2, int64_t esbh,
+                              int64_t t0, int n, int dh, int bh) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)bh * n * dh) return;
+  const int64_t row = i / dh;
+  const int t = (int)(row % n), b = (int)(row / n);
+  const int64_t ei = (int64_t)b * esbh + t0 + t;
+  const float x = g[i], uu = u[i], ee = e[i];
+  const float s = sig(x), sl = x * s, s1 = s * (1.f + x * (1.f - s));
+  o1[i] = e1[ei] * ee * uu * s1;
+  o3[i] = e3[ei] * ee * sl;
+  o2[i] = e2[ei] * sl * uu;
+}
+
+// Chunk gradient, backward.  In: g, u, e (forward products), p1 = k dG1^T,
+// p3 = k dG3^T, p2 = v dG2 ([n][dh] per head).  Out (in place):
+//   g  <- dg (cotangent of g),   u <- du,   e <- dE,
+//   p1 <- eta1 b,  p3 <- eta3 a,  p2 <- eta2 h   (the scaled forward
+//   factors that the dK / dV contractions need),
+// and r1 = b p1, r3 = a p3, r2 = h p2, whose row sums (k_bw_rowsum) are
+// the per-token rate gradients.
+// With s = silu(g), s1 = silu'(g), s2 = silu''(g): h = s u, a = e s,
+// b = e u s1; dh = eta2 p2, da = eta3 p3, db = eta1 p1.
+__global__ void k_bw_grad_bwd(float* g, float* u, float* e, float* p1, float* p3, float* p2,
+                              float* r1, float* r3, float* r2, const float* e1, const float* e3,
+                              const float* e2, int64_t esbh, int64_t t0, int n, int dh, int bh) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)bh * n * dh) return;
+  const int64_t row = i / dh;
+  const int t = (int)(row % n), b = (int)(row / n);
+  const int64_t ei = (int64_t)b * esbh + t0 + t;
+  const float x = g[i], uu = u[i], ee = e[i];
+  const float s = sig(x), sl = x * s, s1 = s * (1.f + x * (1.f - s));
+  const float s2 = s * (1.f - s) * (2.f + x * (1.f - 2.f * s));
+  const float h = sl * uu, a = ee * sl, bb = ee * uu * s1;
+  const float q1 = p1[i], q3 = p3[i], q2 = p2[i];
+  const float et1 = e1[ei], et3 = e3[ei], et2 = e2[ei];
+  const float dh_ = et2 * q2, da = et3 * q3, db = et1 * q1;
+  const float ds = dh_ * uu + da * ee;
+  g[i] = ds * s1 + db * ee * uu * s2;
+  u[i] = dh_ * sl + db * ee * s1;
+  e[i] = da * sl + db * uu * s1;
+  // the rate gradients' terms (summed over the row by k_bw_rowdot)
+  r1[i] = bb * q1;
+  r3[i] = a * q3;
+  r2[i] = h * q2;
+  p1[i] = et1 * bb;
+  p3[i] = et3 * a;
+  p2[i] = et2 * h;
+}
+
+// out[b * osbh + t0 + t] += sum_j x[(b n + t) dh + j], one wave per row, a
+// fixed order (lane-strided partial sums, then a butterfly).
+__global__ void k_bw_rowsum(const float* x, float* out, int64_t osbh, int64_t t0, int n, int dh,
+                            int bh) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= (int64_t)bh * n) return;
+  const float* p = x + row * dh;
+  float s = 0.f;
+  for (int j = lane; j < dh; j += 64) s += p[j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) {
+    const int t = (int)(row % n), b = (int)(row / n);
+    out[(int64_t)b * osbh + t0 + t] += s;
+  }
+}
+
+// ---------------------------------------------------- per-matrix sums ----
+// out[m] = sum over the matrix m (size elements) of x[i] * y[i] (y NULL:
+// x[i]^2), one workgroup per matrix, fixed order.
+__global__ void k_bw_dot(const float* x, const float* y, float* out, int64_t size) {
+  __shared__ float red[4];
+  const float* px = x + (int64_t)blockIdx.x * size;
+  const float* py = y ? y + (int64_t)blockIdx.x * size : nullptr;
+  float s = 0.f;
+  for (int64_t i = threadIdx.x; i < size; i += 256) s += px[i] * (py ? py[i] : px[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// y[m] = alpha[m] x[m] + beta[m] z[m] over matrices of `size` elements, with
+// per-matrix coefficients from arrays (NULL: the scalar a / b).
+__global__ void k_bw_axpby(float* y, const float* x, const float* z, const float* am, float a,
+                           const float* bm, float b, int64_t size, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t m = i / size;
+  const float ca = am ? am[m] : a, cb = bm ? bm[m] : b;
+  float v = ca * x[i];
+  if (z) v += cb * z[i];
+  y[i] = v;
+}
+
+// Batched transpose: out[m][j][i] = in[m][i][j], in [rows][cols].
+__global__ void k_bw_transpose(const float* in, float* out, int rows, int cols, int count) {
+  __shared__ float t[32][33];
+  const int m = blockIdx.z;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const float* pi = in + (int64_t)m * rows * cols;
+  float* po = out + (int64_t)m * rows * cols;
+  for (int r = threadIdx.y; r < 32; r += 8) {
+    const int i = i0 + r, j = j0 + threadIdx.x;
+    if (i < rows && j < cols) t[r][threadIdx.x] = pi[(int64_t)i * cols + j];
+  }
+  __syncthreads();
+  for (int r = threadIdx.y; r < 32; r += 8) {
+    const int j = j0 + r, i = i0 + threadIdx.x;
+    if (i < rows && j < cols) po[(int64_t)j * rows + i] = t[threadIdx.x][r];
+  }
+}
+
+// out = A + A^T for square [n][n] matrices (batched).
+__global__ void k_bw_symm(const float* a, float* out, int n, int count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)count * n * n) return;
+  const int64_t m = i / ((int64_t)n * n);
+  const int r = (int)((i / n) % n), c = (int)(i % n);
+  const float* p = a + m * n * n;
+  out[i] = p[(int64_t)r * n + c] + p[(int64_t)c * n + r];
+}
+
+// ------------------------------------------------------ step + renorm ----
+// Rows of length L: W <- (W + U) rescaled to n0 / (||W + U|| + eps) (renorm)
+// or W + U; one wave per row.
+__global__ void k_bw_step(float* w, const float* u, const float* n0, int64_t rows, int L, int renorm,
+                          float eps) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float* pw = w + row * L;
+  const float* pu = u + row * L;
+  float ss = 0.f;
+  for (int j = lane; j < L; j += 64) {
+    const float r = pw[j] + pu[j];
+    ss += r * r;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float f = renorm ? n0[row] / (sqrtf(ss) + eps) : 1.f;
+  for (int j = lane; j < L; j += 64) pw[j] = (pw[j] + pu[j]) * f;
+}
+
+// Row norms: n[row] = ||w[row]||.
+__global__ void k_bw_rownorm(const float* w, float* n, int64_t rows, int L) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float ss = 0.f;
+  for (int j = lane; j < L; j += 64) ss += w[row * L + j] * w[row * L + j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) n[row] = sqrtf(ss);
+}
+
+// VJP of the step + renorm row by row.  R = W + U (W, U given), dWn the
+// cotangent of the new row:  dR = f dWn - n0 / (r + eps)^2 / r (dWn . R) R,
+// f = n0 / (r + eps);  dn0 += (dWn . R) / (r + eps).  Without renorm dR =
+// dWn.  dR is written to dr (the cotangent of both W and U).
+__global__ void k_bw_step_vjp(const float* w, const float* u, const float* n0, const float* dwn,
+                              float* dr, float* dn0, int64_t rows, int L, int renorm, float eps) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* pw = w + row * L;
+  const float* pu = u + row * L;
+  const float* pd = dwn + row * L;
+  float* po = dr + row * L;
+  if (!renorm) {
+    for (int j = lane; j < L; j += 64) po[j] = pd[j];
+    return;
+  }
+  float ss = 0.f, pr = 0.f;
+  for (int j = lane; j < L; j += 64) {
+    const float r = pw[j] + pu[j];
+    ss += r * r;
+    pr += pd[j] * r;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o);
+    pr += __shfl_xor(pr, o);
+  }
+  const float r = sqrtf(ss), re = r + eps, nn = n0[row];
+  const float f = nn / re;
+  const float k = r > 0.f ? nn / (re * re) / r * pr : 0.f;
+  for (int j = lane; j < L; j += 64) po[j] = f * pd[j] - k * (pw[j] + pu[j]);
+  if (lane == 0) dn0[row] += pr / re;
+}
+
+// dW0 = dW + (dn0 / ||row of W0||) W0, rows of length L.
+__global__ void k_bw_w0(const float* w0, const float* dw, const float* dn0, float* out, int64_t rows,
+                        int L) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float ss = 0.f;
+  for (int j = lane; j < L; j += 64) ss += w0[row * L + j] * w0[row * L + j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float r = sqrtf(ss);
+  const float k = r > 0.f ? dn0[row] / r : 0.f;
+  for (int j = lane; j < L; j += 64) out[row * L + j] = dw[row * L + j] + k * w0[row * L + j];
+}
+
+// Momentum coefficient per head: beta[b] = mean of mom[b * sbh + t0 ..
+// t0 + n) (0 when n = 0); one wave per head.
+__global__ void k_bw_beta(const float* mom, int64_t sbh, int64_t t0, int n, float* beta, int bh) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  float s = 0.f;
+  for (int t = lane; t < n; t += 64) s += mom[(int64_t)b * sbh + t0 + t];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) beta[b] = n > 0 ? s / (float)n : 0.f;
+}
+
+// dmom[b * sbh + t0 + t] += (dbeta[b] + dbeta[bh + b] + dbeta[2 bh + b]) / n
+// (the three matrices' momentum dots of head b, in that order).
+__global__ void k_bw_dmom(const float* dbeta, float* dmom, int64_t sbh, int64_t t0, int n, int bh) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const float db = (dbeta[b] + dbeta[bh + b]) + dbeta[2 * bh + b];
+  dmom[(int64_t)b * sbh + t0 + t] += db / (float)n;
+}
+
+// Activations to fp32 (rows of d of a [bh][T][*] array with the layout's
+// strides): out[(b n + t) d + i] = x[b sbh + (t0 + t) st + i].
+__global__ void k_bw_gather(const void* x, int bf, int64_t sbh, int64_t st, int64_t t0, int n, int d,
+                            int bh, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)bh * n * d) return;
+  const int64_t row = i / d;
+  const int t = (int)(row % n), b = (int)(row / n), c = (int)(i % d);
+  out[i] = ldx(x, (int64_t)b * sbh + (t0 + t) * st + c, bf);
+}
+
+// out[b sbh + (t0 + t) st + i] += x[(b n + t) d + i]
+__global__ void k_bw_scatter_add(const float* x, int64_t sbh, int64_t st, int64_t t0, int n, int d,
+                                 int bh, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)bh * n * d) return;
+  const int64_t row = i / d;
+  const int t = (int)(row % n), b = (int)(row / n), c = (int)(i % d);
+  out[(int64_t)b * sbh + (t0 + t) * st + c] += x[i];
+}
+
+// p[0 .. n) = v
+__global__ void k_bw_fill(float* p, float v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Frobenius normalisation of Newton-Schulz and its VJP, per matrix m with
+// sum of squares ss[m]: c1[m] = 1 / (r + eps), r = sqrt(ss[m]); with dot
+// (= sum dX * G): c2[m] = -dot[m] / ((r + eps)^2 r) (0 when r = 0), so that
+// dG = c1 dX + c2 G.
+__global__ void k_bw_nscoef(const float* ss, const float* dot, float* c1, float* c2, int count, float eps) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= count) return;
+  const float r = sqrtf(ss[m]), re = r + eps;
+  c1[m] = 1.0f / re;
+  if (dot != nullptr) c2[m] = r > 0.f ? -dot[m] / (re * re * r) : 0.f;
+}
+
+// ------------------------------------------------------------ launches ----
+hipError_t bw_fill(float* p, float v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+hipError_t bw_nscoef(const float* ss, const float* dot, float* c1, float* c2, int count, float eps,
+                     hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_nscoef, dim3((unsigned)((count + 63) / 64)), dim3(64), 0, s, ss, dot, c1, c2, count,
+                     eps);
+  return hipGetLastError();
+}
+static dim3 g1(int64_t n, int tpb = 256) { return dim3((unsigned)((n + tpb - 1) / tpb)); }
+static dim3 grows(int64_t rows) { return dim3((unsigned)((rows + 3) / 4)); }
+
+hipError_t bw_read(float* g, float* u, float* dh, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_read, g1(n), dim3(256), 0, s, g, u, dh, n);
+  return hipGetLastError();
+}
+hipError_t bw_grad_fwd(const float* g, const float* u, const float* e, float* o1, float* o3, float* o2,
+                       const float* e1, const float* e3, const float* e2, int64_t esbh, int64_t t0, int n,
+                       int dh, int bh, hipStream_t s) {
+  const int64_t tot = (int64_t)bh * n * dh;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_grad_fwd, g1(tot), dim3(256), 0, s, g, u, e, o1, o3, o2, e1, e3, e2, esbh, t0, n,
+                     dh, bh);
+  return hipGetLastError();
+}
+hipError_t bw_grad_bwd(float* g, float* u, float* e, float* p1, float* p3, float* p2, float* r1, float* r3,
+                       float* r2, const float* e1, const float* e3, const float* e2, int64_t esbh,
+                       int64_t t0, int n, int dh, int bh, hipStream_t s) {
+  const int64_t tot = (int64_t)bh * n * dh;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_grad_bwd, g1(tot), dim3(256), 0, s, g, u, e, p1, p3, p2, r1, r3, r2, e1, e3, e2,
+                     esbh, t0, n, dh, bh);
+  return hipGetLastError();
+}
+hipError_t bw_rowsum(const float* x, float* out, int64_t osbh, int64_t t0, int n, int dh, int bh,
+                     hipStream_t s) {
+  const int64_t rows = (int64_t)bh * n;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_rowsum, grows(rows), dim3(256), 0, s, x, out, osbh, t0, n, dh, bh);
+  return hipGetLastError();
+}
+hipError_t bw_dot(const float* x, const float* y, float* out, int64_t size, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_dot, dim3((unsigned)count), dim3(256), 0, s, x, y, out, size);
+  return hipGetLastError();
+}
+hipError_t bw_axpby(float* y, const float* x, const float* z, const float* am, float a, const float* bm,
+                    float b, int64_t size, int count, hipStream_t s) {
+  const int64_t tot = size * count;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_axpby, g1(tot), dim3(256), 0, s, y, x, z, am, a, bm, b, size, tot);
+  return hipGetLastError();
+}
+hipError_t bw_transpose(const float* in, float* out, int rows, int cols, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32), (unsigned)count);
+  hipLaunchKernelGGL(k_bw_transpose, grid, dim3(32, 8), 0, s, in, out, rows, cols, count);
+  return hipGetLastError();
+}
+hipError_t bw_symm(const float* a, float* out, int n, int count, hipStream_t s) {
+  const int64_t tot = (int64_t)count * n * n;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_symm, g1(tot), dim3(256), 0, s, a, out, n, count);
+  return hipGetLastError();
+}
+hipError_t bw_step(float* w, const float* u, const float* n0, int64_t rows, int L, int renorm, float eps,
+                   hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_step, grows(rows), dim3(256), 0, s, w, u, n0, rows, L, renorm, eps);
+  return hipGetLastError();
+}
+hipError_t bw_rownorm(const float* w, float* n, int64_t rows, int L, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_rownorm, grows(rows), dim3(256), 0, s, w, n, rows, L);
+  return hipGetLastError();
+}
+hipError_t bw_step_vjp(const float* w, const float* u, const float* n0, const float* dwn, float* dr,
+                       float* dn0, int64_t rows, int L, int renorm, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_step_vjp, grows(rows), dim3(256), 0, s, w, u, n0, dwn, dr, dn0, rows, L, renorm,
+                     eps);
+  return hipGetLastError();
+}
+hipError_t bw_w0(const float* w0, const float* dw, const float* dn0, float* out, int64_t rows, int L,
+                 hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_w0, grows(rows), dim3(256), 0, s, w0, dw, dn0, out, rows, L);
+  return hipGetLastError();
+}
+hipError_t bw_beta(const float* mom, int64_t sbh, int64_t t0, int n, float* beta, int bh, hipStream_t s) {
+  if (bh <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_beta, dim3((unsigned)bh), dim3(64), 0, s, mom, sbh, t0, n, beta, bh);
+  return hipGetLastError();
+}
+hipError_t bw_dmom(const float* dbeta, float* dmom, int64_t sbh, int64_t t0, int n, int bh, hipStream_t s) {
+  if (n <= 0 || bh <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_dmom, dim3((unsigned)((n + 255) / 256), (unsigned)bh), dim3(256), 0, s, dbeta,
+                     dmom, sbh, t0, n, bh);
+  return hipGetLastError();
+}
+hipError_t bw_gather(const void* x, int bf, int64_t sbh, int64_t st, int64_t t0, int n, int d, int bh,
+                     float* out, hipStream_t s) {
+  const int64_t tot = (int64_t)bh * n * d;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_gather, g1(tot), dim3(256), 0, s, x, bf, sbh, st, t0, n, d, bh, out);
+  return hipGetLastError();
+}
+hipError_t bw_scatter_add(const float* x, int64_t sbh, int64_t st, int64_t t0, int n, int d, int bh,
+                          float* out, hipStream_t s) {
+  const int64_t tot = (int64_t)bh * n * d;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bw_scatter_add, g1(tot), dim3(256), 0, s, x, sbh, st, t0, n, d, bh, out);
+  return hipGetLastError();
+}
+
+}  // namespace lact

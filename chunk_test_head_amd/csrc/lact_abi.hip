@@ -76,13 +76,15 @@ static int elem_size(int dtype) { return dtype == LACT_BF16 ? 2 : 4; }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-static lact_status check_shape(const lact_shape* sh) {
+// any_f32_d: fp32 activations at every d (the backward, whose kernels are
+// generic); otherwise fp32 activations need d <= 128.
+static lact_status check_shape(const lact_shape* sh, bool any_f32_d = false) {
   if (sh == nullptr) return LACT_ERR_INVALID_ARG;
   if (sh->bh < 1 || sh->d < 1 || sh->dh < 1) return LACT_ERR_INVALID_ARG;
   if (sh->dtype != LACT_F32 && sh->dtype != LACT_BF16) return LACT_ERR_INVALID_ARG;
   if (sh->d != 64 && sh->d != 128 && sh->d != 256) return LACT_ERR_UNSUPPORTED;
   if (sh->dh % 64 != 0 || sh->dh < sh->d || sh->dh > 4096) return LACT_ERR_UNSUPPORTED;
-  if (sh->dtype == LACT_F32 && sh->d > 128) return LACT_ERR_UNSUPPORTED;
+  if (sh->dtype == LACT_F32 && sh->d > 128 && !any_f32_d) return LACT_ERR_UNSUPPORTED;
   return LACT_OK;
 }
 
@@ -1143,6 +1145,460 @@ lact_status lact_check_finite(const int32_t* flag, void* stream) {
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
   return h != 0 ? LACT_ERR_NONFINITE : LACT_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ outer-loop backward --
+// The vector-Jacobian product of lact_sequence (outputs o) with respect to
+// q, k, v, the learning rates, the momentum coefficients and W0, given the
+// cotangent dO: the forward is recomputed in fp32 chunk by chunk (the state
+// before every chunk kept in the workspace), then the chunks are walked
+// backwards through the chain rule of each step (read, chunk gradient,
+// momentum, Newton-Schulz, step + renorm; see k_backward.hip).
+namespace lact {
+
+namespace {
+
+// element (b, i, j) = p[b bs + i s0 + j s1] (bf: bf16 elements)
+struct Mat {
+  const void* p;
+  int bf;
+  int64_t bs, s0, s1;
+};
+
+hipError_t mm(Mat A, Mat B, const float* D, int64_t dbs, int64_t dsm, float* C, int64_t cbs, int64_t csm,
+              int M, int N, int K, int batch, float alpha, float beta, hipStream_t s) {
+  BGemm g;
+  g.A = A.p; g.a_bf16 = A.bf; g.a_bs = A.bs; g.a_sm = A.s0; g.a_sk = A.s1;
+  g.B = B.p; g.b_bf16 = B.bf; g.b_bs = B.bs; g.b_sk = B.s0; g.b_sn = B.s1;
+  g.D = D; g.d_bs = dbs; g.d_sm = dsm;
+  g.C = C; g.c_bs = cbs; g.c_sm = csm;
+  g.M = M; g.N = N; g.K = K; g.batch = batch;
+  g.alpha = alpha; g.beta = beta;
+  return launch_bgemm(g, s);
+}
+
+struct Bw {
+  // shape
+  int bh, d, dh, cmax, nch;
+  bool mom;
+  int64_t msz;  // d dh
+  // buffers (fp32)
+  float *states, *n0, *dst, *dold, *dn0;
+  float *xa, *xb, *xo, *dx;            // [bh][cmax][d]
+  float *ag, *au, *ae, *o1, *o3, *o2, *r1, *r3, *r2;  // [bh][cmax][dh]
+  float *G, *U, *dR;                   // [3][bh][d dh], natural orientation
+  float *Xs;                           // [6][3 bh][d][dh]: Newton-Schulz iterates
+  float *Am, *Bm, *dAm, *dBm, *Sm;     // [3 bh][d][d]
+  float *dXw, *dXn;                    // [3 bh][d][dh]
+  float *beta, *ss, *dot, *c1, *c2, *dbeta;  // scalars
+  int64_t bytes;
+  int nstate() const { return mom ? 6 : 3; }
+  float* state(int c) const { return states + (int64_t)c * nstate() * bh * msz; }
+  // matrix j (0 W1, 1 W3, 2 W2; 3.. the momentum) of a state block
+  static float* mat(float* base, int j, int bh, int64_t msz) { return base + (int64_t)j * bh * msz; }
+};
+
+Bw bw_layout(const lact_shape* sh, int64_t T, int64_t chunk, bool mom, char* base) {
+  Bw w;
+  memset(&w, 0, sizeof(w));
+  w.bh = sh->bh; w.d = sh->d; w.dh = sh->dh;
+  w.cmax = (int)(chunk < T ? chunk : T);
+  if (w.cmax < 1) w.cmax = 1;
+  w.nch = (int)((T + chunk - 1) / chunk);
+  w.mom = mom;
+  w.msz = (int64_t)sh->d * sh->dh;
+  int64_t off = 0;
+  auto take = [&](int64_t floats) {
+    float* p = base ? reinterpret_cast<float*>(base + off) : nullptr;
+    off += align256(floats * 4);
+    return p;
+  };
+  const int64_t bh = w.bh, m3 = 3 * bh * w.msz;
+  w.states = take((int64_t)(w.nch + 1) * w.nstate() * bh * w.msz);
+  w.n0 = take(bh * (2 * w.dh + w.d));
+  w.dst = take(2 * m3);
+  w.dold = take(2 * m3);
+  w.dn0 = take(bh * (2 * w.dh + w.d));
+  const int64_t act_d = bh * w.cmax * w.d, act_h = bh * w.cmax * w.dh;
+  w.xa = take(act_d); w.xb = take(act_d); w.xo = take(act_d); w.dx = take(act_d);
+  w.ag = take(act_h); w.au = take(act_h); w.ae = take(act_h);
+  w.o1 = take(act_h); w.o3 = take(act_h); w.o2 = take(act_h);
+  w.r1 = take(act_h); w.r3 = take(act_h); w.r2 = take(act_h);
+  w.G = take(m3); w.U = take(m3); w.dR = take(m3);
+  w.Xs = take(6 * m3);
+  const int64_t sq = 3 * bh * (int64_t)w.d * w.d;
+  w.Am = take(sq); w.Bm = take(sq); w.dAm = take(sq); w.dBm = take(sq); w.Sm = take(sq);
+  w.dXw = take(m3); w.dXn = take(m3);
+  w.beta = take(bh); w.ss = take(3 * bh); w.dot = take(3 * bh);
+  w.c1 = take(3 * bh); w.c2 = take(3 * bh); w.dbeta = take(3 * bh);
+  w.bytes = off;
+  return w;
+}
+
+// Rows of the three matrices: (pointer offset of block j, rows, row length).
+inline int64_t rows_of(const Bw& w, int j) { return (int64_t)w.bh * (j < 2 ? w.dh : w.d); }
+inline int len_of(const Bw& w, int j) { return j < 2 ? w.d : w.dh; }
+inline float* n0_of(const Bw& w, float* base, int j) {
+  return base + (j == 0 ? 0 : (j == 1 ? (int64_t)w.bh * w.dh : 2 * (int64_t)w.bh * w.dh));
+}
+
+#define BW_TRY(x)                                   \
+  do {                                              \
+    const hipError_t e_ = (x);                      \
+    if (e_ != hipSuccess) return e_;                \
+  } while (0)
+
+// g = X W1^T, u = X W3^T into ag, au and (E: V W2, else skip) e into ae, for
+// n rows of X ([bh][n][d], fp32) with the state W.
+hipError_t bw_products(const Bw& w, const float* W, const float* X, const float* V, int n, hipStream_t s) {
+  const int64_t msz = w.msz;
+  const Mat x{X, 0, (int64_t)n * w.d, w.d, 1};
+  const float* W1 = W;
+  const float* W3 = W + w.bh * msz;
+  const float* W2 = W + 2 * w.bh * msz;
+  BW_TRY(mm(x, Mat{W1, 0, msz, 1, w.d}, nullptr, 0, 0, w.ag, (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
+  BW_TRY(mm(x, Mat{W3, 0, msz, 1, w.d}, nullptr, 0, 0, w.au, (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
+  if (V != nullptr)
+    BW_TRY(mm(Mat{V, 0, (int64_t)n * w.d, w.d, 1}, Mat{W2, 0, msz, w.dh, 1}, nullptr, 0, 0, w.ae,
+              (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
+  return hipSuccess;
+}
+
+// The write's raw gradient G (natural orientation, into w.G) from the state
+// W and the gathered keys / values (xa, xb: n rows); leaves g, u, e in ag,
+// au, ae and the scaled factors in o1, o3, o2.
+hipError_t bw_gradient(const Bw& w, const float* W, int n, const float* e1, const float* e3, const float* e2,
+                       int64_t esbh, int64_t t0, hipStream_t s) {
+  BW_TRY(bw_products(w, W, w.xa, w.xb, n, s));
+  BW_TRY(bw_grad_fwd(w.ag, w.au, w.ae, w.o1, w.o3, w.o2, e1, e3, e2, esbh, t0, n, w.dh, w.bh, s));
+  const int64_t msz = w.msz, nh = (int64_t)n * w.dh, nd = (int64_t)n * w.d;
+  // G1 = o1^T K, G3 = o3^T K  [dh][d];  G2 = V^T o2  [d][dh]
+  BW_TRY(mm(Mat{w.o1, 0, nh, 1, w.dh}, Mat{w.xa, 0, nd, w.d, 1}, nullptr, 0, 0, w.G, msz, w.d, w.dh, w.d, n,
+            w.bh, 1.f, 0.f, s));
+  BW_TRY(mm(Mat{w.o3, 0, nh, 1, w.dh}, Mat{w.xa, 0, nd, w.d, 1}, nullptr, 0, 0, w.G + w.bh * msz, msz, w.d,
+            w.dh, w.d, n, w.bh, 1.f, 0.f, s));
+  BW_TRY(mm(Mat{w.xb, 0, nd, 1, w.d}, Mat{w.o2, 0, nh, w.dh, 1}, nullptr, 0, 0, w.G + 2 * w.bh * msz, msz,
+            w.dh, w.d, w.dh, n, w.bh, 1.f, 0.f, s));
+  return hipSuccess;
+}
+
+// Natural (G1, G3 [dh][d], G2 [d][dh]) <-> wide ([d][dh]) orientation.
+hipError_t bw_to_wide(const Bw& w, const float* nat, float* wide, hipStream_t s) {
+  BW_TRY(bw_transpose(nat, wide, w.dh, w.d, 2 * w.bh, s));
+  return bw_axpby(wide + 2 * w.bh * w.msz, nat + 2 * w.bh * w.msz, nullptr, nullptr, 1.f, nullptr, 0.f, w.msz,
+                  w.bh, s);
+}
+hipError_t bw_from_wide(const Bw& w, const float* wide, float* nat, hipStream_t s) {
+  BW_TRY(bw_transpose(wide, nat, w.d, w.dh, 2 * w.bh, s));
+  return bw_axpby(nat + 2 * w.bh * w.msz, wide + 2 * w.bh * w.msz, nullptr, nullptr, 1.f, nullptr, 0.f, w.msz,
+                  w.bh, s);
+}
+
+// A = X X^T, B = b A + c A A for the 3 bh wide matrices X.
+hipError_t bw_ns_ab(const Bw& w, const float* X, float b, float c, hipStream_t s) {
+  const int cnt = 3 * w.bh, d = w.d, dh = w.dh;
+  const int64_t dd = (int64_t)d * d;
+  BW_TRY(mm(Mat{X, 0, w.msz, dh, 1}, Mat{X, 0, w.msz, 1, dh}, nullptr, 0, 0, w.Am, dd, d, d, d, dh, cnt, 1.f, 0.f, s));
+  return mm(Mat{w.Am, 0, dd, d, 1}, Mat{w.Am, 0, dd, d, 1}, w.Am, dd, d, w.Bm, dd, d, d, d, d, cnt, c, b, s);
+}
+
+// Newton-Schulz of the wide matrices in Xs[0] (normalised here), iterates
+// X_1 .. X_5 into Xs[1 .. 5] (the rebuttal page's quintic coefficients).
+hipError_t bw_ns_forward(const Bw& w, float eps, hipStream_t s) {
+  const int cnt = 3 * w.bh, d = w.d, dh = w.dh;
+  const int64_t m3 = (int64_t)cnt * w.msz, dd = (int64_t)d * d;
+  BW_TRY(bw_dot(w.Xs, nullptr, w.ss, w.msz, cnt, s));
+  BW_TRY(bw_nscoef(w.ss, nullptr, w.c1, nullptr, cnt, eps, s));
+  // keep G (wide) in dXn for the normalisation's VJP
+  BW_TRY(bw_axpby(w.dXn, w.Xs, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
+  BW_TRY(bw_axpby(w.Xs, w.dXn, nullptr, w.c1, 0.f, nullptr, 0.f, w.msz, cnt, s));
+  for (int it = 0; it < 5; ++it) {
+    const float a = kNS[it][0], b = kNS[it][1], c = kNS[it][2];
+    const float* X = w.Xs + it * m3;
+    BW_TRY(bw_ns_ab(w, X, b, c, s));
+    // X' = B X + a X
+    BW_TRY(mm(Mat{w.Bm, 0, dd, d, 1}, Mat{X, 0, w.msz, dh, 1}, X, w.msz, dh, w.Xs + (it + 1) * m3, w.msz, dh,
+              d, dh, d, cnt, 1.f, a, s));
+  }
+  return hipSuccess;
+}
+
+// VJP of Newton-Schulz: dXw holds dU (wide) on entry, dG (wide) on exit;
+// dXn holds G (wide) from bw_ns_forward.
+hipError_t bw_ns_vjp(const Bw& w, float eps, hipStream_t s) {
+  const int cnt = 3 * w.bh, d = w.d, dh = w.dh;
+  const int64_t m3 = (int64_t)cnt * w.msz, dd = (int64_t)d * d;
+  float* dX = w.dXw;
+  float* G = w.dXn;
+  // a separate buffer for the new dX: the U buffer is free here (wide size)
+  float* dY = w.dR;
+  for (int it = 4; it >= 0; --it) {
+    const float a = kNS[it][0], b = kNS[it][1], c = kNS[it][2];
+    const float* X = w.Xs + it * m3;
+    BW_TRY(bw_ns_ab(w, X, b, c, s));
+    // dB = dX X^T
+    BW_TRY(mm(Mat{dX, 0, w.msz, dh, 1}, Mat{X, 0, w.msz, 1, dh}, nullptr, 0, 0, w.dBm, dd, d, d, d, dh, cnt, 1.f,
+              0.f, s));
+    // dY = B dX + a dX   (B symmetric)
+    BW_TRY(mm(Mat{w.Bm, 0, dd, d, 1}, Mat{dX, 0, w.msz, dh, 1}, dX, w.msz, dh, dY, w.msz, dh, d, dh, d, cnt, 1.f,
+              a, s));
+    // dA = b dB + c (dB A + A dB)   (A symmetric)
+    BW_TRY(mm(Mat{w.dBm, 0, dd, d, 1}, Mat{w.Am, 0, dd, d, 1}, w.dBm, dd, d, w.dAm, dd, d, d, d, d, cnt, c, b, s));
+    BW_TRY(mm(Mat{w.Am, 0, dd, d, 1}, Mat{w.dBm, 0, dd, d, 1}, w.dAm, dd, d, w.dAm, dd, d, d, d, d, cnt, c, 1.f, s));
+    // dY += (dA + dA^T) X
+    BW_TRY(bw_symm(w.dAm, w.Sm, d, cnt, s));
+    BW_TRY(mm(Mat{w.Sm, 0, dd, d, 1}, Mat{X, 0, w.msz, dh, 1}, dY, w.msz, dh, dY, w.msz, dh, d, dh, d, cnt, 1.f,
+              1.f, s));
+    BW_TRY(bw_axpby(dX, dY, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
+  }
+  // X0 = G / (||G|| + eps):  dG = c1 dX + c2 G
+  BW_TRY(bw_dot(dX, G, w.dot, w.msz, cnt, s));
+  BW_TRY(bw_nscoef(w.ss, w.dot, w.c1, w.c2, cnt, eps, s));
+  return bw_axpby(dX, dX, G, w.c1, 0.f, w.c2, 0.f, w.msz, cnt, s);
+}
+
+}  // namespace
+}  // namespace lact
+
+extern "C" {
+
+size_t lact_backward_workspace_bytes(const lact_shape* sh, int64_t T, int64_t chunk,
+                                     const lact_update_opts* opts) {
+  if (check_shape(sh, true) != LACT_OK || T < 0 || chunk < 1 || opts == nullptr) return 0;
+  return (size_t)bw_layout(sh, T, chunk, opts->use_momentum != 0, nullptr).bytes;
+}
+
+lact_status lact_sequence_backward(const lact_shape* sh, const float* w1, const float* w3, const float* w2,
+                                   const void* q, lact_layout ql, const void* k, lact_layout kl,
+                                   const void* v, lact_layout vl, const float* dout, const float* e1,
+                                   const float* e3, const float* e2, const float* mom, int64_t esbh,
+                                   int64_t T, int64_t chunk, int32_t order, int64_t sub_off,
+                                   int64_t sub_len, int32_t update_last, const lact_update_opts* op,
+                                   const lact_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  lact_status r;
+  if ((r = check_shape(sh, true)) != LACT_OK) return r;
+  if ((r = check_opts(op)) != LACT_OK) return r;
+  if (op->renorm == 2 || op->eta_per_channel) return LACT_ERR_UNSUPPORTED;
+  if (T < 0 || chunk < 1) return LACT_ERR_INVALID_ARG;
+  if (order != LACT_APPLY_THEN_UPDATE && order != LACT_UPDATE_THEN_APPLY) return LACT_ERR_INVALID_ARG;
+  if (sub_len >= 0 && (sub_off < 0 || sub_off >= chunk)) return LACT_ERR_INVALID_ARG;
+  if (gr == nullptr || esbh < T) return LACT_ERR_INVALID_ARG;
+  if ((r = check_act(sh, q, ql, T)) != LACT_OK) return r;
+  if ((r = check_act(sh, k, kl, T)) != LACT_OK) return r;
+  if ((r = check_act(sh, v, vl, T)) != LACT_OK) return r;
+  const bool mo = op->use_momentum != 0;
+  for (const void* p : {(const void*)w1, (const void*)w3, (const void*)w2, (const void*)gr->dw1,
+                        (const void*)gr->dw3, (const void*)gr->dw2}) {
+    if (p == nullptr) return LACT_ERR_INVALID_ARG;
+    if (!aligned16(p)) return LACT_ERR_ALIGNMENT;
+  }
+  if (T > 0) {
+    for (const void* p : {(const void*)dout, (const void*)e1, (const void*)e3, (const void*)e2,
+                          (const void*)gr->dq, (const void*)gr->dk, (const void*)gr->dv,
+                          (const void*)gr->deta1, (const void*)gr->deta3, (const void*)gr->deta2}) {
+      if (p == nullptr) return LACT_ERR_INVALID_ARG;
+      if (!aligned16(p)) return LACT_ERR_ALIGNMENT;
+    }
+    if (mo && (mom == nullptr || gr->dmom == nullptr)) return LACT_ERR_INVALID_ARG;
+    if (mo && (!aligned16(mom) || !aligned16(gr->dmom))) return LACT_ERR_ALIGNMENT;
+  }
+  Bw w = bw_layout(sh, T, chunk, mo, reinterpret_cast<char*>(ws));
+  if (ws == nullptr || ws_bytes < (size_t)w.bytes) return LACT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LACT_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  const int bh = sh->bh, d = sh->d, dh = sh->dh, bf = sh->dtype == LACT_BF16 ? 1 : 0;
+  const int64_t msz = w.msz, m3 = 3 * (int64_t)bh * msz;
+  const int64_t nd_all = (int64_t)bh * T * d;
+  hipError_t e = hipSuccess;
+#define BW_CALL(x)                         \
+  do {                                     \
+    e = (x);                               \
+    if (e != hipSuccess) return hip_fail(e); \
+  } while (0)
+  // outputs start at zero
+  BW_CALL(bw_fill(gr->dq, 0.f, nd_all, s));
+  BW_CALL(bw_fill(gr->dk, 0.f, nd_all, s));
+  BW_CALL(bw_fill(gr->dv, 0.f, nd_all, s));
+  BW_CALL(bw_fill(gr->deta1, 0.f, (int64_t)bh * esbh, s));
+  if (gr->deta3 != gr->deta1) BW_CALL(bw_fill(gr->deta3, 0.f, (int64_t)bh * esbh, s));
+  if (gr->deta2 != gr->deta1 && gr->deta2 != gr->deta3) BW_CALL(bw_fill(gr->deta2, 0.f, (int64_t)bh * esbh, s));
+  if (mo) BW_CALL(bw_fill(gr->dmom, 0.f, (int64_t)bh * esbh, s));
+  // state 0: W0 (fp32, natural orientation), momentum zero; n0 = row norms
+  float* S0 = w.state(0);
+  BW_CALL(bw_axpby(S0, w1, nullptr, nullptr, 1.f, nullptr, 0.f, msz, bh, s));
+  BW_CALL(bw_axpby(S0 + bh * msz, w3, nullptr, nullptr, 1.f, nullptr, 0.f, msz, bh, s));
+  BW_CALL(bw_axpby(S0 + 2 * bh * msz, w2, nullptr, nullptr, 1.f, nullptr, 0.f, msz, bh, s));
+  if (mo) BW_CALL(bw_fill(S0 + m3, 0.f, m3, s));
+  for (int j = 0; j < 3; ++j)
+    BW_CALL(bw_rownorm(S0 + j * bh * msz, n0_of(w, w.n0, j), rows_of(w, j), len_of(w, j), s));
+  BW_CALL(bw_fill(w.dst, 0.f, 2 * m3, s));
+  BW_CALL(bw_fill(w.dn0, 0.f, (int64_t)bh * (2 * dh + d), s));
+  // chunk plan (the drivers' rule)
+  struct Ch { int64_t s0, e0, a0, a1; bool write; };
+  std::vector<Ch> plan;
+  for (int64_t s0 = 0; s0 < T; s0 += chunk) {
+    const int64_t e0 = s0 + chunk < T ? s0 + chunk : T;
+    const bool last = e0 == T;
+    int64_t a0 = s0, a1 = e0;
+    if (sub_len >= 0) {
+      a0 = s0 + sub_off;
+      a1 = a0 + sub_len < e0 ? a0 + sub_len : e0;
+    }
+    const bool wr = ((order == LACT_UPDATE_THEN_APPLY) || !last || update_last) && a1 > a0;
+    plan.push_back(Ch{s0, e0, a0, a1, wr});
+  }
+  // one write from state `in` to state `out` (fp32 recompute); leaves G~ in
+  // w.G (natural) and, with Muon, the iterates in w.Xs
+  auto write_forward = [&](const Ch& c, const float* in, float* out, bool keep_ns) -> hipError_t {
+    const int n = (int)(c.a1 - c.a0);
+    BW_TRY(bw_gather(k, bf, kl.stride_bh, kl.stride_tok, c.a0, n, d, bh, w.xa, s));
+    BW_TRY(bw_gather(v, bf, vl.stride_bh, vl.stride_tok, c.a0, n, d, bh, w.xb, s));
+    BW_TRY(bw_gradient(w, in, n, e1, e3, e2, esbh, c.a0, s));
+    if (mo) {
+      BW_TRY(bw_beta(mom, esbh, c.a0, n, w.beta, bh, s));
+      for (int j = 0; j < 3; ++j)
+        BW_TRY(bw_axpby(w.G + j * bh * msz, w.G + j * bh * msz, in + (3 + j) * bh * msz, nullptr, 1.f, w.beta,
+                        0.f, msz, bh, s));
+      BW_TRY(bw_axpby(out + m3, w.G, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));  // M <- G~
+    }
+    if (op->use_muon) {
+      BW_TRY(bw_to_wide(w, w.G, w.Xs, s));
+      BW_TRY(bw_ns_forward(w, op->ns_eps, s));
+      BW_TRY(bw_from_wide(w, w.Xs + 5 * m3, w.U, s));
+    } else {
+      BW_TRY(bw_axpby(w.U, w.G, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
+    }
+    (void)keep_ns;
+    BW_TRY(bw_axpby(out, in, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
+    for (int j = 0; j < 3; ++j)
+      BW_TRY(bw_step(out + j * bh * msz, w.U + j * bh * msz, n0_of(w, w.n0, j), rows_of(w, j), len_of(w, j),
+                     op->renorm, op->renorm_eps, s));
+    return hipSuccess;
+  };
+  // forward: the state before every chunk (state nch = the final state)
+  for (size_t ci = 0; ci < plan.size(); ++ci) {
+    float* in = w.state((int)ci);
+    float* out = w.state((int)ci + 1);
+    if (plan[ci].write) {
+      BW_CALL(write_forward(plan[ci], in, out, false));
+    } else {
+      BW_CALL(bw_axpby(out, in, nullptr, nullptr, 1.f, nullptr, 0.f, (int64_t)w.nstate() * bh * msz, 1, s));
+    }
+  }
+  // read VJP of chunk c with state W: dq += dX, dstate W += dW
+  auto read_vjp = [&](const Ch& c, const float* W) -> hipError_t {
+    const int n = (int)(c.e0 - c.s0);
+    const int64_t nd = (int64_t)n * d, nh = (int64_t)n * dh;
+    BW_TRY(bw_gather(q, bf, ql.stride_bh, ql.stride_tok, c.s0, n, d, bh, w.xo, s));
+    BW_TRY(bw_gather(dout, 0, (int64_t)T * d, d, c.s0, n, d, bh, w.dx, s));
+    // g, u into ag, au; dh = dO W2 into ae
+    BW_TRY(bw_products(w, W, w.xo, nullptr, n, s));
+    BW_TRY(mm(Mat{w.dx, 0, nd, d, 1}, Mat{W + 2 * bh * msz, 0, msz, dh, 1}, nullptr, 0, 0, w.ae, nh, dh, n, dh, d,
+              bh, 1.f, 0.f, s));
+    BW_TRY(bw_read(w.ag, w.au, w.ae, (int64_t)bh * nh, s));  // ag = dg, au = du, ae = h
+    float* dW1 = w.dst;
+    float* dW3 = w.dst + bh * msz;
+    float* dW2 = w.dst + 2 * bh * msz;
+    // dW2 += dO^T h, dW1 += dg^T x, dW3 += du^T x
+    BW_TRY(mm(Mat{w.dx, 0, nd, 1, d}, Mat{w.ae, 0, nh, dh, 1}, dW2, msz, dh, dW2, msz, dh, d, dh, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(Mat{w.ag, 0, nh, 1, dh}, Mat{w.xo, 0, nd, d, 1}, dW1, msz, d, dW1, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(Mat{w.au, 0, nh, 1, dh}, Mat{w.xo, 0, nd, d, 1}, dW3, msz, d, dW3, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    // dx = dg W1 + du W3
+    BW_TRY(mm(Mat{w.ag, 0, nh, dh, 1}, Mat{W, 0, msz, d, 1}, nullptr, 0, 0, w.xa, nd, d, n, d, dh, bh, 1.f, 0.f, s));
+    BW_TRY(mm(Mat{w.au, 0, nh, dh, 1}, Mat{W + bh * msz, 0, msz, d, 1}, w.xa, nd, d, w.xa, nd, d, n, d, dh, bh, 1.f,
+              1.f, s));
+    return bw_scatter_add(w.xa, (int64_t)T * d, d, c.s0, n, d, bh, gr->dq, s);
+  };
+  // write VJP of chunk c from state `in` (the state before the write): the
+  // cotangent of the new state is in w.dst, that of `in` replaces it
+  auto write_vjp = [&](const Ch& c, const float* in) -> hipError_t {
+    const int n = (int)(c.a1 - c.a0);
+    const int64_t nd = (int64_t)n * d, nh = (int64_t)n * dh;
+    // recompute G~ (w.G), the iterates, U
+    float* scratch_out = w.dold;  // (overwritten below; only the G~ / U side products matter)
+    BW_TRY(write_forward(c, in, scratch_out, true));
+    // step + renorm VJP: dR (cotangent of W_in and of U)
+    for (int j = 0; j < 3; ++j)
+      BW_TRY(bw_step_vjp(in + j * bh * msz, w.U + j * bh * msz, n0_of(w, w.n0, j), w.dst + j * bh * msz,
+                         w.dR + j * bh * msz, n0_of(w, w.dn0, j), rows_of(w, j), len_of(w, j), op->renorm,
+                         op->renorm_eps, s));
+    // dold W = dR
+    BW_TRY(bw_axpby(w.dold, w.dR, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
+    // dG~ (natural) into w.U
+    if (op->use_muon) {
+      BW_TRY(bw_to_wide(w, w.dR, w.dXw, s));
+      // dXn must hold G~ (wide) for the normalisation VJP: bw_ns_forward
+      // left it there
+      BW_TRY(bw_ns_vjp(w, op->ns_eps, s));
+      BW_TRY(bw_from_wide(w, w.dXw, w.U, s));
+    } else {
+      BW_TRY(bw_axpby(w.U, w.dR, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
+    }
+    if (mo) {
+      // M_new = G~: its cotangent joins dG~; dbeta = sum dG~ . M_old; dM_old = beta dG~
+      BW_TRY(bw_axpby(w.U, w.U, w.dst + m3, nullptr, 1.f, nullptr, 1.f, m3, 1, s));
+      BW_TRY(bw_dot(w.U, in + m3, w.dbeta, msz, 3 * bh, s));
+      for (int j = 0; j < 3; ++j)
+        BW_TRY(bw_axpby(w.dold + m3 + j * bh * msz, w.U + j * bh * msz, nullptr, w.beta, 0.f, nullptr, 0.f, msz,
+                        bh, s));
+      BW_TRY(bw_dmom(w.dbeta, gr->dmom, esbh, c.a0, n, bh, s));
+    }
+    // chunk gradient VJP with dG = w.U (natural): p1 = k dG1^T, p3 = k dG3^T, p2 = v dG2
+    const float* dG1 = w.U;
+    const float* dG3 = w.U + bh * msz;
+    const float* dG2 = w.U + 2 * bh * msz;
+    BW_TRY(bw_products(w, in, w.xa, w.xb, n, s));  // g, u, e (unscaled)
+    BW_TRY(mm(Mat{w.xa, 0, nd, d, 1}, Mat{dG1, 0, msz, 1, d}, nullptr, 0, 0, w.o1, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
+    BW_TRY(mm(Mat{w.xa, 0, nd, d, 1}, Mat{dG3, 0, msz, 1, d}, nullptr, 0, 0, w.o3, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
+    BW_TRY(mm(Mat{w.xb, 0, nd, d, 1}, Mat{dG2, 0, msz, dh, 1}, nullptr, 0, 0, w.o2, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
+    BW_TRY(bw_grad_bwd(w.ag, w.au, w.ae, w.o1, w.o3, w.o2, w.r1, w.r3, w.r2, e1, e3, e2, esbh, c.a0, n, dh, bh, s));
+    BW_TRY(bw_rowsum(w.r1, gr->deta1, esbh, c.a0, n, dh, bh, s));
+    BW_TRY(bw_rowsum(w.r3, gr->deta3, esbh, c.a0, n, dh, bh, s));
+    BW_TRY(bw_rowsum(w.r2, gr->deta2, esbh, c.a0, n, dh, bh, s));
+    // dV = (eta2 h) dG2^T + dE W2^T
+    const float* Win2 = in + 2 * bh * msz;
+    BW_TRY(mm(Mat{w.o2, 0, nh, dh, 1}, Mat{dG2, 0, msz, 1, dh}, nullptr, 0, 0, w.xo, nd, d, n, d, dh, bh, 1.f, 0.f, s));
+    BW_TRY(mm(Mat{w.ae, 0, nh, dh, 1}, Mat{Win2, 0, msz, 1, dh}, w.xo, nd, d, w.xo, nd, d, n, d, dh, bh, 1.f, 1.f, s));
+    BW_TRY(bw_scatter_add(w.xo, (int64_t)T * d, d, c.a0, n, d, bh, gr->dv, s));
+    // dK = (eta3 a) dG3 + (eta1 b) dG1 + dg W1 + du W3
+    BW_TRY(mm(Mat{w.o3, 0, nh, dh, 1}, Mat{dG3, 0, msz, d, 1}, nullptr, 0, 0, w.dx, nd, d, n, d, dh, bh, 1.f, 0.f, s));
+    BW_TRY(mm(Mat{w.o1, 0, nh, dh, 1}, Mat{dG1, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f, 1.f, s));
+    BW_TRY(mm(Mat{w.ag, 0, nh, dh, 1}, Mat{in, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f, 1.f, s));
+    BW_TRY(mm(Mat{w.au, 0, nh, dh, 1}, Mat{in + bh * msz, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f,
+              1.f, s));
+    BW_TRY(bw_scatter_add(w.dx, (int64_t)T * d, d, c.a0, n, d, bh, gr->dk, s));
+    // dW1 += dg^T k, dW3 += du^T k, dW2 += v^T dE (into dold)
+    float* dW1 = w.dold;
+    float* dW3 = w.dold + bh * msz;
+    float* dW2 = w.dold + 2 * bh * msz;
+    BW_TRY(mm(Mat{w.ag, 0, nh, 1, dh}, Mat{w.xa, 0, nd, d, 1}, dW1, msz, d, dW1, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(Mat{w.au, 0, nh, 1, dh}, Mat{w.xa, 0, nd, d, 1}, dW3, msz, d, dW3, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(Mat{w.xb, 0, nd, 1, d}, Mat{w.ae, 0, nh, dh, 1}, dW2, msz, dh, dW2, msz, dh, d, dh, n, bh, 1.f, 1.f, s));
+    // the cotangent of the state before the write
+    if (!mo) BW_TRY(bw_fill(w.dold + m3, 0.f, m3, s));
+    return bw_axpby(w.dst, w.dold, nullptr, nullptr, 1.f, nullptr, 0.f, 2 * m3, 1, s);
+  };
+  for (int ci = (int)plan.size() - 1; ci >= 0; --ci) {
+    const Ch& c = plan[ci];
+    const float* before = w.state(ci);
+    const float* after = w.state(ci + 1);
+    if (order == LACT_UPDATE_THEN_APPLY) BW_CALL(read_vjp(c, after));
+    if (c.write) BW_CALL(write_vjp(c, before));
+    if (order == LACT_APPLY_THEN_UPDATE) BW_CALL(read_vjp(c, before));
+  }
+  // W0: its own cotangent plus the renorm targets (n0 = row norms of W0)
+  const float* w0s[3] = {w1, w3, w2};
+  float* outs[3] = {gr->dw1, gr->dw3, gr->dw2};
+  for (int j = 0; j < 3; ++j) {
+    if (op->renorm)
+      BW_CALL(bw_w0(w0s[j], w.dst + j * bh * msz, n0_of(w, w.dn0, j), outs[j], rows_of(w, j), len_of(w, j), s));
+    else
+      BW_CALL(bw_axpby(outs[j], w.dst + j * bh * msz, nullptr, nullptr, 1.f, nullptr, 0.f, msz, bh, s));
+  }
+#undef BW_CALL
+  return LACT_OK;
 }
 
 }  // extern "C"

@@ -202,4 +202,52 @@ hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int6
                       hipStream_t s);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
 
+
+// ------------------------------------------------ outer-loop backward --
+// Batched fp32 GEMM with strides (k_backward.hip): for b < batch,
+//   C(m, n) = alpha * sum_k A(m, k) B(k, n) + beta * D(m, n)
+//   A(m, k) = A[b a_bs + m a_sm + k a_sk]  (bf16 when a_bf16)
+//   B(k, n) = B[b b_bs + k b_sk + n b_sn]  (bf16 when b_bf16)
+//   D(m, n) = D[b d_bs + m d_sm + n] (D may be C or NULL), C(m, n) =
+//   C[b c_bs + m c_sm + n].
+struct BGemm {
+  const void* A; int a_bf16; int64_t a_bs, a_sm, a_sk;
+  const void* B; int b_bf16; int64_t b_bs, b_sk, b_sn;
+  const float* D; int64_t d_bs, d_sm;
+  float* C; int64_t c_bs, c_sm;
+  int M, N, K, batch;
+  float alpha, beta;
+};
+hipError_t launch_bgemm(const BGemm& g, hipStream_t s);
+hipError_t bw_read(float* g, float* u, float* dh, int64_t n, hipStream_t s);
+hipError_t bw_grad_fwd(const float* g, const float* u, const float* e, float* o1, float* o3, float* o2,
+                       const float* e1, const float* e3, const float* e2, int64_t esbh, int64_t t0, int n,
+                       int dh, int bh, hipStream_t s);
+hipError_t bw_grad_bwd(float* g, float* u, float* e, float* p1, float* p3, float* p2, float* r1, float* r3,
+                       float* r2, const float* e1, const float* e3, const float* e2, int64_t esbh,
+                       int64_t t0, int n, int dh, int bh, hipStream_t s);
+hipError_t bw_rowsum(const float* x, float* out, int64_t osbh, int64_t t0, int n, int dh, int bh,
+                     hipStream_t s);
+hipError_t bw_dot(const float* x, const float* y, float* out, int64_t size, int count, hipStream_t s);
+hipError_t bw_axpby(float* y, const float* x, const float* z, const float* am, float a, const float* bm,
+                    float b, int64_t size, int count, hipStream_t s);
+hipError_t bw_transpose(const float* in, float* out, int rows, int cols, int count, hipStream_t s);
+hipError_t bw_symm(const float* a, float* out, int n, int count, hipStream_t s);
+hipError_t bw_step(float* w, const float* u, const float* n0, int64_t rows, int L, int renorm, float eps,
+                   hipStream_t s);
+hipError_t bw_rownorm(const float* w, float* n, int64_t rows, int L, hipStream_t s);
+hipError_t bw_step_vjp(const float* w, const float* u, const float* n0, const float* dwn, float* dr,
+                       float* dn0, int64_t rows, int L, int renorm, float eps, hipStream_t s);
+hipError_t bw_w0(const float* w0, const float* dw, const float* dn0, float* out, int64_t rows, int L,
+                 hipStream_t s);
+hipError_t bw_beta(const float* mom, int64_t sbh, int64_t t0, int n, float* beta, int bh, hipStream_t s);
+hipError_t bw_dmom(const float* dbeta, float* dmom, int64_t sbh, int64_t t0, int n, int bh, hipStream_t s);
+hipError_t bw_gather(const void* x, int bf, int64_t sbh, int64_t st, int64_t t0, int n, int d, int bh,
+                     float* out, hipStream_t s);
+hipError_t bw_scatter_add(const float* x, int64_t sbh, int64_t st, int64_t t0, int n, int d, int bh,
+                          float* out, hipStream_t s);
+hipError_t bw_fill(float* p, float v, int64_t n, hipStream_t s);
+hipError_t bw_nscoef(const float* ss, const float* dot, float* c1, float* c2, int count, float eps,
+                     hipStream_t s);
+
 }  // namespace lact

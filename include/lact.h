@@ -330,6 +330,54 @@ lact_status lact_linear_sequence(const lact_shape* shape, const lact_linear_stat
                                  int32_t update_last, const lact_update_opts* opts,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Outer-loop backward (how the layer is trained: task-loss gradients flow
+ * back through the earlier writes, uTTT page section 2): the
+ * vector-Jacobian product of lact_sequence.  Given dout = dL/do for the
+ * outputs o of lact_sequence run from the initial weights (w1, w3, w2) with
+ * the same arguments, it writes dL/dq, dL/dk, dL/dv, dL/deta1..3, dL/dmom
+ * and dL/dW0 (through the weights and through the renorm targets, the row
+ * norms of W0).  The forward is recomputed in fp32 (the state before every
+ * chunk kept in the workspace) and the chain rule taken step by step:
+ * read, chunk gradient (with silu''), momentum (beta = mean coefficient),
+ * Newton-Schulz (the five quintic steps as matrix products, whatever
+ * opts->ns_prec), step + row renorm.  renorm 2 and per-channel rates are
+ * not supported (LACT_ERR_UNSUPPORTED); nonfinite is ignored.  fp32
+ * activations are accepted at every supported d (256 included).
+ *   w1, w3 : [bh, dh, d] fp32, w2 : [bh, d, dh] fp32 (W0, natural layout)
+ *   q, k, v : activations of shape.dtype with their layouts
+ *   dout    : [bh, T, d] fp32, contiguous
+ *   eta1, eta3, eta2, mom : [bh, *] fp32 (row stride eta_stride_bh >= T)
+ * Every output is written in full (the call zeroes them first):
+ *   dq, dk, dv : [bh, T, d] fp32 contiguous
+ *   deta1, deta3, deta2, dmom : [bh, eta_stride_bh] fp32 (dmom NULL
+ *       without momentum; the deta pointers may alias, the terms then add)
+ *   dw1, dw3, dw2 : like w1, w3, w2.
+ * Workspace: lact_backward_workspace_bytes(shape, T, chunk, opts) (it holds
+ * one fp32 state per chunk). */
+typedef struct {
+  float* dq;
+  float* dk;
+  float* dv;
+  float* deta1;
+  float* deta3;
+  float* deta2;
+  float* dmom;
+  float* dw1;
+  float* dw3;
+  float* dw2;
+} lact_grads;
+size_t lact_backward_workspace_bytes(const lact_shape* shape, int64_t T, int64_t chunk,
+                                     const lact_update_opts* opts);
+lact_status lact_sequence_backward(const lact_shape* shape, const float* w1, const float* w3,
+                                   const float* w2, const void* q, lact_layout q_layout,
+                                   const void* k, lact_layout k_layout, const void* v,
+                                   lact_layout v_layout, const float* dout, const float* eta1,
+                                   const float* eta3, const float* eta2, const float* mom,
+                                   int64_t eta_stride_bh, int64_t T, int64_t chunk, int32_t order,
+                                   int64_t subset_offset, int64_t subset_len, int32_t update_last,
+                                   const lact_update_opts* opts, const lact_grads* grads,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernel timing for benchmarks.  lact_prof_begin(kind, max_launches)
  * creates 2 * max_launches HIP events; until lact_prof_end, every launch of
  * the kernel `kind` made by the calls above is bracketed by events recorded

@@ -205,3 +205,30 @@ def test_linear_variant_checks(lib):
     assert call(L.opts(use_momentum=True), 1 << 30) == 1          # no momentum buffer
     o = L.opts(use_muon=True)
     assert call(o, L.linear_workspace_bytes(sh, o) - 1) == 4
+
+
+def test_backward_checks(lib):
+    """The outer-loop backward: workspace size grows with the number of
+    chunks (one fp32 state each); the master renorm variant and per-channel
+    rates are unsupported; NULL gradients, a missing momentum output and a
+    short workspace are rejected on the host."""
+    sh = L.Shape(2, 128, 512, L.F32)
+    o = L.opts(use_muon=True, use_momentum=True)
+    a = L.backward_workspace_bytes(sh, 1024, 256, o)
+    b = L.backward_workspace_bytes(sh, 2048, 256, o)
+    assert 0 < a < b
+    assert L.backward_workspace_bytes(L.Shape(2, 96, 512, L.F32), 1024, 256, o) == 0
+    assert L.backward_workspace_bytes(L.Shape(2, 256, 1024, L.F32), 1024, 256, o) > 0
+    lay = L.Layout(1024 * 128, 128)
+    g = L.Grads(*([4096] * 10))
+    def call(o, grads=g, wsb=1 << 34, mom=4096, T=1024):
+        return lib.lact_sequence_backward(ctypes.byref(sh), 256, 256, 256, 512, lay, 768, lay, 1024, lay, 2048,
+                                          4096, 4096, 4096, mom, 1024, T, 256, 0, 0, -1, 0, ctypes.byref(o),
+                                          None if grads is None else ctypes.byref(grads), 8192, wsb, None)
+    assert call(L.opts(use_muon=True, renorm=2)) == 2
+    assert call(L.opts(eta_per_channel=True)) == 2
+    assert call(o, grads=None) == 1
+    assert call(o, mom=None) == 1
+    assert call(o, grads=L.Grads(*([4096] * 6 + [0] + [4096] * 3))) == 1   # no dmom with momentum
+    assert call(o, wsb=a - 1) == 4
+    assert call(o, T=-1) == 1

@@ -5,6 +5,8 @@ float64 on a torch version of the forward written here (matrix-form
 Newton-Schulz, its own loop over chunks).  CPU only."""
 import math
 
+import zlib
+
 import numpy as np
 import pytest
 
@@ -43,7 +45,7 @@ def _loss(W, Q, K, V, e, mom, dO, case):
 @pytest.mark.parametrize("case", list(CASES))
 def test_backward_matches_finite_differences(case):
     T, C, order, subset, muon, momentum, renorm = CASES[case]
-    rng = np.random.default_rng(abs(hash(case)) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
     W, Q, K, V, e, mom, dO = _inputs(rng, T)
     g = B.sequence_vjp(*W, Q, K, V, *e, C, dO, mom=mom if momentum else None, order=order, subset=subset,
                        use_muon=muon, use_momentum=momentum, renorm=renorm)
