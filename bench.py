@@ -37,6 +37,8 @@ def parse():
                    help="Newton-Schulz operand precision")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    p.add_argument("--backward-only", default=None, metavar="WORKLOAD",
+                   help="only time lact_sequence_backward on WORKLOAD (one JSON line)")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="host time budget of the oracle sample (about 10-30 s)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -297,6 +299,70 @@ def time_decode(w, calls=200, warmup=20):
             "amortised_us_per_token_step": us + write_us / C}
 
 
+def backward_gemm_flops(w):
+    """GEMM flops that lact_sequence_backward executes for workload w (all
+    heads), recomputation included: per write of n tokens the forward
+    recompute (12 n d dh, twice: the forward pass and again in the reverse
+    pass) and the write's VJP (30 n d dh); per read of n tokens 16 n d dh;
+    with Muon, per matrix and Newton-Schulz step 4 d^2 dh + 2 d^3 forward
+    (twice) and 8 d^2 dh + 6 d^3 for the VJP."""
+    d, dh = w.d, w.dh
+    per_head = 0.0
+    for _, a, z in w.writes():
+        n = z - a
+        per_head += (2 * 12 + 30) * n * d * dh
+        if w.use_muon:
+            per_head += 3 * 5 * (2 * (4 * d * d * dh + 2 * d ** 3) + (8 * d * d * dh + 6 * d ** 3))
+    for s0, e0 in w.chunk_bounds():
+        per_head += 16 * (e0 - s0) * d * dh
+    return per_head * w.bh
+
+
+def time_backward(w, reps=3):
+    """lact_sequence_backward over the whole sequence of workload w (bf16
+    activations, fp32 compute), seeded random cotangent dO."""
+    import numpy as np
+    import torch
+
+    from chunk_test_head_amd import _lib as L
+    from chunk_test_head_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    W = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in WL.weights(w)]
+    inp = WL.tokens(w, threads=16, values=False)
+    up = lambda n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up("q"), up("k"), up("v")
+    eta = torch.from_numpy(inp["eta"]).to(dev)
+    mom = torch.from_numpy(inp["mom"]).to(dev) if inp["mom"] is not None else None
+    g = torch.Generator(device=dev).manual_seed(w.index)
+    dout = torch.randn(w.bh, w.T, w.d, device=dev, generator=g)
+    shape = L.Shape(w.bh, w.d, w.dh, L.BF16)
+    o = L.opts(use_muon=w.use_muon, use_momentum=w.use_momentum, renorm=w.renorm)
+    grads = {"dq": torch.empty(w.bh, w.T, w.d, device=dev), "dk": torch.empty(w.bh, w.T, w.d, device=dev),
+             "dv": torch.empty(w.bh, w.T, w.d, device=dev), "deta1": torch.empty(w.bh, w.T, device=dev),
+             "dmom": torch.empty(w.bh, w.T, device=dev) if mom is not None else None,
+             "dw1": torch.empty_like(W[0]), "dw3": torch.empty_like(W[1]), "dw2": torch.empty_like(W[2])}
+    grads["deta3"] = grads["deta2"] = grads["deta1"]  # one rate for the three matrices: the terms add
+    ws = torch.empty(L.backward_workspace_bytes(shape, w.T, w.chunk, o), dtype=torch.uint8, device=dev)
+
+    def run():
+        L.lact_sequence_backward(shape, W[0], W[1], W[2], q, k, v, dout, eta, eta, eta, mom, w.T, w.chunk,
+                                 w.order, w.subset, int(w.update_last), o, grads, ws)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    fl = backward_gemm_flops(w)
+    return {"workload": w.name, "ms_per_sequence": ms, "tokens_per_s": w.batch * w.T / (ms * 1e-3),
+            "gemm_tflops_executed": fl / (ms * 1e-3) / 1e12,
+            "pct_of_fp32_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / F32_PEAK_TFLOPS,
+            "workspace_bytes": ws.numel(), "compute": "fp32 (forward recomputed chunk by chunk)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -305,6 +371,10 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.backward_only:
+        from chunk_test_head_amd import workloads as WL
+        print(json.dumps({"outer_loop_backward": time_backward(WL.get(args.backward_only))}), flush=True)
         return
     from chunk_test_head_amd import _lib as L
     from chunk_test_head_amd import workloads as WL
@@ -363,6 +433,7 @@ def main():
                                                "pct_of_peak", "tflops_page_convention")}
         line["other_workloads"] = others
         line["streaming_decode"] = {name: time_decode(WL.get(name)) for name in ("lm-causal", "long-context")}
+        line["outer_loop_backward"] = time_backward(WL.get("lm-causal"))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, W, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -25,55 +25,102 @@ namespace lact {
 __device__ __forceinline__ float ldx(const void* p, int64_t i, int bf) {
   return bf ? (float)reinterpret_cast<const bf16*>(p)[i] : reinterpret_cast<const float*>(p)[i];
 }
+template <bool BF>
+__device__ __forceinline__ float ldt(const void* p, int64_t i) {
+  if constexpr (BF) return (float)reinterpret_cast<const bf16*>(p)[i];
+  else return reinterpret_cast<const float*>(p)[i];
+}
 
-__global__ __launch_bounds__(256) void k_bgemm(BGemm g) {
-  constexpr int T = 64, KS = 32, P = T + 4;
-  __shared__ float sA[KS][P];  // [k][m]
-  __shared__ float sB[KS][P];  // [k][n]
+// One 64 x 64 tile of C over the K range [kb, ke) of matrix b: the next K
+// slab of 32 is loaded into registers while the current one is contracted
+// from LDS (two LDS buffers, one barrier per slab).  With P (split-K) the
+// raw sum goes to P[z][b][m][n] instead of the epilogue.
+template <bool ABF, bool BBF>
+__global__ __launch_bounds__(256) void k_bgemm(BGemm g, int kchunk, float* P) {
+  constexpr int T = 64, KS = 32, PD = T + 4, V = T * KS / 256;
+  __shared__ float sA[2][KS][PD];  // [k][m]
+  __shared__ float sB[2][KS][PD];  // [k][n]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int tn = (g.N + T - 1) / T;
   const int m0 = (blockIdx.x / tn) * T, n0 = (blockIdx.x % tn) * T;
   const int64_t b = blockIdx.y;
-  const char* A = reinterpret_cast<const char*>(g.A) + b * g.a_bs * (g.a_bf16 ? 2 : 4);
-  const char* B = reinterpret_cast<const char*>(g.B) + b * g.b_bs * (g.b_bf16 ? 2 : 4);
+  const int kb = blockIdx.z * kchunk, ke = min(g.K, kb + kchunk);
+  const void* A = reinterpret_cast<const char*>(g.A) + b * g.a_bs * (ABF ? 2 : 4);
+  const void* B = reinterpret_cast<const char*>(g.B) + b * g.b_bs * (BBF ? 2 : 4);
   const bool a_kfast = g.a_sk == 1, b_nfast = g.b_sn == 1;
+  // this thread's elements of a slab: A (m, k) and B (k, n), following the
+  // unit stride so that a wave's loads are contiguous
+  int am[V], ak[V], bn[V], bk[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = tid + 256 * i;
+    am[i] = a_kfast ? e / KS : e % T;
+    ak[i] = a_kfast ? e % KS : e / T;
+    bn[i] = b_nfast ? e % T : e / KS;
+    bk[i] = b_nfast ? e / T : e % KS;
+  }
+  float ra[V], rb[V];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int m = m0 + am[i], k = k0 + ak[i];
+      ra[i] = (m < g.M && k < ke) ? ldt<ABF>(A, (int64_t)m * g.a_sm + (int64_t)k * g.a_sk) : 0.f;
+      const int n = n0 + bn[i], kk = k0 + bk[i];
+      rb[i] = (n < g.N && kk < ke) ? ldt<BBF>(B, (int64_t)kk * g.b_sk + (int64_t)n * g.b_sn) : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      sA[buf][ak[i]][am[i]] = ra[i];
+      sB[buf][bk[i]][bn[i]] = rb[i];
+    }
+  };
   f32x4 acc[2][2];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < g.K; k0 += KS) {
-    // A tile 64 x 32 and B tile 32 x 64, zero outside the matrices; the
-    // thread-to-element map follows the unit stride (coalesced loads)
-#pragma unroll
-    for (int i = 0; i < T * KS / 256; ++i) {
-      const int e = tid + 256 * i;
-      const int m = a_kfast ? e / KS : e % T, k = a_kfast ? e % KS : e / T;
-      float x = 0.f;
-      if (m0 + m < g.M && k0 + k < g.K) x = ldx(A, (int64_t)(m0 + m) * g.a_sm + (int64_t)(k0 + k) * g.a_sk, g.a_bf16);
-      sA[k][m] = x;
-      const int n = b_nfast ? e % T : e / KS, kb = b_nfast ? e / T : e % KS;
-      float y = 0.f;
-      if (n0 + n < g.N && k0 + kb < g.K) y = ldx(B, (int64_t)(k0 + kb) * g.b_sk + (int64_t)(n0 + n) * g.b_sn, g.b_bf16);
-      sB[kb][n] = y;
-    }
-    __syncthreads();
+  const int nslab = ke > kb ? (ke - kb + KS - 1) / KS : 0;
+  if (nslab > 0) {
+    load(kb);
+    store(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < nslab; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nslab) load(kb + (j + 1) * KS);
 #pragma unroll
     for (int s = 0; s < KS / 4; ++s) {
       float fa[2], fb[2];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) fa[x] = sA[4 * s + q][32 * wm + 16 * x + c];
+      for (int x = 0; x < 2; ++x) fa[x] = sA[buf][4 * s + q][32 * wm + 16 * x + c];
 #pragma unroll
-      for (int y = 0; y < 2; ++y) fb[y] = sB[4 * s + q][32 * wn + 16 * y + c];
+      for (int y = 0; y < 2; ++y) fb[y] = sB[buf][4 * s + q][32 * wn + 16 * y + c];
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
+    // buffer buf ^ 1 was last read in slab j - 1, before the previous barrier
+    if (j + 1 < nslab) store(buf ^ 1);
     __syncthreads();
+  }
+  if (P != nullptr) {
+    float* out = P + ((int64_t)blockIdx.z * gridDim.y + b) * g.M * g.N;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 32 * wm + 16 * x + 4 * q + i, n = n0 + 32 * wn + 16 * y + c;
+          if (m < g.M && n < g.N) out[(int64_t)m * g.N + n] = acc[x][y][i];
+        }
+    return;
   }
   const float* D = g.D ? g.D + b * g.d_bs : nullptr;
   float* C = g.C + b * g.c_bs;
@@ -92,10 +139,48 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm g) {
       }
 }
 
-hipError_t launch_bgemm(const BGemm& g, hipStream_t s) {
+// Split-K epilogue: C = alpha * (sum over the splits in order of P) + beta D.
+__global__ void k_bgemm_sum(BGemm g, const float* P, int nsplit) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t mn = (int64_t)g.M * g.N;
+  if (i >= mn * g.batch) return;
+  const int64_t b = i / mn, r = i % mn;
+  const int m = (int)(r / g.N), n = (int)(r % g.N);
+  float acc = 0.f;
+  for (int z = 0; z < nsplit; ++z) acc += P[((int64_t)z * g.batch + b) * mn + r];
+  float v = g.alpha * acc;
+  if (g.D) v += g.beta * g.D[b * g.d_bs + (int64_t)m * g.d_sm + n];
+  g.C[b * g.c_bs + (int64_t)m * g.c_sm + n] = v;
+}
+
+// Split count for a contraction: about two workgroups per CU over all
+// tiles, each split at least 512 deep, at most `max_split` (the partial
+// buffer's capacity in M x N x batch units).
+static int bgemm_splits(const BGemm& g, int max_split) {
+  const int64_t tiles = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64) * g.batch;
+  int ns = 1;
+  while (ns < max_split && tiles * ns * 2 <= 512 && g.K / (2 * ns) >= 512) ns *= 2;
+  return ns;
+}
+
+hipError_t launch_bgemm(const BGemm& g, hipStream_t s, float* partial, int64_t partial_floats) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  const dim3 grid((unsigned)(((g.M + 63) / 64) * ((g.N + 63) / 64)), (unsigned)g.batch);
-  hipLaunchKernelGGL(k_bgemm, grid, dim3(256), 0, s, g);
+  const int64_t mnb = (int64_t)g.M * g.N * g.batch;
+  int ns = 1;
+  if (partial != nullptr && mnb > 0) {
+    const int64_t cap = partial_floats / mnb;
+    ns = bgemm_splits(g, (int)(cap < 64 ? cap : 64));
+  }
+  const int kchunk = ns > 1 ? ((g.K + ns - 1) / ns + 31) / 32 * 32 : (g.K > 0 ? g.K : 1);
+  const dim3 grid((unsigned)(((g.M + 63) / 64) * ((g.N + 63) / 64)), (unsigned)g.batch, (unsigned)ns);
+  float* P = ns > 1 ? partial : nullptr;
+  if (g.a_bf16 && g.b_bf16) hipLaunchKernelGGL((k_bgemm<true, true>), grid, dim3(256), 0, s, g, kchunk, P);
+  else if (g.a_bf16) hipLaunchKernelGGL((k_bgemm<true, false>), grid, dim3(256), 0, s, g, kchunk, P);
+  else if (g.b_bf16) hipLaunchKernelGGL((k_bgemm<false, true>), grid, dim3(256), 0, s, g, kchunk, P);
+  else hipLaunchKernelGGL((k_bgemm<false, false>), grid, dim3(256), 0, s, g, kchunk, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  hipLaunchKernelGGL(k_bgemm_sum, dim3((unsigned)((mnb + 255) / 256)), dim3(256), 0, s, g, P, ns);
   return hipGetLastError();
 }
 

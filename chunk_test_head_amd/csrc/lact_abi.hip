@@ -1167,18 +1167,6 @@ struct Mat {
   int64_t bs, s0, s1;
 };
 
-hipError_t mm(Mat A, Mat B, const float* D, int64_t dbs, int64_t dsm, float* C, int64_t cbs, int64_t csm,
-              int M, int N, int K, int batch, float alpha, float beta, hipStream_t s) {
-  BGemm g;
-  g.A = A.p; g.a_bf16 = A.bf; g.a_bs = A.bs; g.a_sm = A.s0; g.a_sk = A.s1;
-  g.B = B.p; g.b_bf16 = B.bf; g.b_bs = B.bs; g.b_sk = B.s0; g.b_sn = B.s1;
-  g.D = D; g.d_bs = dbs; g.d_sm = dsm;
-  g.C = C; g.c_bs = cbs; g.c_sm = csm;
-  g.M = M; g.N = N; g.K = K; g.batch = batch;
-  g.alpha = alpha; g.beta = beta;
-  return launch_bgemm(g, s);
-}
-
 struct Bw {
   // shape
   int bh, d, dh, cmax, nch;
@@ -1193,6 +1181,8 @@ struct Bw {
   float *Am, *Bm, *dAm, *dBm, *Sm;     // [3 bh][d][d]
   float *dXw, *dXn;                    // [3 bh][d][dh]
   float *beta, *ss, *dot, *c1, *c2, *dbeta;  // scalars
+  float* part;                         // split-K partial sums
+  int64_t part_floats;
   int64_t bytes;
   int nstate() const { return mom ? 6 : 3; }
   float* state(int c) const { return states + (int64_t)c * nstate() * bh * msz; }
@@ -1233,8 +1223,24 @@ Bw bw_layout(const lact_shape* sh, int64_t T, int64_t chunk, bool mom, char* bas
   w.dXw = take(m3); w.dXn = take(m3);
   w.beta = take(bh); w.ss = take(3 * bh); w.dot = take(3 * bh);
   w.c1 = take(3 * bh); w.c2 = take(3 * bh); w.dbeta = take(3 * bh);
+  w.part_floats = 16 * bh * w.msz;
+  w.part = take(w.part_floats);
   w.bytes = off;
   return w;
+}
+
+// The GEMMs of the backward; the workspace's partial buffer lets the long
+// token contractions split K.
+hipError_t mm(const Bw& w, Mat A, Mat B, const float* D, int64_t dbs, int64_t dsm, float* C, int64_t cbs,
+              int64_t csm, int M, int N, int K, int batch, float alpha, float beta, hipStream_t s) {
+  BGemm g;
+  g.A = A.p; g.a_bf16 = A.bf; g.a_bs = A.bs; g.a_sm = A.s0; g.a_sk = A.s1;
+  g.B = B.p; g.b_bf16 = B.bf; g.b_bs = B.bs; g.b_sk = B.s0; g.b_sn = B.s1;
+  g.D = D; g.d_bs = dbs; g.d_sm = dsm;
+  g.C = C; g.c_bs = cbs; g.c_sm = csm;
+  g.M = M; g.N = N; g.K = K; g.batch = batch;
+  g.alpha = alpha; g.beta = beta;
+  return launch_bgemm(g, s, w.part, w.part_floats);
 }
 
 // Rows of the three matrices: (pointer offset of block j, rows, row length).
@@ -1258,10 +1264,10 @@ hipError_t bw_products(const Bw& w, const float* W, const float* X, const float*
   const float* W1 = W;
   const float* W3 = W + w.bh * msz;
   const float* W2 = W + 2 * w.bh * msz;
-  BW_TRY(mm(x, Mat{W1, 0, msz, 1, w.d}, nullptr, 0, 0, w.ag, (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
-  BW_TRY(mm(x, Mat{W3, 0, msz, 1, w.d}, nullptr, 0, 0, w.au, (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
+  BW_TRY(mm(w, x, Mat{W1, 0, msz, 1, w.d}, nullptr, 0, 0, w.ag, (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
+  BW_TRY(mm(w, x, Mat{W3, 0, msz, 1, w.d}, nullptr, 0, 0, w.au, (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
   if (V != nullptr)
-    BW_TRY(mm(Mat{V, 0, (int64_t)n * w.d, w.d, 1}, Mat{W2, 0, msz, w.dh, 1}, nullptr, 0, 0, w.ae,
+    BW_TRY(mm(w, Mat{V, 0, (int64_t)n * w.d, w.d, 1}, Mat{W2, 0, msz, w.dh, 1}, nullptr, 0, 0, w.ae,
               (int64_t)n * w.dh, w.dh, n, w.dh, w.d, w.bh, 1.f, 0.f, s));
   return hipSuccess;
 }
@@ -1275,11 +1281,11 @@ hipError_t bw_gradient(const Bw& w, const float* W, int n, const float* e1, cons
   BW_TRY(bw_grad_fwd(w.ag, w.au, w.ae, w.o1, w.o3, w.o2, e1, e3, e2, esbh, t0, n, w.dh, w.bh, s));
   const int64_t msz = w.msz, nh = (int64_t)n * w.dh, nd = (int64_t)n * w.d;
   // G1 = o1^T K, G3 = o3^T K  [dh][d];  G2 = V^T o2  [d][dh]
-  BW_TRY(mm(Mat{w.o1, 0, nh, 1, w.dh}, Mat{w.xa, 0, nd, w.d, 1}, nullptr, 0, 0, w.G, msz, w.d, w.dh, w.d, n,
+  BW_TRY(mm(w, Mat{w.o1, 0, nh, 1, w.dh}, Mat{w.xa, 0, nd, w.d, 1}, nullptr, 0, 0, w.G, msz, w.d, w.dh, w.d, n,
             w.bh, 1.f, 0.f, s));
-  BW_TRY(mm(Mat{w.o3, 0, nh, 1, w.dh}, Mat{w.xa, 0, nd, w.d, 1}, nullptr, 0, 0, w.G + w.bh * msz, msz, w.d,
+  BW_TRY(mm(w, Mat{w.o3, 0, nh, 1, w.dh}, Mat{w.xa, 0, nd, w.d, 1}, nullptr, 0, 0, w.G + w.bh * msz, msz, w.d,
             w.dh, w.d, n, w.bh, 1.f, 0.f, s));
-  BW_TRY(mm(Mat{w.xb, 0, nd, 1, w.d}, Mat{w.o2, 0, nh, w.dh, 1}, nullptr, 0, 0, w.G + 2 * w.bh * msz, msz,
+  BW_TRY(mm(w, Mat{w.xb, 0, nd, 1, w.d}, Mat{w.o2, 0, nh, w.dh, 1}, nullptr, 0, 0, w.G + 2 * w.bh * msz, msz,
             w.dh, w.d, w.dh, n, w.bh, 1.f, 0.f, s));
   return hipSuccess;
 }
@@ -1300,8 +1306,8 @@ hipError_t bw_from_wide(const Bw& w, const float* wide, float* nat, hipStream_t 
 hipError_t bw_ns_ab(const Bw& w, const float* X, float b, float c, hipStream_t s) {
   const int cnt = 3 * w.bh, d = w.d, dh = w.dh;
   const int64_t dd = (int64_t)d * d;
-  BW_TRY(mm(Mat{X, 0, w.msz, dh, 1}, Mat{X, 0, w.msz, 1, dh}, nullptr, 0, 0, w.Am, dd, d, d, d, dh, cnt, 1.f, 0.f, s));
-  return mm(Mat{w.Am, 0, dd, d, 1}, Mat{w.Am, 0, dd, d, 1}, w.Am, dd, d, w.Bm, dd, d, d, d, d, cnt, c, b, s);
+  BW_TRY(mm(w, Mat{X, 0, w.msz, dh, 1}, Mat{X, 0, w.msz, 1, dh}, nullptr, 0, 0, w.Am, dd, d, d, d, dh, cnt, 1.f, 0.f, s));
+  return mm(w, Mat{w.Am, 0, dd, d, 1}, Mat{w.Am, 0, dd, d, 1}, w.Am, dd, d, w.Bm, dd, d, d, d, d, cnt, c, b, s);
 }
 
 // Newton-Schulz of the wide matrices in Xs[0] (normalised here), iterates
@@ -1319,7 +1325,7 @@ hipError_t bw_ns_forward(const Bw& w, float eps, hipStream_t s) {
     const float* X = w.Xs + it * m3;
     BW_TRY(bw_ns_ab(w, X, b, c, s));
     // X' = B X + a X
-    BW_TRY(mm(Mat{w.Bm, 0, dd, d, 1}, Mat{X, 0, w.msz, dh, 1}, X, w.msz, dh, w.Xs + (it + 1) * m3, w.msz, dh,
+    BW_TRY(mm(w, Mat{w.Bm, 0, dd, d, 1}, Mat{X, 0, w.msz, dh, 1}, X, w.msz, dh, w.Xs + (it + 1) * m3, w.msz, dh,
               d, dh, d, cnt, 1.f, a, s));
   }
   return hipSuccess;
@@ -1339,17 +1345,17 @@ hipError_t bw_ns_vjp(const Bw& w, float eps, hipStream_t s) {
     const float* X = w.Xs + it * m3;
     BW_TRY(bw_ns_ab(w, X, b, c, s));
     // dB = dX X^T
-    BW_TRY(mm(Mat{dX, 0, w.msz, dh, 1}, Mat{X, 0, w.msz, 1, dh}, nullptr, 0, 0, w.dBm, dd, d, d, d, dh, cnt, 1.f,
+    BW_TRY(mm(w, Mat{dX, 0, w.msz, dh, 1}, Mat{X, 0, w.msz, 1, dh}, nullptr, 0, 0, w.dBm, dd, d, d, d, dh, cnt, 1.f,
               0.f, s));
     // dY = B dX + a dX   (B symmetric)
-    BW_TRY(mm(Mat{w.Bm, 0, dd, d, 1}, Mat{dX, 0, w.msz, dh, 1}, dX, w.msz, dh, dY, w.msz, dh, d, dh, d, cnt, 1.f,
+    BW_TRY(mm(w, Mat{w.Bm, 0, dd, d, 1}, Mat{dX, 0, w.msz, dh, 1}, dX, w.msz, dh, dY, w.msz, dh, d, dh, d, cnt, 1.f,
               a, s));
     // dA = b dB + c (dB A + A dB)   (A symmetric)
-    BW_TRY(mm(Mat{w.dBm, 0, dd, d, 1}, Mat{w.Am, 0, dd, d, 1}, w.dBm, dd, d, w.dAm, dd, d, d, d, d, cnt, c, b, s));
-    BW_TRY(mm(Mat{w.Am, 0, dd, d, 1}, Mat{w.dBm, 0, dd, d, 1}, w.dAm, dd, d, w.dAm, dd, d, d, d, d, cnt, c, 1.f, s));
+    BW_TRY(mm(w, Mat{w.dBm, 0, dd, d, 1}, Mat{w.Am, 0, dd, d, 1}, w.dBm, dd, d, w.dAm, dd, d, d, d, d, cnt, c, b, s));
+    BW_TRY(mm(w, Mat{w.Am, 0, dd, d, 1}, Mat{w.dBm, 0, dd, d, 1}, w.dAm, dd, d, w.dAm, dd, d, d, d, d, cnt, c, 1.f, s));
     // dY += (dA + dA^T) X
     BW_TRY(bw_symm(w.dAm, w.Sm, d, cnt, s));
-    BW_TRY(mm(Mat{w.Sm, 0, dd, d, 1}, Mat{X, 0, w.msz, dh, 1}, dY, w.msz, dh, dY, w.msz, dh, d, dh, d, cnt, 1.f,
+    BW_TRY(mm(w, Mat{w.Sm, 0, dd, d, 1}, Mat{X, 0, w.msz, dh, 1}, dY, w.msz, dh, dY, w.msz, dh, d, dh, d, cnt, 1.f,
               1.f, s));
     BW_TRY(bw_axpby(dX, dY, nullptr, nullptr, 1.f, nullptr, 0.f, m3, 1, s));
   }
@@ -1495,19 +1501,19 @@ lact_status lact_sequence_backward(const lact_shape* sh, const float* w1, const 
     BW_TRY(bw_gather(dout, 0, (int64_t)T * d, d, c.s0, n, d, bh, w.dx, s));
     // g, u into ag, au; dh = dO W2 into ae
     BW_TRY(bw_products(w, W, w.xo, nullptr, n, s));
-    BW_TRY(mm(Mat{w.dx, 0, nd, d, 1}, Mat{W + 2 * bh * msz, 0, msz, dh, 1}, nullptr, 0, 0, w.ae, nh, dh, n, dh, d,
+    BW_TRY(mm(w, Mat{w.dx, 0, nd, d, 1}, Mat{W + 2 * bh * msz, 0, msz, dh, 1}, nullptr, 0, 0, w.ae, nh, dh, n, dh, d,
               bh, 1.f, 0.f, s));
     BW_TRY(bw_read(w.ag, w.au, w.ae, (int64_t)bh * nh, s));  // ag = dg, au = du, ae = h
     float* dW1 = w.dst;
     float* dW3 = w.dst + bh * msz;
     float* dW2 = w.dst + 2 * bh * msz;
     // dW2 += dO^T h, dW1 += dg^T x, dW3 += du^T x
-    BW_TRY(mm(Mat{w.dx, 0, nd, 1, d}, Mat{w.ae, 0, nh, dh, 1}, dW2, msz, dh, dW2, msz, dh, d, dh, n, bh, 1.f, 1.f, s));
-    BW_TRY(mm(Mat{w.ag, 0, nh, 1, dh}, Mat{w.xo, 0, nd, d, 1}, dW1, msz, d, dW1, msz, d, dh, d, n, bh, 1.f, 1.f, s));
-    BW_TRY(mm(Mat{w.au, 0, nh, 1, dh}, Mat{w.xo, 0, nd, d, 1}, dW3, msz, d, dW3, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.dx, 0, nd, 1, d}, Mat{w.ae, 0, nh, dh, 1}, dW2, msz, dh, dW2, msz, dh, d, dh, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.ag, 0, nh, 1, dh}, Mat{w.xo, 0, nd, d, 1}, dW1, msz, d, dW1, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.au, 0, nh, 1, dh}, Mat{w.xo, 0, nd, d, 1}, dW3, msz, d, dW3, msz, d, dh, d, n, bh, 1.f, 1.f, s));
     // dx = dg W1 + du W3
-    BW_TRY(mm(Mat{w.ag, 0, nh, dh, 1}, Mat{W, 0, msz, d, 1}, nullptr, 0, 0, w.xa, nd, d, n, d, dh, bh, 1.f, 0.f, s));
-    BW_TRY(mm(Mat{w.au, 0, nh, dh, 1}, Mat{W + bh * msz, 0, msz, d, 1}, w.xa, nd, d, w.xa, nd, d, n, d, dh, bh, 1.f,
+    BW_TRY(mm(w, Mat{w.ag, 0, nh, dh, 1}, Mat{W, 0, msz, d, 1}, nullptr, 0, 0, w.xa, nd, d, n, d, dh, bh, 1.f, 0.f, s));
+    BW_TRY(mm(w, Mat{w.au, 0, nh, dh, 1}, Mat{W + bh * msz, 0, msz, d, 1}, w.xa, nd, d, w.xa, nd, d, n, d, dh, bh, 1.f,
               1.f, s));
     return bw_scatter_add(w.xa, (int64_t)T * d, d, c.s0, n, d, bh, gr->dq, s);
   };
@@ -1550,32 +1556,32 @@ lact_status lact_sequence_backward(const lact_shape* sh, const float* w1, const 
     const float* dG3 = w.U + bh * msz;
     const float* dG2 = w.U + 2 * bh * msz;
     BW_TRY(bw_products(w, in, w.xa, w.xb, n, s));  // g, u, e (unscaled)
-    BW_TRY(mm(Mat{w.xa, 0, nd, d, 1}, Mat{dG1, 0, msz, 1, d}, nullptr, 0, 0, w.o1, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
-    BW_TRY(mm(Mat{w.xa, 0, nd, d, 1}, Mat{dG3, 0, msz, 1, d}, nullptr, 0, 0, w.o3, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
-    BW_TRY(mm(Mat{w.xb, 0, nd, d, 1}, Mat{dG2, 0, msz, dh, 1}, nullptr, 0, 0, w.o2, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
+    BW_TRY(mm(w, Mat{w.xa, 0, nd, d, 1}, Mat{dG1, 0, msz, 1, d}, nullptr, 0, 0, w.o1, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
+    BW_TRY(mm(w, Mat{w.xa, 0, nd, d, 1}, Mat{dG3, 0, msz, 1, d}, nullptr, 0, 0, w.o3, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
+    BW_TRY(mm(w, Mat{w.xb, 0, nd, d, 1}, Mat{dG2, 0, msz, dh, 1}, nullptr, 0, 0, w.o2, nh, dh, n, dh, d, bh, 1.f, 0.f, s));
     BW_TRY(bw_grad_bwd(w.ag, w.au, w.ae, w.o1, w.o3, w.o2, w.r1, w.r3, w.r2, e1, e3, e2, esbh, c.a0, n, dh, bh, s));
     BW_TRY(bw_rowsum(w.r1, gr->deta1, esbh, c.a0, n, dh, bh, s));
     BW_TRY(bw_rowsum(w.r3, gr->deta3, esbh, c.a0, n, dh, bh, s));
     BW_TRY(bw_rowsum(w.r2, gr->deta2, esbh, c.a0, n, dh, bh, s));
     // dV = (eta2 h) dG2^T + dE W2^T
     const float* Win2 = in + 2 * bh * msz;
-    BW_TRY(mm(Mat{w.o2, 0, nh, dh, 1}, Mat{dG2, 0, msz, 1, dh}, nullptr, 0, 0, w.xo, nd, d, n, d, dh, bh, 1.f, 0.f, s));
-    BW_TRY(mm(Mat{w.ae, 0, nh, dh, 1}, Mat{Win2, 0, msz, 1, dh}, w.xo, nd, d, w.xo, nd, d, n, d, dh, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.o2, 0, nh, dh, 1}, Mat{dG2, 0, msz, 1, dh}, nullptr, 0, 0, w.xo, nd, d, n, d, dh, bh, 1.f, 0.f, s));
+    BW_TRY(mm(w, Mat{w.ae, 0, nh, dh, 1}, Mat{Win2, 0, msz, 1, dh}, w.xo, nd, d, w.xo, nd, d, n, d, dh, bh, 1.f, 1.f, s));
     BW_TRY(bw_scatter_add(w.xo, (int64_t)T * d, d, c.a0, n, d, bh, gr->dv, s));
     // dK = (eta3 a) dG3 + (eta1 b) dG1 + dg W1 + du W3
-    BW_TRY(mm(Mat{w.o3, 0, nh, dh, 1}, Mat{dG3, 0, msz, d, 1}, nullptr, 0, 0, w.dx, nd, d, n, d, dh, bh, 1.f, 0.f, s));
-    BW_TRY(mm(Mat{w.o1, 0, nh, dh, 1}, Mat{dG1, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f, 1.f, s));
-    BW_TRY(mm(Mat{w.ag, 0, nh, dh, 1}, Mat{in, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f, 1.f, s));
-    BW_TRY(mm(Mat{w.au, 0, nh, dh, 1}, Mat{in + bh * msz, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f,
+    BW_TRY(mm(w, Mat{w.o3, 0, nh, dh, 1}, Mat{dG3, 0, msz, d, 1}, nullptr, 0, 0, w.dx, nd, d, n, d, dh, bh, 1.f, 0.f, s));
+    BW_TRY(mm(w, Mat{w.o1, 0, nh, dh, 1}, Mat{dG1, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.ag, 0, nh, dh, 1}, Mat{in, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.au, 0, nh, dh, 1}, Mat{in + bh * msz, 0, msz, d, 1}, w.dx, nd, d, w.dx, nd, d, n, d, dh, bh, 1.f,
               1.f, s));
     BW_TRY(bw_scatter_add(w.dx, (int64_t)T * d, d, c.a0, n, d, bh, gr->dk, s));
     // dW1 += dg^T k, dW3 += du^T k, dW2 += v^T dE (into dold)
     float* dW1 = w.dold;
     float* dW3 = w.dold + bh * msz;
     float* dW2 = w.dold + 2 * bh * msz;
-    BW_TRY(mm(Mat{w.ag, 0, nh, 1, dh}, Mat{w.xa, 0, nd, d, 1}, dW1, msz, d, dW1, msz, d, dh, d, n, bh, 1.f, 1.f, s));
-    BW_TRY(mm(Mat{w.au, 0, nh, 1, dh}, Mat{w.xa, 0, nd, d, 1}, dW3, msz, d, dW3, msz, d, dh, d, n, bh, 1.f, 1.f, s));
-    BW_TRY(mm(Mat{w.xb, 0, nd, 1, d}, Mat{w.ae, 0, nh, dh, 1}, dW2, msz, dh, dW2, msz, dh, d, dh, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.ag, 0, nh, 1, dh}, Mat{w.xa, 0, nd, d, 1}, dW1, msz, d, dW1, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.au, 0, nh, 1, dh}, Mat{w.xa, 0, nd, d, 1}, dW3, msz, d, dW3, msz, d, dh, d, n, bh, 1.f, 1.f, s));
+    BW_TRY(mm(w, Mat{w.xb, 0, nd, 1, d}, Mat{w.ae, 0, nh, dh, 1}, dW2, msz, dh, dW2, msz, dh, d, dh, n, bh, 1.f, 1.f, s));
     // the cotangent of the state before the write
     if (!mo) BW_TRY(bw_fill(w.dold + m3, 0.f, m3, s));
     return bw_axpby(w.dst, w.dold, nullptr, nullptr, 1.f, nullptr, 0.f, 2 * m3, 1, s);

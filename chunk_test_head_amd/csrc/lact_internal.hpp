@@ -218,7 +218,10 @@ struct BGemm {
   int M, N, K, batch;
   float alpha, beta;
 };
-hipError_t launch_bgemm(const BGemm& g, hipStream_t s);
+// partial: NULL, or a scratch of partial_floats floats for split-K
+// partial sums (used when the tiles alone would leave the GPU idle).
+hipError_t launch_bgemm(const BGemm& g, hipStream_t s, float* partial = nullptr,
+                        int64_t partial_floats = 0);
 hipError_t bw_read(float* g, float* u, float* dh, int64_t n, hipStream_t s);
 hipError_t bw_grad_fwd(const float* g, const float* u, const float* e, float* o1, float* o3, float* o2,
                        const float* e1, const float* e3, const float* e2, int64_t esbh, int64_t t0, int n,

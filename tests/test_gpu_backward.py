@@ -32,6 +32,9 @@ CASES = {
     "video-subset-bf16": (128, 256, "bf16", 4 * 64, 64, A2U, (32, 32), True, False, True),
     "bidirectional-subset": (64, 192, "f32", 160, 160, U2A, (0, 100), False, False, True),
     "d256-muon-momentum": (256, 512, "f32", 2 * 96 + 30, 96, A2U, None, True, True, True),
+    # 2048-token chunks: the token contractions split K (partial sums added
+    # in split order by a second launch)
+    "long-chunks-split-k": (64, 128, "f32", 2 * 2048 + 100, 2048, A2U, None, True, True, True),
 }
 TOL = 1e-4
 
