@@ -7,8 +7,9 @@ sequences of every ordering and option the backward supports.
 
 The GPU recomputes the forward and runs the chain rule in fp32; the bar is
 the fp32 bar of the forward, a relative Frobenius error of 1e-4 per
-gradient (fp32 products over a few hundred tokens, through up to five
-Newton-Schulz VJP steps; measured 3e-7 without Muon, up to 3e-5 with it)."""
+gradient (fp32 products over up to a few thousand tokens, through up to
+five Newton-Schulz VJP steps; measured 3e-7 without Muon, up to 4e-5 with
+it), and 1e-3 for the momentum coefficients (below)."""
 import math
 
 import zlib
@@ -37,6 +38,11 @@ CASES = {
     "long-chunks-split-k": (64, 128, "f32", 2 * 2048 + 100, 2048, A2U, None, True, True, True),
 }
 TOL = 1e-4
+# dL/dmom is one number per write (the momentum buffer projected on the
+# cotangent of the pre-Newton-Schulz sum, spread over the write's tokens):
+# when the two are nearly orthogonal its relative error is the cotangent's
+# divided by that cosine (measured up to 2.8e-4 on 2048-token chunks)
+TOL_MOM = 1e-3
 
 
 def _inputs(rng, bh, T, d, dh):
@@ -96,7 +102,7 @@ def test_backward_matches_oracle(device, case):
         errs = {key: H.rel(got[name][b], ref[key]) for key, name in keys.items()}
         print("  head", b, " ".join(f"{key} {x:.1e}" for key, x in errs.items()), flush=True)
         for key, x in errs.items():
-            assert x < TOL, (case, b, key, x)
+            assert x < (TOL_MOM if key == "mom" else TOL), (case, b, key, x)
 
 
 def test_backward_zero_tokens(device):
