@@ -208,6 +208,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
       LACT_APPLY_GLOAD(sb);
       LACT_APPLY_LSTORE(sb);
     }
+  wait_global_loads();  // the q fragments: complete before the loop
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
     if (late && st > 0) LACT_APPLY_OPROD(((st + NBUF - 1) % NBUF) * SUB + SUB - 1);  // deferred

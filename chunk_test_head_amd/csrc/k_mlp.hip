@@ -122,6 +122,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_grad(GradArgs a) {
       b3[jt][ks] = ld8(w3 + off);
       b2[jt][ks] = ld8(w2t + off);
     }
+  wait_global_loads();
 
   f32x4 G1[IT][JT], G3[IT][JT], G2[IT][JT];
 #pragma unroll
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       b2[h][ks] = ld8(sb + a.sh.off_w2t + row + 32 * ks);
     }
   }
+  wait_global_loads();
   f32x4 G1[HT][IT], G3[HT][IT], G2[HT][IT];
 #pragma unroll
   for (int h = 0; h < HT; ++h)

@@ -118,6 +118,15 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Waits until every global load the wave has issued has returned (vmcnt(0);
+// expcnt and lgkmcnt left open).  Called after the loads of register-resident
+// operands that a loop then reuses (weight fragments): the compiler's wait
+// analysis then counts them as complete inside the loop.  Without it, a loop
+// whose own loads are conditional (the tile loads of a ragged tail) cannot
+// bound how many loads follow them, and waits for every outstanding load,
+// the next tile's prefetch included, at their first use in every iteration.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Mean of x[0 .. n) by the whole workgroup in a fixed order (thread-strided
 // partial sums, wave butterflies, waves in index order), returned to every
 // thread; every thread must call it.
