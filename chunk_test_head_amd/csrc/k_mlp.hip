@@ -379,16 +379,35 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   const int er = tid % NT;
   uint4 rk[VPT], rv[VPT];
   float re = 0.f;
+  // A whole tile inside the split, when every thread moves a vector of it
+  // (d = 128): vector x of a thread is row tid / (D / 8) + x RX, piece
+  // tid % (D / 8), loaded from a uniform row base plus the thread's 32-bit
+  // byte offset (token strides below 2^24 elements keep it in range).  Else
+  // every row is checked and rows past the split read as zeros.
+  constexpr bool kWhole = NV % NTH == 0;
+  constexpr int RX = NTH / (D / 8);
+  const bool fast_ok = kWhole && a.k_st < (1 << 24) && a.v_st < (1 << 24);
+  const uint32_t kob = (uint32_t)(((tid / (D / 8)) * (uint32_t)a.k_st + (tid % (D / 8)) * 8) * 2u);
+  const uint32_t vob = (uint32_t)(((tid / (D / 8)) * (uint32_t)a.v_st + (tid % (D / 8)) * 8) * 2u);
 #define LACT_GRAD_GLOAD(T0)                                                         \
   {                                                                                 \
-    _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                               \
-      const int vi = tid + x * NTH;                                                 \
-      const int64_t t = (T0) + vi / (D / 8);                                        \
-      rk[x] = uint4{0u, 0u, 0u, 0u};                                                \
-      rv[x] = uint4{0u, 0u, 0u, 0u};                                                \
-      if (vi < NV && t < s1) {                                                      \
-        rk[x] = *reinterpret_cast<const uint4*>(kp + t * a.k_st + (vi % (D / 8)) * 8); \
-        rv[x] = *reinterpret_cast<const uint4*>(vp + t * a.v_st + (vi % (D / 8)) * 8); \
+    if (fast_ok && (T0) + NT <= s1) {                                               \
+      _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
+        const char* kb_ = reinterpret_cast<const char*>(kp + ((T0) + x * RX) * a.k_st); \
+        const char* vb_ = reinterpret_cast<const char*>(vp + ((T0) + x * RX) * a.v_st); \
+        rk[x] = *reinterpret_cast<const uint4*>(kb_ + kob);                         \
+        rv[x] = *reinterpret_cast<const uint4*>(vb_ + vob);                         \
+      }                                                                             \
+    } else {                                                                        \
+      _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
+        const int vi = tid + x * NTH;                                               \
+        const int64_t t = (T0) + vi / (D / 8);                                      \
+        rk[x] = uint4{0u, 0u, 0u, 0u};                                              \
+        rv[x] = uint4{0u, 0u, 0u, 0u};                                              \
+        if (vi < NV && t < s1) {                                                    \
+          rk[x] = *reinterpret_cast<const uint4*>(kp + t * a.k_st + (vi % (D / 8)) * 8); \
+          rv[x] = *reinterpret_cast<const uint4*>(vp + t * a.v_st + (vi % (D / 8)) * 8); \
+        }                                                                           \
       }                                                                             \
     }                                                                               \
     if (tid < 3 * NT) re = ((T0) + er < s1) ? ep[(T0) + er] : 0.f;                  \
@@ -407,11 +426,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
     if (tid < 3 * NT) sEta[BUF][tid / NT][er] = re;                                 \
   }
 
+  // per-lane element offsets in a tile, laundered so that each read below is
+  // this base plus an immediate: forward fragments (row c, features 8 g ..)
+  // and transpose reads (rows 4 g + c / 4, features 4 (c % 4) ..)
+  const int fo = opaque(tpad<D>(c, 8 * g));
+  const int to = opaque(tpad<D>(4 * g + (c >> 2), 4 * (c & 3)));
   // forward contractions of one tile: P = W1 k, U = W3 k, E = W2^T v
 #define LACT_GRAD_FWD(BUF)                                                          \
   {                                                                                 \
-    const bf16* sK_ = sKV[BUF];                                                     \
-    const bf16* sV_ = sK_ + TILE;                                                   \
+    const bf16* pk_ = sKV[BUF] + fo;                                                \
     _Pragma("unroll") for (int h = 0; h < HT; ++h)                                  \
       _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                            \
         P[h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
@@ -420,8 +443,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
       }                                                                             \
     _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
       _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                            \
-        const bf16x8 ak = ld8(sK_ + tpad<D>(16 * tt + c, 32 * ks + 8 * g));           \
-        const bf16x8 av = ld8(sV_ + tpad<D>(16 * tt + c, 32 * ks + 8 * g));           \
+        const bf16x8 ak = ld8(pk_ + 16 * tt * (D + 16) + 32 * ks);                  \
+        const bf16x8 av = ld8(pk_ + TILE + 16 * tt * (D + 16) + 32 * ks);           \
         _Pragma("unroll") for (int h = 0; h < HT; ++h) {                            \
           mma(P[h][tt], ak, b1[h][ks]);                                             \
           mma(U[h][tt], ak, b3[h][ks]);                                             \
@@ -467,14 +490,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
   // fragment with tokens in kappa order.
 #define LACT_GRAD_GG(BUF)                                                           \
   {                                                                                 \
-    const bf16* sK_ = sKV[BUF];                                                     \
-    const bf16* sV_ = sK_ + TILE;                                                   \
-    const int cq_ = opaque(c), gq_ = opaque(g);                                     \
-    const int tr = 4 * gq_ + (cq_ >> 2);                                            \
+    const bf16* qk_ = sKV[BUF] + to;                                                \
     _Pragma("unroll") for (int it = 0; it < IT; ++it) {                             \
-      const int fc = 16 * it + 4 * (cq_ & 3);                                       \
-      const bf16x8 akt = cat8(ld_tr4(sK_ + tpad<D>(tr, fc)), ld_tr4(sK_ + tpad<D>(tr + 16, fc))); \
-      const bf16x8 avt = cat8(ld_tr4(sV_ + tpad<D>(tr, fc)), ld_tr4(sV_ + tpad<D>(tr + 16, fc))); \
+      const bf16x8 akt = cat8(ld_tr4(qk_ + 16 * it), ld_tr4(qk_ + 16 * (D + 16) + 16 * it)); \
+      const bf16x8 avt = cat8(ld_tr4(qk_ + TILE + 16 * it),                         \
+                              ld_tr4(qk_ + TILE + 16 * (D + 16) + 16 * it));        \
       _Pragma("unroll") for (int h = 0; h < HT; ++h) {                              \
         mma(G1[h][it], akt, fg[h]);                                                 \
         mma(G3[h][it], akt, fu[h]);                                                 \
@@ -638,11 +658,12 @@ void k_grad_solo(GradArgs a) {
   // tile checks every row and reads rows past the end as zeros.
   constexpr int RX = NTH / (D / 8);
   static_assert(NTH % (D / 8) == 0, "rows per vector step");
-  const uint32_t kob = (uint32_t)((tid / (D / 8)) * a.k_st + (tid % (D / 8)) * 8) * 2u;
-  const uint32_t vob = (uint32_t)((tid / (D / 8)) * a.v_st + (tid % (D / 8)) * 8) * 2u;
+  const bool fast_ok = a.k_st < (1 << 24) && a.v_st < (1 << 24);  // offsets fit 32 bits
+  const uint32_t kob = (uint32_t)(((tid / (D / 8)) * (uint32_t)a.k_st + (tid % (D / 8)) * 8) * 2u);
+  const uint32_t vob = (uint32_t)(((tid / (D / 8)) * (uint32_t)a.v_st + (tid % (D / 8)) * 8) * 2u);
 #define LACT_GS_GLOAD(T0)                                                           \
   {                                                                                 \
-    if ((T0) + NT <= s1) {                                                          \
+    if (fast_ok && (T0) + NT <= s1) {                                               \
       _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
         const char* kb_ = reinterpret_cast<const char*>(kp + ((T0) + x * RX) * a.k_st); \
         const char* vb_ = reinterpret_cast<const char*>(vp + ((T0) + x * RX) * a.v_st); \
