@@ -139,6 +139,147 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm g, int kchunk, float* P) {
       }
 }
 
+// One 128 x 128 tile of C over [kb, ke) of matrix b, for the large
+// products: four waves of 64 x 64 (4 x 4 MFMA tiles each), K slabs of KS
+// through two LDS buffers.  A slab's rows are stored permuted, row 16 x + c
+// of each 64-row half at position 4 c + x, so that the values a lane needs
+// for its four row tiles are one 16-byte read.  Each thread moves runs of 4
+// elements along the operand's unit stride: as one 16-byte load for a slab
+// inside the matrix when the operand is 16-byte aligned (vec_*), else
+// element by element with bounds checks.  Logical workgroup ids are dealt
+// by XCD: neighbouring tiles of one matrix share an L2.
+template <bool ABF, bool BBF, int KS>
+__global__ __launch_bounds__(256) void k_bgemm128(BGemm g, int kchunk, float* P, int vec_a, int vec_b,
+                                                 int ntile) {
+  constexpr int T = 128, PD = T + 4;
+  constexpr int NQ = T * KS / 1024;  // runs of 4 per thread per operand per slab
+  __shared__ __attribute__((aligned(16))) float sA[2][KS][PD];  // [k][permuted m]
+  __shared__ __attribute__((aligned(16))) float sB[2][KS][PD];  // [k][permuted n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tile = lid % ntile, rest = lid / ntile;
+  const int64_t b = rest % g.batch;
+  const int z = rest / g.batch;
+  const int tn = (g.N + T - 1) / T;
+  const int m0 = (tile / tn) * T, n0 = (tile % tn) * T;
+  const int kb = z * kchunk, ke = min(g.K, kb + kchunk);
+  const void* A = reinterpret_cast<const char*>(g.A) + b * g.a_bs * (ABF ? 2 : 4);
+  const void* B = reinterpret_cast<const char*>(g.B) + b * g.b_bs * (BBF ? 2 : 4);
+  const bool a_kfast = g.a_sk == 1, b_nfast = g.b_sn == 1;
+  const bool a_full = vec_a && m0 + T <= g.M, b_full = vec_b && n0 + T <= g.N;
+  // this thread's runs: (row, k) of the first element and the run direction
+  // (along k for a k-contiguous operand, along rows otherwise)
+  int ar[NQ], ak[NQ], br[NQ], bk[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int x = tid + 256 * i;
+    ar[i] = a_kfast ? x / (KS / 4) : 4 * (x % (T / 4));
+    ak[i] = a_kfast ? 4 * (x % (KS / 4)) : x / (T / 4);
+    br[i] = b_nfast ? 4 * (x % (T / 4)) : x / (KS / 4);
+    bk[i] = b_nfast ? x / (T / 4) : 4 * (x % (KS / 4));
+  }
+  f32x4 ra[NQ], rb[NQ];
+  auto load = [&](int k0) {
+    const bool in_k = k0 + KS <= ke;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int m = m0 + ar[i], k = k0 + ak[i];
+      if (!ABF && a_full && in_k) {
+        ra[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(A) + (int64_t)m * g.a_sm +
+                                                 (int64_t)k * g.a_sk);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int mj = a_kfast ? m : m + j, kj = a_kfast ? k + j : k;
+          ra[i][j] = (mj < g.M && kj < ke) ? ldt<ABF>(A, (int64_t)mj * g.a_sm + (int64_t)kj * g.a_sk) : 0.f;
+        }
+      }
+      const int n = n0 + br[i], kk = k0 + bk[i];
+      if (!BBF && b_full && in_k) {
+        rb[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(B) + (int64_t)kk * g.b_sk +
+                                                 (int64_t)n * g.b_sn);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int nj = b_nfast ? n + j : n, kj = b_nfast ? kk : kk + j;
+          rb[i][j] = (nj < g.N && kj < ke) ? ldt<BBF>(B, (int64_t)kj * g.b_sk + (int64_t)nj * g.b_sn) : 0.f;
+        }
+      }
+    }
+  };
+  auto pos = [](int r) { return (r & 64) + 4 * (r & 15) + ((r >> 4) & 3); };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (a_kfast) sA[buf][ak[i] + j][pos(ar[i])] = ra[i][j];
+        else sA[buf][ak[i]][pos(ar[i]) + 4 * j] = ra[i][j];  // rows ar .. ar + 3: one 16-row group
+        if (b_nfast) sB[buf][bk[i]][pos(br[i]) + 4 * j] = rb[i][j];
+        else sB[buf][bk[i] + j][pos(br[i])] = rb[i][j];
+      }
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nslab = ke > kb ? (ke - kb + KS - 1) / KS : 0;
+  if (nslab > 0) {
+    load(kb);
+    store(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < nslab; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nslab) load(kb + (j + 1) * KS);
+#pragma unroll
+    for (int st = 0; st < KS / 4; ++st) {
+      const f32x4 fa = *reinterpret_cast<const f32x4*>(&sA[buf][4 * st + q][64 * wm + 4 * c]);
+      const f32x4 fb = *reinterpret_cast<const f32x4*>(&sB[buf][4 * st + q][64 * wn + 4 * c]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    // buffer buf ^ 1 was last read in slab j - 1, before the previous barrier
+    if (j + 1 < nslab) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (P != nullptr) {
+    float* out = P + ((int64_t)z * g.batch + b) * g.M * g.N;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 64 * wm + 16 * x + 4 * q + i, n = n0 + 64 * wn + 16 * y + c;
+          if (m < g.M && n < g.N) out[(int64_t)m * g.N + n] = acc[x][y][i];
+        }
+    return;
+  }
+  const float* D = g.D ? g.D + b * g.d_bs : nullptr;
+  float* C = g.C + b * g.c_bs;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 64 * wm + 16 * x + 4 * q + i, n = n0 + 64 * wn + 16 * y + c;
+        if (m < g.M && n < g.N) {
+          float v = g.alpha * acc[x][y][i];
+          if (D) v += g.beta * D[(int64_t)m * g.d_sm + n];
+          C[(int64_t)m * g.c_sm + n] = v;
+        }
+      }
+}
+
 // Split-K epilogue: C = alpha * (sum over the splits in order of P) + beta D.
 __global__ void k_bgemm_sum(BGemm g, const float* P, int nsplit) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -163,21 +304,53 @@ static int bgemm_splits(const BGemm& g, int max_split) {
   return ns;
 }
 
+// 16-byte loads of an operand need its base, batch stride and the stride
+// of its non-contiguous dimension to be multiples of 4 floats.
+static bool vec_ok(const void* p, int bf, int64_t bs, int64_t s_row, int64_t s_k, bool kfast) {
+  return !bf && ((uintptr_t)p & 15u) == 0 && bs % 4 == 0 && (kfast ? s_row : s_k) % 4 == 0;
+}
+
+// The 128 x 128 kernel for products with at least 128 rows and columns and
+// enough tiles (after splitting K) to give every CU two workgroups (fewer
+// leave CUs idle: the 64 x 64 kernel is then faster);
+// its split count: the smallest power of two reaching 512 workgroups with
+// slabs of at least 256, at most max_split.
+static int bgemm128_splits(const BGemm& g, int max_split) {
+  if (g.M < 128 || g.N < 128 || (g.a_sk != 1 && g.a_sm != 1) || (g.b_sn != 1 && g.b_sk != 1)) return 0;
+  const int64_t tiles = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch;
+  int ns = 1;
+  while (ns < max_split && tiles * ns < 512 && g.K / (2 * ns) >= 256) ns *= 2;
+  return tiles * ns >= 512 ? ns : 0;
+}
+
 hipError_t launch_bgemm(const BGemm& g, hipStream_t s, float* partial, int64_t partial_floats) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   const int64_t mnb = (int64_t)g.M * g.N * g.batch;
-  int ns = 1;
+  int cap = 1;
   if (partial != nullptr && mnb > 0) {
-    const int64_t cap = partial_floats / mnb;
-    ns = bgemm_splits(g, (int)(cap < 64 ? cap : 64));
+    const int64_t c = partial_floats / mnb;
+    cap = (int)(c < 64 ? (c > 1 ? c : 1) : 64);
   }
+  const int ns128 = bgemm128_splits(g, cap);
+  int ns = ns128 > 0 ? ns128 : (cap > 1 ? bgemm_splits(g, cap) : 1);
   const int kchunk = ns > 1 ? ((g.K + ns - 1) / ns + 31) / 32 * 32 : (g.K > 0 ? g.K : 1);
-  const dim3 grid((unsigned)(((g.M + 63) / 64) * ((g.N + 63) / 64)), (unsigned)g.batch, (unsigned)ns);
   float* P = ns > 1 ? partial : nullptr;
-  if (g.a_bf16 && g.b_bf16) hipLaunchKernelGGL((k_bgemm<true, true>), grid, dim3(256), 0, s, g, kchunk, P);
-  else if (g.a_bf16) hipLaunchKernelGGL((k_bgemm<true, false>), grid, dim3(256), 0, s, g, kchunk, P);
-  else if (g.b_bf16) hipLaunchKernelGGL((k_bgemm<false, true>), grid, dim3(256), 0, s, g, kchunk, P);
-  else hipLaunchKernelGGL((k_bgemm<false, false>), grid, dim3(256), 0, s, g, kchunk, P);
+  if (ns128 > 0) {
+    const int ntile = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+    const int va = vec_ok(g.A, g.a_bf16, g.a_bs, g.a_sm, g.a_sk, g.a_sk == 1);
+    const int vb = vec_ok(g.B, g.b_bf16, g.b_bs, g.b_sn, g.b_sk, g.b_sk == 1);
+    const dim3 grid((unsigned)((int64_t)ntile * g.batch * ns));
+    if (g.a_bf16 && g.b_bf16) hipLaunchKernelGGL((k_bgemm128<true, true, 16>), grid, dim3(256), 0, s, g, kchunk, P, va, vb, ntile);
+    else if (g.a_bf16) hipLaunchKernelGGL((k_bgemm128<true, false, 16>), grid, dim3(256), 0, s, g, kchunk, P, va, vb, ntile);
+    else if (g.b_bf16) hipLaunchKernelGGL((k_bgemm128<false, true, 16>), grid, dim3(256), 0, s, g, kchunk, P, va, vb, ntile);
+    else hipLaunchKernelGGL((k_bgemm128<false, false, 16>), grid, dim3(256), 0, s, g, kchunk, P, va, vb, ntile);
+  } else {
+    const dim3 grid((unsigned)(((g.M + 63) / 64) * ((g.N + 63) / 64)), (unsigned)g.batch, (unsigned)ns);
+    if (g.a_bf16 && g.b_bf16) hipLaunchKernelGGL((k_bgemm<true, true>), grid, dim3(256), 0, s, g, kchunk, P);
+    else if (g.a_bf16) hipLaunchKernelGGL((k_bgemm<true, false>), grid, dim3(256), 0, s, g, kchunk, P);
+    else if (g.b_bf16) hipLaunchKernelGGL((k_bgemm<false, true>), grid, dim3(256), 0, s, g, kchunk, P);
+    else hipLaunchKernelGGL((k_bgemm<false, false>), grid, dim3(256), 0, s, g, kchunk, P);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   hipLaunchKernelGGL(k_bgemm_sum, dim3((unsigned)((mnb + 255) / 256)), dim3(256), 0, s, g, P, ns);
@@ -257,15 +430,19 @@ __global__ void k_bw_grad_bwd(float* g, float* u, float* e, float* p1, float* p3
 }
 
 // out[b * osbh + t0 + t] += sum_j x[(b n + t) dh + j], one wave per row, a
-// fixed order (lane-strided partial sums, then a butterfly).
+// fixed order (lane-strided 16-byte partial sums, then a butterfly; dh is a
+// multiple of 64 and the rows are 16-byte aligned).
 __global__ void k_bw_rowsum(const float* x, float* out, int64_t osbh, int64_t t0, int n, int dh,
                             int bh) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= (int64_t)bh * n) return;
-  const float* p = x + row * dh;
+  const f32x4* p = reinterpret_cast<const f32x4*>(x + row * dh);
   float s = 0.f;
-  for (int j = lane; j < dh; j += 64) s += p[j];
+  for (int j = lane; j < dh / 4; j += 64) {
+    const f32x4 v = p[j];
+    s += (v[0] + v[1]) + (v[2] + v[3]);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) {
@@ -276,18 +453,37 @@ __global__ void k_bw_rowsum(const float* x, float* out, int64_t osbh, int64_t t0
 
 // ---------------------------------------------------- per-matrix sums ----
 // out[m] = sum over the matrix m (size elements) of x[i] * y[i] (y NULL:
-// x[i]^2), one workgroup per matrix, fixed order.
-__global__ void k_bw_dot(const float* x, const float* y, float* out, int64_t size) {
-  __shared__ float red[4];
+// x[i]^2), one workgroup of 1024 threads per matrix, fixed order: each
+// thread sums its 16-byte vectors (VEC: size % 4 == 0, aligned operands) or
+// elements, strided by the workgroup, then the 16 waves in index order.
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_bw_dot(const float* x, const float* y, float* out, int64_t size) {
+  __shared__ float red[16];
   const float* px = x + (int64_t)blockIdx.x * size;
-  const float* py = y ? y + (int64_t)blockIdx.x * size : nullptr;
+  const float* py = y ? y + (int64_t)blockIdx.x * size : px;
   float s = 0.f;
-  for (int64_t i = threadIdx.x; i < size; i += 256) s += px[i] * (py ? py[i] : px[i]);
+  if constexpr (VEC) {
+    const f32x4* vx = reinterpret_cast<const f32x4*>(px);
+    const f32x4* vy = reinterpret_cast<const f32x4*>(py);
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < size / 4; i += 1024) {
+      const f32x4 a = vx[i], b = vy[i];
+      s += (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]);
+    }
+  } else {
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < size; i += 1024) s += px[i] * py[i];
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) out[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += red[w];
+    out[blockIdx.x] = t;
+  }
 }
 
 // y[m] = alpha[m] x[m] + beta[m] z[m] over matrices of `size` elements, with
@@ -438,6 +634,26 @@ __global__ void k_bw_dmom(const float* dbeta, float* dmom, int64_t sbh, int64_t 
 
 // Activations to fp32 (rows of d of a [bh][T][*] array with the layout's
 // strides): out[(b n + t) d + i] = x[b sbh + (t0 + t) st + i].
+// Four consecutive features per thread (d % 4 == 0; the token rows 8-byte
+// (bf16) or 16-byte (fp32) aligned): one load, one 16-byte store.
+template <bool BF>
+__global__ void k_bw_gather4(const void* x, int64_t sbh, int64_t st, int64_t t0, int n, int d4, int bh,
+                             float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)bh * n * d4) return;
+  const int64_t row = i / d4;
+  const int c = 4 * (int)(i - row * d4);
+  const int t = (int)(row % n), b = (int)(row / n);
+  const int64_t src = (int64_t)b * sbh + (t0 + t) * st + c;
+  f32x4 v;
+  if constexpr (BF) {
+    const bf16x4 h = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(x) + src);
+    v = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else {
+    v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + src);
+  }
+  *reinterpret_cast<f32x4*>(out + 4 * i) = v;
+}
 __global__ void k_bw_gather(const void* x, int bf, int64_t sbh, int64_t st, int64_t t0, int n, int d,
                             int bh, float* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -448,6 +664,19 @@ __global__ void k_bw_gather(const void* x, int bf, int64_t sbh, int64_t st, int6
 }
 
 // out[b sbh + (t0 + t) st + i] += x[(b n + t) d + i]
+__global__ void k_bw_scatter_add4(const float* x, int64_t sbh, int64_t st, int64_t t0, int n, int d4,
+                                  int bh, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)bh * n * d4) return;
+  const int64_t row = i / d4;
+  const int c = 4 * (int)(i - row * d4);
+  const int t = (int)(row % n), b = (int)(row / n);
+  f32x4* o = reinterpret_cast<f32x4*>(out + (int64_t)b * sbh + (t0 + t) * st + c);
+  const f32x4 a = *reinterpret_cast<const f32x4*>(x + 4 * i);
+  f32x4 v = *o;
+  v[0] += a[0]; v[1] += a[1]; v[2] += a[2]; v[3] += a[3];
+  *o = v;
+}
 __global__ void k_bw_scatter_add(const float* x, int64_t sbh, int64_t st, int64_t t0, int n, int d,
                                  int bh, float* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -521,9 +750,13 @@ hipError_t bw_rowsum(const float* x, float* out, int64_t osbh, int64_t t0, int n
   hipLaunchKernelGGL(k_bw_rowsum, grows(rows), dim3(256), 0, s, x, out, osbh, t0, n, dh, bh);
   return hipGetLastError();
 }
+static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 hipError_t bw_dot(const float* x, const float* y, float* out, int64_t size, int count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bw_dot, dim3((unsigned)count), dim3(256), 0, s, x, y, out, size);
+  if (size % 4 == 0 && al16(x) && (y == nullptr || al16(y)))
+    hipLaunchKernelGGL(k_bw_dot<true>, dim3((unsigned)count), dim3(1024), 0, s, x, y, out, size);
+  else
+    hipLaunchKernelGGL(k_bw_dot<false>, dim3((unsigned)count), dim3(1024), 0, s, x, y, out, size);
   return hipGetLastError();
 }
 hipError_t bw_axpby(float* y, const float* x, const float* z, const float* am, float a, const float* bm,
@@ -584,14 +817,26 @@ hipError_t bw_gather(const void* x, int bf, int64_t sbh, int64_t st, int64_t t0,
                      float* out, hipStream_t s) {
   const int64_t tot = (int64_t)bh * n * d;
   if (tot <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bw_gather, g1(tot), dim3(256), 0, s, x, bf, sbh, st, t0, n, d, bh, out);
+  // runs of 4 features as one load each when every run is aligned
+  if (d % 4 == 0 && sbh % 4 == 0 && st % 4 == 0 && ((uintptr_t)x & (bf ? 7u : 15u)) == 0 && al16(out)) {
+    const int64_t nv = tot / 4;
+    if (bf)
+      hipLaunchKernelGGL(k_bw_gather4<true>, g1(nv), dim3(256), 0, s, x, sbh, st, t0, n, d / 4, bh, out);
+    else
+      hipLaunchKernelGGL(k_bw_gather4<false>, g1(nv), dim3(256), 0, s, x, sbh, st, t0, n, d / 4, bh, out);
+  } else {
+    hipLaunchKernelGGL(k_bw_gather, g1(tot), dim3(256), 0, s, x, bf, sbh, st, t0, n, d, bh, out);
+  }
   return hipGetLastError();
 }
 hipError_t bw_scatter_add(const float* x, int64_t sbh, int64_t st, int64_t t0, int n, int d, int bh,
                           float* out, hipStream_t s) {
   const int64_t tot = (int64_t)bh * n * d;
   if (tot <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bw_scatter_add, g1(tot), dim3(256), 0, s, x, sbh, st, t0, n, d, bh, out);
+  if (d % 4 == 0 && sbh % 4 == 0 && st % 4 == 0 && al16(out) && al16(x))
+    hipLaunchKernelGGL(k_bw_scatter_add4, g1(tot / 4), dim3(256), 0, s, x, sbh, st, t0, n, d / 4, bh, out);
+  else
+    hipLaunchKernelGGL(k_bw_scatter_add, g1(tot), dim3(256), 0, s, x, sbh, st, t0, n, d, bh, out);
   return hipGetLastError();
 }
 
