@@ -309,6 +309,8 @@ __global__ __launch_bounds__(256) void k_nsn_part(NsIn g, float* part, int64_t n
   const int64_t per = n / NSN_B;
   const float* p = g.at(blockIdx.y, n) + (int64_t)blockIdx.x * per;
   float s = 0.f;
+  // unrolled so that the loads are in flight together (the sum keeps its order)
+#pragma unroll 8
   for (int64_t e = 4 * tid; e < per; e += 1024) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(p + e);
     s += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
@@ -329,6 +331,7 @@ __global__ __launch_bounds__(256) void k_nsn_scale(NsIn g, const float* part, fl
   const int64_t per = n / NSN_B;
   const int64_t base = (int64_t)blockIdx.y * n + (int64_t)blockIdx.x * per;
   const float* gp = g.at(blockIdx.y, n) + (int64_t)blockIdx.x * per;
+#pragma unroll 8
   for (int64_t e = 4 * tid; e < per; e += 1024) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(gp + e) * scale;
     *reinterpret_cast<f32x4*>(x + base + e) = v;

@@ -159,14 +159,26 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
     if (k < nk) w[k] = *reinterpret_cast<const f32x4*>(W + (int64_t)(r0 + rstep * k) * d + c4);
   if (U != nullptr) {
     U += (int64_t)head * msz + j0;
-    // U[i][j0 + 4q .. +3] -> ut[4q .. 4q+3][i]
-    for (int e = tid; e < d * (RB / 4); e += 256) {
-      const int i = e / (RB / 4), q = e % (RB / 4);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(U + (int64_t)i * dh + 4 * q);
-      ut[(4 * q + 0) * pt + i] = v[0];
-      ut[(4 * q + 1) * pt + i] = v[1];
-      ut[(4 * q + 2) * pt + i] = v[2];
-      ut[(4 * q + 3) * pt + i] = v[3];
+    // U[i][j0 + 4q .. +3] -> ut[4q .. 4q+3][i]: every load of the thread is
+    // issued before the first store (one memory latency, not one per vector)
+    constexpr int UMAX = 256 * (RB / 4) / 256;  // vectors per thread, d <= 256
+    f32x4 uv[UMAX];
+#pragma unroll
+    for (int k = 0; k < UMAX; ++k) {
+      const int e = tid + 256 * k;
+      if (e < d * (RB / 4))
+        uv[k] = *reinterpret_cast<const f32x4*>(U + (int64_t)(e / (RB / 4)) * dh + 4 * (e % (RB / 4)));
+    }
+#pragma unroll
+    for (int k = 0; k < UMAX; ++k) {
+      const int e = tid + 256 * k;
+      if (e < d * (RB / 4)) {
+        const int i = e / (RB / 4), q = e % (RB / 4);
+        ut[(4 * q + 0) * pt + i] = uv[k][0];
+        ut[(4 * q + 1) * pt + i] = uv[k][1];
+        ut[(4 * q + 2) * pt + i] = uv[k][2];
+        ut[(4 * q + 3) * pt + i] = uv[k][3];
+      }
     }
     __syncthreads();
   }
@@ -212,23 +224,35 @@ __device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
   const int i0 = 8 * ib;
   const bool write_w = a.u2 != nullptr || a.renorm;
   T* sb = reinterpret_cast<T*>(a.sh.base) + (int64_t)head * a.sh.per_head;
-  // float4 columns 4 lane + 256 k, k <= KMAX (dh <= 256 (KMAX + 1))
+  // float4 columns 4 lane + 256 k, k <= KMAX (dh <= 256 (KMAX + 1)); the
+  // wave's two rows (wave, wave + 4) are loaded before anything is stored
   const int nk = dh / 256, rem = dh % 256;
+  f32x4 w[2][KMAX + 1];
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const int row = wave + 4 * rr;  // 0..7
-    float* W = a.w2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh;
+    const float* W = a.w2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh;
     const float* U = a.u2 != nullptr ? a.u2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh : nullptr;
-    f32x4 w[KMAX + 1];
-    float ss = 0.f;
 #pragma unroll
     for (int k = 0; k <= KMAX; ++k) {
       const int col = 4 * lane + 256 * k;
       if (k < nk || (k == nk && 4 * lane < rem)) {
-        w[k] = *reinterpret_cast<const f32x4*>(W + col);
-        if (U != nullptr) w[k] += *reinterpret_cast<const f32x4*>(U + col);
-        ss += w[k][0] * w[k][0] + w[k][1] * w[k][1] + w[k][2] * w[k][2] + w[k][3] * w[k][3];
+        w[rr][k] = *reinterpret_cast<const f32x4*>(W + col);
+        if (U != nullptr) w[rr][k] += *reinterpret_cast<const f32x4*>(U + col);
       }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = wave + 4 * rr;  // 0..7
+    float* W = a.w2 + (int64_t)head * msz + (int64_t)(i0 + row) * dh;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k <= KMAX; ++k) {
+      const int col = 4 * lane + 256 * k;
+      if (k < nk || (k == nk && 4 * lane < rem))
+        ss += w[rr][k][0] * w[rr][k][0] + w[rr][k][1] * w[rr][k][1] + w[rr][k][2] * w[rr][k][2] +
+              w[rr][k][3] * w[rr][k][3];
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
@@ -241,8 +265,8 @@ __device__ __forceinline__ void step_w2(const StepArgs& a, int blk, T* tl) {
     for (int k = 0; k <= KMAX; ++k) {
       const int col = 4 * lane + 256 * k;
       if (k < nk || (k == nk && 4 * lane < rem)) {
-        const f32x4 v = w[k] * f;
-        if (write_w) *reinterpret_cast<f32x4*>(W + col) = a.renorm == 2 ? w[k] : v;
+        const f32x4 v = w[rr][k] * f;
+        if (write_w) *reinterpret_cast<f32x4*>(W + col) = a.renorm == 2 ? w[rr][k] : v;
         st4(S + col, v[0], v[1], v[2], v[3]);
         st4(tl + row * dh + col, v[0], v[1], v[2], v[3]);
       }
