@@ -141,11 +141,21 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int tn = a.N / NSG_T;
   // one launch-wide id per (matrix, tile), dealt so that the tiles of a
-  // matrix run on one or two XCDs and share their L2's copy of the operands
-  const int ntile = (a.M / NSG_T) * tn;
+  // matrix run on one or two XCDs and share their L2's copy of the operands;
+  // a symmetric product has tn (tn + 1) / 2 tiles (tm <= tn) per matrix
+  const int ntile = a.sym ? tn * (tn + 1) / 2 : (a.M / NSG_T) * tn;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tile = lid % ntile;
-  const int m0 = (tile / tn) * NSG_T, n0 = (tile % tn) * NSG_T;
+  int tmi = tile / tn, tni = tile % tn;
+  if (a.sym) {
+    // row tm holds tiles tm .. tn - 1: walk the rows
+    int t = tile;
+    tmi = 0;
+    while (t >= tn - tmi) t -= tn - tmi++;
+    tni = tmi + t;
+  }
+  const int m0 = tmi * NSG_T, n0 = tni * NSG_T;
+  const bool mirror = a.sym && tmi != tni;
   const int64_t bidx = lid / ntile;
   const bf16* A = a.A + bidx * a.a_bs;
   const bf16* B = a.B + bidx * a.b_bs;
@@ -182,12 +192,13 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
   }
   // the epilogue's own loads go out first: the D tile and the shift's partials
   const float* D = a.D ? a.D + bidx * a.d_bs : nullptr;
-  f32x4 dv[4];
+  f32x4 dv[4], dt[4];
   if (D) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
       dv[x] = *reinterpret_cast<const f32x4*>(D + (int64_t)(m0 + r) * a.N + n0 + c4);
+      if (mirror) dt[x] = *reinterpret_cast<const f32x4*>(D + (int64_t)(n0 + r) * a.N + m0 + c4);
     }
   }
   float mu_t = 0.f;
@@ -277,6 +288,21 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
     if (C) *reinterpret_cast<f32x4*>(C + o) = v;
     if (Ch) st4(Ch + o, v[0], v[1], v[2], v[3]);
   }
+  if (mirror) {
+    // the transposed tile at (tn, tm): row r of it is column r of the result
+    // tile (off the diagonal: no diagonal term)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
+      const int64_t o = (int64_t)(n0 + r) * a.N + m0 + c4;
+      f32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = sc[(c4 + j) * NSG_PC + r] * a.alpha;
+      if (D) v += dt[x] * be;
+      if (C) *reinterpret_cast<f32x4*>(C + o) = v;
+      if (Ch) st4(Ch + o, v[0], v[1], v[2], v[3]);
+    }
+  }
   if (a.ss_part != nullptr) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
@@ -289,7 +315,9 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
 }
 
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s) {
-  const dim3 grid((unsigned)((a.M / NSG_T) * (a.N / NSG_T) * batch));
+  const int tm = a.M / NSG_T, tn = a.N / NSG_T;
+  if (a.sym && (a.M != a.N || a.ss_part != nullptr)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.sym ? tn * (tn + 1) / 2 : tm * tn) * batch));
   if (b_kn)
     hipLaunchKernelGGL(k_nsgemm<true>, grid, dim3(256), 0, s, a);
   else

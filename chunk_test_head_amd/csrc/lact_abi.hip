@@ -292,18 +292,18 @@ static hipError_t run_ns(int prec, int count, int rows, int cols, NsIn g, float*
       const float* mp = shf ? ssp + (int64_t)(it & 1) * count * tiles : nullptr;
       // A = X X^T (fp32 for the b A term, bf16 operand)
       NsGemmArgs ga{xc, m, cols, xc, m, cols, nullptr, 0, bm, ah, rr, rows, rows, cols, 1.f, 0.f,
-                    mp, tiles, (float)rows, 0.f, 0.f, -1.f, nullptr};
+                    mp, tiles, (float)rows, 0.f, 0.f, -1.f, nullptr, 1};
       if ((e = launch_nsgemm(false, ga, count, s)) != hipSuccess) return e;
       // B = c A A + b A (A symmetric: its rows are the B operand)
       NsGemmArgs gb{ah, rr, rows, ah, rr, rows, bm, rr, nullptr, bh, rr, rows, rows, rows, cc, cb,
-                    mp, tiles, (float)rows, 2.f * cc, 0.f, 0.f, nullptr};
+                    mp, tiles, (float)rows, 2.f * cc, 0.f, 0.f, nullptr, 1};
       if ((e = launch_nsgemm(false, gb, count, s)) != hipSuccess) return e;
       // X' = B X + a X (and its tile sums of squares for a shifted next step)
       const bool last = it == 4;
       NsGemmArgs gx{bh, rr, rows, xc, m, cols, x, m, last ? u : y, last ? nullptr : yc, m,
                     rows, cols, rows, 1.f, ca, mp, tiles, (float)rows, cb, cc, 0.f,
                     (!last && it + 1 >= shift_from) ? ssp + (int64_t)((it + 1) & 1) * count * tiles
-                                                    : nullptr};
+                                                    : nullptr, 0};
       if ((e = launch_nsgemm(true, gx, count, s)) != hipSuccess) return e;
       std::swap(x, y);
       std::swap(xc, yc);

@@ -112,6 +112,11 @@ struct NsGemmArgs {
   // NULL, or [batch][tiles]: sum of squares of each 64 x 64 tile of the fp32
   // result, in tile order (the next step's mu)
   float* ss_part;
+  // 1: the product is symmetric (M == N; A B^T with B = A, or a product of
+  // commuting symmetric factors): only the tiles on and above the diagonal
+  // are computed, each written also transposed below it (D, if any, must be
+  // symmetric too; ss_part must be NULL)
+  int sym;
 };
 
 // Input matrices of a Newton-Schulz batch: matrix m is p[m / per] +
