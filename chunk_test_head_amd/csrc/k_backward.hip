@@ -335,10 +335,11 @@ hipError_t launch_bgemm(const BGemm& g, hipStream_t s, float* partial, int64_t p
   int ns = ns128 > 0 ? ns128 : (cap > 1 ? bgemm_splits(g, cap) : 1);
   const int kchunk = ns > 1 ? ((g.K + ns - 1) / ns + 31) / 32 * 32 : (g.K > 0 ? g.K : 1);
   float* P = ns > 1 ? partial : nullptr;
+  // 16-byte runs only along a unit stride
+  const int va = vec_ok(g.A, g.a_bf16, g.a_bs, g.a_sm, g.a_sk, g.a_sk == 1) && (g.a_sk == 1 || g.a_sm == 1);
+  const int vb = vec_ok(g.B, g.b_bf16, g.b_bs, g.b_sn, g.b_sk, g.b_sk == 1) && (g.b_sk == 1 || g.b_sn == 1);
   if (ns128 > 0) {
     const int ntile = ((g.M + 127) / 128) * ((g.N + 127) / 128);
-    const int va = vec_ok(g.A, g.a_bf16, g.a_bs, g.a_sm, g.a_sk, g.a_sk == 1);
-    const int vb = vec_ok(g.B, g.b_bf16, g.b_bs, g.b_sn, g.b_sk, g.b_sk == 1);
     const dim3 grid((unsigned)((int64_t)ntile * g.batch * ns));
     if (g.a_bf16 && g.b_bf16) hipLaunchKernelGGL((k_bgemm128<true, true, 16>), grid, dim3(256), 0, s, g, kchunk, P, va, vb, ntile);
     else if (g.a_bf16) hipLaunchKernelGGL((k_bgemm128<true, false, 16>), grid, dim3(256), 0, s, g, kchunk, P, va, vb, ntile);

@@ -36,7 +36,12 @@ CASES = {
     # 2048-token chunks: the token contractions split K (partial sums added
     # in split order by a second launch)
     "long-chunks-split-k": (64, 128, "f32", 2 * 2048 + 100, 2048, A2U, None, True, True, True),
+    # eight heads of the lm-causal shape: the token contractions take the
+    # 128 x 128 tile kernel (512 tiles), split-K included; two heads checked
+    "lm-shape-128-tiles": (128, 512, "bf16", 2 * 2048 + 64, 2048, A2U, None, True, True, True),
 }
+# (number of heads, heads compared with the oracle); default 2, all
+HEADS = {"lm-shape-128-tiles": (8, (0, 7))}
 TOL = 1e-4
 # dL/dmom is one number per write (the momentum buffer projected on the
 # cotangent of the pre-Newton-Schulz sum, spread over the write's tokens):
@@ -64,7 +69,7 @@ def _inputs(rng, bh, T, d, dh):
 def test_backward_matches_oracle(device, case):
     import torch
     d, dh, dt, T, C, order, subset, muon, momentum, renorm = CASES[case]
-    bh = 2
+    bh, check = HEADS.get(case, (2, (0, 1)))
     rng = np.random.default_rng(zlib.crc32(case.encode()))
     W, Q, K, V, e, mom, dO = _inputs(rng, bh, T, d, dh)
     act = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -86,7 +91,7 @@ def test_backward_matches_oracle(device, case):
         if t is not None:
             t.fill_(float("nan"))
     ws = torch.full(((L.backward_workspace_bytes(shape, T, C, o) + 3) // 4,), float("nan"), device=device)
-    print(f"backward {case}: d={d} dh={dh} T={T} chunk={C}", flush=True)
+    print(f"backward {case}: bh={bh} d={d} dh={dh} T={T} chunk={C}", flush=True)
     L.lact_sequence_backward(shape, dev(W[0]), dev(W[1]), dev(W[2]), q, k, v, dev(dO), dev(e[0]), dev(e[1]),
                              dev(e[2]), dev(mom) if momentum else None, T, C, order, subset, 0, o, grads, ws)
     torch.cuda.synchronize()
@@ -95,7 +100,7 @@ def test_backward_matches_oracle(device, case):
             "W3": "dw3", "W2": "dw2"}
     if momentum:
         keys["mom"] = "dmom"
-    for b in range(bh):
+    for b in check:
         ref = B.sequence_vjp(W[0][b], W[1][b], W[2][b], Q64[b], K64[b], V64[b], e[0][b], e[1][b], e[2][b], C,
                              dO[b], mom=mom[b] if momentum else None, order=order, subset=subset,
                              use_muon=muon, use_momentum=momentum, renorm=renorm)
