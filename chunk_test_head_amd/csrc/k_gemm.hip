@@ -350,11 +350,11 @@ __global__ __launch_bounds__(256) void k_nsn_part(NsIn g, float* part, int64_t n
   if (tid == 0) part[blockIdx.y * NSN_B + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__global__ __launch_bounds__(256) void k_nsn_scale(NsIn g, const float* part, float* x,
+__global__ __launch_bounds__(256) void k_nsn_scale(NsIn g, const float* part, int np, float* x,
                                                    bf16* xh, int64_t n, float eps) {
   const int tid = threadIdx.x;
   float tot = 0.f;
-  for (int b = 0; b < NSN_B; ++b) tot += part[blockIdx.y * NSN_B + b];
+  for (int b = 0; b < np; ++b) tot += part[blockIdx.y * np + b];
   const float scale = 1.0f / (sqrtf(tot) + eps);
   const int64_t per = n / NSN_B;
   const int64_t base = (int64_t)blockIdx.y * n + (int64_t)blockIdx.x * per;
@@ -368,13 +368,16 @@ __global__ __launch_bounds__(256) void k_nsn_scale(NsIn g, const float* part, fl
 }
 
 hipError_t launch_nsn(NsIn g, float* part, float* x, bf16* xh, int count, int64_t n, float eps,
-                      hipStream_t s) {
+                      hipStream_t s, int pre_np) {
   if (n % (4 * NSN_B) != 0) return hipErrorInvalidValue;
   const dim3 grid(NSN_B, (unsigned)count);
-  hipLaunchKernelGGL(k_nsn_part, grid, dim3(256), 0, s, g, part, n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_nsn_scale, grid, dim3(256), 0, s, g, part, x, xh, n, eps);
+  if (pre_np <= 0) {
+    hipLaunchKernelGGL(k_nsn_part, grid, dim3(256), 0, s, g, part, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_nsn_scale, grid, dim3(256), 0, s, g, part, pre_np > 0 ? pre_np : NSN_B, x, xh, n,
+                     eps);
   return hipGetLastError();
 }
 

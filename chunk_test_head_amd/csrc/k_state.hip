@@ -20,6 +20,7 @@ namespace lact {
 // and write the wide [i][j] result.
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   __shared__ float tile[64][65];
+  __shared__ float red[4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int jt = a.dh / 64, itn = a.d / 64;
   int id = blockIdx.x;
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   }
   __syncthreads();
   const float beta = m != nullptr ? a.beta[head] : 0.f;
+  float ss = 0.f;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int i = ty + 16 * rr;
@@ -87,6 +89,16 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
       *reinterpret_cast<f32x4*>(m + off) = v;
     }
     if (out != nullptr) *reinterpret_cast<f32x4*>(out + off) = v;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  if (a.ss_part != nullptr) {
+    // the tile's sum of squares, waves in index order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    if (tid == 0)
+      a.ss_part[((int64_t)mat * a.bh + head) * (jt * itn) + tj * itn + ti] = (red[0] + red[1]) + (red[2] + red[3]);
   }
 }
 

@@ -259,9 +259,12 @@ static int64_t ns_ws_bytes(int count, int rows, int cols) {
          align256(2 * (int64_t)count * tiles * 4);
 }
 
+// pre_np > 0: bm already holds pre_np partial sums of squares per matrix of
+// the input (the split sum wrote them), for the normalisation of the
+// batched-GEMM path.
 static hipError_t run_ns(int prec, int count, int rows, int cols, NsIn g, float* u,
                          float eps, float* xa, float* xb, float* xh, float* am, float* bm,
-                         float* ssp, hipStream_t s) {
+                         float* ssp, hipStream_t s, int pre_np = 0) {
   const int64_t m = (int64_t)rows * cols;
   const int shift_from = ns_shift_from(prec);
   hipError_t e = hipErrorNotSupported;
@@ -277,7 +280,7 @@ static hipError_t run_ns(int prec, int count, int rows, int cols, NsIn g, float*
     bf16* bh = ah + (int64_t)count * rows * rows;
     const int64_t rr = (int64_t)rows * rows;
     const int tiles = (rows / 64) * (cols / 64);
-    if ((e = launch_nsn(g, bm, xa, xh0, count, m, eps, s)) != hipSuccess) return e;
+    if ((e = launch_nsn(g, bm, xa, xh0, count, m, eps, s, pre_np)) != hipSuccess) return e;
     float* x = xa;
     float* y = xb;
     bf16* xc = xh0;
@@ -447,7 +450,8 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
                            const Workspace& w, int nsplit, float* o1, float* o3, float* o2,
                            float* m1, float* m3, float* m2, const float* mom, hipStream_t s,
                            bool reduce = true, int eta_per_channel = 0,
-                           const SideStream* side = nullptr, const ApplyJob* job = nullptr) {
+                           const SideStream* side = nullptr, const ApplyJob* job = nullptr,
+                           float* ss_part = nullptr) {
   GradArgs a;
   a.k = k; a.k_sbh = kl.stride_bh; a.k_st = kl.stride_tok;
   a.v = v; a.v_sbh = vl.stride_bh; a.v_st = vl.stride_tok;
@@ -479,7 +483,7 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
     if (rr != LACT_OK) return rr;
   }
   if (!reduce) return LACT_OK;  // the consumer sums the partials itself
-  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta};
+  ReduceArgs r{w.partial, nsplit, sh->bh, sh->d, sh->dh, o1, o3, o2, m1, m3, m2, w.beta, ss_part};
   {
     ProfScope p(LACT_PROF_REDUCE, s);
     e = launch_reduce(r, s);
@@ -541,11 +545,14 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   // the events are shared by every caller on the device
   std::unique_lock<std::mutex> side_lock;
   if (fork) side_lock = std::unique_lock<std::mutex>(side->mu);
+  // with Newton-Schulz after the split sum, the sum also takes the first
+  // pass of its Frobenius normalisation (per-tile sums of squares)
+  const bool pre_norm = op->use_muon && !nsstep;
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
                           mo ? nullptr : g1, mo ? nullptr : g3, mo ? nullptr : g2,
                           mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr,
                           mo ? mom : nullptr, s, !nsstep, op->eta_per_channel,
-                          fork ? side : nullptr, fork ? job : nullptr);
+                          fork ? side : nullptr, fork ? job : nullptr, pre_norm ? w.bmat : nullptr);
   if (r != LACT_OK) return r;
   const float* u1 = mo ? st->m1 : g1;
   const float* u3 = mo ? st->m3 : g3;
@@ -574,7 +581,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
       return e == hipSuccess ? LACT_OK : hip_fail(e);
     }
     e = run_ns(ns_prec_of(sh, op), 3 * sh->bh, sh->d, sh->dh, in, w.g, op->ns_eps, w.xa, w.xb,
-               w.xh, w.amat, w.bmat, w.ssp, s);
+               w.xh, w.amat, w.bmat, w.ssp, s, (sh->d / 64) * (sh->dh / 64));
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
   }

@@ -82,6 +82,10 @@ struct ReduceArgs {
   float* out1; float* out3; float* out2;  // [bh][d][dh] each (NULL: only M holds the result)
   float* m1; float* m3; float* m2;        // momentum (NULL = off)
   const float* beta;                      // [bh] coefficient of M (from the gradient launch)
+  // NULL, or [3 bh][tiles]: sum of squares of each 64 x 64 tile of the
+  // result, matrix mat bh + head (the Newton-Schulz input order), tiles in
+  // launch order (the first pass of the Frobenius normalisation)
+  float* ss_part;
 };
 
 
@@ -203,8 +207,10 @@ hipError_t launch_ns_step_apply(int count, int rows, int cols, const NsGrad& gr,
 hipError_t launch_copy16(void* dst, const void* src, int64_t bytes, hipStream_t s);
 hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s);
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s);
+// pre_np > 0: part already holds pre_np partial sums of squares per matrix
+// (written by the split sum), so only the scaling pass runs.
 hipError_t launch_nsn(NsIn g, float* part, float* x, __bf16* xh, int count, int64_t n, float eps,
-                      hipStream_t s);
+                      hipStream_t s, int pre_np = 0);
 hipError_t launch_step(int dtype, const StepArgs& a, hipStream_t s);
 
 
