@@ -149,7 +149,7 @@ hipError_t launch_ns_norm(const NsNormArgs& a, hipStream_t s) {
 //     hidden unit per 16-byte store.
 template <class T>
 __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) {
-  constexpr int RB = 32;  // rows per workgroup; ut: [RB][d + 1]
+  constexpr int RB = 16;  // rows per workgroup (16: two workgroups per CU); ut: [RB][d + 1]
   const int tid = threadIdx.x;
   const int d = a.d, dh = a.dh, pt = d + 1;
   const int nb = dh / RB;
@@ -319,13 +319,13 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a, int n13) {
 
 template <class T, int KMAX>
 static hipError_t run_step(const StepArgs& a, hipStream_t s) {
-  const size_t l13 = (size_t)32 * (a.d + 1) * sizeof(float);
+  const size_t l13 = (size_t)16 * (a.d + 1) * sizeof(float);
   const size_t l2 = (size_t)8 * a.dh * sizeof(T);
   const size_t lds = l13 > l2 ? l13 : l2;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_step<T, KMAX>),
                                    (int)(8 * 4096 * sizeof(T)));
   if (e != hipSuccess) return e;
-  const int n13 = a.bh * 2 * (a.dh / 32), n2 = a.bh * (a.d / 8);
+  const int n13 = a.bh * 2 * (a.dh / 16), n2 = a.bh * (a.d / 8);
   hipLaunchKernelGGL((k_step<T, KMAX>), dim3((unsigned)(n13 + n2)), dim3(256), lds, s, a, n13);
   return hipGetLastError();
 }
