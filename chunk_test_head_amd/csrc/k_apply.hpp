@@ -281,7 +281,10 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
 // (D / 4 VGPRs) and the o^T accumulators (D / 2, in AGPRs) - no partial
 // exchange and no duplicated silu(g) u as when two waves per SIMD split the
 // features (measured 14-16 % slower).  4 waves = 128 tokens per workgroup.  The hidden dim is streamed in blocks of 32 through
-// three LDS stages (W1 / W3 block rows at swz<D>, the W2 block at swz32),
+// three LDS stages (W1 / W3 block rows at the padded pitch tpad<D>, the W2
+// block at swz32; 150 KiB), staged by buffer loads (uniform descriptors,
+// per-lane 32-bit offsets) so that neither the loads nor the LDS stores and
+// fragment reads spend per-lane address arithmetic inside the loop,
 // software-pipelined: iteration jb runs the gate / up contractions of block
 // jb + 1 with h = silu(g) u of block jb between them, then
 // o^T += W2[:, block jb] h^T with the staging stores of block jb + 2 between
@@ -289,7 +292,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
 template <int D>
 struct ApplySoloLds {
   static constexpr int HB = 32;
-  static constexpr int STAGE = 2 * HB * D + D * HB;
+  static constexpr int STAGE = 2 * HB * (D + 16) + D * HB;
   static constexpr int ELEMS = 3 * STAGE;
 };
 
@@ -300,13 +303,14 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
   constexpr int NTH = 256, HB = 32;
   constexpr int KS = D / 32;     // K slabs of the gate / up contractions
   constexpr int IT = D / 16;     // output feature tiles
-  constexpr int S1 = HB * D;     // one W1 / W3 block, [HB][D]
+  constexpr int G1 = HB * D;     // one W1 / W3 block in memory, [HB][D]
+  constexpr int S1 = HB * (D + 16);  // the same in LDS (tpad)
   constexpr int S2 = D * HB;     // W2 block, [D][HB] (kappa slot order)
   constexpr int STAGE = 2 * S1 + S2;
   constexpr int NBUF = 3;
-  constexpr int NV1 = S1 / 8 / NTH, NV2 = S2 / 8 / NTH;
+  constexpr int NV1 = G1 / 8 / NTH, NV2 = S2 / 8 / NTH;
   constexpr int NST = 2 * KS;    // gate / up steps (K slab, hidden tile)
-  static_assert(NV1 * 8 * NTH == S1 && NV2 * 8 * NTH == S2, "stage split");
+  static_assert(NV1 * 8 * NTH == G1 && NV2 * 8 * NTH == S2 && NTH % (D / 8) == 0, "stage split");
   static_assert(NST == 16 && 2 * NV1 + 2 * NV2 <= IT, "step plan");
   static_assert(ApplySoloLds<D>::STAGE == STAGE, "layout");
 
@@ -348,46 +352,56 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
 
   const int NB = dh / HB;
   bf16x8 r1[NV1], r3[NV1], r2[NV2];
-  // block JB of W1 / W3 rows and W2 columns (W2 rows of HB hidden units in
-  // kappa slot order, swz32)
+  // block JB of W1 / W3 rows (contiguous: vector x of a thread is elements
+  // 8 (tid + x NTH) ..) and of W2 columns (vector x: row tid / 4 + 64 x,
+  // columns JB HB + 8 (tid % 4) ..), through one descriptor per matrix and
+  // block: per-lane offsets go1 / go2, the x part uniform
+  const uint32_t go1 = (uint32_t)tid * 16u;
+  const uint32_t go2 = (uint32_t)(((tid >> 2) * dh + (tid & 3) * 8) * 2);
+  const uint32_t n2 = (uint32_t)(((D - 1) * dh + HB) * 2);
 #define LACT_AS_GLOAD(JB)                                                              \
   {                                                                                    \
+    const __amdgpu_buffer_rsrc_t b1_ = buf_rsrc(w1 + (int64_t)(JB) * G1, G1 * 2);      \
+    const __amdgpu_buffer_rsrc_t b3_ = buf_rsrc(w3 + (int64_t)(JB) * G1, G1 * 2);      \
+    const __amdgpu_buffer_rsrc_t b2_ = buf_rsrc(w2 + (int64_t)(JB) * HB, n2);          \
     _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      r1[x] = ld8(w1 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
-      r3[x] = ld8(w3 + (int64_t)(JB) * S1 + (int64_t)vi * 8);                          \
+      r1[x] = buf_ld8(b1_, go1, x * NTH * 16);                                         \
+      r3[x] = buf_ld8(b3_, go1, x * NTH * 16);                                         \
     }                                                                                  \
-    _Pragma("unroll") for (int x = 0; x < NV2; ++x) {                                  \
-      const int vi = tid + x * NTH;                                                    \
-      r2[x] = ld8(w2 + (int64_t)(vi >> 2) * dh + (JB) * HB + (vi & 3) * 8);          \
-    }                                                                                  \
+    _Pragma("unroll") for (int x = 0; x < NV2; ++x) r2[x] = buf_ld8(b2_, go2, x * (NTH / 4) * dh * 2); \
   }
-  // staging store number X of the block (X < 2 NV1 + 2 NV2)
+  // staging store number X of the block (X < 2 NV1 + 2 NV2), at a per-lane
+  // base plus an immediate: W1 / W3 vector x is row tid / (D / 8) + x RX of
+  // the padded block; W2 vector x is row tid / 4 + 64 x, whose swz32 key
+  // repeats every 16 rows (slot pair ru = 2 (tid % 4) + half)
+  constexpr int RX = NTH / (D / 8);
+  const int so1 = opaque(tpad<D>(tid / (D / 8), (tid % (D / 8)) * 8));
+  int so2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ru = 2 * (tid & 3) + h;
+    so2[h] = opaque(swz32(tid >> 2, 2 * (ru & 3) + (ru >> 2)));
+  }
 #define LACT_AS_LSTORE1(S_, X)                                                         \
   {                                                                                    \
     if ((X) < 2 * NV1) {                                                               \
-      const int x_ = (X) >> 1, vi = tid + x_ * NTH;                                    \
-      const int o_ = swz<D>(vi / (D / 8), (vi % (D / 8)) * 8);                         \
-      if (((X) & 1) == 0) *reinterpret_cast<bf16x8*>((S_) + o_) = r1[x_];              \
-      else *reinterpret_cast<bf16x8*>((S_) + S1 + o_) = r3[x_];                        \
+      const int x_ = (X) >> 1;                                                         \
+      bf16* d_ = (S_) + so1 + (((X) & 1) ? S1 : 0) + x_ * RX * (D + 16);               \
+      *reinterpret_cast<bf16x8*>(d_) = ((X) & 1) ? r3[x_] : r1[x_];                    \
     } else {                                                                           \
-      const int y_ = (X) - 2 * NV1, x_ = y_ >> 1, vi = tid + x_ * NTH;                 \
-      const int row = vi >> 2, ru = 2 * (vi & 3) + (y_ & 1);                           \
-      bf16* s2_ = (S_) + 2 * S1;                                                       \
+      const int y_ = (X) - 2 * NV1, x_ = y_ >> 1;                                      \
+      bf16* s2_ = (S_) + 2 * S1 + so2[y_ & 1] + x_ * (NTH / 4) * HB;                   \
       if ((y_ & 1) == 0)                                                               \
-        *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru & 3) + (ru >> 2))) =       \
-            __builtin_shufflevector(r2[x_], r2[x_], 0, 1, 2, 3);                       \
+        *reinterpret_cast<bf16x4*>(s2_) = __builtin_shufflevector(r2[x_], r2[x_], 0, 1, 2, 3); \
       else                                                                             \
-        *reinterpret_cast<bf16x4*>(s2_ + swz32(row, 2 * (ru & 3) + (ru >> 2))) =       \
-            __builtin_shufflevector(r2[x_], r2[x_], 4, 5, 6, 7);                       \
+        *reinterpret_cast<bf16x4*>(s2_) = __builtin_shufflevector(r2[x_], r2[x_], 4, 5, 6, 7); \
     }                                                                                  \
   }
 
   // per-lane offsets (laundered: the stage is a runtime choice, every read
   // should be this base + an immediate): gate / up A fragments (row c,
   // features 8 g ..) and W2 A fragments (row c, slots 2 g, 2 g + 1)
-  const int fo = opaque(c * D);
-  const int key = opaque(swz_key<D>(c));
+  const int fo = opaque(tpad<D>(c, 8 * g));
   const int wo = opaque(swz32(c, 2 * g));
   f32x4 P[2][2], U[2][2];  // [hidden tile jt][token half tt]
   bf16x8 hf[2];
@@ -402,15 +416,13 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
         Pn[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         Un[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    const bf16* s1 = lds + buf * STAGE + fo;
+    const bf16* s1 = lds + opaque(buf * STAGE + fo);  // every read below: s1 + an immediate
     bf16x8 f1[3], f3[3];
-    // step s = 2 ks + jt: rows 16 jt + c, features 32 ks + 8 g .. (chunk
-    // 4 ks + g XOR the row key)
+    // step s = 2 ks + jt: rows 16 jt + c, features 32 ks + 8 g ..
 #define LACT_AS_FRAG(S)                                                                \
   {                                                                                    \
-    const int ch_ = ((4 * ((S) >> 1) + g) ^ key) << 3;                                 \
-    f1[(S) % 3] = ld8(s1 + 16 * ((S) & 1) * D + ch_);                                  \
-    f3[(S) % 3] = ld8(s1 + S1 + 16 * ((S) & 1) * D + ch_);                             \
+    f1[(S) % 3] = ld8(s1 + 16 * ((S) & 1) * (D + 16) + 32 * ((S) >> 1));               \
+    f3[(S) % 3] = ld8(s1 + S1 + 16 * ((S) & 1) * (D + 16) + 32 * ((S) >> 1));          \
   }
     LACT_AS_FRAG(0);
     LACT_AS_FRAG(1);
@@ -455,7 +467,7 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
     // ---- region 2: o^T += W2[:, block jb] h^T, W2 reads two steps ahead,
     // the staging stores of block jb + 2 between them ----
     {
-      const bf16* s2 = lds + cb * STAGE + 2 * S1 + wo;
+      const bf16* s2 = lds + opaque(cb * STAGE + 2 * S1 + wo);
       bf16* sl = lds + lb * STAGE;
       bf16x8 f2[3];
       f2[0] = ld8(s2);

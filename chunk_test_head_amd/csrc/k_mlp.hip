@@ -589,9 +589,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
 // the SwiGLU backward are shared; one η row per token in registers).
 // RING, TRING: fragment buffers of the forward and of the gradient
 // contractions (reads RING - 1, TRING - 1 steps ahead of their MFMAs).
-// Measured on long-context: SAME with TRING = 4 is 1 % faster than three
-// rates with 3 / 3; three rates with TRING = 4 is 2.5 % slower (the
-// register allocation, not the instruction count, moves the time).
+// Measured on long-context (4 heads x 16384 tokens): with one rate,
+// TRING = 6 (226 us per launch) beats 4 (231), 5 (228) and 8 (226-227),
+// RING = 2 is 5 % slower; three rates keep 3 / 3 (TRING = 4 was 2.5 %
+// slower there: the register allocation, not the instruction count, moves
+// the time).
 template <int D, int HW, bool SAME = false, int RING = 3, int TRING = 3>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_grad_solo(GradArgs a) {
@@ -658,29 +660,44 @@ void k_grad_solo(GradArgs a) {
   const int er = tid % NT;
   uint4 rk[VPT], rv[VPT];
   float re = 0.f;
-  // A whole tile inside the split (every tile but a split's last): vector
-  // x of a thread is row tid / (D / 8) + x RX, piece tid % (D / 8), loaded
-  // from a uniform row base plus the thread's 32-bit byte offset (no
-  // per-lane 64-bit address arithmetic, no bounds checks).  A split's last
-  // tile checks every row and reads rows past the end as zeros.
+  // Staging loads through one buffer descriptor per tensor and tile: base =
+  // the tile's first row, range = the split's rows from there on (rows past
+  // the split, and whole tiles past the last, read as zeros: the range
+  // check); vector x of a thread is row tid / (D / 8) + x RX, piece
+  // tid % (D / 8), at a 32-bit byte offset from the base (token strides
+  // below 2^24 elements).  Larger strides take a checked per-lane path.
   constexpr int RX = NTH / (D / 8);
   static_assert(NTH % (D / 8) == 0, "rows per vector step");
-  const bool fast_ok = a.k_st < (1 << 24) && a.v_st < (1 << 24);  // offsets fit 32 bits
-  const uint32_t kob = (uint32_t)(((tid / (D / 8)) * (uint32_t)a.k_st + (tid % (D / 8)) * 8) * 2u);
-  const uint32_t vob = (uint32_t)(((tid / (D / 8)) * (uint32_t)a.v_st + (tid % (D / 8)) * 8) * 2u);
+  const bool fast_ok = a.k_st < (1 << 24) && a.v_st < (1 << 24) && s1 - s0 < (1 << 30);
+  const int nrow = (int)(s1 - s0);
+  uint32_t kox[VPT], vox[VPT];
+#pragma unroll
+  for (int x = 0; x < VPT; ++x) {
+    const uint32_t row = (uint32_t)(tid / (D / 8) + x * RX), piece = (uint32_t)(tid % (D / 8)) * 16u;
+    kox[x] = row * (uint32_t)a.k_st * 2u + piece;
+    vox[x] = row * (uint32_t)a.v_st * 2u + piece;
+  }
+  // bytes from row t0 to the end of the tile's last row inside the split (0
+  // from s1 on)
+  auto span = [&](int64_t t0, int st) -> uint32_t {
+    const int rows = min(nrow - (int)(t0 - s0), NT);
+    return rows <= 0 ? 0u : (uint32_t)(((rows - 1) * st + D) * 2);
+  };
 #define LACT_GS_GLOAD(T0)                                                           \
   {                                                                                 \
-    if (fast_ok && (T0) + NT <= s1) {                                               \
+    if (fast_ok) {                                                                  \
+      const __amdgpu_buffer_rsrc_t kr_ = buf_rsrc(kp + (T0) * a.k_st, span((T0), (int)a.k_st)); \
+      const __amdgpu_buffer_rsrc_t vr_ = buf_rsrc(vp + (T0) * a.v_st, span((T0), (int)a.v_st)); \
       _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
-        const char* kb_ = reinterpret_cast<const char*>(kp + ((T0) + x * RX) * a.k_st); \
-        const char* vb_ = reinterpret_cast<const char*>(vp + ((T0) + x * RX) * a.v_st); \
-        rk[x] = *reinterpret_cast<const uint4*>(kb_ + kob);                         \
-        rv[x] = *reinterpret_cast<const uint4*>(vb_ + vob);                         \
+        rk[x] = buf_ld16(kr_, kox[x]);                                              \
+        rv[x] = buf_ld16(vr_, vox[x]);                                              \
       }                                                                             \
     } else {                                                                        \
+      /* (an opaque row base: no per-lane pointers carried across tiles) */         \
+      const int64_t t0_ = opaque_s(T0);                                             \
       _Pragma("unroll") for (int x = 0; x < VPT; ++x) {                             \
         const int vi = tid + x * NTH;                                               \
-        const int64_t t = (T0) + vi / (D / 8);                                      \
+        const int64_t t = t0_ + vi / (D / 8);                                       \
         rk[x] = uint4{0u, 0u, 0u, 0u};                                              \
         rv[x] = uint4{0u, 0u, 0u, 0u};                                              \
         if (t < s1) {                                                               \
@@ -924,7 +941,7 @@ static hipError_t run_grad_solo(const GradArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)(a.dh / (64 * HW)) * a.nsplit * a.bh;
   if (blocks <= 0) return hipSuccess;
   if (a.eta1 == a.eta3 && a.eta3 == a.eta2)
-    hipLaunchKernelGGL((k_grad_solo<D, HW, true, 3, 4>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_grad_solo<D, HW, true, 3, 6>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((k_grad_solo<D, HW, false, 3, 3>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -68,6 +68,22 @@ __device__ __forceinline__ f32x8 ld4x2(const float* p0, const float* p1) {
   return r;
 }
 
+// Raw buffer loads: a wave-uniform descriptor over [base, base + bytes)
+// (gfx9 descriptor word 3: 32-bit data format) and a per-lane 32-bit byte
+// offset; a load past the range returns zeros (the hardware's range check),
+// and no 64-bit address arithmetic runs per lane.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// 8 bf16 at the per-lane offset plus a wave-uniform one (bytes)
+__device__ __forceinline__ bf16x8 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+
 // LDS transpose read (ds_read_b64_tr_b16), per 16-lane group: lane j gives
 // the address of 4 consecutive 16-bit elements of row j/4 (columns
 // 4 (j%4) .. +3) of a 4 x 16 block; lane i receives column i of the 4 rows.
@@ -115,6 +131,11 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
 // registers (one per distinct swizzled address).
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
+  return x;
+}
+// The same for a wave-uniform 64-bit value (kept in a scalar register pair).
+__device__ __forceinline__ int64_t opaque_s(int64_t x) {
+  asm volatile("" : "+s"(x));
   return x;
 }
 
