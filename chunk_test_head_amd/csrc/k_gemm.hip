@@ -130,6 +130,9 @@ constexpr int NSG_SA = NSG_T * NSG_PA;                // elements per A stage
 constexpr int NSG_SB = NSG_T * NSG_PA > NSG_K * NSG_PB ? NSG_T * NSG_PA : NSG_K * NSG_PB;
 constexpr int NSG_PC = NSG_T + 4;                     // fp32 result tile pitch
 constexpr int NSG_PD = 4;                             // K slabs in flight
+// slab j sits in register slot j % NSG_PD and LDS buffer slot % 2: with an
+// even slot count the two buffers alternate from slab to slab
+static_assert(NSG_PD % 2 == 0, "the LDS buffers alternate by slot parity");
 }
 
 template <bool BKN>
