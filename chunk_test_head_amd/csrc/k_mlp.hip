@@ -572,11 +572,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
 // ------------------------------------------------- gradient, bf16, solo --
 // One wave per SIMD holding 16 HW hidden units over all D features: its W
 // fragments (3 HW D / 8 registers) and G1^T, G3^T, G2 accumulators
-// (6 HW D / 4, in AGPRs) take a whole SIMD's register file; D = 256: HW = 1,
-// D = 128: HW = 2 (every k / v fragment then feeds two hidden tiles, half
-// the LDS reads of one 16-unit tile per wave).  (For d = 256, two waves per
-// SIMD would have to split the features, exchange the forward partials
-// through LDS and both run the SwiGLU backward: measured 20-30 % slower.)
+// (6 HW D / 4, in AGPRs) take a whole SIMD's register file.  Launched for
+// D = 256 with HW = 1 only: at D = 128, HW = 2 (every k / v fragment feeding
+// two hidden tiles) measured slower than k_grad_bf16 (77.5 vs 73.3 us on
+// 32 heads x 2048 tokens, dh = 512).  (For d = 256, two waves per SIMD
+// would have to split the features, exchange the forward partials through
+// LDS and both run the SwiGLU backward: measured 20-30 % slower.)
 // 4 waves = 64 HW hidden units share the staged k / v tiles.  Software
 // pipeline over 32-token tiles, three stage buffers, one barrier per tile:
 // iteration n runs the forward contractions of tile n + 1 with the SwiGLU
