@@ -280,20 +280,26 @@ __device__ __forceinline__ void apply_block(const ApplyArgs& a, int lid, T* lds)
 // One wave per SIMD holding 32 tokens over all D features: q fragments
 // (D / 4 VGPRs) and the o^T accumulators (D / 2, in AGPRs) - no partial
 // exchange and no duplicated silu(g) u as when two waves per SIMD split the
-// features (measured 14-16 % slower).  4 waves = 128 tokens per workgroup.  The hidden dim is streamed in blocks of 32 through
-// three LDS stages (W1 / W3 block rows at the padded pitch tpad<D>, the W2
-// block at swz32; 150 KiB), staged by buffer loads (uniform descriptors,
-// per-lane 32-bit offsets) so that neither the loads nor the LDS stores and
-// fragment reads spend per-lane address arithmetic inside the loop,
-// software-pipelined: iteration jb runs the gate / up contractions of block
-// jb + 1 with h = silu(g) u of block jb between them, then
-// o^T += W2[:, block jb] h^T with the staging stores of block jb + 2 between
-// those; fragment reads two steps ahead, the order held by scheduling fences.
+// features (measured 14-16 % slower).  4 waves = 128 tokens per workgroup.
+// The hidden dim is streamed in blocks of 32 through two LDS stages of the
+// W1 / W3 block rows (padded pitch tpad<D>) and two of the W2 block (swz32),
+// 100 KiB, staged by buffer loads (uniform descriptors, per-lane 32-bit
+// offsets) so that neither the loads nor the LDS stores and fragment reads
+// spend per-lane address arithmetic inside the loop; software-pipelined:
+// iteration jb runs the gate / up contractions of block jb + 1 with
+// h = silu(g) u of block jb between them, then o^T += W2[:, block jb] h^T
+// with the staging stores (W1 / W3 of block jb + 2, W2 of block jb + 1)
+// between those; fragment reads two steps ahead, the order held by
+// scheduling fences.  (Three stages of both, 150 KiB, measured 1 % slower
+// on 8 heads x 49152 tokens.)
 template <int D>
 struct ApplySoloLds {
   static constexpr int HB = 32;
-  static constexpr int STAGE = 2 * HB * (D + 16) + D * HB;
-  static constexpr int ELEMS = 3 * STAGE;
+  static constexpr int S13 = 2 * HB * (D + 16), S2 = D * HB;
+  static constexpr int ELEMS = 2 * (S13 + S2);
+  // stage b (0, 1) of the W1 / W3 rows and of the W2 block (elements)
+  static constexpr int w13(int b) { return b * S13; }
+  static constexpr int w2(int b) { return 2 * S13 + b * S2; }
 };
 
 // Body of one workgroup (256 threads, one wave per SIMD): logical block lid
@@ -306,8 +312,6 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
   constexpr int G1 = HB * D;     // one W1 / W3 block in memory, [HB][D]
   constexpr int S1 = HB * (D + 16);  // the same in LDS (tpad)
   constexpr int S2 = D * HB;     // W2 block, [D][HB] (kappa slot order)
-  constexpr int STAGE = 2 * S1 + S2;
-  constexpr int NBUF = 3;
   constexpr int NV1 = G1 / 8 / NTH, NV2 = S2 / 8 / NTH;
   constexpr int NST = 2 * KS;    // gate / up steps (K slab, hidden tile)
   // fragment buffers of the gate / up and of the W2 contractions (reads
@@ -315,7 +319,8 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
   constexpr int FR = 3, WR = 3;
   static_assert(NV1 * 8 * NTH == G1 && NV2 * 8 * NTH == S2 && NTH % (D / 8) == 0, "stage split");
   static_assert(NST == 16 && 2 * NV1 + 2 * NV2 <= IT, "step plan");
-  static_assert(ApplySoloLds<D>::STAGE == STAGE, "layout");
+  using LY = ApplySoloLds<D>;
+  static_assert(LY::S13 == 2 * S1 && LY::S2 == S2, "layout");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -362,15 +367,18 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
   const uint32_t go1 = (uint32_t)tid * 16u;
   const uint32_t go2 = (uint32_t)(((tid >> 2) * dh + (tid & 3) * 8) * 2);
   const uint32_t n2 = (uint32_t)(((D - 1) * dh + HB) * 2);
-#define LACT_AS_GLOAD(JB)                                                              \
+#define LACT_AS_GLOAD13(JB)                                                            \
   {                                                                                    \
     const __amdgpu_buffer_rsrc_t b1_ = buf_rsrc(w1 + (int64_t)(JB) * G1, G1 * 2);      \
     const __amdgpu_buffer_rsrc_t b3_ = buf_rsrc(w3 + (int64_t)(JB) * G1, G1 * 2);      \
-    const __amdgpu_buffer_rsrc_t b2_ = buf_rsrc(w2 + (int64_t)(JB) * HB, n2);          \
     _Pragma("unroll") for (int x = 0; x < NV1; ++x) {                                  \
       r1[x] = buf_ld8(b1_, go1, x * NTH * 16);                                         \
       r3[x] = buf_ld8(b3_, go1, x * NTH * 16);                                         \
     }                                                                                  \
+  }
+#define LACT_AS_GLOAD2(JB)                                                             \
+  {                                                                                    \
+    const __amdgpu_buffer_rsrc_t b2_ = buf_rsrc(w2 + (int64_t)(JB) * HB, n2);          \
     _Pragma("unroll") for (int x = 0; x < NV2; ++x) r2[x] = buf_ld8(b2_, go2, x * (NTH / 4) * dh * 2); \
   }
   // staging store number X of the block (X < 2 NV1 + 2 NV2), at a per-lane
@@ -385,15 +393,15 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
     const int ru = 2 * (tid & 3) + h;
     so2[h] = opaque(swz32(tid >> 2, 2 * (ru & 3) + (ru >> 2)));
   }
-#define LACT_AS_LSTORE1(S_, X)                                                         \
+#define LACT_AS_LSTORE1(S13_, S2_, X)                                                  \
   {                                                                                    \
     if ((X) < 2 * NV1) {                                                               \
       const int x_ = (X) >> 1;                                                         \
-      bf16* d_ = (S_) + so1 + (((X) & 1) ? S1 : 0) + x_ * RX * (D + 16);               \
+      bf16* d_ = (S13_) + so1 + (((X) & 1) ? S1 : 0) + x_ * RX * (D + 16);             \
       *reinterpret_cast<bf16x8*>(d_) = ((X) & 1) ? r3[x_] : r1[x_];                    \
     } else {                                                                           \
       const int y_ = (X) - 2 * NV1, x_ = y_ >> 1;                                      \
-      bf16* s2_ = (S_) + 2 * S1 + so2[y_ & 1] + x_ * (NTH / 4) * HB;                   \
+      bf16* s2_ = (S2_) + so2[y_ & 1] + x_ * (NTH / 4) * HB;                           \
       if ((y_ & 1) == 0)                                                               \
         *reinterpret_cast<bf16x4*>(s2_) = __builtin_shufflevector(r2[x_], r2[x_], 0, 1, 2, 3); \
       else                                                                             \
@@ -419,7 +427,7 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
         Pn[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         Un[jt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    const bf16* s1 = lds + opaque(buf * STAGE + fo);  // every read below: s1 + an immediate
+    const bf16* s1 = lds + opaque(LY::w13(buf) + fo);  // every read below: s1 + an immediate
     bf16x8 f1[FR], f3[FR];
     // step s = 2 ks + jt: rows 16 jt + c, features 32 ks + 8 g ..
 #define LACT_AS_FRAG(S)                                                                \
@@ -449,29 +457,40 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
 #undef LACT_AS_FRAG
   };
 
-  LACT_AS_GLOAD(0);
+  // Two stages each: the W1 / W3 rows of block b in their stage b % 2,
+  // staged two iterations ahead (its gate / up run one iteration ahead of
+  // its W2 contraction), the W2 block in its stage b % 2, staged one
+  // iteration ahead: in iteration jb the gate / up read W1 / W3 stage
+  // (jb + 1) % 2 and the W2 contraction W2 stage jb % 2, while the stores
+  // fill W1 / W3 stage jb % 2 and W2 stage (jb + 1) % 2, whose last readers
+  // were before the previous barrier.
+  LACT_AS_GLOAD13(0);
+  LACT_AS_GLOAD2(0);
 #pragma unroll
-  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds, x);
-  LACT_AS_GLOAD(min(1, NB - 1));
+  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds + LY::w13(0), lds + LY::w2(0), x);
+  LACT_AS_GLOAD13(min(1, NB - 1));
 #pragma unroll
-  for (int x = 0; x < 2 * NV1 + 2 * NV2; ++x) LACT_AS_LSTORE1(lds + STAGE, x);
+  for (int x = 0; x < 2 * NV1; ++x) LACT_AS_LSTORE1(lds + LY::w13(1), lds + LY::w2(1), x);
   __syncthreads();
   forward(0, P, U, false, P, U);
   for (int jb = 0; jb < NB; ++jb) {
-    const int cb = jb % NBUF, nb = (jb + 1) % NBUF, lb = (jb + 2) % NBUF;
-    // block jb + 2 (the last one again at the end: its copy lands in a free
-    // stage)
-    LACT_AS_GLOAD(min(jb + 2, NB - 1));
+    const int cb = jb % 2, nb = (jb + 1) % 2;
+    // W1 / W3 of block jb + 2 and W2 of block jb + 1 (the last block again
+    // at the end: its copy lands in a free stage)
+    LACT_AS_GLOAD13(min(jb + 2, NB - 1));
+    LACT_AS_GLOAD2(min(jb + 1, NB - 1));
     __builtin_amdgcn_sched_barrier(0);
     // ---- region 1: gate / up of block jb + 1 (past the last block: stale
     // stage, results unused) with h of block jb ----
     f32x4 Pn[2][2], Un[2][2];
     forward(nb, Pn, Un, true, P, U);
     // ---- region 2: o^T += W2[:, block jb] h^T, W2 reads two steps ahead,
-    // the staging stores of block jb + 2 between them ----
+    // the staging stores of W1 / W3 block jb + 2 and W2 block jb + 1
+    // between them ----
     {
-      const bf16* s2 = lds + opaque(cb * STAGE + 2 * S1 + wo);
-      bf16* sl = lds + lb * STAGE;
+      const bf16* s2 = lds + opaque(LY::w2(cb) + wo);
+      bf16* sl13 = lds + LY::w13(cb);
+      bf16* sl2 = lds + LY::w2(nb);
       bf16x8 f2[WR];
 #pragma unroll
       for (int i_ = 0; i_ < WR - 1; ++i_) f2[i_] = ld8(s2 + 16 * HB * i_);
@@ -480,7 +499,7 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
         if (it + WR - 1 < IT) f2[(it + WR - 1) % WR] = ld8(s2 + 16 * HB * (it + WR - 1));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) mma(acc[it][tt], f2[it % WR], hf[tt]);
-        if (it < 2 * NV1 + 2 * NV2) LACT_AS_LSTORE1(sl, it);
+        if (it < 2 * NV1 + 2 * NV2) LACT_AS_LSTORE1(sl13, sl2, it);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -493,7 +512,8 @@ __device__ __forceinline__ void apply_solo_block(const ApplyArgs& a, int lid, bf
         U[jt][tt] = Un[jt][tt];
       }
   }
-#undef LACT_AS_GLOAD
+#undef LACT_AS_GLOAD13
+#undef LACT_AS_GLOAD2
 #undef LACT_AS_LSTORE1
 
 #pragma unroll
