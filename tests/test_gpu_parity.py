@@ -77,6 +77,49 @@ def test_gradient(device, wi, n_tok):
             assert H.rel(x, ref) < H.TOL[w.dtype], (name, b, H.rel(x, ref))
 
 
+@pytest.mark.parametrize("dh", [256, 320, 448])
+def test_d256_hidden_sizes(device, dh):
+    """d = 256 with hidden sizes other than the workloads' 1024: the read
+    streams dh / 32 hidden blocks through its two LDS stages of W1 / W3 rows
+    and of W2 (8, 10 and 14 blocks here), the gradient launches dh / 64
+    hidden-block workgroups; ragged token counts span several tiles and,
+    for the gradient, several splits."""
+    import dataclasses
+    import torch
+    base = dataclasses.replace(WL.WORKLOADS[4], dh=dh, name=f"long-context-dh{dh}")
+    for n_tok in (130, 613):
+        w = base.scaled(heads=1, batch=2, T=n_tok, chunk=n_tok)
+        W, inp = inputs(w)
+        fw = H.make_state(w, W, device)
+        q = H.act_to_dev(w, inp, "q", device)
+        out = H.out_buffer(w, n_tok, device)
+        print(f"apply d=256 dh={dh} bh={w.bh} n={n_tok}", flush=True)
+        L.lact_apply(fw.shape, fw, q, out)
+        torch.cuda.synchronize()
+        got = H.to64(out)
+        for b in range(w.bh):
+            ref = O.apply(W[0][b], W[1][b], W[2][b], inp["q"][b])
+            assert H.rel(got[b], ref) < H.TOL[w.dtype], ("apply", n_tok, b, H.rel(got[b], ref))
+    n_tok = 1500
+    w = base.scaled(heads=1, batch=2, T=n_tok, chunk=n_tok)
+    W, inp = inputs(w)
+    fw = H.make_state(w, W, device)
+    k = H.act_to_dev(w, inp, "k", device)
+    v = H.act_to_dev(w, inp, "v", device)
+    eta = torch.from_numpy(inp["eta"]).to(device)
+    g = [torch.full((w.bh, w.d, w.dh), float("nan"), device=device) for _ in range(3)]
+    ws = H.workspace(w, n_tok, device, muon=False)
+    print(f"gradient d=256 dh={dh} bh={w.bh} n={n_tok}", flush=True)
+    L.lact_gradient(fw.shape, fw, k, v, eta, eta, eta, g[0], g[1], g[2], ws)
+    torch.cuda.synchronize()
+    got = [H.to64(x) for x in g]
+    for b in range(w.bh):
+        e = inp["eta"][b]
+        G1, G3, G2 = O.chunk_gradient(W[0][b], W[1][b], W[2][b], inp["k"][b], inp["v"][b], e, e, e)
+        for name, x, ref in (("G1", got[0][b].T, G1), ("G3", got[1][b].T, G3), ("G2", got[2][b], G2)):
+            assert H.rel(x, ref) < H.TOL[w.dtype], (name, b, H.rel(x, ref))
+
+
 def test_gradient_distinct_etas(device):
     """eta1 / eta3 / eta2 reach only their own matrix."""
     import torch
