@@ -277,6 +277,7 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
   const float be = a.beta + (a.beta_mu + a.beta_mu2 * mu) * mu;
   const float dg = a.diag_mu * mu;
   float ss = 0.f;
+  f32x4 ctv[4];  // (c_tall: the tile's values, written transposed below)
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
@@ -288,8 +289,28 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
       for (int j = 0; j < 4; ++j) v[j] += (m0 + r == n0 + c4 + j) ? dg : 0.f;
     }
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-    if (C) *reinterpret_cast<f32x4*>(C + o) = v;
+    if ((int)bidx < a.c_tall) ctv[x] = v;
+    else if (C) *reinterpret_cast<f32x4*>(C + o) = v;
     if (Ch) st4(Ch + o, v[0], v[1], v[2], v[3]);
+  }
+  if ((int)bidx < a.c_tall) {
+    // C transposed: the finished tile back into LDS, then its columns out as
+    // rows of C^T (16-byte pieces of row n0 + r)
+    __syncthreads();  // every read of the result tile done
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
+      *reinterpret_cast<f32x4*>(sc + r * NSG_PC + c4) = ctv[x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int vi = tid + 256 * x, r = vi >> 4, c4 = 4 * (vi & 15);
+      f32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = sc[(c4 + j) * NSG_PC + r];
+      *reinterpret_cast<f32x4*>(C + (int64_t)(n0 + r) * a.M + m0 + c4) = v;
+    }
   }
   if (mirror) {
     // the transposed tile at (tn, tm): row r of it is column r of the result
@@ -320,6 +341,8 @@ __global__ __launch_bounds__(256) void k_nsgemm(NsGemmArgs a) {
 hipError_t launch_nsgemm(bool b_kn, const NsGemmArgs& a, int batch, hipStream_t s) {
   const int tm = a.M / NSG_T, tn = a.N / NSG_T;
   if (a.sym && (a.M != a.N || a.ss_part != nullptr)) return hipErrorInvalidValue;
+  if (a.c_tall > 0 && (a.sym || a.Ch != nullptr || a.ss_part != nullptr || a.C == nullptr))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.sym ? tn * (tn + 1) / 2 : tm * tn) * batch));
   if (b_kn)
     hipLaunchKernelGGL(k_nsgemm<true>, grid, dim3(256), 0, s, a);

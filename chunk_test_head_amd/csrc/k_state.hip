@@ -161,7 +161,9 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
   // The RB x d block of W is contiguous: thread tid takes float4 number
   // tid + 256 k (row (tid + 256 k) / (d/4)); the d/4 threads of a row are
   // consecutive lanes and combine their sums of squares by shuffles.  W is
-  // requested first so that its loads overlap the transpose of U.
+  // requested first so that its loads overlap the transpose of U (wide U);
+  // with u13_tall the update arrives in W's own layout and is added row for
+  // row, without the transpose.
   const int q4 = d / 4, nk = RB * q4 / 256, rstep = 256 / q4;
   const int r0 = tid / q4, c4 = 4 * (tid % q4);
   constexpr int KMAX = RB / 4;  // d <= 256
@@ -169,6 +171,19 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
     if (k < nk) w[k] = *reinterpret_cast<const f32x4*>(W + (int64_t)(r0 + rstep * k) * d + c4);
+  const bool add_u = U != nullptr;
+  if (U != nullptr && a.u13_tall) {
+    // U in the layout of W: the same rows, read like W
+    const float* Ut = U + (int64_t)head * msz + (int64_t)j0 * d;
+    f32x4 uv[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < nk) uv[k] = *reinterpret_cast<const f32x4*>(Ut + (int64_t)(r0 + rstep * k) * d + c4);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < nk) w[k] += uv[k];
+    U = nullptr;  // (added)
+  }
   if (U != nullptr) {
     U += (int64_t)head * msz + j0;
     // U[i][j0 + 4q .. +3] -> ut[4q .. 4q+3][i]: every load of the thread is
@@ -208,7 +223,7 @@ __device__ __forceinline__ void step_w13(const StepArgs& a, int blk, float* ut) 
       if (a.nonfinite != nullptr && c4 == 0 && !(ss[k] <= 3.402823466e38f)) atomicOr(a.nonfinite, 1);
     }
   }
-  const bool write_w = U != nullptr || a.renorm;
+  const bool write_w = add_u || a.renorm;
   float* N0 = (mat == 0 ? a.n1 : a.n3) + (int64_t)head * dh + j0;
   T* S = reinterpret_cast<T*>(a.sh.base) + (int64_t)head * a.sh.per_head +
          (mat == 0 ? a.sh.off_w1 : a.sh.off_w3) + (int64_t)j0 * d;

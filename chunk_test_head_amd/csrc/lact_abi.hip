@@ -262,9 +262,14 @@ static int64_t ns_ws_bytes(int count, int rows, int cols) {
 // pre_np > 0: bm already holds pre_np partial sums of squares per matrix of
 // the input (the split sum wrote them), for the normalisation of the
 // batched-GEMM path.
+// u_tall: NULL, or the number of leading matrices whose result may be
+// written transposed ([cols][rows]); set to the number actually written so
+// (the batched-GEMM path honours it, the one-workgroup kernels do not).
 static hipError_t run_ns(int prec, int count, int rows, int cols, NsIn g, float* u,
                          float eps, float* xa, float* xb, float* xh, float* am, float* bm,
-                         float* ssp, hipStream_t s, int pre_np = 0) {
+                         float* ssp, hipStream_t s, int pre_np = 0, int* u_tall = nullptr) {
+  const int want_tall = u_tall != nullptr ? *u_tall : 0;
+  if (u_tall != nullptr) *u_tall = 0;
   const int64_t m = (int64_t)rows * cols;
   const int shift_from = ns_shift_from(prec);
   hipError_t e = hipErrorNotSupported;
@@ -306,11 +311,12 @@ static hipError_t run_ns(int prec, int count, int rows, int cols, NsIn g, float*
       NsGemmArgs gx{bh, rr, rows, xc, m, cols, x, m, last ? u : y, last ? nullptr : yc, m,
                     rows, cols, rows, 1.f, ca, mp, tiles, (float)rows, cb, cc, 0.f,
                     (!last && it + 1 >= shift_from) ? ssp + (int64_t)((it + 1) & 1) * count * tiles
-                                                    : nullptr, 0};
+                                                    : nullptr, 0, last ? want_tall : 0};
       if ((e = launch_nsgemm(true, gx, count, s)) != hipSuccess) return e;
       std::swap(x, y);
       std::swap(xc, yc);
     }
+    if (u_tall != nullptr) *u_tall = want_tall;
     return hipSuccess;
   }
   NsNormArgs na{g, xa, count, m, eps};
@@ -493,11 +499,12 @@ static lact_status do_grad(const lact_shape* sh, const lact_state* st, const voi
 
 static lact_status do_step(const lact_shape* sh, const lact_state* st, const float* u1,
                            const float* u3, const float* u2, int renorm, float eps,
-                           int* nonfinite, void* shadow_out, hipStream_t s) {
+                           int* nonfinite, void* shadow_out, hipStream_t s, int u13_tall = 0) {
   StepArgs a;
   memset(&a, 0, sizeof(a));
   a.w1 = st->w1; a.w3 = st->w3; a.w2 = st->w2;
   a.u1 = u1; a.u3 = u3; a.u2 = u2;
+  a.u13_tall = u13_tall;
   a.n1 = st->n1; a.n3 = st->n3; a.n2 = st->n2;
   a.sh = make_shadow(shadow_out, sh->d, sh->dh);
   a.bh = sh->bh; a.d = sh->d; a.dh = sh->dh;
@@ -548,6 +555,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
   // with Newton-Schulz after the split sum, the sum also takes the first
   // pass of its Frobenius normalisation (per-tile sums of squares)
   const bool pre_norm = op->use_muon && !nsstep;
+  int tall = 0;  // leading matrices of the Newton-Schulz output in W's layout
   lact_status r = do_grad(sh, st, k, kl, v, vl, e1, e3, e2, esbh, n_tok, w, nsplit,
                           mo ? nullptr : g1, mo ? nullptr : g3, mo ? nullptr : g2,
                           mo ? st->m1 : nullptr, mo ? st->m3 : nullptr, mo ? st->m2 : nullptr,
@@ -580,8 +588,11 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
                                ns_shift_from(ns_prec_of(sh, op)), ns, aa, s);
       return e == hipSuccess ? LACT_OK : hip_fail(e);
     }
+    // the W1 and W3 updates (the first 2 bh matrices) written in the layout
+    // of W1 and W3 when the path allows it: the step then reads them as rows
+    tall = 2 * sh->bh;
     e = run_ns(ns_prec_of(sh, op), 3 * sh->bh, sh->d, sh->dh, in, w.g, op->ns_eps, w.xa, w.xb,
-               w.xh, w.amat, w.bmat, w.ssp, s, (sh->d / 64) * (sh->dh / 64));
+               w.xh, w.amat, w.bmat, w.ssp, s, (sh->d / 64) * (sh->dh / 64), &tall);
     if (e != hipSuccess) return hip_fail(e);
     u1 = g1; u3 = g3; u2 = g2;
   }
@@ -591,7 +602,7 @@ static lact_status do_update(const lact_shape* sh, const lact_state* st, const v
     if (e != hipSuccess) return hip_fail(e);
   }
   return do_step(sh, st, u1, u3, u2, op->renorm, op->renorm_eps, op->nonfinite, shadow_out,
-                 s);
+                 s, tall > 0 ? 1 : 0);
 }
 
 static lact_status check_update_args(const lact_shape* sh, const lact_state* st, const void* k,

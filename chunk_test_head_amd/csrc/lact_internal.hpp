@@ -121,6 +121,9 @@ struct NsGemmArgs {
   // are computed, each written also transposed below it (D, if any, must be
   // symmetric too; ss_part must be NULL)
   int sym;
+  // the first c_tall matrices of the batch get C written transposed ([N][M],
+  // row pitch M, in the same c_bs slot; not with sym, Ch or ss_part)
+  int c_tall;
 };
 
 // Input matrices of a Newton-Schulz batch: matrix m is p[m / per] +
@@ -142,6 +145,7 @@ struct NsNormArgs {
 struct StepArgs {
   float* w1; float* w3; float* w2;
   const float* u1; const float* u3; const float* u2;  // wide [bh][d][dh]; NULL = no add
+  int u13_tall;  // 1: u1, u3 are [bh][dh][d] (the layout of w1, w3)
   float* n1; float* n3; float* n2;                    // renorm targets
   Shadow sh;
   int bh, d, dh;
