@@ -584,8 +584,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_grad_bf16(GradArgs a) {
 // backward of tile n spread between them, then the gradient contractions
 // of tile n with the staging stores of tile n + 2 between its last steps
 // (as late as possible: the tile's loads, issued at the top of the
-// iteration, then have both regions to arrive); fragment reads two steps
-// ahead of their MFMAs, the order held by scheduling fences.
+// iteration, then have both regions to arrive); fragment reads ahead of
+// their MFMAs (below), the order held by scheduling fences.
 // SAME: one learning-rate array for the three matrices (the η products of
 // the SwiGLU backward are shared; one η row per token in registers).
 // RING, TRING: fragment buffers of the forward and of the gradient
@@ -662,9 +662,9 @@ void k_grad_solo(GradArgs a) {
   uint4 rk[VPT], rv[VPT];
   float re = 0.f;
   // Staging loads through one buffer descriptor per tensor and tile: base =
-  // the tile's first row, range = the split's rows from there on (rows past
-  // the split, and whole tiles past the last, read as zeros: the range
-  // check); vector x of a thread is row tid / (D / 8) + x RX, piece
+  // the tile's first row, range = the tile's rows that lie inside the split
+  // (rows past the split, and whole tiles past the last, read as zeros: the
+  // range check); vector x of a thread is row tid / (D / 8) + x RX, piece
   // tid % (D / 8), at a 32-bit byte offset from the base (token strides
   // below 2^24 elements).  Larger strides take a checked per-lane path.
   constexpr int RX = NTH / (D / 8);
